@@ -1,0 +1,9 @@
+"""CPU oracle for the frame-wise Gated DeltaNet forward.
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's CPU
+baseline may import this package.  It shares no code with the GPU library.
+"""
+from .gdn_ref import (as_f64, frame_maps, transition, gdn_head, gdn_head_residual,
+                      build_maps_head, state_pass_head, output_head, compose,
+                      state_pass_chunked, tokenwise_gated_delta, gdn_forward,
+                      gdn_forward_streamed, flops_per_head_frame)
