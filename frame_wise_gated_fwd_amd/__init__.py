@@ -1,0 +1,10 @@
+"""Frame-wise Gated DeltaNet forward on AMD Instinct MI355X (gfx950).
+
+The computation lives in libgdn.so (HIP kernels behind the C ABI in
+include/gdn.h); this package only marshals torch tensors into it.
+"""
+from .api import frame_fwd, build_maps, state_pass, output, workspace_bytes
+from ._lib import lib, GDNError, LIB_PATH
+
+__all__ = ["frame_fwd", "build_maps", "state_pass", "output", "workspace_bytes", "lib",
+           "GDNError", "LIB_PATH"]

@@ -1,0 +1,146 @@
+"""Python entry points over the C ABI (argument marshalling only).
+
+Tensors are torch tensors on a ROCm device; torch provides device memory and
+the current stream, and every step of the computation runs in libgdn's HIP
+kernels.  Names mirror include/gdn.h.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import GDN_BF16, GDN_F32, Shape, check, lib
+
+_DT = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported dtype {t}; expected float32 or bfloat16")
+    return _DT[t]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def shape_of(q: torch.Tensor) -> Shape:
+    if q.dim() != 5:
+        raise ValueError("q must be [B, H, T, S, D]")
+    B, H, T, S, D = q.shape
+    return Shape(B, H, T, S, D)
+
+
+def workspace_bytes(B: int, H: int, T: int, S: int, D: int, in_dtype: torch.dtype) -> int:
+    shp = Shape(B, H, T, S, D)
+    return int(lib().gdn_workspace_bytes(ctypes.byref(shp), _dtype_code(in_dtype)))
+
+
+def frame_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
+              beta: torch.Tensor, state: Optional[torch.Tensor] = None,
+              out_dtype: torch.dtype = torch.float32, *, out: Optional[torch.Tensor] = None,
+              state_out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Frame-wise GDN forward (gdn_frame_fwd).
+
+    q, k, v: [B, H, T, S, D] bf16 or f32 (k already scaled by 1/sqrt(D*S));
+    gamma, beta: [B, H, T] f32; state: [B, H, D, D] f32 or None (zeros).
+    Returns (out [B, H, T, S, D] out_dtype, state_out [B, H, D, D] f32).
+    state_out may be the same tensor as state (in-place streaming)."""
+    shp = shape_of(q)
+    B, H, T, S, D = q.shape
+    dev = q.device
+    _need(q, "q", (B, H, T, S, D), None, dev)
+    _need(k, "k", (B, H, T, S, D), q.dtype, dev)
+    _need(v, "v", (B, H, T, S, D), q.dtype, dev)
+    _need(gamma, "gamma", (B, H, T), torch.float32, dev)
+    _need(beta, "beta", (B, H, T), torch.float32, dev)
+    if state is not None:
+        _need(state, "state", (B, H, D, D), torch.float32, dev)
+    in_code, out_code = _dtype_code(q.dtype), _dtype_code(out_dtype)
+    if out is None:
+        out = torch.empty((B, H, T, S, D), dtype=out_dtype, device=dev)
+    _need(out, "out", (B, H, T, S, D), out_dtype, dev)
+    if state_out is None:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    _need(state_out, "state_out", (B, H, D, D), torch.float32, dev)
+    L = lib()
+    wsb = int(L.gdn_workspace_bytes(ctypes.byref(shp), in_code))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = L.gdn_frame_fwd(ctypes.byref(shp), in_code, out_code, _ptr(q), _ptr(k), _ptr(v),
+                         _ptr(gamma), _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out),
+                         _ptr(workspace), workspace.numel(), _stream(dev))
+    check(st, "gdn_frame_fwd")
+    return out, state_out
+
+
+def build_maps(k: torch.Tensor, v: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Stage 1 (gdn_build_maps): G_t = K_t^T K_t and U_t = V_t^T K_t, [B,H,T,D,D] f32."""
+    shp = shape_of(k)
+    B, H, T, S, D = k.shape
+    dev = k.device
+    _need(k, "k", (B, H, T, S, D), None, dev)
+    _need(v, "v", (B, H, T, S, D), k.dtype, dev)
+    G = torch.empty((B, H, T, D, D), dtype=torch.float32, device=dev)
+    U = torch.empty_like(G)
+    st = lib().gdn_build_maps(ctypes.byref(shp), _dtype_code(k.dtype), _ptr(k), _ptr(v), _ptr(G),
+                              _ptr(U), _stream(dev))
+    check(st, "gdn_build_maps")
+    return G, U
+
+
+def state_pass(G: torch.Tensor, U: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
+               state: Optional[torch.Tensor] = None, keep_all: bool = True):
+    """Stage 2 (gdn_state_pass): returns (M_all [B,H,T,D,D] or None, state_out [B,H,D,D])."""
+    B, H, T, D, _ = G.shape
+    dev = G.device
+    shp = Shape(B, H, T, 1, D)
+    _need(G, "G", (B, H, T, D, D), torch.float32, dev)
+    _need(U, "U", (B, H, T, D, D), torch.float32, dev)
+    _need(gamma, "gamma", (B, H, T), torch.float32, dev)
+    _need(beta, "beta", (B, H, T), torch.float32, dev)
+    if state is not None:
+        _need(state, "state", (B, H, D, D), torch.float32, dev)
+    M_all = torch.empty_like(G) if keep_all else None
+    state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    st = lib().gdn_state_pass(ctypes.byref(shp), _ptr(G), _ptr(U), _ptr(gamma), _ptr(beta),
+                              _ptr(state), _ptr(M_all), _ptr(state_out), _stream(dev))
+    check(st, "gdn_state_pass")
+    return M_all, state_out
+
+
+def output(q: torch.Tensor, M_all: torch.Tensor, out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Stage 3 (gdn_output): O_t = Q_t M_t^T."""
+    shp = shape_of(q)
+    B, H, T, S, D = q.shape
+    dev = q.device
+    _need(q, "q", (B, H, T, S, D), None, dev)
+    _need(M_all, "M_all", (B, H, T, D, D), torch.float32, dev)
+    out = torch.empty((B, H, T, S, D), dtype=out_dtype, device=dev)
+    st = lib().gdn_output(ctypes.byref(shp), _dtype_code(q.dtype), _dtype_code(out_dtype), _ptr(q),
+                          _ptr(M_all), _ptr(out), _stream(dev))
+    check(st, "gdn_output")
+    return out

@@ -1,0 +1,129 @@
+// Per-frame maps of the frame-wise GDN on bf16 MFMA (gfx950), head dim 128:
+//   G_t = K_t^T K_t   and   U_t = V_t^T K_t,
+// both reducing over the S tokens of one latent frame (one recurrent step
+// consumes a whole frame: bilibili cv49203711, fourth key point).  Products
+// of two bf16 numbers are exact in float32; accumulation is float32.
+//
+// One workgroup (4 waves) per frame.  The reduction index (tokens) is the
+// slow index of the [S, 128] storage while an MFMA operand wants 8
+// consecutive reduction values per lane, so every wave loads a 32-token x
+// 128-dim slab with 16-byte loads (lane = token group g = l/16 of 8 tokens,
+// dim group c = l%16 of 8 dims) and transposes 8x8 bf16 blocks in registers.
+// That yields 8 operand fragments per slab; fragment j holds, in lane
+// (g, c), the 8 tokens of group g at dim 8c + j, so MFMA row m of fragment j
+// is dim 8m + j.  Fragments go to LDS once and every wave reads the ones it
+// needs.  Wave w owns the output rows {8m + j : j in {2w, 2w+1}} of both G and
+// U (32 accumulators of 16x16), which makes every lane's final row segment 8
+// contiguous floats.
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int D = 128;
+constexpr int kIterTok = 64;  // tokens per loop iteration: two 32-token slabs of K and of V
+
+__global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, float* __restrict__ G,
+    float* __restrict__ U, int S) {
+  // frag[unit][j][lane]; unit 0,1 = K slab 0,1; unit 2,3 = V slab 0,1.
+  __shared__ u32x4 frag[4][8][kWave];
+
+  const int64_t f = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63;
+  const int g = l >> 4, c = l & 15;
+  const uint16_t* src = (w < 2 ? K : V) + f * (int64_t)S * D;
+  const int slab = w & 1;
+
+  u32x4 x[8];
+  auto load = [&](int it) {
+    const int base = it * kIterTok + slab * 32 + 8 * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = base + i;
+      if (s < S)
+        x[i] = ld_nt(reinterpret_cast<const u32x4*>(src + (int64_t)s * D + 8 * c));
+      else
+        x[i] = (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+
+  f32x4 accG[2][8], accU[2][8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      accG[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      accU[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int iters = (S + kIterTok - 1) / kIterTok;
+  load(0);
+  for (int it = 0; it < iters; ++it) {
+    __syncthreads();  // every wave is done reading the previous fragments
+    // 8x8 transpose: fragment j, dword p = (token 2p, token 2p+1) at dim 8c+j.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t a = x[2 * p][j >> 1], b = x[2 * p + 1][j >> 1];
+        o[p] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      frag[w][j][l] = o;
+    }
+    __syncthreads();
+    if (it + 1 < iters) load(it + 1);  // next slab in flight during the MFMAs
+
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      u32x4 kf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kf[j] = frag[sl][j][l];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const u32x4 kr = frag[sl][2 * w + jj][l];
+        const u32x4 vr = frag[2 + sl][2 * w + jj][l];
+#pragma unroll
+        for (int jp = 0; jp < 8; ++jp) {
+          accG[jj][jp] = mfma16x16x32(kr, kf[jp], accG[jj][jp]);
+          accU[jj][jp] = mfma16x16x32(vr, kf[jp], accU[jj][jp]);
+        }
+      }
+    }
+  }
+
+  // Lane (g, c), register i of block (j, jp) holds X[32g + 8i + j][8c + jp].
+  float* Gf = G + f * (int64_t)D * D;
+  float* Uf = U + f * (int64_t)D * D;
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int j = 2 * w + jj;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 32 * g + 8 * i + j;
+      f32x4 g0 = {accG[jj][0][i], accG[jj][1][i], accG[jj][2][i], accG[jj][3][i]};
+      f32x4 g1 = {accG[jj][4][i], accG[jj][5][i], accG[jj][6][i], accG[jj][7][i]};
+      f32x4 u0 = {accU[jj][0][i], accU[jj][1][i], accU[jj][2][i], accU[jj][3][i]};
+      f32x4 u1 = {accU[jj][4][i], accU[jj][5][i], accU[jj][6][i], accU[jj][7][i]};
+      f32x4* gp = reinterpret_cast<f32x4*>(Gf + row * D + 8 * c);
+      f32x4* up = reinterpret_cast<f32x4*>(Uf + row * D + 8 * c);
+      gp[0] = g0;
+      gp[1] = g1;
+      up[0] = u0;
+      up[1] = u1;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, float* G, float* U,
+                                  int64_t frames, int S, hipStream_t st) {
+  hipLaunchKernelGGL(k1_build_bf16_d128, dim3((unsigned)frames), dim3(256), 0, st, k, v, G, U, S);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

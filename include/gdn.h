@@ -1,0 +1,133 @@
+/*
+ * gdn.h -- C ABI of the frame-wise Gated DeltaNet forward on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What is computed.  The SANA-WM pages ("SANA-WM: NVIDIA puts a one-minute
+ * world model on a single GPU", zhichai.net, section "1. Hybrid Linear
+ * Attention -- Gated DeltaNet + Softmax") describe a recurrent state of
+ * constant D x D size per head, a learned decay scalar gamma that multiplies
+ * the previous state, a delta-rule strength beta that corrects only the
+ * residual between prediction and target, and keys scaled by 1/sqrt(D*S).
+ * bilibili cv49203711 (fourth key point) makes the recurrence frame-wise: one
+ * step consumes a whole latent frame of S tokens.  This library implements,
+ * per batch b, head h and frame t (K_t, V_t, Q_t are S x D):
+ *
+ *     G_t = K_t^T K_t                  (key x key)
+ *     U_t = V_t^T K_t                  (value x key)
+ *     M_t = M_{t-1} gamma_t (I - beta_t G_t) + beta_t U_t
+ *     O_t = Q_t M_t^T
+ *
+ * with M_0 = state_in (zeros when NULL) and state_out = M_T.  The library
+ * applies no key scaling: the caller passes keys already multiplied by
+ * 1/sqrt(D*S).
+ *
+ * Layout.  All tensors are dense, row-major, innermost index last:
+ *     q, k, v, out   [B, H, T, S, D]
+ *     gamma, beta    [B, H, T]          float32
+ *     state_in/out   [B, H, D, D]       float32, state[b,h,i,j]: i value, j key
+ *     G, U, M_all    [B, H, T, D, D]    float32 (stage entry points)
+ *
+ * Pointers.  Every tensor pointer is a device pointer owned by the caller.
+ * The library allocates no device memory and keeps no per-call state; the
+ * workspace is caller-provided.  `stream` is a hipStream_t (NULL: the null
+ * stream).  Calls are asynchronous on that stream.
+ *
+ * Errors.  Argument errors are detected on the host before anything is
+ * enqueued and returned synchronously; nothing is written then.  A failed
+ * launch returns GDN_E_HIP.  Faults during execution surface at the caller's
+ * next synchronisation.  Non-finite inputs are not checked: they propagate.
+ *
+ * Aliasing.  state_out may equal state_in exactly (in-place streaming).  Any
+ * other overlap between an output and any other buffer is GDN_E_ALIAS.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_E_NULLPTR = 1,        /* a required pointer is NULL                     */
+  GDN_E_SHAPE = 2,          /* a size is < 1, too large, or overflows 64 bits */
+  GDN_E_DTYPE = 3,          /* unknown or unsupported dtype                   */
+  GDN_E_UNSUPPORTED_D = 4,  /* head dim not one of the supported sizes        */
+  GDN_E_WORKSPACE = 5,      /* workspace NULL or smaller than required        */
+  GDN_E_ALIAS = 6,          /* an output overlaps another buffer              */
+  GDN_E_HIP = 7             /* a HIP runtime call or launch failed            */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef struct {
+  int64_t B, H, T, S, D;
+} gdn_shape;
+
+/* ABI version (GDN_ABI_VERSION of the built library). */
+int gdn_abi_version(void);
+
+/* Static, human-readable name of a status code; never NULL. */
+const char* gdn_status_str(int status);
+
+/* Supported head dims: D in {16, 32, 48, ..., 128} (multiples of 16 up to
+ * 128).  bf16 inputs with D == 128 take the MFMA path; every other
+ * combination takes a plain float32 path. */
+int gdn_supports_d(int64_t D);
+
+/*
+ * Workspace bytes gdn_frame_fwd needs for this shape and input dtype: room
+ * for G_t, U_t and M_t of every frame, 3 * B*H*T*D*D*4 bytes, rounded up to
+ * 256.  A pure function of its arguments.  Returns 0 when the shape is
+ * invalid.
+ */
+size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype);
+
+/*
+ * The whole forward: O and M_T from q, k, v, gamma, beta and M_0.
+ *   in_dtype   GDN_BF16 or GDN_F32: dtype of q, k, v.
+ *   out_dtype  GDN_F32 (recommended) or GDN_BF16: dtype of out.
+ *   state_in   M_0 or NULL for zeros.   state_out: M_T (may equal state_in).
+ *   workspace  at least gdn_workspace_bytes(shape, in_dtype) bytes of device
+ *              memory, 256-byte aligned; its contents on return are
+ *              unspecified.
+ */
+int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype,
+                  const void* q, const void* k, const void* v,
+                  const float* gamma, const float* beta,
+                  const float* state_in, void* out, float* state_out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 1, the per-frame maps: G_t = K_t^T K_t and U_t = V_t^T K_t for every
+ * (b, h, t), reducing over the S tokens of the frame.  G, U: [B,H,T,D,D] f32.
+ */
+int gdn_build_maps(const gdn_shape* shape, int in_dtype, const void* k, const void* v,
+                   float* G, float* U, void* stream);
+
+/*
+ * Stage 2, the state pass: M_t = M_{t-1} gamma_t (I - beta_t G_t) + beta_t U_t
+ * for t = 1..T in float32.  Writes every M_t to M_all ([B,H,T,D,D], may be
+ * NULL when only the final state is wanted) and M_T to state_out.  The S
+ * field of the shape is ignored.
+ */
+int gdn_state_pass(const gdn_shape* shape, const float* G, const float* U,
+                   const float* gamma, const float* beta, const float* state_in,
+                   float* M_all, float* state_out, void* stream);
+
+/*
+ * Stage 3, the output: O_t = Q_t M_t^T for every (b, h, t), M_t from M_all.
+ */
+int gdn_output(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q,
+               const float* M_all, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

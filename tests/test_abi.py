@@ -1,0 +1,125 @@
+"""The C ABI on the host, with no GPU: the library loads, exports every symbol
+include/gdn.h declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import frame_wise_gated_fwd_amd as F
+from frame_wise_gated_fwd_amd._lib import SIGNATURES, Shape
+
+HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "gdn.h")
+
+OK, NULLPTR, SHAPE, DTYPE, UNSUP_D, WORKSPACE, ALIAS, HIP = range(8)
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    L = F.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.gdn_abi_version() == 1
+
+
+def test_status_strings():
+    L = F.lib()
+    for s in range(8):
+        assert L.gdn_status_str(s)
+    assert L.gdn_status_str(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("D,ok", [(16, 1), (32, 1), (64, 1), (112, 1), (128, 1), (0, 0), (8, 0),
+                                  (100, 0), (144, 0), (256, 0)])
+def test_supported_head_dims(D, ok):
+    assert F.lib().gdn_supports_d(D) == ok
+
+
+def _shape(B=1, H=2, T=3, S=40, D=128):
+    return Shape(B, H, T, S, D)
+
+
+def test_workspace_bytes():
+    L = F.lib()
+    s = _shape(1, 16, 961, 880, 128)
+    per = 16 * 961 * 128 * 128 * 4
+    assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == 3 * ((per + 255) // 256 * 256)
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(T=0)), BF16) == 0
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(D=100)), BF16) == 0
+    assert L.gdn_workspace_bytes(ctypes.byref(s), 7) == 0
+    assert L.gdn_workspace_bytes(None, BF16) == 0
+
+
+# Fake, never-dereferenced device addresses, far apart.
+P = [0x10_0000_0000 * (i + 1) for i in range(12)]
+
+
+def fwd(shape, in_dt=BF16, out_dt=F32, q=P[0], k=P[1], v=P[2], gamma=P[3], beta=P[4],
+        state_in=None, out=P[5], state_out=P[6], ws=P[7], wsb=None):
+    L = F.lib()
+    if wsb is None:
+        wsb = L.gdn_workspace_bytes(ctypes.byref(shape), in_dt) if shape else 0
+    return L.gdn_frame_fwd(ctypes.byref(shape) if shape else None, in_dt, out_dt, q, k, v, gamma,
+                           beta, state_in, out, state_out, ws, wsb, None)
+
+
+def test_frame_fwd_argument_errors():
+    s = _shape()
+    assert fwd(None) == NULLPTR
+    for bad in ({"q": None}, {"k": None}, {"v": None}, {"gamma": None}, {"beta": None},
+                {"out": None}, {"state_out": None}):
+        assert fwd(s, **bad) == NULLPTR, bad
+    assert fwd(_shape(B=0)) == SHAPE
+    assert fwd(_shape(T=-1)) == SHAPE
+    assert fwd(_shape(S=0)) == SHAPE
+    assert fwd(_shape(D=100)) == UNSUP_D
+    assert fwd(_shape(B=1 << 40, H=1 << 40)) == SHAPE
+    assert fwd(_shape(B=1 << 12, H=1 << 12, T=2)) == SHAPE  # more frames than one launch can hold
+    assert fwd(s, in_dt=5) == DTYPE
+    assert fwd(s, out_dt=9) == DTYPE
+    assert fwd(s, ws=None) == WORKSPACE
+    assert fwd(s, wsb=1000) == WORKSPACE
+    assert fwd(s, ws=P[7] + 8) == WORKSPACE  # misaligned
+
+
+def test_frame_fwd_alias_errors():
+    s = _shape()
+    assert fwd(s, out=P[0]) == ALIAS                 # out over q
+    assert fwd(s, state_out=P[5] + 64) == ALIAS      # state_out inside out
+    assert fwd(s, state_in=P[6] + 4) == ALIAS        # partial overlap with state_out
+    assert fwd(s, ws=P[1]) == ALIAS                  # workspace over k
+    assert fwd(s, gamma=P[6]) == ALIAS               # state_out over gamma
+
+
+def test_stage_argument_errors():
+    L = F.lib()
+    s = _shape()
+    assert L.gdn_build_maps(ctypes.byref(s), BF16, None, P[1], P[2], P[3], None) == NULLPTR
+    assert L.gdn_build_maps(ctypes.byref(s), 3, P[0], P[1], P[2], P[3], None) == DTYPE
+    assert L.gdn_build_maps(ctypes.byref(s), BF16, P[0], P[1], P[0], P[3], None) == ALIAS
+    assert L.gdn_build_maps(ctypes.byref(s), BF16, P[0], P[1], P[2], P[2] + 4, None) == ALIAS
+    assert L.gdn_state_pass(ctypes.byref(s), P[0], P[1], P[2], P[3], None, P[4], None, None) == NULLPTR
+    assert L.gdn_state_pass(ctypes.byref(_shape(D=48 + 1)), P[0], P[1], P[2], P[3], None, P[4], P[5],
+                            None) == UNSUP_D
+    assert L.gdn_state_pass(ctypes.byref(s), P[0], P[1], P[2], P[3], None, P[0], P[5], None) == ALIAS
+    assert L.gdn_output(ctypes.byref(s), BF16, F32, P[0], P[1], P[1], None) == ALIAS
+    assert L.gdn_output(ctypes.byref(s), BF16, 4, P[0], P[1], P[2], None) == DTYPE
+    assert L.gdn_output(ctypes.byref(_shape(S=0)), BF16, F32, P[0], P[1], P[2], None) == SHAPE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from frame_wise_gated_fwd_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Tolerances: relative L2 <= 1e-5 for float32 inputs and
+<= 2e-3 for bf16 inputs with float32 accumulation, for the output and for the
+final state.  Stage tests hold float32-accumulation arithmetic to 1e-5."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import frame_wise_gated_fwd_amd as F
+from synth import TINY_F32, CLIP_5S, SEQ_60S, STREAM_60S, STRESS_B4, Workload, head_inputs
+
+from gpu_util import device_inputs, oracle_heads, RelL2, rel_l2, sample_frames, log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.numpy().astype(np.float64)
+
+
+def _bf16(a: np.ndarray) -> torch.Tensor:
+    from synth import f32_to_bf16_bits
+    return torch.from_numpy(f32_to_bf16_bits(a.astype(np.float32)).view(np.int16)).view(torch.bfloat16)
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# stage 1: G_t = K^T K, U_t = V^T K
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,H,T,S,D,dt", [
+    (1, 2, 3, 880, 128, "bf16"),     # MFMA path, full frame
+    (1, 1, 2, 100, 128, "bf16"),     # MFMA path, ragged token tail (100 = 64 + 36)
+    (1, 1, 2, 1, 128, "bf16"),       # single token
+    (1, 2, 3, 37, 64, "bf16"),       # plain path
+    (1, 2, 2, 16, 32, "f32"),        # plain path, float32
+    (2, 1, 2, 70, 112, "f32"),
+])
+def test_build_maps_stage(B, H, T, S, D, dt):
+    log(f"build_maps B={B} H={H} T={T} S={S} D={D} {dt}")
+    rng = np.random.Generator(np.random.PCG64(S * 1000 + D))
+    k = (rng.standard_normal((B, H, T, S, D)) / np.sqrt(D * S)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, S, D)).astype(np.float32)
+    if dt == "bf16":
+        kt, vt = _bf16(k), _bf16(v)
+    else:
+        kt, vt = torch.from_numpy(k), torch.from_numpy(v)
+    G, U = F.build_maps(kt.to(DEV), vt.to(DEV))
+    torch.cuda.synchronize()
+    kx, vx = _to_np(kt), _to_np(vt)
+    rg, ru = RelL2(), RelL2()
+    for b in range(B):
+        for h in range(H):
+            Gr, Ur = oracle.build_maps_head(kx[b, h], vx[b, h])
+            rg.add(_to_np(G[b, h]), Gr)
+            ru.add(_to_np(U[b, h]), Ur)
+    log(f"  relL2 G={rg.value:.3e} U={ru.value:.3e}")
+    assert rg.value <= 1e-5 and ru.value <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# stage 2: the state pass
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("H,T,D,with_state", [(3, 40, 128, True), (2, 17, 128, False),
+                                              (2, 9, 64, True), (1, 5, 32, False)])
+def test_state_pass_stage(H, T, D, with_state):
+    log(f"state_pass H={H} T={T} D={D} state={with_state}")
+    rng = np.random.Generator(np.random.PCG64(T * 100 + D))
+    S = 200
+    k = rng.standard_normal((1, H, T, S, D)) / np.sqrt(D * S)
+    v = rng.standard_normal((1, H, T, S, D))
+    G = np.einsum("bhtsi,bhtsj->bhtij", k, k).astype(np.float32)
+    U = np.einsum("bhtsi,bhtsj->bhtij", v, k).astype(np.float32)
+    gamma = rng.uniform(0.9, 1.0, (1, H, T)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (1, H, T)).astype(np.float32)
+    st = (rng.standard_normal((1, H, D, D)) * 0.1).astype(np.float32) if with_state else None
+    M_all, so = F.state_pass(*(torch.from_numpy(a).to(DEV) for a in (G, U, gamma, beta)),
+                             None if st is None else torch.from_numpy(st).to(DEV))
+    torch.cuda.synchronize()
+    rm, rs = RelL2(), RelL2()
+    for h in range(H):
+        ref = oracle.state_pass_head(G[0, h], U[0, h], gamma[0, h], beta[0, h],
+                                     None if st is None else st[0, h])
+        rm.add(_to_np(M_all[0, h]), ref)
+        rs.add(_to_np(so[0, h]), ref[-1])
+    log(f"  relL2 M_all={rm.value:.3e} state={rs.value:.3e}")
+    assert rm.value <= 1e-5 and rs.value <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# stage 3: the output
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,S,D,dt,odt", [(3, 880, 128, "bf16", "f32"), (2, 45, 128, "bf16", "f32"),
+                                          (2, 130, 128, "bf16", "bf16"), (2, 70, 64, "bf16", "f32"),
+                                          (2, 33, 48, "f32", "f32")])
+def test_output_stage(T, S, D, dt, odt):
+    log(f"output T={T} S={S} D={D} in={dt} out={odt}")
+    rng = np.random.Generator(np.random.PCG64(S + D))
+    H = 2
+    q = rng.standard_normal((1, H, T, S, D)).astype(np.float32)
+    M = rng.standard_normal((1, H, T, D, D)).astype(np.float32)
+    qt = _bf16(q) if dt == "bf16" else torch.from_numpy(q)
+    out_dtype = torch.bfloat16 if odt == "bf16" else torch.float32
+    O = F.output(qt.to(DEV), torch.from_numpy(M).to(DEV), out_dtype)
+    torch.cuda.synchronize()
+    qx = _to_np(qt)
+    r = RelL2()
+    for h in range(H):
+        r.add(_to_np(O[0, h]), oracle.output_head(qx[0, h], M[0, h]))
+    # a bf16 output is float32 arithmetic followed by one rounding (<= 2^-9 relative)
+    tol = 2.0 ** -9 * 1.01 + 1e-5 if odt == "bf16" else 1e-5
+    log(f"  relL2 O={r.value:.3e} (tol {tol:.2e})")
+    assert r.value <= tol
+
+
+# ---------------------------------------------------------------------------
+# the whole forward on the seeded workloads
+# ---------------------------------------------------------------------------
+def _forward_parity(w: Workload, frames=None, heads=None, chunks=None):
+    """Run the GPU forward on w (optionally streamed in `chunks`), compare O at
+    `frames` (all when None) for `heads` (all when None) and the final state."""
+    log(f"workload {w.name}: B={w.B} H={w.H} T={w.T} S={w.S} D={w.D} {w.in_dtype}"
+        f"{' streamed ' + str(len(chunks)) + ' calls' if chunks else ''}")
+    x = device_inputs(w, DEV)
+    log("  inputs on device")
+    if chunks:
+        out = torch.empty(x["q"].shape, dtype=torch.float32, device=DEV)
+        state = x["state"].clone() if x["state"] is not None else \
+            torch.zeros((w.B, w.H, w.D, w.D), dtype=torch.float32, device=DEV)
+        t0 = 0
+        for c in chunks:
+            sl = slice(t0, t0 + c)
+            o, _ = F.frame_fwd(x["q"][:, :, sl].contiguous(), x["k"][:, :, sl].contiguous(),
+                               x["v"][:, :, sl].contiguous(), x["gamma"][:, :, sl].contiguous(),
+                               x["beta"][:, :, sl].contiguous(), state, state_out=state)
+            out[:, :, sl] = o
+            t0 += c
+        st = state
+    else:
+        out, st = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    torch.cuda.synchronize()
+    log("  GPU forward done")
+    hs = heads or [(b, h) for b in range(w.B) for h in range(w.H)]
+    ro, rs = RelL2(), RelL2()
+    for b, h, O, M in oracle_heads(w, hs, frames):
+        og = out[b, h] if frames is None else out[b, h, list(frames)]
+        ro.add(_to_np(og), O)
+        rs.add(_to_np(st[b, h]), M)
+    log(f"  relL2 O={ro.value:.3e} state={rs.value:.3e} (tol {w.tol:g}); max|dO|={ro.max_abs:.3e}")
+    assert np.isfinite(ro.value) and np.isfinite(rs.value)
+    assert ro.value <= w.tol and rs.value <= w.tol
+    return out, st, x
+
+
+def test_forward_tiny_f32():
+    _forward_parity(TINY_F32)
+
+
+def test_forward_clip5s_bf16():
+    _forward_parity(CLIP_5S)
+
+
+def test_forward_seq60s_full_size():
+    _forward_parity(SEQ_60S, frames=sample_frames(SEQ_60S.T, seed=3))
+
+
+def test_forward_stream60s_matches_single_call():
+    w = STREAM_60S
+    out_s, st_s, x = _forward_parity(w, frames=sample_frames(w.T, seed=4), chunks=w.stream_chunks)
+    out1, st1 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    torch.cuda.synchronize()
+    # same kernels, same arithmetic, state handed over in float32: bit-identical
+    assert torch.equal(out_s, out1)
+    assert torch.equal(st_s, st1)
+
+
+def test_forward_stress_b4_sampled():
+    w = STRESS_B4
+    heads = [(0, 0), (1, 5), (2, 10), (3, 15), (3, 0), (0, 15)]
+    _forward_parity(w, frames=sample_frames(w.T, seed=5), heads=heads)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,S,D,dt", [(1, 880, 128, "bf16"), (5, 1, 128, "bf16"), (4, 17, 128, "bf16"),
+                                      (3, 130, 16, "bf16"), (3, 50, 112, "bf16"), (2, 8, 64, "f32"),
+                                      (6, 100, 128, "f32")])
+def test_forward_edge_shapes(T, S, D, dt):
+    w = Workload(name=f"edge_{T}_{S}_{D}_{dt}", B=2, H=2, T=T, S=S, D=D, in_dtype=dt, seed=40 + T + S,
+                 gamma_range=(0.9, 1.0), beta_kind="sigmoid_normal", state_std=0.05,
+                 tol=1e-5 if dt == "f32" else 2e-3)
+    _forward_parity(w)
+
+
+def test_forward_bf16_output():
+    w = CLIP_5S.with_(T=7, name="clip_t7")
+    x = device_inputs(w, DEV)
+    o32, s32 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"])
+    o16, s16 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(s32, s16)
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_zero_state_equals_none_and_in_place_state():
+    w = CLIP_5S.with_(T=6, name="clip_t6", state_std=0.02)
+    x = device_inputs(w, DEV)
+    z = torch.zeros_like(x["state"])
+    o1, s1 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], None)
+    o2, s2 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], z)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    ref_o, ref_s = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    st = x["state"].clone()
+    o3, s3 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], st, state_out=st)
+    torch.cuda.synchronize()
+    assert s3.data_ptr() == st.data_ptr()
+    assert torch.equal(o3, ref_o) and torch.equal(st, ref_s)
+
+
+def test_deterministic_bitwise():
+    w = CLIP_5S.with_(T=12, name="clip_t12")
+    x = device_inputs(w, DEV)
+    a = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"])
+    b = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_nan_propagates_within_its_head_only():
+    w = CLIP_5S.with_(T=5, H=2, name="clip_nan")
+    x = device_inputs(w, DEV)
+    x["k"][0, 1, 2, 7, 3] = float("nan")
+    o, s = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o[0, 0]).all() and torch.isfinite(s[0, 0]).all()
+    assert torch.isfinite(o[0, 1, :2]).all()
+    assert torch.isnan(o[0, 1, 2:]).any() and torch.isnan(s[0, 1]).any()
+
+
+def test_binding_rejects_bad_arguments():
+    q = torch.zeros((1, 1, 2, 16, 128), dtype=torch.bfloat16, device=DEV)
+    g = torch.ones((1, 1, 2), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):
+        F.frame_fwd(q, q, q[:, :, :1].contiguous(), g, g)
+    with pytest.raises(TypeError):
+        F.frame_fwd(q, q.float(), q, g, g)
+    with pytest.raises(F.GDNError):
+        bad = torch.zeros((1, 1, 2, 16, 100), dtype=torch.bfloat16, device=DEV)
+        F.frame_fwd(bad, bad, bad, g, g)
