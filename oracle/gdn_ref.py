@@ -72,22 +72,26 @@ def transition(g_t: np.ndarray, gamma_t: float, beta_t: float) -> np.ndarray:
     return gamma_t * (np.eye(d) - beta_t * g_t)
 
 
-def gdn_head(q, k, v, gamma, beta, state=None, keep_states: bool = False):
+def gdn_head(q, k, v, gamma, beta, state=None, keep_states: bool = False, out_frames=None):
     """Frame-wise GDN forward of one head.
 
     q, k, v: [T, S, D]; gamma, beta: [T]; state: [D, D] or None (zeros).
     Returns (O [T, S, D], M_T [D, D]) and, with keep_states, also the stacked
-    states M_1..M_T [T, D, D]."""
+    states M_1..M_T [T, D, D].  With out_frames (a list of frame indices) only
+    those frames' outputs are formed and O is [len(out_frames), S, D]."""
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     gamma, beta = as_f64(gamma), as_f64(beta)
     T, S, D = q.shape
     M = np.zeros((D, D)) if state is None else as_f64(state).copy()
-    O = np.empty((T, S, D))
+    wanted = list(range(T)) if out_frames is None else list(out_frames)
+    slot = {t: i for i, t in enumerate(wanted)}
+    O = np.empty((len(wanted), S, D))
     states = np.empty((T, D, D)) if keep_states else None
     for t in range(T):
         G, U = frame_maps(k[t], v[t])
         M = M @ transition(G, gamma[t], beta[t]) + beta[t] * U
-        O[t] = q[t] @ M.T
+        if t in slot:
+            O[slot[t]] = q[t] @ M.T
         if keep_states:
             states[t] = M
     if keep_states:
