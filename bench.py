@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Throughput of the frame-wise GDN forward on one MI355X.
+
+A step is one gdn_frame_fwd call over the whole 60 s, 720p workload
+(B=1, H=16, T=961 latent frames, S=880 tokens per frame, D=128, bf16 q/k/v,
+float32 state and output) with every input already resident in HBM.
+value = frame-steps/s = B*T / seconds per step.  One JSON line is printed.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --copy-calibration     # plain copy of a known size, for counters
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "frame_wise_gated_fwd_amd", "csrc")
+
+# kernel -> (source file, launch symbol fragment)
+KERNELS = {
+    "build": ("k1_build.hip", "k1_build_bf16_d128"),
+    "state": ("k2_state.hip", "k2_state_d128"),
+    "output": ("k3_output.hip", "k3_output_bf16_d128"),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def per_head_frame_bytes(S, D, in_bytes=2, out_bytes=4):
+    """Algorithmic HBM bytes of one head-frame for each kernel and the step."""
+    qkv = S * D * in_bytes
+    o = S * D * out_bytes
+    dd = D * D * 4
+    return {
+        "build": 2 * qkv + 2 * dd,      # read K, V; write G, U
+        "state": 2 * dd + dd,           # read G, U; write M_t
+        "output": qkv + dd + o,         # read Q, M_t; write O
+        "step": 3 * qkv + o,            # q, k, v in; O out (state in/out per head is extra)
+    }
+
+
+def per_head_frame_flops(S, D):
+    return {"build": 4 * S * D * D, "state": 2 * D ** 3, "output": 2 * S * D * D,
+            "step": 6 * S * D * D + 2 * D ** 3}
+
+
+def device_inputs(w, dev):
+    import torch
+    from synth import iter_heads
+    B, H, T, S, D = w.B, w.H, w.T, w.S, w.D
+    x = {key: torch.empty((B, H, T, S, D), dtype=torch.bfloat16, device=dev) for key in "qkv"}
+    x["gamma"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    x["beta"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    x["state"] = None if w.state_std is None else torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    for b, h, d in iter_heads(w):
+        for key in "qkv":
+            x[key][b, h].copy_(torch.from_numpy(d[key].view(np.int16)).view(torch.bfloat16))
+        x["gamma"][b, h].copy_(torch.from_numpy(d["gamma"]))
+        x["beta"][b, h].copy_(torch.from_numpy(d["beta"]))
+        if x["state"] is not None:
+            x["state"][b, h].copy_(torch.from_numpy(d["state"]))
+    torch.cuda.synchronize()
+    return x
+
+
+def source_hash(fname):
+    with open(os.path.join(CSRC, fname), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload_name):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current source of that kernel; else None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k_, v_ = line.split("=", 1)
+            kv[k_.strip()] = v_.strip()
+    if kv.get("source_sha256_16") != source_hash(KERNELS[kernel][0]):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, frames, workers):
+    """The fp64 oracle timed on the host on a bounded sample of the workload:
+    every head, the first `frames` frames, one single-threaded process per head."""
+    from concurrent.futures import ProcessPoolExecutor
+    ws = w.with_(T=frames)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    with ProcessPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(_oracle_warm, range(workers)))
+        t0 = time.perf_counter()
+        secs = list(ex.map(_oracle_head_timed, [(ws, b, h) for b, h in heads]))
+        wall = time.perf_counter() - t0
+    return {"value": round(w.B * frames / wall, 3), "unit": "frame-steps/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"{len(heads)} heads x first {frames} of {w.T} frames of {w.name}, fp64 NumPy oracle, "
+                      f"one single-threaded process per head, {wall:.1f} s wall "
+                      f"(per-head compute {min(secs):.1f}-{max(secs):.1f} s; input generation untimed)"}
+
+
+def _oracle_warm(_):
+    return 0
+
+
+def _oracle_head_timed(args):
+    ws, b, h = args
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from synth import head_inputs
+    with threadpool_limits(1):
+        d = head_inputs(ws, b, h)
+        t0 = time.perf_counter()
+        oracle.gdn_head(d["q"], d["k"], d["v"], d["gamma"], d["beta"], d["state"])
+        return time.perf_counter() - t0
+
+
+def copy_calibration(gib=1.0, reps=5):
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms": ms,
+                      "GBps_read_plus_write": 2 * n * 4 / ms / 1e6}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-frames", type=int, default=None,
+                    help="frames per head in the CPU oracle sample (default: sized for ~10-30 s)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every box has a single "
+              "MI355X); run it with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import frame_wise_gated_fwd_amd as F
+    from frame_wise_gated_fwd_amd._lib import Shape, lib, check, GDN_BF16, GDN_F32
+    from synth import WORKLOADS, BENCH_WORKLOAD, default_workers
+
+    w = WORKLOADS[args.workload] if args.workload else BENCH_WORKLOAD
+    if w.in_dtype != "bf16" or w.stream_chunks:
+        raise SystemExit("bench.py times single-call bf16 workloads")
+    dev = torch.device("cuda:0")
+    B, H, T, S, D = w.B, w.H, w.T, w.S, w.D
+    log(f"bench: {w.name} B={B} H={H} T={T} S={S} D={D}; generating inputs")
+    t0 = time.perf_counter()
+    x = device_inputs(w, dev)
+    log(f"inputs on device in {time.perf_counter() - t0:.1f} s")
+
+    L = lib()
+    shp = Shape(B, H, T, S, D)
+    out = torch.empty((B, H, T, S, D), dtype=torch.float32, device=dev)
+    st_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    wsb = L.gdn_workspace_bytes(ctypes.byref(shp), GDN_BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    def step():
+        check(L.gdn_frame_fwd(ctypes.byref(shp), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]), P(x["v"]),
+                              P(x["gamma"]), P(x["beta"]), P(x["state"]), P(out), P(st_out), P(ws),
+                              wsb, stream), "gdn_frame_fwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"step: {ms:.3f} ms (events), {wall / args.steps * 1e3:.3f} ms (wall)")
+
+    # Per-kernel durations of the same call: gdn_frame_fwd_timed records HIP
+    # events on the launch stream between the three kernels.
+    kms_acc = {k: [] for k in KERNELS}
+    kbuf = (ctypes.c_float * 3)()
+    for _ in range(args.steps):
+        check(L.gdn_frame_fwd_timed(ctypes.byref(shp), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]),
+                                    P(x["v"]), P(x["gamma"]), P(x["beta"]), P(x["state"]), P(out),
+                                    P(st_out), P(ws), wsb, stream, kbuf), "gdn_frame_fwd_timed")
+        for i, k in enumerate(KERNELS):
+            kms_acc[k].append(kbuf[i])
+    kms = {k: float(np.mean(v)) for k, v in kms_acc.items()}
+    log("kernels (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in kms.items()))
+
+    hf = B * H * T
+    bytes_hf = per_head_frame_bytes(S, D)
+    flops_hf = per_head_frame_flops(S, D)
+    dom = max(kms, key=kms.get)
+    achieved = bytes_hf[dom] * hf / (kms[dom] * 1e-3) / 1e9
+    traffic = measured_traffic(dom, w.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": KERNELS[dom][1], "kernel_ms": round(kms[dom], 4),
+                "bytes_per_launch": bytes_hf[dom] * hf}
+    step_bytes = bytes_hf["step"] * hf + (2 if x["state"] is not None else 1) * B * H * D * D * 4
+    step_gbs = step_bytes / (ms * 1e-3) / 1e9
+    step_tflops = flops_hf["step"] * hf / (ms * 1e-3) / 1e12
+    kernels = {}
+    for k, v in kms.items():
+        gbs = bytes_hf[k] * hf / (v * 1e-3) / 1e9
+        kernels[k] = {"ms": round(v, 4), "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "TFLOPs": round(flops_hf[k] * hf / (v * 1e-3) / 1e12, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = min(default_workers(), B * H)
+        # about 25 s of wall time at ~4.2 ms per single-threaded oracle head-frame
+        frames = args.cpu_frames or max(8, min(T, int(25.0 * workers / (B * H * 0.0042))))
+        log(f"cpu baseline: {frames} frames x {B * H} heads on {workers} processes")
+        cpu = cpu_baseline(w, frames, workers)
+        log(f"cpu baseline: {cpu['value']} frame-steps/s")
+
+    res = {
+        "metric": "GDN frame-steps/s at H=16,D=128,S=880,T=961; % bf16 MFMA peak, HBM GB/s",
+        "value": round(B * T / (ms * 1e-3), 1),
+        "unit": "frame-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, keys scaled by 1/sqrt(D*S), gamma~U(0.95,1), "
+                "beta=sigmoid(N(0,1)), N(0,0.02) fp32 initial state)",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "S": S, "D": D, "in_dtype": "bf16",
+                   "out_dtype": "f32", "state_dtype": "f32", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step_roofline": {"algorithmic_bytes": step_bytes, "GBps": round(step_gbs, 1),
+                          "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                          "TFLOPs": round(step_tflops, 2),
+                          "mfma_frac": round(step_tflops / BF16_PEAK_TFLOPS, 4)},
+        "kernels": kernels,
+        "head_frame_steps_per_s": round(hf / (ms * 1e-3), 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,7 +25,7 @@ SOURCES = ["gdn_api.cpp", "k1_build.hip", "k2_state.hip", "k3_output.hip", "k_ge
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-result",

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <limits>
+#include <mutex>
 
 #include "gdn_launch.h"
 
@@ -135,8 +136,8 @@ int gdn_build_maps(const gdn_shape* shape, int in_dtype, const void* k, const vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fast_path(in_dtype, d.D))
     return hip_status(gdn::launch_build_bf16_d128(static_cast<const uint16_t*>(k),
-                                                  static_cast<const uint16_t*>(v), G, U, d.frames,
-                                                  (int)d.S, s));
+                                                  static_cast<const uint16_t*>(v), G, false, U,
+                                                  d.frames, (int)d.S, s));
   return hip_status(gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, G, U, d.frames, (int)d.S,
                                               (int)d.D, s));
 }
@@ -154,8 +155,8 @@ int gdn_state_pass(const gdn_shape* shape, const float* G, const float* U, const
   if (!aliasing_ok(outs, 2, ins, 5, state_out, state_in)) return GDN_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.D == 128)
-    return hip_status(gdn::launch_state_d128(G, U, gamma, beta, state_in, M_all, state_out, d.heads,
-                                             d.T, s));
+    return hip_status(gdn::launch_state_d128(G, false, U, gamma, beta, state_in, M_all, state_out,
+                                             d.heads, d.T, s));
   return hip_status(gdn::launch_state_generic(G, U, gamma, beta, state_in, M_all, state_out,
                                               d.heads, d.T, (int)d.D, s));
 }
@@ -174,16 +175,66 @@ int gdn_output(const gdn_shape* shape, int in_dtype, int out_dtype, const void* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool ob = out_dtype == GDN_BF16;
   if (fast_path(in_dtype, d.D))
-    return hip_status(gdn::launch_output_bf16_d128(static_cast<const uint16_t*>(q), M_all, out, ob,
-                                                   d.frames, (int)d.S, s));
+    return hip_status(gdn::launch_output_bf16_d128(static_cast<const uint16_t*>(q), M_all, false, out,
+                                                   ob, d.frames, (int)d.S, s));
   return hip_status(gdn::launch_output_generic(q, in_dtype == GDN_BF16, M_all, out, ob, d.frames,
                                                (int)d.S, (int)d.D, s));
 }
+
+namespace {
+
+// Events for gdn_frame_fwd_timed, one set per device, created on first use.
+constexpr int kMaxDevices = 64;
+hipEvent_t g_events[kMaxDevices][4];
+bool g_events_ready[kMaxDevices];
+std::mutex g_events_mu;
+
+int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
+                   const void* v, const float* gamma, const float* beta, const float* state_in,
+                   void* out, float* state_out, void* workspace, size_t workspace_bytes,
+                   void* stream, hipEvent_t* ev);
+
+}  // namespace
 
 int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
                   const void* v, const float* gamma, const float* beta, const float* state_in,
                   void* out, float* state_out, void* workspace, size_t workspace_bytes,
                   void* stream) {
+  return frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, gamma, beta, state_in, out, state_out,
+                        workspace, workspace_bytes, stream, nullptr);
+}
+
+int gdn_frame_fwd_timed(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q,
+                        const void* k, const void* v, const float* gamma, const float* beta,
+                        const float* state_in, void* out, float* state_out, void* workspace,
+                        size_t workspace_bytes, void* stream, float* kernel_ms) {
+  if (!kernel_ms) return GDN_E_NULLPTR;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_E_HIP;
+  {
+    std::lock_guard<std::mutex> lock(g_events_mu);
+    if (!g_events_ready[dev]) {
+      for (int i = 0; i < 4; ++i)
+        if (hipEventCreate(&g_events[dev][i]) != hipSuccess) return GDN_E_HIP;
+      g_events_ready[dev] = true;
+    }
+  }
+  hipEvent_t* ev = g_events[dev];
+  const int st = frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, gamma, beta, state_in, out,
+                                state_out, workspace, workspace_bytes, stream, ev);
+  if (st != GDN_OK) return st;
+  if (hipEventSynchronize(ev[3]) != hipSuccess) return GDN_E_HIP;
+  for (int i = 0; i < 3; ++i)
+    if (hipEventElapsedTime(&kernel_ms[i], ev[i], ev[i + 1]) != hipSuccess) return GDN_E_HIP;
+  return GDN_OK;
+}
+
+namespace {
+
+int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
+                   const void* v, const float* gamma, const float* beta, const float* state_in,
+                   void* out, float* state_out, void* workspace, size_t workspace_bytes,
+                   void* stream, hipEvent_t* ev) {
   Dims d;
   int st = check_shape(shape, true, &d);
   if (st != GDN_OK) return st;
@@ -199,34 +250,43 @@ int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype, const voi
                        {state_in, state_in ? stb : 0}};
   if (!aliasing_ok(outs, 3, ins, 6, state_out, state_in)) return GDN_E_ALIAS;
 
+  // Workspace: G_t (split form on the MFMA path), U_t, M_t (split form on the MFMA path).
   const size_t slot = round256(d.map_elems * sizeof(float));
   char* ws = static_cast<char*>(workspace);
-  float* G = reinterpret_cast<float*>(ws);
+  void* G = ws;
   float* U = reinterpret_cast<float*>(ws + slot);
-  float* M_all = reinterpret_cast<float*>(ws + 2 * slot);
+  void* M_all = ws + 2 * slot;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fast = fast_path(in_dtype, d.D);
   const bool ob = out_dtype == GDN_BF16;
   hipError_t e;
+  if (ev && hipEventRecord(ev[0], s) != hipSuccess) return GDN_E_HIP;
   if (fast)
     e = gdn::launch_build_bf16_d128(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                                    G, U, d.frames, (int)d.S, s);
+                                    G, true, U, d.frames, (int)d.S, s);
   else
-    e = gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, G, U, d.frames, (int)d.S, (int)d.D, s);
+    e = gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, static_cast<float*>(G), U, d.frames,
+                                  (int)d.S, (int)d.D, s);
   if (e != hipSuccess) return GDN_E_HIP;
+  if (ev && hipEventRecord(ev[1], s) != hipSuccess) return GDN_E_HIP;
   if (fast)
-    e = gdn::launch_state_d128(G, U, gamma, beta, state_in, M_all, state_out, d.heads, d.T, s);
+    e = gdn::launch_state_d128(G, true, U, gamma, beta, state_in, M_all, state_out, d.heads, d.T, s);
   else
-    e = gdn::launch_state_generic(G, U, gamma, beta, state_in, M_all, state_out, d.heads, d.T,
-                                  (int)d.D, s);
+    e = gdn::launch_state_generic(static_cast<float*>(G), U, gamma, beta, state_in,
+                                  static_cast<float*>(M_all), state_out, d.heads, d.T, (int)d.D, s);
   if (e != hipSuccess) return GDN_E_HIP;
+  if (ev && hipEventRecord(ev[2], s) != hipSuccess) return GDN_E_HIP;
   if (fast)
-    e = gdn::launch_output_bf16_d128(static_cast<const uint16_t*>(q), M_all, out, ob, d.frames,
+    e = gdn::launch_output_bf16_d128(static_cast<const uint16_t*>(q), M_all, true, out, ob, d.frames,
                                      (int)d.S, s);
   else
-    e = gdn::launch_output_generic(q, in_dtype == GDN_BF16, M_all, out, ob, d.frames, (int)d.S,
-                                   (int)d.D, s);
-  return hip_status(e);
+    e = gdn::launch_output_generic(q, in_dtype == GDN_BF16, static_cast<float*>(M_all), out, ob,
+                                   d.frames, (int)d.S, (int)d.D, s);
+  if (e != hipSuccess) return GDN_E_HIP;
+  if (ev && hipEventRecord(ev[3], s) != hipSuccess) return GDN_E_HIP;
+  return GDN_OK;
 }
+
+}  // namespace
 
 }  // extern "C"

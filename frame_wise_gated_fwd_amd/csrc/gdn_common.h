@@ -13,24 +13,38 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
-// float -> bfloat16 bits, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (a in the low half), round to nearest even.
+// gfx950 does this in one instruction (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt2bf(float a, float b) {
+  const bf16x2 h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
 }
+
+// float -> bfloat16 bits (round to nearest even) in the low 16 bits.
+__device__ __forceinline__ uint32_t f2bf(float f) { return cvt2bf(f, 0.f) & 0xffffu; }
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Split x into bf16 hi + bf16 lo with hi + lo == x to about 2^-17 relative.
-__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
-  hi = f2bf(x);
-  lo = f2bf(x - bf2f(hi));
+// Split the pair (a, b) into a packed bf16 hi word (.x) and lo word (.y) with
+// hi + lo equal to the inputs to about 2^-17 relative: hi = bf16(x),
+// lo = bf16(x - hi).
+__device__ __forceinline__ u32x2 split2(float a, float b) {
+  const uint32_t hi = cvt2bf(a, b);
+  const uint32_t lo = cvt2bf(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+  return (u32x2){hi, lo};
 }
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) {
   return (lo16 & 0xffffu) | (hi16 << 16);
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads, so prefetches issued
+// before the barrier stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -8,15 +8,19 @@
 namespace gdn {
 
 // ---- MFMA path: bf16 inputs, D == 128 --------------------------------------
-// G_t = K_t^T K_t, U_t = V_t^T K_t for `frames` frames of S tokens.
-hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, float* G, float* U,
-                                  int64_t frames, int S, hipStream_t st);
-// State pass over T frames for `heads` heads; M_all may be null.
-hipError_t launch_state_d128(const float* G, const float* U, const float* gamma,
-                             const float* beta, const float* state_in, float* M_all,
+// The per-frame matrices G_t, U_t, M_t pass between the three kernels either
+// as float32 row-major (the stage entry points) or "packed" (gdn_packed.h:
+// G_t and M_t as bf16 hi/lo pairs, all three in the order the consumer's
+// waves read them), which is what gdn_frame_fwd uses.
+hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
+                                  float* U, int64_t frames, int S, hipStream_t st);
+// State pass over T frames for `heads` heads.  G, U and M_out are all packed
+// or all float32; M_out may be null.
+hipError_t launch_state_d128(const void* G, bool packed, const float* U, const float* gamma,
+                             const float* beta, const float* state_in, void* M_out,
                              float* state_out, int64_t heads, int64_t T, hipStream_t st);
 // O_t = Q_t M_t^T; out_bf16 selects the output dtype.
-hipError_t launch_output_bf16_d128(const uint16_t* q, const float* M_all, void* out,
+hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool packed_m, void* out,
                                    bool out_bf16, int64_t frames, int S, hipStream_t st);
 
 // ---- plain float32 path: any supported D, f32 or bf16 inputs ---------------

@@ -17,6 +17,7 @@
 // contiguous floats.
 #include "gdn_common.h"
 #include "gdn_launch.h"
+#include "gdn_packed.h"
 
 namespace gdn {
 namespace {
@@ -24,11 +25,17 @@ namespace {
 constexpr int D = 128;
 constexpr int kIterTok = 64;  // tokens per loop iteration: two 32-token slabs of K and of V
 
+// kPacked: write G_t (as bf16 hi/lo) and U_t in the packed layouts the state
+// pass reads (gdn_packed.h); otherwise both are float32 row-major.
+template <bool kPacked>
 __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
-    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, float* __restrict__ G,
-    float* __restrict__ U, int S) {
-  // frag[unit][j][lane]; unit 0,1 = K slab 0,1; unit 2,3 = V slab 0,1.
-  __shared__ u32x4 frag[4][8][kWave];
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, void* __restrict__ Gout,
+    float* __restrict__ Uout, int S) {
+  // During the token loop: frag[unit][j][lane] (32 KB); unit 0,1 = K slab 0,1;
+  // unit 2,3 = V slab 0,1.  Afterwards the whole buffer (64 KB) stages the
+  // packed output so that it leaves in contiguous 4 KB rows of stores.
+  __shared__ u32x4 lds[kPacked ? 4096 : 2048];
+  u32x4 (*frag)[8][kWave] = reinterpret_cast<u32x4 (*)[8][kWave]>(lds);
 
   const int64_t f = blockIdx.x;
   const int tid = threadIdx.x;
@@ -96,33 +103,63 @@ __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
   }
 
   // Lane (g, c), register i of block (j, jp) holds X[32g + 8i + j][8c + jp].
-  float* Gf = G + f * (int64_t)D * D;
-  float* Uf = U + f * (int64_t)D * D;
+  const int64_t fo = f * (int64_t)D * D;
+  if constexpr (kPacked) {
+    char* stage = reinterpret_cast<char*>(lds);
+    // pass 0: G_t as bf16 hi/lo (Gp); pass 1: U_t as float32 (Up)
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int j = 2 * w + jj;
+    for (int pass = 0; pass < 2; ++pass) {
+      __syncthreads();  // previous readers of the LDS buffer are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 32 * g + 8 * i + j;
-      f32x4 g0 = {accG[jj][0][i], accG[jj][1][i], accG[jj][2][i], accG[jj][3][i]};
-      f32x4 g1 = {accG[jj][4][i], accG[jj][5][i], accG[jj][6][i], accG[jj][7][i]};
-      f32x4 u0 = {accU[jj][0][i], accU[jj][1][i], accU[jj][2][i], accU[jj][3][i]};
-      f32x4 u1 = {accU[jj][4][i], accU[jj][5][i], accU[jj][6][i], accU[jj][7][i]};
-      f32x4* gp = reinterpret_cast<f32x4*>(Gf + row * D + 8 * c);
-      f32x4* up = reinterpret_cast<f32x4*>(Uf + row * D + 8 * c);
-      gp[0] = g0;
-      gp[1] = g1;
-      up[0] = u0;
-      up[1] = u1;
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * w + jj;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 32 * g + 8 * i + j;
+          if (pass == 0) {
+            const u32x2 p0 = split2(accG[jj][0][i], accG[jj][1][i]), p1 = split2(accG[jj][2][i], accG[jj][3][i]);
+            const u32x2 p2 = split2(accG[jj][4][i], accG[jj][5][i]), p3 = split2(accG[jj][6][i], accG[jj][7][i]);
+            *reinterpret_cast<u32x4*>(stage + packed::g_chunk(row, 8 * c, 0)) = (u32x4){p0.x, p1.x, p2.x, p3.x};
+            *reinterpret_cast<u32x4*>(stage + packed::g_chunk(row, 8 * c, 1)) = (u32x4){p0.y, p1.y, p2.y, p3.y};
+          } else {
+            *reinterpret_cast<f32x4*>(stage + packed::u_chunk(row, 8 * c)) =
+                (f32x4){accU[jj][0][i], accU[jj][1][i], accU[jj][2][i], accU[jj][3][i]};
+            *reinterpret_cast<f32x4*>(stage + packed::u_chunk(row, 8 * c + 4)) =
+                (f32x4){accU[jj][4][i], accU[jj][5][i], accU[jj][6][i], accU[jj][7][i]};
+          }
+        }
+      }
+      __syncthreads();
+      u32x4* dst = reinterpret_cast<u32x4*>((pass == 0 ? static_cast<char*>(Gout) : reinterpret_cast<char*>(Uout)) + fo * 4);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) dst[k * 256 + tid] = lds[k * 256 + tid];
+    }
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * w + jj;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 32 * g + 8 * i + j;
+        f32x4* gp = reinterpret_cast<f32x4*>(static_cast<float*>(Gout) + fo + row * D + 8 * c);
+        f32x4* up = reinterpret_cast<f32x4*>(Uout + fo + row * D + 8 * c);
+        gp[0] = (f32x4){accG[jj][0][i], accG[jj][1][i], accG[jj][2][i], accG[jj][3][i]};
+        gp[1] = (f32x4){accG[jj][4][i], accG[jj][5][i], accG[jj][6][i], accG[jj][7][i]};
+        up[0] = (f32x4){accU[jj][0][i], accU[jj][1][i], accU[jj][2][i], accU[jj][3][i]};
+        up[1] = (f32x4){accU[jj][4][i], accU[jj][5][i], accU[jj][6][i], accU[jj][7][i]};
+      }
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, float* G, float* U,
-                                  int64_t frames, int S, hipStream_t st) {
-  hipLaunchKernelGGL(k1_build_bf16_d128, dim3((unsigned)frames), dim3(256), 0, st, k, v, G, U, S);
+hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
+                                  float* U, int64_t frames, int S, hipStream_t st) {
+  if (packed_out)
+    hipLaunchKernelGGL(k1_build_bf16_d128<true>, dim3((unsigned)frames), dim3(256), 0, st, k, v, G, U, S);
+  else
+    hipLaunchKernelGGL(k1_build_bf16_d128<false>, dim3((unsigned)frames), dim3(256), 0, st, k, v, G, U, S);
   return hipGetLastError();
 }
 

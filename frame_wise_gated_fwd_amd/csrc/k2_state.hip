@@ -6,33 +6,48 @@
 // puts a one-minute world model on a single GPU", zhichai.net, section 1).
 //
 // Rows of M evolve independently (row i of M_t needs only row i of M_{t-1}),
-// so each head's 128 rows are split over kParts workgroups that never talk
+// so each head's 128 rows are split over D/kRows workgroups that never talk
 // to each other.  A workgroup keeps its rows of M in registers (float32
 // master copy) and in LDS as a bf16 hi/lo pair, double-buffered.  The
 // product X = M G runs on bf16 MFMA as three passes, Ghi*Mhi + Glo*Mhi +
 // Ghi*Mlo, each split term exact to about 2^-17 relative, with float32
 // accumulation; the dropped lo*lo term is ~2^-16 of a term that is itself a
 // few per cent of M.  Computed transposed, X^T = G M^T (G_t = K_t^T K_t is
-// symmetric, so its rows serve as its columns), so that each lane ends up
-// owning 4 consecutive columns of one row of M.
+// symmetric, so its rows serve as its columns): wave w owns rows
+// 32w .. 32w+31 of G (= columns of X) and all of the workgroup's rows of M,
+// so each lane ends up owning 4 consecutive columns of one row of M.
 //
-// Workgroups of one head are placed on one XCD (dispatch is round-robin over
-// the 8 XCDs), so the G_t and U_t rows they share come from one L2.
+// Two data forms.  Packed (gdn_packed.h): G_t, U_t and M_t in the order
+// the waves read or write them, each wave access one contiguous block; this
+// is what gdn_frame_fwd uses.  Plain: float32 row-major (the stage entry
+// point); the bf16 split of G_t then happens here.
+//
+// The per-frame data (this wave's G_t rows and U_t elements) streams
+// through a ring of kDepth register buffers: frame t + kDepth is requested
+// as soon as frame t's buffer is consumed.  The per-frame barrier only waits
+// for LDS traffic, so those loads stay in flight across it.  Workgroups of
+// one head are placed on one XCD (dispatch is round-robin over the 8 XCDs),
+// so the G_t they all read comes from one L2.
 #include "gdn_common.h"
 #include "gdn_launch.h"
+#include "gdn_packed.h"
+
+#include <type_traits>
+#include <utility>
 
 namespace gdn {
 namespace {
 
 constexpr int D = 128;
-constexpr int kRows = 64;              // rows of M per workgroup
-constexpr int kParts = D / kRows;      // workgroups per head
-constexpr int kLdsW = D + 8;           // padded LDS row (bf16 elements)
+constexpr int kLdsW = D + 8;  // padded LDS row (bf16 elements)
 
+template <int kRows, bool kPacked, int kDepth>
 __global__ __launch_bounds__(256, 1) void k2_state_d128(
-    const float* __restrict__ G, const float* __restrict__ U, const float* __restrict__ gamma,
-    const float* __restrict__ beta, const float* state_in, float* __restrict__ M_all,
+    const void* __restrict__ Gin, const float* __restrict__ U, const float* __restrict__ gamma,
+    const float* __restrict__ beta, const float* state_in, void* __restrict__ Mout,
     float* state_out, int heads, int T) {
+  constexpr int kRB = kRows / 16;     // 16-row blocks of M per workgroup
+  constexpr int kParts = D / kRows;   // workgroups per head
   // [buffer][hi|lo][row][col]
   __shared__ uint16_t Ml[2][2][kRows][kLdsW];
 
@@ -48,138 +63,240 @@ __global__ __launch_bounds__(256, 1) void k2_state_d128(
   const int n = l & 15, g = l >> 4;
 
   // This lane's elements of M: row r0 + 16rb + n, columns 32w + 16cb + 4g .. +3.
-  f32x4 Mreg[2][4];
-  const int64_t hoff = (int64_t)head * D * D;
-  auto elem_off = [&](int cb, int rb) { return (r0 + 16 * rb + n) * D + 32 * w + 16 * cb + 4 * g; };
+  auto row_of = [&](int rb) { return r0 + 16 * rb + n; };
+  auto col_of = [&](int cb) { return 32 * w + 16 * cb + 4 * g; };
 
+  const int64_t hoff = (int64_t)head * D * D;
+  f32x4 Mreg[2][kRB];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+      Mreg[cb][rb] = state_in ? *reinterpret_cast<const f32x4*>(state_in + hoff + row_of(rb) * D + col_of(cb))
+                              : (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  // hi/lo words of this lane's M elements (4 consecutive columns each)
+  u32x2 mh[2][kRB], ml[2][kRB];
+  auto split_m = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const u32x2 p0 = split2(Mreg[cb][rb][0], Mreg[cb][rb][1]);
+        const u32x2 p1 = split2(Mreg[cb][rb][2], Mreg[cb][rb][3]);
+        mh[cb][rb] = (u32x2){p0.x, p1.x};
+        ml[cb][rb] = (u32x2){p0.y, p1.y};
+      }
+  };
   auto put_lds = [&](int buf) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        uint32_t h[4], lo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) split_bf16(Mreg[cb][rb][i], h[i], lo[i]);
-        const int row = 16 * rb + n, col = 32 * w + 16 * cb + 4 * g;
-        *reinterpret_cast<u32x2*>(&Ml[buf][0][row][col]) = (u32x2){pack2(h[0], h[1]), pack2(h[2], h[3])};
-        *reinterpret_cast<u32x2*>(&Ml[buf][1][row][col]) = (u32x2){pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
+      for (int rb = 0; rb < kRB; ++rb) {
+        *reinterpret_cast<u32x2*>(&Ml[buf][0][16 * rb + n][col_of(cb)]) = mh[cb][rb];
+        *reinterpret_cast<u32x2*>(&Ml[buf][1][16 * rb + n][col_of(cb)]) = ml[cb][rb];
       }
   };
-
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-      Mreg[cb][rb] = state_in ? *reinterpret_cast<const f32x4*>(state_in + hoff + elem_off(cb, rb))
-                              : (f32x4){0.f, 0.f, 0.f, 0.f};
+  split_m();
   put_lds(0);
 
-  // A operand: rows 32w + 16cb + m of G_t (m = l%16), 8 floats at column 32kb + 8g.
-  const int m = n;
-  f32x4 graw[2][4][2];
-  auto load_g = [&](int t) {
-    const float* Gt = G + ((int64_t)head * T + t) * D * D;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(Gt + (32 * w + 16 * cb + m) * D + 32 * kb + 8 * g);
-        graw[cb][kb][0] = p[0];
-        graw[cb][kb][1] = p[1];
-      }
-  };
-  load_g(0);
-  __syncthreads();
+  // Ring of per-frame register buffers: the A-operand fragments of G_t
+  // (packed: hi/lo words; plain: raw floats) and this lane's U_t elements.
+  u32x4 rgh[kDepth][2][4], rgl[kDepth][2][4];
+  f32x4 rg32[kDepth][2][4][2];
+  f32x4 ru[kDepth][2][kRB];
 
-  for (int t = 0; t < T; ++t) {
+  auto load_frame = [&](auto jc, int t) {
+    constexpr int j = decltype(jc)::value;
+    if (t >= T) return;
+    const int64_t fo = ((int64_t)head * T + t) * D * D;
+    if constexpr (kPacked) {
+      const char* Gp = static_cast<const char*>(Gin) + fo * 4;
+      const char* Up = reinterpret_cast<const char*>(U) + fo * 4;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int unit = ((2 * w + cb) * 4 + kb) * 2;
+          rgh[j][cb][kb] = *reinterpret_cast<const u32x4*>(Gp + (unit << 10) + 16 * l);
+          rgl[j][cb][kb] = *reinterpret_cast<const u32x4*>(Gp + ((unit + 1) << 10) + 16 * l);
+        }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          ru[j][cb][rb] = *reinterpret_cast<const f32x4*>(Up + ((((r0 >> 4) + rb) * 8 + 2 * w + cb) << 10) + 16 * l);
+    } else {
+      const float* Gt = static_cast<const float*>(Gin) + fo;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const float* p = Gt + (32 * w + 16 * cb + n) * D + 32 * kb + 8 * g;
+          rg32[j][cb][kb][0] = *reinterpret_cast<const f32x4*>(p);
+          rg32[j][cb][kb][1] = *reinterpret_cast<const f32x4*>(p + 4);
+        }
+      const float* Ut = U + fo;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          ru[j][cb][rb] = *reinterpret_cast<const f32x4*>(Ut + row_of(rb) * D + col_of(cb));
+    }
+  };
+
+  // gamma_t, beta_t arrive through vector loads, a 64-frame window per lane
+  // (lane i holds frame t0 + i) fetched one window ahead, and are read with
+  // readlane.  Scalar loads here would share the LDS wait counter and stall
+  // every frame's first LDS read on an L2 round trip.
+  const float* gh = gamma + (int64_t)head * T;
+  const float* bh = beta + (int64_t)head * T;
+  auto win_load = [&](int t0, float& gv, float& bv) {
+    const int tt = t0 + l;
+    gv = tt < T ? gh[tt] : 0.f;
+    bv = tt < T ? bh[tt] : 0.f;
+  };
+  float gwin, bwin, gnxt, bnxt;
+  win_load(0, gwin, bwin);
+  win_load(64, gnxt, bnxt);
+
+  [&]<int... js>(std::integer_sequence<int, js...>) {
+    (load_frame(std::integral_constant<int, js>{}, js), ...);
+  }(std::make_integer_sequence<int, kDepth>{});
+  lds_barrier();
+
+  auto step = [&](auto jc, int t) {
+    constexpr int j = decltype(jc)::value;
     const int buf = t & 1;
-    const float gm = gamma[(int64_t)head * T + t];
-    const float bt = beta[(int64_t)head * T + t];
+    const int tw = t & 63;
+    const float gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwin), tw));
+    const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwin), tw));
+    if (tw == 63) {  // move to the next window and fetch the one after it
+      gwin = gnxt;
+      bwin = bnxt;
+      win_load(t + 65, gnxt, bnxt);
+    }
 
     u32x4 ahi[2][4], alo[2][4];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        uint32_t h[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          split_bf16(graw[cb][kb][0][e], h[e], lo[e]);
-          split_bf16(graw[cb][kb][1][e], h[4 + e], lo[4 + e]);
+        if constexpr (kPacked) {
+          ahi[cb][kb] = rgh[j][cb][kb];
+          alo[cb][kb] = rgl[j][cb][kb];
+        } else {
+          const u32x2 p0 = split2(rg32[j][cb][kb][0][0], rg32[j][cb][kb][0][1]);
+          const u32x2 p1 = split2(rg32[j][cb][kb][0][2], rg32[j][cb][kb][0][3]);
+          const u32x2 p2 = split2(rg32[j][cb][kb][1][0], rg32[j][cb][kb][1][1]);
+          const u32x2 p3 = split2(rg32[j][cb][kb][1][2], rg32[j][cb][kb][1][3]);
+          ahi[cb][kb] = (u32x4){p0.x, p1.x, p2.x, p3.x};
+          alo[cb][kb] = (u32x4){p0.y, p1.y, p2.y, p3.y};
         }
-        ahi[cb][kb] = (u32x4){pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
-        alo[cb][kb] = (u32x4){pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])};
       }
-    if (t + 1 < T) load_g(t + 1);
-
-    f32x4 ureg[2][4];
-    const float* Ut = U + ((int64_t)head * T + t) * D * D;
+    f32x4 ureg[2][kRB];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        ureg[cb][rb] = *reinterpret_cast<const f32x4*>(Ut + elem_off(cb, rb));
+      for (int rb = 0; rb < kRB; ++rb) ureg[cb][rb] = ru[j][cb][rb];
+    load_frame(jc, t + kDepth);  // refill this ring slot kDepth frames ahead
 
-    f32x4 acc[2][4];
+    f32x4 acc[2][kRB];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) acc[cb][rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
+      for (int rb = 0; rb < kRB; ++rb) acc[cb][rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      // B operand: row 16rb + n of this workgroup's M (as M^T column), 8 bf16 at column 32kb + 8g.
+      u32x4 bhi[kRB], blo[kRB];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        // B operand: row r0 + 16rb + n of M (as M^T column), 8 bf16 at column 32kb + 8g.
-        const u32x4 bhi = *reinterpret_cast<const u32x4*>(&Ml[buf][0][16 * rb + n][32 * kb + 8 * g]);
-        const u32x4 blo = *reinterpret_cast<const u32x4*>(&Ml[buf][1][16 * rb + n][32 * kb + 8 * g]);
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          acc[cb][rb] = mfma16x16x32(ahi[cb][kb], bhi, acc[cb][rb]);
-          acc[cb][rb] = mfma16x16x32(alo[cb][kb], bhi, acc[cb][rb]);
-          acc[cb][rb] = mfma16x16x32(ahi[cb][kb], blo, acc[cb][rb]);
-        }
+      for (int rb = 0; rb < kRB; ++rb) {
+        bhi[rb] = *reinterpret_cast<const u32x4*>(&Ml[buf][0][16 * rb + n][32 * kb + 8 * g]);
+        blo[rb] = *reinterpret_cast<const u32x4*>(&Ml[buf][1][16 * rb + n][32 * kb + 8 * g]);
       }
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(ahi[cb][kb], bhi[rb], acc[cb][rb]);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(alo[cb][kb], bhi[rb], acc[cb][rb]);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(ahi[cb][kb], blo[rb], acc[cb][rb]);
+    }
 
-    // acc[cb][rb][i] = X[r0 + 16rb + n][32w + 16cb + 4g + i]
+    // acc[cb][rb][i] = X[row_of(rb)][col_of(cb) + i]
     const float gb = gm * bt;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           Mreg[cb][rb][i] = fmaf(gm, Mreg[cb][rb][i], fmaf(-gb, acc[cb][rb][i], bt * ureg[cb][rb][i]));
-
-    if (M_all) {
-      float* Mt = M_all + ((int64_t)head * T + t) * D * D;
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) *reinterpret_cast<f32x4*>(Mt + elem_off(cb, rb)) = Mreg[cb][rb];
-    }
+    split_m();
     put_lds(buf ^ 1);
-    __syncthreads();
+
+    if (Mout) {
+      const int64_t fo = ((int64_t)head * T + t) * D * D;
+      if constexpr (kPacked) {
+        char* Mp = static_cast<char*>(Mout) + fo * 4;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) {
+            *reinterpret_cast<u32x2*>(Mp + packed::m_chunk(row_of(rb), col_of(cb), 0)) = mh[cb][rb];
+            *reinterpret_cast<u32x2*>(Mp + packed::m_chunk(row_of(rb), col_of(cb), 1)) = ml[cb][rb];
+          }
+      } else {
+        float* Mt = static_cast<float*>(Mout) + fo;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+            *reinterpret_cast<f32x4*>(Mt + row_of(rb) * D + col_of(cb)) = Mreg[cb][rb];
+      }
+    }
+    lds_barrier();
+  };
+
+  for (int t0 = 0; t0 < T; t0 += kDepth) {
+    [&]<int... js>(std::integer_sequence<int, js...>) {
+      ((t0 + js < T ? step(std::integral_constant<int, js>{}, t0 + js) : void()), ...);
+    }(std::make_integer_sequence<int, kDepth>{});
   }
 
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-      *reinterpret_cast<f32x4*>(state_out + hoff + elem_off(cb, rb)) = Mreg[cb][rb];
+    for (int rb = 0; rb < kRB; ++rb)
+      *reinterpret_cast<f32x4*>(state_out + hoff + row_of(rb) * D + col_of(cb)) = Mreg[cb][rb];
+}
+
+template <int kRows, bool kPacked, int kDepth>
+hipError_t launch_rows(const void* G, const float* U, const float* gamma, const float* beta,
+                       const float* state_in, void* M_out, float* state_out, int64_t heads,
+                       int64_t T, hipStream_t st) {
+  // Workgroup ids are grouped so that the workgroups of a head share id % 8.
+  const int64_t groups = (heads + 7) / 8;
+  const unsigned grid = (unsigned)(groups * 8 * (D / kRows));
+  hipLaunchKernelGGL((k2_state_d128<kRows, kPacked, kDepth>), dim3(grid), dim3(256), 0, st, G, U, gamma,
+                     beta, state_in, M_out, state_out, (int)heads, (int)T);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_state_d128(const float* G, const float* U, const float* gamma,
-                             const float* beta, const float* state_in, float* M_all,
+hipError_t launch_state_d128(const void* G, bool packed, const float* U, const float* gamma,
+                             const float* beta, const float* state_in, void* M_out,
                              float* state_out, int64_t heads, int64_t T, hipStream_t st) {
-  // Workgroup ids are grouped so that the kParts workgroups of a head share id % 8.
-  const int64_t groups = (heads + 7) / 8;
-  const unsigned grid = (unsigned)(groups * 8 * kParts);
-  hipLaunchKernelGGL(k2_state_d128, dim3(grid), dim3(256), 0, st, G, U, gamma, beta, state_in,
-                     M_all, state_out, (int)heads, (int)T);
-  return hipGetLastError();
+  if (packed)
+    return launch_rows<32, true, 2>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, st);
+  return launch_rows<32, false, 2>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, st);
 }
 
 }  // namespace gdn

@@ -7,12 +7,15 @@
 // Two index permutations make every global access a contiguous run:
 //  * the reduction (key) index: MFMA k-slot (kb, g, e) is key dim
 //    32g + 8kb + e, so lane (m, g) reads 64 contiguous bytes of its Q row;
-//  * the value index: column n of output block nb is value dim 8n + nb, so
-//    after all 8 blocks a lane holds 8 contiguous floats of its output row.
-// LDS row nb*16 + n holds M row 8n + nb, which makes the B-operand reads of
-// 16 lanes land on 16 distinct 4-bank groups.
+//  * the value index: column n of output block nb is value dim sigma(nb, n).
+//    For a float32 output sigma = 64(nb / 4) + 4n + nb % 4, so one store of
+//    blocks 0-3 (4-7) from 16 lanes is the first (second) 256 bytes of a
+//    row; for a bf16 output sigma = 8n + nb and one store covers the row.
+// LDS row nb*16 + n holds M row sigma(nb, n), which makes the B-operand reads
+// of 16 lanes land on 16 distinct 4-bank groups.
 #include "gdn_common.h"
 #include "gdn_launch.h"
+#include "gdn_packed.h"
 
 namespace gdn {
 namespace {
@@ -21,9 +24,18 @@ constexpr int D = 128;
 constexpr int kLdsW = D + 8;
 constexpr int kTile = 32;  // tokens per wave iteration
 
+// LDS row holding M row r (the inverse of sigma above).
 template <bool kOutBf16>
+__device__ __forceinline__ int lds_row(int r) {
+  if constexpr (kOutBf16) return (r & 7) * 16 + (r >> 3);
+  else return (((r >> 6) << 2) + (r & 3)) * 16 + ((r & 63) >> 2);
+}
+
+// kPackedM: M_t arrives packed (bf16 hi/lo, gdn_packed.h), as the state pass
+// writes it inside gdn_frame_fwd, instead of float32 row-major.
+template <bool kPackedM, bool kOutBf16>
 __global__ __launch_bounds__(256, 2) void k3_output_bf16_d128(
-    const uint16_t* __restrict__ Q, const float* __restrict__ M_all, void* __restrict__ out, int S) {
+    const uint16_t* __restrict__ Q, const void* __restrict__ M_all, void* __restrict__ out, int S) {
   __shared__ uint16_t Ml[2][D][kLdsW];  // [hi|lo][permuted row][key dim]
 
   const int64_t f = blockIdx.x;
@@ -31,16 +43,26 @@ __global__ __launch_bounds__(256, 2) void k3_output_bf16_d128(
   const int w = tid >> 6, l = tid & 63;
   const int n = l & 15, g = l >> 4;
 
-  const float* Mt = M_all + f * (int64_t)D * D;
-  for (int idx = tid; idx < D * D / 4; idx += 256) {
-    const int r = idx >> 5, c4 = (idx & 31) * 4;
-    const f32x4 mv = *reinterpret_cast<const f32x4*>(Mt + r * D + c4);
-    uint32_t h[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) split_bf16(mv[i], h[i], lo[i]);
-    const int rho = (r & 7) * 16 + (r >> 3);
-    *reinterpret_cast<u32x2*>(&Ml[0][rho][c4]) = (u32x2){pack2(h[0], h[1]), pack2(h[2], h[3])};
-    *reinterpret_cast<u32x2*>(&Ml[1][rho][c4]) = (u32x2){pack2(lo[0], lo[1]), pack2(lo[2], lo[3])};
+  if constexpr (kPackedM) {
+    // 8-byte chunk q: unit q / 64 = (row block, column block, plane), lane q % 64
+    const char* Mp = static_cast<const char*>(M_all) + f * packed::kFrameBytes;
+    for (int q = tid; q < D * D * 2 / 4; q += 256) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(Mp + 8 * q);
+      const int unit = q >> 6, ln = q & 63;
+      const int plane = unit & 1, rb = unit >> 4, cb = (unit >> 1) & 7;
+      const int r = 16 * rb + (ln & 15), c = 16 * cb + 4 * (ln >> 4);
+      *reinterpret_cast<u32x2*>(&Ml[plane][lds_row<kOutBf16>(r)][c]) = v;
+    }
+  } else {
+    const float* Mt = static_cast<const float*>(M_all) + f * (int64_t)D * D;
+    for (int idx = tid; idx < D * D / 4; idx += 256) {
+      const int r = idx >> 5, c4 = (idx & 31) * 4;
+      const f32x4 mv = *reinterpret_cast<const f32x4*>(Mt + r * D + c4);
+      const u32x2 p0 = split2(mv[0], mv[1]), p1 = split2(mv[2], mv[3]);
+      const int rho = lds_row<kOutBf16>(r);
+      *reinterpret_cast<u32x2*>(&Ml[0][rho][c4]) = (u32x2){p0.x, p1.x};
+      *reinterpret_cast<u32x2*>(&Ml[1][rho][c4]) = (u32x2){p0.y, p1.y};
+    }
   }
   __syncthreads();
 
@@ -90,24 +112,23 @@ __global__ __launch_bounds__(256, 2) void k3_output_bf16_d128(
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Lane (n, g), register i of block nb: O[tok0 + 16rb + 4g + i][8n + nb].
+    // Lane (n, g), register i of block nb: O[tok0 + 16rb + 4g + i][sigma(nb, n)].
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = tok0 + 16 * rb + 4 * g + i;
         if (s >= S) continue;
-        const int64_t off = (f * (int64_t)S + s) * D + 8 * n;
+        const int64_t row = (f * (int64_t)S + s) * D;
         if constexpr (kOutBf16) {
           u32x4 pk;
 #pragma unroll
-          for (int p = 0; p < 4; ++p)
-            pk[p] = pack2(f2bf(acc[rb][2 * p][i]), f2bf(acc[rb][2 * p + 1][i]));
-          st_nt(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + off), pk);
+          for (int p = 0; p < 4; ++p) pk[p] = cvt2bf(acc[rb][2 * p][i], acc[rb][2 * p + 1][i]);
+          st_nt(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + row + 8 * n), pk);
         } else {
-          float* o = static_cast<float*>(out) + off;
+          float* o = static_cast<float*>(out) + row + 4 * n;
           st_nt(reinterpret_cast<f32x4*>(o), (f32x4){acc[rb][0][i], acc[rb][1][i], acc[rb][2][i], acc[rb][3][i]});
-          st_nt(reinterpret_cast<f32x4*>(o + 4), (f32x4){acc[rb][4][i], acc[rb][5][i], acc[rb][6][i], acc[rb][7][i]});
+          st_nt(reinterpret_cast<f32x4*>(o + 64), (f32x4){acc[rb][4][i], acc[rb][5][i], acc[rb][6][i], acc[rb][7][i]});
         }
       }
 #pragma unroll
@@ -119,13 +140,22 @@ __global__ __launch_bounds__(256, 2) void k3_output_bf16_d128(
 
 }  // namespace
 
-hipError_t launch_output_bf16_d128(const uint16_t* q, const float* M_all, void* out,
-                                   bool out_bf16, int64_t frames, int S, hipStream_t st) {
+template <bool kPackedM>
+hipError_t launch_out(const uint16_t* q, const void* M_all, void* out, bool out_bf16, int64_t frames,
+                      int S, hipStream_t st) {
   if (out_bf16)
-    hipLaunchKernelGGL(k3_output_bf16_d128<true>, dim3((unsigned)frames), dim3(256), 0, st, q, M_all, out, S);
+    hipLaunchKernelGGL((k3_output_bf16_d128<kPackedM, true>), dim3((unsigned)frames), dim3(256), 0, st, q,
+                       M_all, out, S);
   else
-    hipLaunchKernelGGL(k3_output_bf16_d128<false>, dim3((unsigned)frames), dim3(256), 0, st, q, M_all, out, S);
+    hipLaunchKernelGGL((k3_output_bf16_d128<kPackedM, false>), dim3((unsigned)frames), dim3(256), 0, st, q,
+                       M_all, out, S);
   return hipGetLastError();
+}
+
+hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool packed_m, void* out,
+                                   bool out_bf16, int64_t frames, int S, hipStream_t st) {
+  return packed_m ? launch_out<true>(q, M_all, out, out_bf16, frames, S, st)
+                 : launch_out<false>(q, M_all, out, out_bf16, frames, S, st);
 }
 
 }  // namespace gdn

@@ -104,6 +104,22 @@ int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_frame_fwd, plus per-kernel durations: HIP events are recorded on
+ * `stream` before and after each of the three kernels (build, state pass,
+ * output) and the call waits for the last one, then writes the three
+ * elapsed times in milliseconds to kernel_ms[0..2] (host memory).  Results
+ * are identical to gdn_frame_fwd.  The events are created on the first call
+ * on each device and kept for the life of the process; this entry point is
+ * for profiling and is not meant for graph capture.
+ */
+int gdn_frame_fwd_timed(const gdn_shape* shape, int in_dtype, int out_dtype,
+                        const void* q, const void* k, const void* v,
+                        const float* gamma, const float* beta,
+                        const float* state_in, void* out, float* state_out,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        float* kernel_ms);
+
+/*
  * Stage 1, the per-frame maps: G_t = K_t^T K_t and U_t = V_t^T K_t for every
  * (b, h, t), reducing over the S tokens of the frame.  G, U: [B,H,T,D,D] f32.
  */

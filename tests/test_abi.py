@@ -101,6 +101,14 @@ def test_frame_fwd_alias_errors():
     assert fwd(s, gamma=P[6]) == ALIAS               # state_out over gamma
 
 
+def test_timed_needs_output_array():
+    L = F.lib()
+    s = _shape()
+    wsb = L.gdn_workspace_bytes(ctypes.byref(s), BF16)
+    assert L.gdn_frame_fwd_timed(ctypes.byref(s), BF16, F32, P[0], P[1], P[2], P[3], P[4], None, P[5],
+                                 P[6], P[7], wsb, None, None) == NULLPTR
+
+
 def test_stage_argument_errors():
     L = F.lib()
     s = _shape()

@@ -258,3 +258,26 @@ def test_binding_rejects_bad_arguments():
     with pytest.raises(F.GDNError):
         bad = torch.zeros((1, 1, 2, 16, 100), dtype=torch.bfloat16, device=DEV)
         F.frame_fwd(bad, bad, bad, g, g)
+
+
+def test_timed_entry_point_matches_and_reports():
+    import ctypes
+    from frame_wise_gated_fwd_amd._lib import Shape, lib, GDN_BF16, GDN_F32
+    w = CLIP_5S.with_(T=9, name="clip_t9", state_std=0.02)
+    x = device_inputs(w, DEV)
+    ref_o, ref_s = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    L = lib()
+    shp = Shape(w.B, w.H, w.T, w.S, w.D)
+    wsb = L.gdn_workspace_bytes(ctypes.byref(shp), GDN_BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(ref_o)
+    so = torch.empty_like(ref_s)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    ms = (ctypes.c_float * 3)()
+    st = L.gdn_frame_fwd_timed(ctypes.byref(shp), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]), P(x["v"]),
+                               P(x["gamma"]), P(x["beta"]), P(x["state"]), P(out), P(so), P(ws), wsb,
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), ms)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_o) and torch.equal(so, ref_s)
+    assert all(v > 0 for v in ms)
