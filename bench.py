@@ -29,12 +29,16 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "frame_wise_gated_fwd_amd", "csrc")
 
-# kernel -> (source file, launch symbol fragment)
-KERNELS = {
-    "build": ("k1_build.hip", "k1_build_bf16_d128"),
-    "state": ("k2_state.hip", "k2_state_d128"),
-    "output": ("k3_output.hip", "k3_output_bf16_d128"),
+# The kernels each path launches, in the order gdn_frame_fwd_timed reports
+# them: name -> (source file, kernel symbol).
+PATH_KERNELS = {
+    1: {"build": ("k1_build.hip", "k1_build_bf16_d128"),
+        "state": ("k2_state.hip", "k2_state_d128"),
+        "output": ("k3_output.hip", "k3_output_bf16_d128")},
+    2: {"reset": ("k_pipeline.hip", "k_pipeline_init"),
+        "pipeline": ("k_pipeline.hip", "k_pipeline")},
 }
+KERNELS = {k: v for d in PATH_KERNELS.values() for k, v in d.items()}
 
 
 def log(msg):
@@ -50,13 +54,17 @@ def per_head_frame_bytes(S, D, in_bytes=2, out_bytes=4):
         "build": 2 * qkv + 2 * dd,      # read K, V; write G, U
         "state": 2 * dd + dd,           # read G, U; write M_t
         "output": qkv + dd + o,         # read Q, M_t; write O
+        "pipeline": 3 * qkv + o,        # q, k, v in; O out; G, U, M stay on chip
+        "reset": 0,
         "step": 3 * qkv + o,            # q, k, v in; O out (state in/out per head is extra)
     }
 
 
 def per_head_frame_flops(S, D):
-    return {"build": 4 * S * D * D, "state": 2 * D ** 3, "output": 2 * S * D * D,
-            "step": 6 * S * D * D + 2 * D ** 3}
+    f = {"build": 4 * S * D * D, "state": 2 * D ** 3, "output": 2 * S * D * D, "reset": 0,
+         "step": 6 * S * D * D + 2 * D ** 3}
+    f["pipeline"] = f["step"]
+    return f
 
 
 def device_inputs(w, dev):
@@ -78,9 +86,14 @@ def device_inputs(w, dev):
     return x
 
 
-def source_hash(fname):
-    with open(os.path.join(CSRC, fname), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(fname=None):
+    """Hash of the HIP sources the measured kernel is built from (all of csrc,
+    so that a change to any shared header invalidates old counter figures)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload_name):
@@ -94,7 +107,7 @@ def measured_traffic(kernel, workload_name):
         if "=" in line and not line.lstrip().startswith("#"):
             k_, v_ = line.split("=", 1)
             kv[k_.strip()] = v_.strip()
-    if kv.get("source_sha256_16") != source_hash(KERNELS[kernel][0]):
+    if kv.get("source_sha256_16") != source_hash():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -221,13 +234,15 @@ def main():
 
     # Per-kernel durations of the same call: gdn_frame_fwd_timed records HIP
     # events on the launch stream between the three kernels.
-    kms_acc = {k: [] for k in KERNELS}
+    path = L.gdn_path(ctypes.byref(shp), GDN_BF16)
+    names = list(PATH_KERNELS[path])
+    kms_acc = {k: [] for k in names}
     kbuf = (ctypes.c_float * 3)()
     for _ in range(args.steps):
         check(L.gdn_frame_fwd_timed(ctypes.byref(shp), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]),
                                     P(x["v"]), P(x["gamma"]), P(x["beta"]), P(x["state"]), P(out),
                                     P(st_out), P(ws), wsb, stream, kbuf), "gdn_frame_fwd_timed")
-        for i, k in enumerate(KERNELS):
+        for i, k in enumerate(names):
             kms_acc[k].append(kbuf[i])
     kms = {k: float(np.mean(v)) for k, v in kms_acc.items()}
     log("kernels (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in kms.items()))
@@ -236,20 +251,21 @@ def main():
     bytes_hf = per_head_frame_bytes(S, D)
     flops_hf = per_head_frame_flops(S, D)
     dom = max(kms, key=kms.get)
+    kfile, ksym = PATH_KERNELS[path][dom]
     achieved = bytes_hf[dom] * hf / (kms[dom] * 1e-3) / 1e9
     traffic = measured_traffic(dom, w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": KERNELS[dom][1], "kernel_ms": round(kms[dom], 4),
+                "kernel": ksym, "kernel_ms": round(kms[dom], 4),
                 "bytes_per_launch": bytes_hf[dom] * hf}
     step_bytes = bytes_hf["step"] * hf + (2 if x["state"] is not None else 1) * B * H * D * D * 4
     step_gbs = step_bytes / (ms * 1e-3) / 1e9
     step_tflops = flops_hf["step"] * hf / (ms * 1e-3) / 1e12
     kernels = {}
     for k, v in kms.items():
-        gbs = bytes_hf[k] * hf / (v * 1e-3) / 1e9
+        gbs = bytes_hf[k] * hf / (v * 1e-3) / 1e9 if v > 0 else 0.0
         kernels[k] = {"ms": round(v, 4), "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                      "TFLOPs": round(flops_hf[k] * hf / (v * 1e-3) / 1e12, 2)}
+                      "TFLOPs": round(flops_hf[k] * hf / (v * 1e-3) / 1e12, 2) if v > 0 else 0.0}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -274,6 +290,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) q/k/v, keys scaled by 1/sqrt(D*S), gamma~U(0.95,1), "
                 "beta=sigmoid(N(0,1)), N(0,0.02) fp32 initial state)",
+        "path": {1: "three MFMA kernels", 2: "pipelined kernel"}.get(path, str(path)),
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "S": S, "D": D, "in_dtype": "bf16",
                    "out_dtype": "f32", "state_dtype": "f32", "parallelism": "single GPU"},
         "roofline": roofline,

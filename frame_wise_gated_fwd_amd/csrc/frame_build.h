@@ -1,0 +1,175 @@
+// Per-frame maps of the frame-wise GDN on bf16 MFMA (gfx950), head dim 128,
+// one frame per call of build_frame by a 256-thread workgroup:
+//   G_t = K_t^T K_t   and   U_t = V_t^T K_t,
+// both reducing over the S tokens of one latent frame (one recurrent step
+// consumes a whole frame: bilibili cv49203711, fourth key point).  Products
+// of two bf16 numbers are exact in float32; accumulation is float32.
+//
+// One workgroup (4 waves) per frame.  The reduction index (tokens) is the
+// slow index of the [S, 128] storage while an MFMA operand wants 8
+// consecutive reduction values per lane, so every wave loads a 32-token x
+// 128-dim slab with 16-byte loads (lane = token group g = l/16 of 8 tokens,
+// dim group c = l%16 of 8 dims) and transposes 8x8 bf16 blocks in registers.
+// That yields 8 operand fragments per slab; fragment j holds, in lane
+// (g, c), the 8 tokens of group g at dim 8c + j, so MFMA row m of fragment j
+// is dim 8m + j.  Fragments go to LDS once and every wave reads the ones it
+// needs.  Wave w owns the output rows {8m + j : j in {2w, 2w+1}} of both G and
+// U (32 accumulators of 16x16), which makes every lane's final row segment 8
+// contiguous floats.
+#pragma once
+
+#include "gdn_common.h"
+#include "gdn_packed.h"
+
+#include <type_traits>
+#include <utility>
+
+namespace gdn {
+
+constexpr int kBuildIterTok = 64;  // tokens per loop iteration: two 32-token slabs of K and of V
+
+// LDS the build needs: 64 KB when kPacked (the output is staged there), else 32 KB.
+template <bool kPacked>
+constexpr int build_lds_bytes() { return kPacked ? 65536 : 32768; }
+
+// G_t = K_t^T K_t and U_t = V_t^T K_t of one frame.  Kf, Vf: the frame's
+// [S, 128] bf16 rows.  kPacked: Gout receives the packed bf16 hi/lo form
+// and Uout the packed float32 form (gdn_packed.h); otherwise both are
+// float32 row-major 128 x 128.  `lds` must hold build_lds_bytes<kPacked>().
+// kDepth: token iterations loaded ahead (register buffers of 32 VGPRs each).
+// All 256 threads of the workgroup must call it.  On return this thread's
+// stores are issued, not necessarily complete.
+template <bool kPacked, int kDepth = 1>
+__device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, const uint16_t* __restrict__ Vf,
+                                            int S, u32x4* __restrict__ lds, void* __restrict__ Gout,
+                                            float* __restrict__ Uout) {
+  constexpr int D = 128;
+  constexpr int kIterTok = kBuildIterTok;
+  // During the token loop: frag[unit][j][lane] (32 KB); unit 0,1 = K slab 0,1;
+  // unit 2,3 = V slab 0,1.  Afterwards the whole buffer (64 KB) stages the
+  // packed output so that it leaves in contiguous 4 KB rows of stores.
+  u32x4 (*frag)[8][kWave] = reinterpret_cast<u32x4 (*)[8][kWave]>(lds);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63;
+  const int g = l >> 4, c = l & 15;
+  const uint16_t* src = w < 2 ? Kf : Vf;
+  const int slab = w & 1;
+
+  u32x4 x[kDepth][8];
+  auto load = [&](auto jc, int it) {
+    constexpr int jb = decltype(jc)::value;
+    const int base = it * kIterTok + slab * 32 + 8 * g;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = base + i;
+      if (s < S)
+        x[jb][i] = ld_nt(reinterpret_cast<const u32x4*>(src + (int64_t)s * D + 8 * c));
+      else
+        x[jb][i] = (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+
+  f32x4 accG[2][8], accU[2][8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      accG[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      accU[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int iters = (S + kIterTok - 1) / kIterTok;
+  auto iteration = [&](auto jc, int it) {
+    constexpr int jb = decltype(jc)::value;
+    __syncthreads();  // every wave is done reading the previous fragments
+    // 8x8 transpose: fragment j, dword p = (token 2p, token 2p+1) at dim 8c+j.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t a = x[jb][2 * p][j >> 1], b = x[jb][2 * p + 1][j >> 1];
+        o[p] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      frag[w][j][l] = o;
+    }
+    __syncthreads();
+    if (it + kDepth < iters) load(jc, it + kDepth);  // in flight during the MFMAs
+
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      u32x4 kf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kf[j] = frag[sl][j][l];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const u32x4 kr = frag[sl][2 * w + jj][l];
+        const u32x4 vr = frag[2 + sl][2 * w + jj][l];
+#pragma unroll
+        for (int jp = 0; jp < 8; ++jp) {
+          accG[jj][jp] = mfma16x16x32(kr, kf[jp], accG[jj][jp]);
+          accU[jj][jp] = mfma16x16x32(vr, kf[jp], accU[jj][jp]);
+        }
+      }
+    }
+  };
+  [&]<int... js>(std::integer_sequence<int, js...>) {
+    ((js < iters ? load(std::integral_constant<int, js>{}, js) : void()), ...);
+  }(std::make_integer_sequence<int, kDepth>{});
+  for (int it0 = 0; it0 < iters; it0 += kDepth) {
+    [&]<int... js>(std::integer_sequence<int, js...>) {
+      ((it0 + js < iters ? iteration(std::integral_constant<int, js>{}, it0 + js) : void()), ...);
+    }(std::make_integer_sequence<int, kDepth>{});
+  }
+
+  // Lane (g, c), register i of block (j, jp) holds X[32g + 8i + j][8c + jp].
+  if constexpr (kPacked) {
+    char* stage = reinterpret_cast<char*>(lds);
+    // pass 0: G_t as bf16 hi/lo (Gp); pass 1: U_t as float32 (Up)
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      __syncthreads();  // previous readers of the LDS buffer are done
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * w + jj;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 32 * g + 8 * i + j;
+          if (pass == 0) {
+            const u32x2 p0 = split2(accG[jj][0][i], accG[jj][1][i]), p1 = split2(accG[jj][2][i], accG[jj][3][i]);
+            const u32x2 p2 = split2(accG[jj][4][i], accG[jj][5][i]), p3 = split2(accG[jj][6][i], accG[jj][7][i]);
+            *reinterpret_cast<u32x4*>(stage + packed::g_chunk(row, 8 * c, 0)) = (u32x4){p0.x, p1.x, p2.x, p3.x};
+            *reinterpret_cast<u32x4*>(stage + packed::g_chunk(row, 8 * c, 1)) = (u32x4){p0.y, p1.y, p2.y, p3.y};
+          } else {
+            *reinterpret_cast<f32x4*>(stage + packed::u_chunk(row, 8 * c)) =
+                (f32x4){accU[jj][0][i], accU[jj][1][i], accU[jj][2][i], accU[jj][3][i]};
+            *reinterpret_cast<f32x4*>(stage + packed::u_chunk(row, 8 * c + 4)) =
+                (f32x4){accU[jj][4][i], accU[jj][5][i], accU[jj][6][i], accU[jj][7][i]};
+          }
+        }
+      }
+      __syncthreads();
+      u32x4* dst = reinterpret_cast<u32x4*>(pass == 0 ? static_cast<char*>(Gout) : reinterpret_cast<char*>(Uout));
+#pragma unroll
+      for (int k = 0; k < 16; ++k) dst[k * 256 + tid] = lds[k * 256 + tid];
+    }
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * w + jj;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 32 * g + 8 * i + j;
+        f32x4* gp = reinterpret_cast<f32x4*>(static_cast<float*>(Gout) + row * D + 8 * c);
+        f32x4* up = reinterpret_cast<f32x4*>(Uout + row * D + 8 * c);
+        gp[0] = (f32x4){accG[jj][0][i], accG[jj][1][i], accG[jj][2][i], accG[jj][3][i]};
+        gp[1] = (f32x4){accG[jj][4][i], accG[jj][5][i], accG[jj][6][i], accG[jj][7][i]};
+        up[0] = (f32x4){accU[jj][0][i], accU[jj][1][i], accU[jj][2][i], accU[jj][3][i]};
+        up[1] = (f32x4){accU[jj][4][i], accU[jj][5][i], accU[jj][6][i], accU[jj][7][i]};
+      }
+    }
+  }
+}
+
+}  // namespace gdn

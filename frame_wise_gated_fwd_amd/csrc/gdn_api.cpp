@@ -90,6 +90,23 @@ bool aliasing_ok(const Range* outs, int nout, const Range* ins, int nin,
 
 bool fast_path(int in_dtype, int64_t D) { return in_dtype == GDN_BF16 && D == 128; }
 
+bool pipelined(int in_dtype, const Dims& d) {
+  return fast_path(in_dtype, d.D) && gdn::pipeline_supported(d.heads, d.S);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t{255}; }
@@ -116,9 +133,17 @@ const char* gdn_status_str(int s) {
 
 int gdn_supports_d(int64_t D) { return D >= 16 && D <= 128 && D % 16 == 0; }
 
+int gdn_path(const gdn_shape* shape, int in_dtype) {
+  Dims d;
+  if (!valid_dtype(in_dtype) || check_shape(shape, true, &d) != GDN_OK) return -1;
+  if (pipelined(in_dtype, d)) return GDN_PATH_PIPELINED;
+  return fast_path(in_dtype, d.D) ? GDN_PATH_MFMA : GDN_PATH_PLAIN;
+}
+
 size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype) {
   Dims d;
   if (!valid_dtype(in_dtype) || check_shape(shape, true, &d) != GDN_OK) return 0;
+  if (pipelined(in_dtype, d)) return round256((size_t)gdn::pipeline_workspace_bytes(d.heads));
   return 3 * round256(d.map_elems * sizeof(float));
 }
 
@@ -250,7 +275,15 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
                        {state_in, state_in ? stb : 0}};
   if (!aliasing_ok(outs, 3, ins, 6, state_out, state_in)) return GDN_E_ALIAS;
 
-  // Workspace: G_t (split form on the MFMA path), U_t, M_t (split form on the MFMA path).
+  if (pipelined(in_dtype, d)) {
+    const int cus = device_cus();
+    if (cus <= 0) return GDN_E_HIP;
+    return hip_status(gdn::launch_pipeline(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        gamma, beta, state_in, out, out_dtype == GDN_BF16, state_out, workspace, d.heads, d.T, (int)d.S, cus,
+        static_cast<hipStream_t>(stream), ev));
+  }
+  // Workspace: G_t, U_t, M_t of every frame (packed forms on the MFMA path).
   const size_t slot = round256(d.map_elems * sizeof(float));
   char* ws = static_cast<char*>(workspace);
   void* G = ws;

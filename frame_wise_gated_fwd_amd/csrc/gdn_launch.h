@@ -23,6 +23,16 @@ hipError_t launch_state_d128(const void* G, bool packed, const float* U, const f
 hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool packed_m, void* out,
                                    bool out_bf16, int64_t frames, int S, hipStream_t st);
 
+// ---- pipelined MFMA path: the three stages in one persistent kernel ---------
+// Eligible when bf16, D == 128 and heads <= pipeline_max_heads.  The
+// workspace holds a control block, per-head flags and per-head ring buffers.
+bool pipeline_supported(int64_t heads, int64_t S);
+int64_t pipeline_workspace_bytes(int64_t heads);
+hipError_t launch_pipeline(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
+                           const float* beta, const float* state_in, void* out, bool out_bf16,
+                           float* state_out, void* workspace, int64_t heads, int64_t T, int S,
+                           int num_cus, hipStream_t st, hipEvent_t* ev);
+
 // ---- plain float32 path: any supported D, f32 or bf16 inputs ---------------
 hipError_t launch_build_generic(const void* k, const void* v, bool in_bf16, float* G, float* U,
                                 int64_t frames, int S, int D, hipStream_t st);

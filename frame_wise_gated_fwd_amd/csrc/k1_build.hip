@@ -1,4 +1,5 @@
-// Per-frame maps of the frame-wise GDN on bf16 MFMA (gfx950), head dim 128:
+// Per-frame maps of the frame-wise GDN on bf16 MFMA (gfx950), head dim 128,
+// one workgroup per frame:
 //   G_t = K_t^T K_t   and   U_t = V_t^T K_t,
 // both reducing over the S tokens of one latent frame (one recurrent step
 // consumes a whole frame: bilibili cv49203711, fourth key point).  Products
@@ -15,141 +16,22 @@
 // needs.  Wave w owns the output rows {8m + j : j in {2w, 2w+1}} of both G and
 // U (32 accumulators of 16x16), which makes every lane's final row segment 8
 // contiguous floats.
-#include "gdn_common.h"
+#include "frame_build.h"
 #include "gdn_launch.h"
-#include "gdn_packed.h"
 
 namespace gdn {
 namespace {
 
-constexpr int D = 128;
-constexpr int kIterTok = 64;  // tokens per loop iteration: two 32-token slabs of K and of V
-
-// kPacked: write G_t (as bf16 hi/lo) and U_t in the packed layouts the state
-// pass reads (gdn_packed.h); otherwise both are float32 row-major.
 template <bool kPacked>
 __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, void* __restrict__ Gout,
     float* __restrict__ Uout, int S) {
-  // During the token loop: frag[unit][j][lane] (32 KB); unit 0,1 = K slab 0,1;
-  // unit 2,3 = V slab 0,1.  Afterwards the whole buffer (64 KB) stages the
-  // packed output so that it leaves in contiguous 4 KB rows of stores.
-  __shared__ u32x4 lds[kPacked ? 4096 : 2048];
-  u32x4 (*frag)[8][kWave] = reinterpret_cast<u32x4 (*)[8][kWave]>(lds);
-
+  constexpr int D = 128;
+  __shared__ u32x4 lds[build_lds_bytes<kPacked>() / 16];
   const int64_t f = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63;
-  const int g = l >> 4, c = l & 15;
-  const uint16_t* src = (w < 2 ? K : V) + f * (int64_t)S * D;
-  const int slab = w & 1;
-
-  u32x4 x[8];
-  auto load = [&](int it) {
-    const int base = it * kIterTok + slab * 32 + 8 * g;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = base + i;
-      if (s < S)
-        x[i] = ld_nt(reinterpret_cast<const u32x4*>(src + (int64_t)s * D + 8 * c));
-      else
-        x[i] = (u32x4){0u, 0u, 0u, 0u};
-    }
-  };
-
-  f32x4 accG[2][8], accU[2][8];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      accG[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      accU[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
-
-  const int iters = (S + kIterTok - 1) / kIterTok;
-  load(0);
-  for (int it = 0; it < iters; ++it) {
-    __syncthreads();  // every wave is done reading the previous fragments
-    // 8x8 transpose: fragment j, dword p = (token 2p, token 2p+1) at dim 8c+j.
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 o;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t a = x[2 * p][j >> 1], b = x[2 * p + 1][j >> 1];
-        o[p] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-      }
-      frag[w][j][l] = o;
-    }
-    __syncthreads();
-    if (it + 1 < iters) load(it + 1);  // next slab in flight during the MFMAs
-
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      u32x4 kf[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) kf[j] = frag[sl][j][l];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const u32x4 kr = frag[sl][2 * w + jj][l];
-        const u32x4 vr = frag[2 + sl][2 * w + jj][l];
-#pragma unroll
-        for (int jp = 0; jp < 8; ++jp) {
-          accG[jj][jp] = mfma16x16x32(kr, kf[jp], accG[jj][jp]);
-          accU[jj][jp] = mfma16x16x32(vr, kf[jp], accU[jj][jp]);
-        }
-      }
-    }
-  }
-
-  // Lane (g, c), register i of block (j, jp) holds X[32g + 8i + j][8c + jp].
-  const int64_t fo = f * (int64_t)D * D;
-  if constexpr (kPacked) {
-    char* stage = reinterpret_cast<char*>(lds);
-    // pass 0: G_t as bf16 hi/lo (Gp); pass 1: U_t as float32 (Up)
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      __syncthreads();  // previous readers of the LDS buffer are done
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = 2 * w + jj;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 32 * g + 8 * i + j;
-          if (pass == 0) {
-            const u32x2 p0 = split2(accG[jj][0][i], accG[jj][1][i]), p1 = split2(accG[jj][2][i], accG[jj][3][i]);
-            const u32x2 p2 = split2(accG[jj][4][i], accG[jj][5][i]), p3 = split2(accG[jj][6][i], accG[jj][7][i]);
-            *reinterpret_cast<u32x4*>(stage + packed::g_chunk(row, 8 * c, 0)) = (u32x4){p0.x, p1.x, p2.x, p3.x};
-            *reinterpret_cast<u32x4*>(stage + packed::g_chunk(row, 8 * c, 1)) = (u32x4){p0.y, p1.y, p2.y, p3.y};
-          } else {
-            *reinterpret_cast<f32x4*>(stage + packed::u_chunk(row, 8 * c)) =
-                (f32x4){accU[jj][0][i], accU[jj][1][i], accU[jj][2][i], accU[jj][3][i]};
-            *reinterpret_cast<f32x4*>(stage + packed::u_chunk(row, 8 * c + 4)) =
-                (f32x4){accU[jj][4][i], accU[jj][5][i], accU[jj][6][i], accU[jj][7][i]};
-          }
-        }
-      }
-      __syncthreads();
-      u32x4* dst = reinterpret_cast<u32x4*>((pass == 0 ? static_cast<char*>(Gout) : reinterpret_cast<char*>(Uout)) + fo * 4);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) dst[k * 256 + tid] = lds[k * 256 + tid];
-    }
-  } else {
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * w + jj;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 32 * g + 8 * i + j;
-        f32x4* gp = reinterpret_cast<f32x4*>(static_cast<float*>(Gout) + fo + row * D + 8 * c);
-        f32x4* up = reinterpret_cast<f32x4*>(Uout + fo + row * D + 8 * c);
-        gp[0] = (f32x4){accG[jj][0][i], accG[jj][1][i], accG[jj][2][i], accG[jj][3][i]};
-        gp[1] = (f32x4){accG[jj][4][i], accG[jj][5][i], accG[jj][6][i], accG[jj][7][i]};
-        up[0] = (f32x4){accU[jj][0][i], accU[jj][1][i], accU[jj][2][i], accU[jj][3][i]};
-        up[1] = (f32x4){accU[jj][4][i], accU[jj][5][i], accU[jj][6][i], accU[jj][7][i]};
-      }
-    }
-  }
+  const int64_t in_off = f * (int64_t)S * D, mat_off = f * (int64_t)D * D;
+  build_frame<kPacked>(K + in_off, V + in_off, S, lds, static_cast<char*>(Gout) + mat_off * 4,
+                       Uout + mat_off);
 }
 
 }  // namespace

@@ -81,15 +81,35 @@ const char* gdn_status_str(int status);
 int gdn_supports_d(int64_t D);
 
 /*
- * Workspace bytes gdn_frame_fwd needs for this shape and input dtype: room
- * for G_t, U_t and M_t of every frame, 3 * B*H*T*D*D*4 bytes, rounded up to
- * 256.  A pure function of its arguments.  Returns 0 when the shape is
- * invalid.
+ * Which implementation gdn_frame_fwd uses for this shape and input dtype (a
+ * pure function of its arguments):
+ *   GDN_PATH_PIPELINED  bf16, D == 128, B*H <= 16: one persistent kernel in
+ *                       which build, state pass and output overlap, each head
+ *                       on one XCD, intermediates passed through that XCD's L2;
+ *   GDN_PATH_MFMA       bf16, D == 128, larger B*H: three bf16-MFMA kernels
+ *                       (build, state pass, output) with intermediates in the
+ *                       workspace;
+ *   GDN_PATH_PLAIN      every other supported case: three float32 kernels;
+ *   -1                  invalid arguments.
+ */
+enum { GDN_PATH_PLAIN = 0, GDN_PATH_MFMA = 1, GDN_PATH_PIPELINED = 2 };
+int gdn_path(const gdn_shape* shape, int in_dtype);
+
+/*
+ * Workspace bytes gdn_frame_fwd needs for this shape and input dtype, a pure
+ * function of its arguments; 0 when the shape is invalid.  Pipelined path:
+ * a control block, per-head flags and per-head rings (about 1.3 MB per
+ * head).  Other paths: G_t, U_t and M_t of every frame, 3 * B*H*T*D*D*4
+ * bytes, rounded up to 256.
  */
 size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype);
 
 /*
- * The whole forward: O and M_T from q, k, v, gamma, beta and M_0.
+ * The whole forward: O and M_T from q, k, v, gamma, beta and M_0.  On the
+ * pipelined path all workgroups of the kernel must be able to run at the
+ * same time (one per compute unit); if the GPU is so busy with other work
+ * that its waits cannot complete, the kernel gives up after a few seconds
+ * and state_out is NaN.
  *   in_dtype   GDN_BF16 or GDN_F32: dtype of q, k, v.
  *   out_dtype  GDN_F32 (recommended) or GDN_BF16: dtype of out.
  *   state_in   M_0 or NULL for zeros.   state_out: M_T (may equal state_in).
@@ -105,12 +125,13 @@ int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype,
 
 /*
  * gdn_frame_fwd, plus per-kernel durations: HIP events are recorded on
- * `stream` before and after each of the three kernels (build, state pass,
- * output) and the call waits for the last one, then writes the three
- * elapsed times in milliseconds to kernel_ms[0..2] (host memory).  Results
- * are identical to gdn_frame_fwd.  The events are created on the first call
- * on each device and kept for the life of the process; this entry point is
- * for profiling and is not meant for graph capture.
+ * `stream` between the kernels of the call, the call waits for the last one
+ * and writes elapsed milliseconds to kernel_ms[0..2] (host memory): build,
+ * state pass and output on the three-kernel paths; flag reset, pipelined
+ * kernel and 0 on the pipelined path.  Results are identical to
+ * gdn_frame_fwd.  The events are created on the first call on each device
+ * and kept for the life of the process; this entry point is for profiling
+ * and is not meant for graph capture.
  */
 int gdn_frame_fwd_timed(const gdn_shape* shape, int in_dtype, int out_dtype,
                         const void* q, const void* k, const void* v,

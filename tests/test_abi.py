@@ -49,14 +49,29 @@ def _shape(B=1, H=2, T=3, S=40, D=128):
     return Shape(B, H, T, S, D)
 
 
+def test_path_selection():
+    L = F.lib()
+    assert L.gdn_path(ctypes.byref(_shape(1, 16, 961, 880, 128)), BF16) == 2
+    assert L.gdn_path(ctypes.byref(_shape(4, 16, 961, 880, 128)), BF16) == 1
+    assert L.gdn_path(ctypes.byref(_shape(1, 16, 961, 880, 128)), F32) == 0
+    assert L.gdn_path(ctypes.byref(_shape(1, 2, 8, 16, 64)), BF16) == 0
+    assert L.gdn_path(ctypes.byref(_shape(D=100)), BF16) == -1
+    assert L.gdn_path(None, BF16) == -1
+
+
 def test_workspace_bytes():
     L = F.lib()
-    s = _shape(1, 16, 961, 880, 128)
-    per = 16 * 961 * 128 * 128 * 4
+    s = _shape(4, 16, 961, 880, 128)
+    per = 64 * 961 * 128 * 128 * 4
     assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == 3 * ((per + 255) // 256 * 256)
+    # the pipelined path needs rings, not whole-sequence intermediates
+    small = L.gdn_workspace_bytes(ctypes.byref(_shape(1, 16, 961, 880, 128)), BF16)
+    assert 0 < small < 64 << 20
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(T=0)), BF16) == 0
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(D=100)), BF16) == 0
     assert L.gdn_workspace_bytes(ctypes.byref(s), 7) == 0
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(1, 16, 961, 880, 128)), F32) == \
+        3 * ((16 * 961 * 128 * 128 * 4 + 255) // 256 * 256)
     assert L.gdn_workspace_bytes(None, BF16) == 0
 
 
