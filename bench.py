@@ -29,16 +29,14 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, TFLOP/s
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "frame_wise_gated_fwd_amd", "csrc")
 
-# The kernels each path launches, in the order gdn_frame_fwd_timed reports
-# them: name -> (source file, kernel symbol).
+# The kernels each path launches, by the kind index gdn_frame_fwd_timed
+# reports them under: kind -> (name, source file, kernel symbol).
 PATH_KERNELS = {
-    1: {"build": ("k1_build.hip", "k1_build_bf16_d128"),
-        "state": ("k2_state.hip", "k2_state_d128"),
-        "output": ("k3_output.hip", "k3_output_bf16_d128")},
-    2: {"reset": ("k_pipeline.hip", "k_pipeline_init"),
-        "pipeline": ("k_pipeline.hip", "k_pipeline")},
+    1: {0: ("build", "k1_build.hip", "k1_build_bf16_d128"),
+        1: ("state", "k2_state.hip", "k2_state_d128"),
+        2: ("output", "k3_output.hip", "k3_output_bf16_d128")},
 }
-KERNELS = {k: v for d in PATH_KERNELS.values() for k, v in d.items()}
+KERNELS = {n: (f, k) for d in PATH_KERNELS.values() for n, f, k in d.values()}
 
 
 def log(msg):
@@ -54,16 +52,13 @@ def per_head_frame_bytes(S, D, in_bytes=2, out_bytes=4):
         "build": 2 * qkv + 2 * dd,      # read K, V; write G, U
         "state": 2 * dd + dd,           # read G, U; write M_t
         "output": qkv + dd + o,         # read Q, M_t; write O
-        "pipeline": 3 * qkv + o,        # q, k, v in; O out; G, U, M stay on chip
-        "reset": 0,
         "step": 3 * qkv + o,            # q, k, v in; O out (state in/out per head is extra)
     }
 
 
 def per_head_frame_flops(S, D):
-    f = {"build": 4 * S * D * D, "state": 2 * D ** 3, "output": 2 * S * D * D, "reset": 0,
+    f = {"build": 4 * S * D * D, "state": 2 * D ** 3, "output": 2 * S * D * D,
          "step": 6 * S * D * D + 2 * D ** 3}
-    f["pipeline"] = f["step"]
     return f
 
 
@@ -181,8 +176,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (every box has a single "
-              "MI355X); run it with --gpus 1.", file=sys.stderr, flush=True)
+        print("bench.py measures one GPU: the library has no multi-GPU path (heads would shard over "
+              "GPUs with no communication); run it with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import torch
@@ -232,39 +227,47 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"step: {ms:.3f} ms (events), {wall / args.steps * 1e3:.3f} ms (wall)")
 
-    # Per-kernel durations of the same call: gdn_frame_fwd_timed records HIP
-    # events on the launch stream between the three kernels.
+    # Per-kernel durations of the same call: gdn_frame_fwd_timed records a
+    # pair of HIP events around every launch, on the stream it is launched on.
     path = L.gdn_path(ctypes.byref(shp), GDN_BF16)
-    names = list(PATH_KERNELS[path])
-    kms_acc = {k: [] for k in names}
-    kbuf = (ctypes.c_float * 3)()
+    kinds = PATH_KERNELS[path]
+    tot = {kinds[i][0]: 0.0 for i in kinds}
+    nl = {kinds[i][0]: 0 for i in kinds}
+    kbuf, lbuf = (ctypes.c_float * 3)(), (ctypes.c_int * 3)()
     for _ in range(args.steps):
         check(L.gdn_frame_fwd_timed(ctypes.byref(shp), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]),
                                     P(x["v"]), P(x["gamma"]), P(x["beta"]), P(x["state"]), P(out),
-                                    P(st_out), P(ws), wsb, stream, kbuf), "gdn_frame_fwd_timed")
-        for i, k in enumerate(names):
-            kms_acc[k].append(kbuf[i])
-    kms = {k: float(np.mean(v)) for k, v in kms_acc.items()}
-    log("kernels (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in kms.items()))
+                                    P(st_out), P(ws), wsb, stream, kbuf, lbuf), "gdn_frame_fwd_timed")
+        for i, (name, _, _) in kinds.items():
+            tot[name] += kbuf[i]
+            nl[name] += lbuf[i]
+    kms = {k: tot[k] / args.steps for k in tot}          # per call, summed over its launches
+    launches = {k: nl[k] // args.steps for k in nl}      # launches per call
+    log("kernels (ms per call, launches): " + ", ".join(f"{k} {kms[k]:.3f} x{launches[k]}" for k in kms))
 
     hf = B * H * T
     bytes_hf = per_head_frame_bytes(S, D)
     flops_hf = per_head_frame_flops(S, D)
     dom = max(kms, key=kms.get)
-    kfile, ksym = PATH_KERNELS[path][dom]
-    achieved = bytes_hf[dom] * hf / (kms[dom] * 1e-3) / 1e9
+    kfile, ksym = KERNELS[dom]
+    # Average launch of the dominant kernel: its algorithmic bytes per launch
+    # over its average launch duration.
+    avg_ms = kms[dom] / launches[dom]
+    per_launch = bytes_hf[dom] * hf / launches[dom]
+    achieved = per_launch / (avg_ms * 1e-3) / 1e9
     traffic = measured_traffic(dom, w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": ksym, "kernel_ms": round(kms[dom], 4),
-                "bytes_per_launch": bytes_hf[dom] * hf}
+                "kernel": ksym, "launches_per_step": launches[dom], "avg_launch_ms": round(avg_ms, 5),
+                "bytes_per_launch": round(per_launch)}
     step_bytes = bytes_hf["step"] * hf + (2 if x["state"] is not None else 1) * B * H * D * D * 4
     step_gbs = step_bytes / (ms * 1e-3) / 1e9
     step_tflops = flops_hf["step"] * hf / (ms * 1e-3) / 1e12
     kernels = {}
     for k, v in kms.items():
         gbs = bytes_hf[k] * hf / (v * 1e-3) / 1e9 if v > 0 else 0.0
-        kernels[k] = {"ms": round(v, 4), "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        kernels[k] = {"ms": round(v, 4), "launches": launches[k], "GBps": round(gbs, 1),
+                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "TFLOPs": round(flops_hf[k] * hf / (v * 1e-3) / 1e12, 2) if v > 0 else 0.0}
 
     cpu = None
@@ -290,7 +293,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) q/k/v, keys scaled by 1/sqrt(D*S), gamma~U(0.95,1), "
                 "beta=sigmoid(N(0,1)), N(0,0.02) fp32 initial state)",
-        "path": {1: "three MFMA kernels", 2: "pipelined kernel"}.get(path, str(path)),
+        "path": "three MFMA kernels, overlapped over frame segments",
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "S": S, "D": D, "in_dtype": "bf16",
                    "out_dtype": "f32", "state_dtype": "f32", "parallelism": "single GPU"},
         "roofline": roofline,

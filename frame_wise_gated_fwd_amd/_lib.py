@@ -14,7 +14,7 @@ LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
 GDN_OK = 0
 GDN_F32 = 0
 GDN_BF16 = 1
-GDN_PATH_PLAIN, GDN_PATH_MFMA, GDN_PATH_PIPELINED = 0, 1, 2
+GDN_PATH_PLAIN, GDN_PATH_MFMA = 0, 1
 
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_E_NULLPTR", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE",
                 4: "GDN_E_UNSUPPORTED_D", 5: "GDN_E_WORKSPACE", 6: "GDN_E_ALIAS", 7: "GDN_E_HIP"}
@@ -39,7 +39,7 @@ SIGNATURES = {
     "gdn_workspace_bytes": (_sz, [_PS, _i]),
     "gdn_frame_fwd": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp]),
     "gdn_frame_fwd_timed": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp,
-                                 ctypes.POINTER(ctypes.c_float)]),
+                                 ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
     "gdn_build_maps": (_i, [_PS, _i, _cvp, _cvp, _vp, _vp, _vp]),
     "gdn_state_pass": (_i, [_PS, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp]),
     "gdn_output": (_i, [_PS, _i, _i, _cvp, _cvp, _vp, _vp]),

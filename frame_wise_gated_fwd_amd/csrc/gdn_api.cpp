@@ -5,14 +5,17 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <limits>
 #include <mutex>
+#include <vector>
 
 #include "gdn_launch.h"
 
 namespace {
 
 constexpr int64_t kMaxFrames = (int64_t{1} << 24) - 1;  // B*H*T: one workgroup per frame
+constexpr int64_t kSegmentFrames = 32;                   // frames per segment, overlapped schedule
 
 struct Dims {
   int64_t B, H, T, S, D;
@@ -90,26 +93,210 @@ bool aliasing_ok(const Range* outs, int nout, const Range* ins, int nin,
 
 bool fast_path(int in_dtype, int64_t D) { return in_dtype == GDN_BF16 && D == 128; }
 
-bool pipelined(int in_dtype, const Dims& d) {
-  return fast_path(in_dtype, d.D) && gdn::pipeline_supported(d.heads, d.S);
-}
-
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (!cache[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t{255}; }
+
+}  // namespace
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Per-launch HIP events of gdn_frame_fwd_timed: a pair around every kernel,
+// on the stream that kernel is launched on.  One pool per device, grown on
+// demand and kept for the life of the process.
+struct Recorder {
+  std::vector<hipEvent_t>* pool;
+  std::vector<int> kind;  // kernel kind of pair i
+  hipError_t begin(hipStream_t st) {
+    const size_t i = 2 * kind.size();
+    while (pool->size() < i + 2) {
+      hipEvent_t e;
+      hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) return err;
+      pool->push_back(e);
+    }
+    return hipEventRecord((*pool)[i], st);
+  }
+  hipError_t end(hipStream_t st, int k) {
+    hipError_t err = hipEventRecord((*pool)[2 * kind.size() + 1], st);
+    if (err == hipSuccess) kind.push_back(k);
+    return err;
+  }
+};
+std::vector<hipEvent_t> g_timing_pool[kMaxDevices];
+std::mutex g_timing_mu;
+
+// Side streams of the overlapped schedule, one pair per device, created on
+// first use (non-blocking, default priority) and kept for the life of the
+// process, with the events that chain them.  g_side_mu serialises the
+// enqueue of a whole call, so calls from several host threads never
+// interleave their records and waits on these events.
+struct Side {
+  hipStream_t state_st, out_st;
+  hipEvent_t fork, built, stated, state_done, out_done;
+  bool ready;
+};
+Side g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+hipError_t side_init(Side& sd) {
+  if (sd.ready) return hipSuccess;
+  hipError_t e;
+  if ((e = hipStreamCreateWithFlags(&sd.state_st, hipStreamNonBlocking)) != hipSuccess) return e;
+  if ((e = hipStreamCreateWithFlags(&sd.out_st, hipStreamNonBlocking)) != hipSuccess) return e;
+  for (hipEvent_t* ev : {&sd.fork, &sd.built, &sd.stated, &sd.state_done, &sd.out_done})
+    if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
+  sd.ready = true;
+  return hipSuccess;
+}
+
+// Frames per segment of the overlapped schedule (GDN_SEGMENT_FRAMES
+// overrides the default; read once).
+int64_t segment_frames() {
+  static const int64_t f = [] {
+    const char* e = std::getenv("GDN_SEGMENT_FRAMES");
+    const long v = e ? std::strtol(e, nullptr, 10) : 0;
+    return v >= 1 && v <= (1L << 24) ? (int64_t)v : int64_t{kSegmentFrames};
+  }();
+  return f;
+}
+
+int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
+                   const void* v, const float* gamma, const float* beta, const float* state_in,
+                   void* out, float* state_out, void* workspace, size_t workspace_bytes,
+                   void* stream, Recorder* rec);
+
+}  // namespace
+
+namespace {
+
+// One kernel launch, bracketed by timing events when rec is set.
+template <typename F>
+hipError_t timed(Recorder* rec, hipStream_t st, int kind, F&& launch) {
+  hipError_t e;
+  if (rec && (e = rec->begin(st)) != hipSuccess) return e;
+  if ((e = launch()) != hipSuccess) return e;
+  return rec ? rec->end(st, kind) : hipSuccess;
+}
+
+// The MFMA path: build, state pass and output over ceil(T / F) segments of
+// (nearly) equal length.  Segment i's state pass needs its own build and segment
+// i-1's state pass; its output needs its own state pass.  Builds run on the
+// caller's stream, state passes and outputs on the two side streams, so
+// build(i+1), state(i) and output(i-1) overlap: the state pass is a chain of
+// short latency-bound steps on a few CUs, while build and output stream
+// from HBM on the rest.  With one segment everything runs on the caller's
+// stream.
+hipError_t run_mfma(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const float* gamma, const float* beta, const float* state_in, void* out,
+                    bool out_bf16, float* state_out, void* G, float* U, void* M_all, hipStream_t s,
+                    Recorder* rec) {
+  const int64_t F = segment_frames();
+  const int64_t nseg = (d.T + F - 1) / F;
+  const int S = (int)d.S;
+  auto build = [&](hipStream_t st, int64_t t0, int64_t t1) {
+    return timed(rec, st, 0, [&] {
+      return gdn::launch_build_bf16_d128(k, v, G, true, U, d.heads, d.T, t0, t1, S, st);
+    });
+  };
+  auto state = [&](hipStream_t st, int64_t t0, int64_t t1) {
+    return timed(rec, st, 1, [&] {
+      return gdn::launch_state_d128(G, true, U, gamma, beta, t0 ? state_out : state_in, M_all, state_out,
+                                    d.heads, d.T, t0, t1, st);
+    });
+  };
+  auto output = [&](hipStream_t st, int64_t t0, int64_t t1) {
+    return timed(rec, st, 2, [&] {
+      return gdn::launch_output_bf16_d128(q, M_all, true, out, out_bf16, d.heads, d.T, t0, t1, S, st);
+    });
+  };
+  hipError_t e;
+  if (nseg == 1) {
+    if ((e = build(s, 0, d.T)) != hipSuccess) return e;
+    if ((e = state(s, 0, d.T)) != hipSuccess) return e;
+    return output(s, 0, d.T);
+  }
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  Side& sd = g_side[dev];
+  if ((e = side_init(sd)) != hipSuccess) return e;
+  // fork: the side streams start after everything already on the caller's stream
+  if ((e = hipEventRecord(sd.fork, s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sd.state_st, sd.fork, 0)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sd.out_st, sd.fork, 0)) != hipSuccess) return e;
+  hipError_t err = hipSuccess;
+  for (int64_t i = 0; i < nseg && err == hipSuccess; ++i) {
+    const int64_t t0 = i * d.T / nseg, t1 = (i + 1) * d.T / nseg;  // balanced, at most F frames
+    if ((err = build(s, t0, t1)) != hipSuccess) break;
+    if ((err = hipEventRecord(sd.built, s)) != hipSuccess) break;
+    if ((err = hipStreamWaitEvent(sd.state_st, sd.built, 0)) != hipSuccess) break;
+    if ((err = state(sd.state_st, t0, t1)) != hipSuccess) break;
+    if ((err = hipEventRecord(sd.stated, sd.state_st)) != hipSuccess) break;
+    if ((err = hipStreamWaitEvent(sd.out_st, sd.stated, 0)) != hipSuccess) break;
+    err = output(sd.out_st, t0, t1);
+  }
+  // join, also after a failed launch, so the caller's stream stays ordered
+  // after whatever was enqueued
+  if ((e = hipEventRecord(sd.state_done, sd.state_st)) != hipSuccess) return e;
+  if ((e = hipEventRecord(sd.out_done, sd.out_st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(s, sd.state_done, 0)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(s, sd.out_done, 0)) != hipSuccess) return e;
+  return err;
+}
+
+int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
+                   const void* v, const float* gamma, const float* beta, const float* state_in,
+                   void* out, float* state_out, void* workspace, size_t workspace_bytes,
+                   void* stream, Recorder* rec) {
+  Dims d;
+  int st = check_shape(shape, true, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GDN_E_DTYPE;
+  if (!q || !k || !v || !gamma || !beta || !out || !state_out) return GDN_E_NULLPTR;
+  const size_t need = gdn_workspace_bytes(shape, in_dtype);
+  if (!workspace || workspace_bytes < need) return GDN_E_WORKSPACE;
+  if ((uintptr_t)workspace % 256 != 0) return GDN_E_WORKSPACE;
+  const size_t inb = d.in_elems * dsize(in_dtype), outb = d.in_elems * dsize(out_dtype);
+  const size_t stb = d.state_elems * 4, gb = (size_t)d.frames * 4;
+  const Range outs[] = {{out, outb}, {state_out, stb}, {workspace, need}};
+  const Range ins[] = {{q, inb}, {k, inb}, {v, inb}, {gamma, gb}, {beta, gb},
+                       {state_in, state_in ? stb : 0}};
+  if (!aliasing_ok(outs, 3, ins, 6, state_out, state_in)) return GDN_E_ALIAS;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // Workspace: G_t, U_t, M_t of every frame (packed forms on the MFMA path).
+  const size_t slot = round256(d.map_elems * sizeof(float));
+  char* ws = static_cast<char*>(workspace);
+  void* G = ws;
+  float* U = reinterpret_cast<float*>(ws + slot);
+  void* M_all = ws + 2 * slot;
+  const bool ob = out_dtype == GDN_BF16;
+  if (fast_path(in_dtype, d.D))
+    return hip_status(run_mfma(d, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                               static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out, G,
+                               U, M_all, s, rec));
+  hipError_t e;
+  if ((e = timed(rec, s, 0, [&] {
+         return gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, static_cast<float*>(G), U, d.frames,
+                                          (int)d.S, (int)d.D, s);
+       })) != hipSuccess)
+    return GDN_E_HIP;
+  if ((e = timed(rec, s, 1, [&] {
+         return gdn::launch_state_generic(static_cast<float*>(G), U, gamma, beta, state_in,
+                                          static_cast<float*>(M_all), state_out, d.heads, d.T, (int)d.D, s);
+       })) != hipSuccess)
+    return GDN_E_HIP;
+  if ((e = timed(rec, s, 2, [&] {
+         return gdn::launch_output_generic(q, in_dtype == GDN_BF16, static_cast<float*>(M_all), out, ob,
+                                           d.frames, (int)d.S, (int)d.D, s);
+       })) != hipSuccess)
+    return GDN_E_HIP;
+  return GDN_OK;
+}
 
 }  // namespace
 
@@ -136,14 +323,12 @@ int gdn_supports_d(int64_t D) { return D >= 16 && D <= 128 && D % 16 == 0; }
 int gdn_path(const gdn_shape* shape, int in_dtype) {
   Dims d;
   if (!valid_dtype(in_dtype) || check_shape(shape, true, &d) != GDN_OK) return -1;
-  if (pipelined(in_dtype, d)) return GDN_PATH_PIPELINED;
   return fast_path(in_dtype, d.D) ? GDN_PATH_MFMA : GDN_PATH_PLAIN;
 }
 
 size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype) {
   Dims d;
   if (!valid_dtype(in_dtype) || check_shape(shape, true, &d) != GDN_OK) return 0;
-  if (pipelined(in_dtype, d)) return round256((size_t)gdn::pipeline_workspace_bytes(d.heads));
   return 3 * round256(d.map_elems * sizeof(float));
 }
 
@@ -162,7 +347,7 @@ int gdn_build_maps(const gdn_shape* shape, int in_dtype, const void* k, const vo
   if (fast_path(in_dtype, d.D))
     return hip_status(gdn::launch_build_bf16_d128(static_cast<const uint16_t*>(k),
                                                   static_cast<const uint16_t*>(v), G, false, U,
-                                                  d.frames, (int)d.S, s));
+                                                  d.heads, d.T, 0, d.T, (int)d.S, s));
   return hip_status(gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, G, U, d.frames, (int)d.S,
                                               (int)d.D, s));
 }
@@ -181,7 +366,7 @@ int gdn_state_pass(const gdn_shape* shape, const float* G, const float* U, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.D == 128)
     return hip_status(gdn::launch_state_d128(G, false, U, gamma, beta, state_in, M_all, state_out,
-                                             d.heads, d.T, s));
+                                             d.heads, d.T, 0, d.T, s));
   return hip_status(gdn::launch_state_generic(G, U, gamma, beta, state_in, M_all, state_out,
                                               d.heads, d.T, (int)d.D, s));
 }
@@ -201,25 +386,11 @@ int gdn_output(const gdn_shape* shape, int in_dtype, int out_dtype, const void* 
   const bool ob = out_dtype == GDN_BF16;
   if (fast_path(in_dtype, d.D))
     return hip_status(gdn::launch_output_bf16_d128(static_cast<const uint16_t*>(q), M_all, false, out,
-                                                   ob, d.frames, (int)d.S, s));
+                                                   ob, d.heads, d.T, 0, d.T, (int)d.S, s));
   return hip_status(gdn::launch_output_generic(q, in_dtype == GDN_BF16, M_all, out, ob, d.frames,
                                                (int)d.S, (int)d.D, s));
 }
 
-namespace {
-
-// Events for gdn_frame_fwd_timed, one set per device, created on first use.
-constexpr int kMaxDevices = 64;
-hipEvent_t g_events[kMaxDevices][4];
-bool g_events_ready[kMaxDevices];
-std::mutex g_events_mu;
-
-int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
-                   const void* v, const float* gamma, const float* beta, const float* state_in,
-                   void* out, float* state_out, void* workspace, size_t workspace_bytes,
-                   void* stream, hipEvent_t* ev);
-
-}  // namespace
 
 int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
                   const void* v, const float* gamma, const float* beta, const float* state_in,
@@ -232,94 +403,27 @@ int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype, const voi
 int gdn_frame_fwd_timed(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q,
                         const void* k, const void* v, const float* gamma, const float* beta,
                         const float* state_in, void* out, float* state_out, void* workspace,
-                        size_t workspace_bytes, void* stream, float* kernel_ms) {
-  if (!kernel_ms) return GDN_E_NULLPTR;
+                        size_t workspace_bytes, void* stream, float* kernel_ms, int* launches) {
+  if (!kernel_ms || !launches) return GDN_E_NULLPTR;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_E_HIP;
-  {
-    std::lock_guard<std::mutex> lock(g_events_mu);
-    if (!g_events_ready[dev]) {
-      for (int i = 0; i < 4; ++i)
-        if (hipEventCreate(&g_events[dev][i]) != hipSuccess) return GDN_E_HIP;
-      g_events_ready[dev] = true;
-    }
-  }
-  hipEvent_t* ev = g_events[dev];
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  Recorder rec{&g_timing_pool[dev], {}};
   const int st = frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, gamma, beta, state_in, out,
-                                state_out, workspace, workspace_bytes, stream, ev);
+                                state_out, workspace, workspace_bytes, stream, &rec);
   if (st != GDN_OK) return st;
-  if (hipEventSynchronize(ev[3]) != hipSuccess) return GDN_E_HIP;
-  for (int i = 0; i < 3; ++i)
-    if (hipEventElapsedTime(&kernel_ms[i], ev[i], ev[i + 1]) != hipSuccess) return GDN_E_HIP;
-  return GDN_OK;
-}
-
-namespace {
-
-int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
-                   const void* v, const float* gamma, const float* beta, const float* state_in,
-                   void* out, float* state_out, void* workspace, size_t workspace_bytes,
-                   void* stream, hipEvent_t* ev) {
-  Dims d;
-  int st = check_shape(shape, true, &d);
-  if (st != GDN_OK) return st;
-  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GDN_E_DTYPE;
-  if (!q || !k || !v || !gamma || !beta || !out || !state_out) return GDN_E_NULLPTR;
-  const size_t need = gdn_workspace_bytes(shape, in_dtype);
-  if (!workspace || workspace_bytes < need) return GDN_E_WORKSPACE;
-  if ((uintptr_t)workspace % 256 != 0) return GDN_E_WORKSPACE;
-  const size_t inb = d.in_elems * dsize(in_dtype), outb = d.in_elems * dsize(out_dtype);
-  const size_t stb = d.state_elems * 4, gb = (size_t)d.frames * 4;
-  const Range outs[] = {{out, outb}, {state_out, stb}, {workspace, need}};
-  const Range ins[] = {{q, inb}, {k, inb}, {v, inb}, {gamma, gb}, {beta, gb},
-                       {state_in, state_in ? stb : 0}};
-  if (!aliasing_ok(outs, 3, ins, 6, state_out, state_in)) return GDN_E_ALIAS;
-
-  if (pipelined(in_dtype, d)) {
-    const int cus = device_cus();
-    if (cus <= 0) return GDN_E_HIP;
-    return hip_status(gdn::launch_pipeline(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-        gamma, beta, state_in, out, out_dtype == GDN_BF16, state_out, workspace, d.heads, d.T, (int)d.S, cus,
-        static_cast<hipStream_t>(stream), ev));
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return GDN_E_HIP;
+  for (int i = 0; i < 3; ++i) {
+    kernel_ms[i] = 0.f;
+    launches[i] = 0;
   }
-  // Workspace: G_t, U_t, M_t of every frame (packed forms on the MFMA path).
-  const size_t slot = round256(d.map_elems * sizeof(float));
-  char* ws = static_cast<char*>(workspace);
-  void* G = ws;
-  float* U = reinterpret_cast<float*>(ws + slot);
-  void* M_all = ws + 2 * slot;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fast = fast_path(in_dtype, d.D);
-  const bool ob = out_dtype == GDN_BF16;
-  hipError_t e;
-  if (ev && hipEventRecord(ev[0], s) != hipSuccess) return GDN_E_HIP;
-  if (fast)
-    e = gdn::launch_build_bf16_d128(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                                    G, true, U, d.frames, (int)d.S, s);
-  else
-    e = gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, static_cast<float*>(G), U, d.frames,
-                                  (int)d.S, (int)d.D, s);
-  if (e != hipSuccess) return GDN_E_HIP;
-  if (ev && hipEventRecord(ev[1], s) != hipSuccess) return GDN_E_HIP;
-  if (fast)
-    e = gdn::launch_state_d128(G, true, U, gamma, beta, state_in, M_all, state_out, d.heads, d.T, s);
-  else
-    e = gdn::launch_state_generic(static_cast<float*>(G), U, gamma, beta, state_in,
-                                  static_cast<float*>(M_all), state_out, d.heads, d.T, (int)d.D, s);
-  if (e != hipSuccess) return GDN_E_HIP;
-  if (ev && hipEventRecord(ev[2], s) != hipSuccess) return GDN_E_HIP;
-  if (fast)
-    e = gdn::launch_output_bf16_d128(static_cast<const uint16_t*>(q), M_all, true, out, ob, d.frames,
-                                     (int)d.S, s);
-  else
-    e = gdn::launch_output_generic(q, in_dtype == GDN_BF16, static_cast<float*>(M_all), out, ob,
-                                   d.frames, (int)d.S, (int)d.D, s);
-  if (e != hipSuccess) return GDN_E_HIP;
-  if (ev && hipEventRecord(ev[3], s) != hipSuccess) return GDN_E_HIP;
+  for (size_t i = 0; i < rec.kind.size(); ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, (*rec.pool)[2 * i], (*rec.pool)[2 * i + 1]) != hipSuccess) return GDN_E_HIP;
+    kernel_ms[rec.kind[i]] += ms;
+    launches[rec.kind[i]] += 1;
+  }
   return GDN_OK;
 }
-
-}  // namespace
 
 }  // extern "C"

@@ -11,27 +11,22 @@ namespace gdn {
 // The per-frame matrices G_t, U_t, M_t pass between the three kernels either
 // as float32 row-major (the stage entry points) or "packed" (gdn_packed.h:
 // G_t and M_t as bf16 hi/lo pairs, all three in the order the consumer's
-// waves read them), which is what gdn_frame_fwd uses.
+// waves read them), which is what gdn_frame_fwd uses.  Every per-frame array
+// is laid out [head][T]; each launcher covers frames [t0, t1) of every head.
 hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
-                                  float* U, int64_t frames, int S, hipStream_t st);
-// State pass over T frames for `heads` heads.  G, U and M_out are all packed
-// or all float32; M_out may be null.
+                                  float* U, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
+                                  hipStream_t st);
+// State pass over frames [t0, t1) for `heads` heads, starting from state_in
+// (M_{t0-1}; null = zero) and leaving M_{t1-1} in state_out (which may equal
+// state_in).  G, U and M_out are all packed or all float32; M_out may be null.
 hipError_t launch_state_d128(const void* G, bool packed, const float* U, const float* gamma,
                              const float* beta, const float* state_in, void* M_out,
-                             float* state_out, int64_t heads, int64_t T, hipStream_t st);
-// O_t = Q_t M_t^T; out_bf16 selects the output dtype.
+                             float* state_out, int64_t heads, int64_t T, int64_t t0, int64_t t1,
+                             hipStream_t st);
+// O_t = Q_t M_t^T for frames [t0, t1); out_bf16 selects the output dtype.
 hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool packed_m, void* out,
-                                   bool out_bf16, int64_t frames, int S, hipStream_t st);
-
-// ---- pipelined MFMA path: the three stages in one persistent kernel ---------
-// Eligible when bf16, D == 128 and heads <= pipeline_max_heads.  The
-// workspace holds a control block, per-head flags and per-head ring buffers.
-bool pipeline_supported(int64_t heads, int64_t S);
-int64_t pipeline_workspace_bytes(int64_t heads);
-hipError_t launch_pipeline(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
-                           const float* beta, const float* state_in, void* out, bool out_bf16,
-                           float* state_out, void* workspace, int64_t heads, int64_t T, int S,
-                           int num_cus, hipStream_t st, hipEvent_t* ev);
+                                   bool out_bf16, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
+                                   hipStream_t st);
 
 // ---- plain float32 path: any supported D, f32 or bf16 inputs ---------------
 hipError_t launch_build_generic(const void* k, const void* v, bool in_bf16, float* G, float* U,

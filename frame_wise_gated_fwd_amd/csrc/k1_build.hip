@@ -25,10 +25,11 @@ namespace {
 template <bool kPacked>
 __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, void* __restrict__ Gout,
-    float* __restrict__ Uout, int S) {
+    float* __restrict__ Uout, int S, int64_t T, int t0, int nt) {
   constexpr int D = 128;
   __shared__ u32x4 lds[build_lds_bytes<kPacked>() / 16];
-  const int64_t f = blockIdx.x;
+  // workgroup i: frame t0 + i % nt of head i / nt (frames are [head][T])
+  const int64_t f = (int64_t)(blockIdx.x / nt) * T + t0 + blockIdx.x % nt;
   const int64_t in_off = f * (int64_t)S * D, mat_off = f * (int64_t)D * D;
   build_frame<kPacked>(K + in_off, V + in_off, S, lds, static_cast<char*>(Gout) + mat_off * 4,
                        Uout + mat_off);
@@ -37,11 +38,14 @@ __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
 }  // namespace
 
 hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
-                                  float* U, int64_t frames, int S, hipStream_t st) {
+                                  float* U, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
+                                  hipStream_t st) {
+  const int nt = (int)(t1 - t0);
+  const dim3 grid((unsigned)(heads * nt));
   if (packed_out)
-    hipLaunchKernelGGL(k1_build_bf16_d128<true>, dim3((unsigned)frames), dim3(256), 0, st, k, v, G, U, S);
+    hipLaunchKernelGGL(k1_build_bf16_d128<true>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt);
   else
-    hipLaunchKernelGGL(k1_build_bf16_d128<false>, dim3((unsigned)frames), dim3(256), 0, st, k, v, G, U, S);
+    hipLaunchKernelGGL(k1_build_bf16_d128<false>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ template <int kRows, bool kPacked, int kDepth>
 __global__ __launch_bounds__(256, 1) void k2_state_d128(
     const void* __restrict__ Gin, const float* __restrict__ U, const float* __restrict__ gamma,
     const float* __restrict__ beta, const float* state_in, void* __restrict__ Mout,
-    float* state_out, int heads, int T) {
+    float* state_out, int heads, int T, int tb, int te) {
   constexpr int kRB = kRows / 16;     // 16-row blocks of M per workgroup
   constexpr int kParts = D / kRows;   // workgroups per head
   // [buffer][hi|lo][row][col]
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256, 1) void k2_state_d128(
 
   auto load_frame = [&](auto jc, int t) {
     constexpr int j = decltype(jc)::value;
-    if (t >= T) return;
+    if (t >= te) return;
     const int64_t fo = ((int64_t)head * T + t) * D * D;
     if constexpr (kPacked) {
       const char* Gp = static_cast<const char*>(Gin) + fo * 4;
@@ -153,22 +153,22 @@ __global__ __launch_bounds__(256, 1) void k2_state_d128(
   const float* bh = beta + (int64_t)head * T;
   auto win_load = [&](int t0, float& gv, float& bv) {
     const int tt = t0 + l;
-    gv = tt < T ? gh[tt] : 0.f;
-    bv = tt < T ? bh[tt] : 0.f;
+    gv = tt < te ? gh[tt] : 0.f;
+    bv = tt < te ? bh[tt] : 0.f;
   };
   float gwin, bwin, gnxt, bnxt;
-  win_load(0, gwin, bwin);
-  win_load(64, gnxt, bnxt);
+  win_load(tb, gwin, bwin);
+  win_load(tb + 64, gnxt, bnxt);
 
   [&]<int... js>(std::integer_sequence<int, js...>) {
-    (load_frame(std::integral_constant<int, js>{}, js), ...);
+    (load_frame(std::integral_constant<int, js>{}, tb + js), ...);
   }(std::make_integer_sequence<int, kDepth>{});
   lds_barrier();
 
   auto step = [&](auto jc, int t) {
     constexpr int j = decltype(jc)::value;
-    const int buf = t & 1;
-    const int tw = t & 63;
+    const int buf = (t - tb) & 1;
+    const int tw = (t - tb) & 63;
     const float gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwin), tw));
     const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwin), tw));
     if (tw == 63) {  // move to the next window and fetch the one after it
@@ -264,9 +264,9 @@ __global__ __launch_bounds__(256, 1) void k2_state_d128(
     lds_barrier();
   };
 
-  for (int t0 = 0; t0 < T; t0 += kDepth) {
+  for (int t0 = tb; t0 < te; t0 += kDepth) {
     [&]<int... js>(std::integer_sequence<int, js...>) {
-      ((t0 + js < T ? step(std::integral_constant<int, js>{}, t0 + js) : void()), ...);
+      ((t0 + js < te ? step(std::integral_constant<int, js>{}, t0 + js) : void()), ...);
     }(std::make_integer_sequence<int, kDepth>{});
   }
 
@@ -280,12 +280,12 @@ __global__ __launch_bounds__(256, 1) void k2_state_d128(
 template <int kRows, bool kPacked, int kDepth>
 hipError_t launch_rows(const void* G, const float* U, const float* gamma, const float* beta,
                        const float* state_in, void* M_out, float* state_out, int64_t heads,
-                       int64_t T, hipStream_t st) {
+                       int64_t T, int64_t tb, int64_t te, hipStream_t st) {
   // Workgroup ids are grouped so that the workgroups of a head share id % 8.
   const int64_t groups = (heads + 7) / 8;
   const unsigned grid = (unsigned)(groups * 8 * (D / kRows));
   hipLaunchKernelGGL((k2_state_d128<kRows, kPacked, kDepth>), dim3(grid), dim3(256), 0, st, G, U, gamma,
-                     beta, state_in, M_out, state_out, (int)heads, (int)T);
+                     beta, state_in, M_out, state_out, (int)heads, (int)T, (int)tb, (int)te);
   return hipGetLastError();
 }
 
@@ -293,10 +293,11 @@ hipError_t launch_rows(const void* G, const float* U, const float* gamma, const 
 
 hipError_t launch_state_d128(const void* G, bool packed, const float* U, const float* gamma,
                              const float* beta, const float* state_in, void* M_out,
-                             float* state_out, int64_t heads, int64_t T, hipStream_t st) {
+                             float* state_out, int64_t heads, int64_t T, int64_t tb, int64_t te,
+                             hipStream_t st) {
   if (packed)
-    return launch_rows<32, true, 2>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, st);
-  return launch_rows<32, false, 2>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, st);
+    return launch_rows<16, true, 2>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, st);
+  return launch_rows<32, false, 2>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, st);
 }
 
 }  // namespace gdn

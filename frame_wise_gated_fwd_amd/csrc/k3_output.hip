@@ -22,10 +22,12 @@ namespace {
 
 template <bool kPackedM, bool kOutBf16>
 __global__ __launch_bounds__(256, 2) void k3_output_bf16_d128(
-    const uint16_t* __restrict__ Q, const void* __restrict__ M_all, void* __restrict__ out, int S) {
+    const uint16_t* __restrict__ Q, const void* __restrict__ M_all, void* __restrict__ out, int S,
+    int64_t T, int t0, int nt) {
   constexpr int D = 128;
   __shared__ uint16_t Ml[2][D][kOutLdsW];
-  const int64_t f = blockIdx.x;
+  // workgroup i: frame t0 + i % nt of head i / nt (frames are [head][T])
+  const int64_t f = (int64_t)(blockIdx.x / nt) * T + t0 + blockIdx.x % nt;
   const int64_t in_off = f * (int64_t)S * D;
   const char* Mt = static_cast<const char*>(M_all) + f * packed::kFrameBytes;
   void* Of = static_cast<char*>(out) + in_off * (kOutBf16 ? 2 : 4);
@@ -35,21 +37,24 @@ __global__ __launch_bounds__(256, 2) void k3_output_bf16_d128(
 }  // namespace
 
 template <bool kPackedM>
-hipError_t launch_out(const uint16_t* q, const void* M_all, void* out, bool out_bf16, int64_t frames,
-                      int S, hipStream_t st) {
+hipError_t launch_out(const uint16_t* q, const void* M_all, void* out, bool out_bf16, int64_t heads,
+                      int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st) {
+  const int nt = (int)(t1 - t0);
+  const dim3 grid((unsigned)(heads * nt));
   if (out_bf16)
-    hipLaunchKernelGGL((k3_output_bf16_d128<kPackedM, true>), dim3((unsigned)frames), dim3(256), 0, st, q,
-                       M_all, out, S);
+    hipLaunchKernelGGL((k3_output_bf16_d128<kPackedM, true>), grid, dim3(256), 0, st, q, M_all, out, S, T,
+                       (int)t0, nt);
   else
-    hipLaunchKernelGGL((k3_output_bf16_d128<kPackedM, false>), dim3((unsigned)frames), dim3(256), 0, st, q,
-                       M_all, out, S);
+    hipLaunchKernelGGL((k3_output_bf16_d128<kPackedM, false>), grid, dim3(256), 0, st, q, M_all, out, S, T,
+                       (int)t0, nt);
   return hipGetLastError();
 }
 
 hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool packed_m, void* out,
-                                   bool out_bf16, int64_t frames, int S, hipStream_t st) {
-  return packed_m ? launch_out<true>(q, M_all, out, out_bf16, frames, S, st)
-                 : launch_out<false>(q, M_all, out, out_bf16, frames, S, st);
+                                   bool out_bf16, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
+                                   hipStream_t st) {
+  return packed_m ? launch_out<true>(q, M_all, out, out_bf16, heads, T, t0, t1, S, st)
+                 : launch_out<false>(q, M_all, out, out_bf16, heads, T, t0, t1, S, st);
 }
 
 }  // namespace gdn

@@ -83,33 +83,37 @@ int gdn_supports_d(int64_t D);
 /*
  * Which implementation gdn_frame_fwd uses for this shape and input dtype (a
  * pure function of its arguments):
- *   GDN_PATH_PIPELINED  bf16, D == 128, B*H <= 16: one persistent kernel in
- *                       which build, state pass and output overlap, each head
- *                       on one XCD, intermediates passed through that XCD's L2;
- *   GDN_PATH_MFMA       bf16, D == 128, larger B*H: three bf16-MFMA kernels
- *                       (build, state pass, output) with intermediates in the
- *                       workspace;
- *   GDN_PATH_PLAIN      every other supported case: three float32 kernels;
- *   -1                  invalid arguments.
+ *   GDN_PATH_MFMA   bf16, D == 128: three bf16-MFMA kernels (build, state
+ *                   pass, output) with the per-frame intermediates in the
+ *                   workspace.  When T > 32 the frames are cut into
+ *                   ceil(T / 32) segments of nearly equal length and the
+ *                   build of segment i+1, the state pass of segment i and
+ *                   the output of segment i-1 overlap: builds run on
+ *                   `stream`, state passes and outputs on two
+ *                   library-owned streams (created on first use per device,
+ *                   non-blocking, default priority) that fork from and join
+ *                   back to `stream` through events, so the call is ordered
+ *                   on `stream` like a single kernel.  The environment
+ *                   variable GDN_SEGMENT_FRAMES (read once per process)
+ *                   replaces the 32.  Otherwise all three run on `stream`;
+ *   GDN_PATH_PLAIN  every other supported case: three float32 kernels on
+ *                   `stream`;
+ *   -1              invalid arguments.
+ * Results do not depend on the segmentation: the state pass carries the
+ * float32 state exactly from one segment to the next.
  */
-enum { GDN_PATH_PLAIN = 0, GDN_PATH_MFMA = 1, GDN_PATH_PIPELINED = 2 };
+enum { GDN_PATH_PLAIN = 0, GDN_PATH_MFMA = 1 };
 int gdn_path(const gdn_shape* shape, int in_dtype);
 
 /*
  * Workspace bytes gdn_frame_fwd needs for this shape and input dtype, a pure
- * function of its arguments; 0 when the shape is invalid.  Pipelined path:
- * a control block, per-head flags and per-head rings (about 1.3 MB per
- * head).  Other paths: G_t, U_t and M_t of every frame, 3 * B*H*T*D*D*4
- * bytes, rounded up to 256.
+ * function of its arguments; 0 when the shape is invalid: G_t, U_t and M_t
+ * of every frame, 3 * B*H*T*D*D*4 bytes, each of the three rounded up to 256.
  */
 size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype);
 
 /*
- * The whole forward: O and M_T from q, k, v, gamma, beta and M_0.  On the
- * pipelined path all workgroups of the kernel must be able to run at the
- * same time (one per compute unit); if the GPU is so busy with other work
- * that its waits cannot complete, the kernel gives up after a few seconds
- * and state_out is NaN.
+ * The whole forward: O and M_T from q, k, v, gamma, beta and M_0.
  *   in_dtype   GDN_BF16 or GDN_F32: dtype of q, k, v.
  *   out_dtype  GDN_F32 (recommended) or GDN_BF16: dtype of out.
  *   state_in   M_0 or NULL for zeros.   state_out: M_T (may equal state_in).
@@ -124,21 +128,24 @@ int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * gdn_frame_fwd, plus per-kernel durations: HIP events are recorded on
- * `stream` between the kernels of the call, the call waits for the last one
- * and writes elapsed milliseconds to kernel_ms[0..2] (host memory): build,
- * state pass and output on the three-kernel paths; flag reset, pipelined
- * kernel and 0 on the pipelined path.  Results are identical to
- * gdn_frame_fwd.  The events are created on the first call on each device
- * and kept for the life of the process; this entry point is for profiling
- * and is not meant for graph capture.
+ * gdn_frame_fwd, plus per-kernel durations: a pair of HIP events is recorded
+ * around every kernel launch of the call, on the stream that launch uses;
+ * the call waits for `stream` (which the call joins back to) and writes,
+ * for kernel kinds 0 = build, 1 = state pass, 2 = output, the summed
+ * elapsed milliseconds to
+ * kernel_ms[kind] and the number of launches to launches[kind] (both host
+ * arrays of 3).  Launches of different kinds may overlap in time, so the
+ * three sums can add up to more than the call.  Results are identical to
+ * gdn_frame_fwd.  The events are created as needed and kept for the life of
+ * the process; this entry point is for profiling and is not meant for graph
+ * capture.
  */
 int gdn_frame_fwd_timed(const gdn_shape* shape, int in_dtype, int out_dtype,
                         const void* q, const void* k, const void* v,
                         const float* gamma, const float* beta,
                         const float* state_in, void* out, float* state_out,
                         void* workspace, size_t workspace_bytes, void* stream,
-                        float* kernel_ms);
+                        float* kernel_ms, int* launches);
 
 /*
  * Stage 1, the per-frame maps: G_t = K_t^T K_t and U_t = V_t^T K_t for every

@@ -51,7 +51,7 @@ def _shape(B=1, H=2, T=3, S=40, D=128):
 
 def test_path_selection():
     L = F.lib()
-    assert L.gdn_path(ctypes.byref(_shape(1, 16, 961, 880, 128)), BF16) == 2
+    assert L.gdn_path(ctypes.byref(_shape(1, 16, 961, 880, 128)), BF16) == 1
     assert L.gdn_path(ctypes.byref(_shape(4, 16, 961, 880, 128)), BF16) == 1
     assert L.gdn_path(ctypes.byref(_shape(1, 16, 961, 880, 128)), F32) == 0
     assert L.gdn_path(ctypes.byref(_shape(1, 2, 8, 16, 64)), BF16) == 0
@@ -61,17 +61,14 @@ def test_path_selection():
 
 def test_workspace_bytes():
     L = F.lib()
-    s = _shape(4, 16, 961, 880, 128)
-    per = 64 * 961 * 128 * 128 * 4
-    assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == 3 * ((per + 255) // 256 * 256)
-    # the pipelined path needs rings, not whole-sequence intermediates
-    small = L.gdn_workspace_bytes(ctypes.byref(_shape(1, 16, 961, 880, 128)), BF16)
-    assert 0 < small < 64 << 20
+    for s in (_shape(4, 16, 961, 880, 128), _shape(1, 16, 961, 880, 128)):
+        per = s.B * s.H * s.T * 128 * 128 * 4
+        assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == 3 * ((per + 255) // 256 * 256)
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(T=0)), BF16) == 0
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(D=100)), BF16) == 0
-    assert L.gdn_workspace_bytes(ctypes.byref(s), 7) == 0
-    assert L.gdn_workspace_bytes(ctypes.byref(_shape(1, 16, 961, 880, 128)), F32) == \
-        3 * ((16 * 961 * 128 * 128 * 4 + 255) // 256 * 256)
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape()), 7) == 0
+    s = _shape(1, 3, 5, 7, 48)
+    assert L.gdn_workspace_bytes(ctypes.byref(s), F32) == 3 * ((15 * 48 * 48 * 4 + 255) // 256 * 256)
     assert L.gdn_workspace_bytes(None, BF16) == 0
 
 
@@ -120,8 +117,11 @@ def test_timed_needs_output_array():
     L = F.lib()
     s = _shape()
     wsb = L.gdn_workspace_bytes(ctypes.byref(s), BF16)
+    ms, nl = (ctypes.c_float * 3)(), (ctypes.c_int * 3)()
     assert L.gdn_frame_fwd_timed(ctypes.byref(s), BF16, F32, P[0], P[1], P[2], P[3], P[4], None, P[5],
-                                 P[6], P[7], wsb, None, None) == NULLPTR
+                                 P[6], P[7], wsb, None, None, nl) == NULLPTR
+    assert L.gdn_frame_fwd_timed(ctypes.byref(s), BF16, F32, P[0], P[1], P[2], P[3], P[4], None, P[5],
+                                 P[6], P[7], wsb, None, ms, None) == NULLPTR
 
 
 def test_stage_argument_errors():
