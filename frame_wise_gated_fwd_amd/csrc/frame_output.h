@@ -5,10 +5,13 @@
 // pair carries M_t to about 2^-17 relative, so O keeps float32 accuracy.
 //
 // M_t is split into hi/lo once and kept in LDS.
-// Two index permutations make every global access a contiguous run:
-//  * the reduction (key) index: MFMA k-slot (kb, g, e) is key dim
-//    32g + 8kb + e, so lane (m, g) reads 64 contiguous bytes of its Q row;
-//  * the value index: column n of output block nb is value dim sigma(nb, n).
+// Global accesses:
+//  * Q: MFMA k-slot (kb, g, e) is key dim 32kb + 8g + e, so one load
+//    instruction (fixed kb) reads 64 contiguous bytes of 16 rows, and the
+//    instructions for kb and kb + 1 complete each 128-byte line.  These are
+//    ordinary (temporal) loads: the second half of a line then hits in L2,
+//    where a non-temporal load could re-fetch it from HBM;
+//  * O: column n of output block nb is value dim sigma(nb, n).
 //    For a float32 output sigma = 64(nb / 4) + 4n + nb % 4, so one store of
 //    blocks 0-3 (4-7) from 16 lanes is the first (second) 256 bytes of a
 //    row; for a bf16 output sigma = 8n + nb and one store covers the row.
@@ -79,7 +82,7 @@ __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, co
 
   const int ntiles = (S + kTile - 1) / kTile;
   // A operand of a 32-token tile: lane (m, g) holds tokens tok0 + 16rb + m,
-  // key dims 32g + 8kb .. +7 (64 contiguous bytes per row and rb).
+  // key dims 32kb + 8g .. +7.
   auto load_a = [&](int tile, u32x4 (&a)[2][4]) {
     const int tok0 = tile * kTile;
 #pragma unroll
@@ -88,7 +91,7 @@ __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, co
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
         a[rb][kb] = (tile < ntiles && s < S)
-                        ? ld_nt(reinterpret_cast<const u32x4*>(Qf + (int64_t)s * D + 32 * g + 8 * kb))
+                        ? *reinterpret_cast<const u32x4*>(Qf + (int64_t)s * D + 32 * kb + 8 * g)
                         : (u32x4){0u, 0u, 0u, 0u};
     }
   };
@@ -111,8 +114,8 @@ __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, co
       u32x4 bh[4], bl[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        bh[kb] = *reinterpret_cast<const u32x4*>(&Ml[0][nb * 16 + n][32 * g + 8 * kb]);
-        bl[kb] = *reinterpret_cast<const u32x4*>(&Ml[1][nb * 16 + n][32 * g + 8 * kb]);
+        bh[kb] = *reinterpret_cast<const u32x4*>(&Ml[0][nb * 16 + n][32 * kb + 8 * g]);
+        bl[kb] = *reinterpret_cast<const u32x4*>(&Ml[1][nb * 16 + n][32 * kb + 8 * g]);
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)

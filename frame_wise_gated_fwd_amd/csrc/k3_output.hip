@@ -4,16 +4,8 @@
 // M_t enters the MFMA as a bf16 hi/lo pair (two passes, Q*Mhi + Q*Mlo); the
 // pair carries M_t to about 2^-17 relative, so O keeps float32 accuracy.
 //
-// One workgroup per frame.  M_t is split into hi/lo once and kept in LDS.
-// Two index permutations make every global access a contiguous run:
-//  * the reduction (key) index: MFMA k-slot (kb, g, e) is key dim
-//    32g + 8kb + e, so lane (m, g) reads 64 contiguous bytes of its Q row;
-//  * the value index: column n of output block nb is value dim sigma(nb, n).
-//    For a float32 output sigma = 64(nb / 4) + 4n + nb % 4, so one store of
-//    blocks 0-3 (4-7) from 16 lanes is the first (second) 256 bytes of a
-//    row; for a bf16 output sigma = 8n + nb and one store covers the row.
-// LDS row nb*16 + n holds M row sigma(nb, n), which makes the B-operand reads
-// of 16 lanes land on 16 distinct 4-bank groups.
+// One workgroup per frame (frame_output.h has the tiling and the access
+// patterns); frames [t0, t0 + nt) of every head per launch.
 #include "frame_output.h"
 #include "gdn_launch.h"
 
