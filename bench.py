@@ -144,6 +144,71 @@ def _oracle_head_timed(args):
         return time.perf_counter() - t0
 
 
+def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
+    """The same tensors processed as successive calls that carry the float32
+    state (24 calls of 40 frames and one of 1 frame for T = 961), and the
+    latency of a single-frame (T = 1) call.  Inputs are sliced into
+    contiguous per-call tensors before timing."""
+    import torch
+    from frame_wise_gated_fwd_amd._lib import Shape, check, GDN_BF16, GDN_F32
+    B, H, T, S, D = w.B, w.H, w.T, w.S, w.D
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    chunks, t0 = [], 0
+    while t0 < T:
+        c = min(40, T - t0)
+        sl = slice(t0, t0 + c)
+        chunks.append({k: x[k][:, :, sl].contiguous() for k in ("q", "k", "v", "gamma", "beta")})
+        t0 += c
+    state = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda:0")
+    out = torch.empty((B, H, 40, S, D), dtype=torch.float32, device="cuda:0")
+    wsb = max(L.gdn_workspace_bytes(ctypes.byref(Shape(B, H, c["q"].shape[2], S, D)), GDN_BF16) for c in chunks)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+
+    def call(c, st_in):
+        n = c["q"].shape[2]
+        shp = Shape(B, H, n, S, D)
+        check(L.gdn_frame_fwd(ctypes.byref(shp), GDN_BF16, GDN_F32, P(c["q"]), P(c["k"]), P(c["v"]),
+                              P(c["gamma"]), P(c["beta"]), P(st_in), P(out), P(state), P(ws), wsb, stream),
+              "gdn_frame_fwd")
+
+    def pass_():
+        state.copy_(x["state"])
+        for c in chunks:
+            call(c, state)
+
+    pass_()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        pass_()
+    e1.record()
+    torch.cuda.synchronize()
+    stream_ms = e0.elapsed_time(e1) / reps
+
+    one = chunks[-1] if chunks[-1]["q"].shape[2] == 1 else \
+        {k: v[:, :, :1].contiguous() for k, v in chunks[0].items()}
+    for _ in range(10):
+        call(one, state)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(t1_reps):
+        call(one, state)
+    e1.record()
+    torch.cuda.synchronize()
+    back_to_back = e0.elapsed_time(e1) / t1_reps * 1e3
+    iso = []
+    for _ in range(50):
+        e0.record()
+        call(one, state)
+        e1.record()
+        e1.synchronize()
+        iso.append(e0.elapsed_time(e1) * 1e3)
+    return {"calls": len(chunks), "ms": round(stream_ms, 4),
+            "frame_steps_per_s": round(B * T / (stream_ms * 1e-3), 1)}, \
+           {"isolated_us_median": round(float(np.median(iso)), 2), "back_to_back_us": round(back_to_back, 2)}
+
+
 def copy_calibration(gib=1.0, reps=5):
     import torch
     n = int(gib * (1 << 30)) // 4
@@ -173,6 +238,8 @@ def main():
                     help="frames per head in the CPU oracle sample (default: sized for ~10-30 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the streamed-calls and single-frame latency measurements")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -270,6 +337,12 @@ def main():
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "TFLOPs": round(flops_hf[k] * hf / (v * 1e-3) / 1e12, 2) if v > 0 else 0.0}
 
+    streamed = t1 = None
+    if not args.no_extras:
+        log("streaming calls and T=1 latency")
+        streamed, t1 = streaming_and_t1(x, L, w, stream)
+        log(f"streamed: {streamed}; T=1: {t1}")
+
     cpu = None
     if not args.no_cpu_baseline:
         workers = min(default_workers(), B * H)
@@ -304,6 +377,8 @@ def main():
                           "mfma_frac": round(step_tflops / BF16_PEAK_TFLOPS, 4)},
         "kernels": kernels,
         "head_frame_steps_per_s": round(hf / (ms * 1e-3), 1),
+        "streamed_calls": streamed,
+        "t1_call": t1,
     }
     print(json.dumps(res), flush=True)
 

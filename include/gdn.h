@@ -85,8 +85,8 @@ int gdn_supports_d(int64_t D);
  * pure function of its arguments):
  *   GDN_PATH_MFMA   bf16, D == 128: three bf16-MFMA kernels (build, state
  *                   pass, output) with the per-frame intermediates in the
- *                   workspace.  When T > 32 the frames are cut into
- *                   ceil(T / 32) segments of nearly equal length and the
+ *                   workspace.  When T > 64 the frames are cut into
+ *                   ceil(T / 64) segments of nearly equal length and the
  *                   build of segment i+1, the state pass of segment i and
  *                   the output of segment i-1 overlap: builds run on
  *                   `stream`, state passes and outputs on two
@@ -95,7 +95,7 @@ int gdn_supports_d(int64_t D);
  *                   back to `stream` through events, so the call is ordered
  *                   on `stream` like a single kernel.  The environment
  *                   variable GDN_SEGMENT_FRAMES (read once per process)
- *                   replaces the 32.  Otherwise all three run on `stream`;
+ *                   replaces the 64.  Otherwise all three run on `stream`;
  *   GDN_PATH_PLAIN  every other supported case: three float32 kernels on
  *                   `stream`;
  *   -1              invalid arguments.
