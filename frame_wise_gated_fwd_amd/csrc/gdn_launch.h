@@ -13,6 +13,12 @@ namespace gdn {
 // G_t and M_t as bf16 hi/lo pairs, all three in the order the consumer's
 // waves read them), which is what gdn_frame_fwd uses.  Every per-frame array
 // is laid out [head][T]; each launcher covers frames [t0, t1) of every head.
+// Launches of at most this many frames (heads x frames in the range) take the
+// small-launch variants: a build with more loads in flight per workgroup and
+// an output that splits each frame's tokens over several workgroups.  Both
+// give bit-identical results to the full-size variants.
+constexpr int64_t kFewFrames = 128;
+
 hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
                                   float* U, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
                                   hipStream_t st);

@@ -35,6 +35,20 @@ __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
                        Uout + mat_off);
 }
 
+// The same work for launches too small to fill the GPU (a few frames):
+// one workgroup per CU and four token iterations in flight per wave instead
+// of one, so a lone workgroup keeps more bytes in flight.  The accumulation
+// order is the same as above, so results are bit-identical.
+__global__ __launch_bounds__(256, 1) void k1_build_bf16_d128_deep(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, void* __restrict__ Gout,
+    float* __restrict__ Uout, int S, int64_t T, int t0, int nt) {
+  constexpr int D = 128;
+  __shared__ u32x4 lds[build_lds_bytes<true>() / 16];
+  const int64_t f = (int64_t)(blockIdx.x / nt) * T + t0 + blockIdx.x % nt;
+  const int64_t in_off = f * (int64_t)S * D, mat_off = f * (int64_t)D * D;
+  build_frame<true, 4>(K + in_off, V + in_off, S, lds, static_cast<char*>(Gout) + mat_off * 4, Uout + mat_off);
+}
+
 }  // namespace
 
 hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
@@ -42,7 +56,9 @@ hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G,
                                   hipStream_t st) {
   const int nt = (int)(t1 - t0);
   const dim3 grid((unsigned)(heads * nt));
-  if (packed_out)
+  if (packed_out && heads * nt <= kFewFrames)
+    hipLaunchKernelGGL(k1_build_bf16_d128_deep, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt);
+  else if (packed_out)
     hipLaunchKernelGGL(k1_build_bf16_d128<true>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt);
   else
     hipLaunchKernelGGL(k1_build_bf16_d128<false>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt);

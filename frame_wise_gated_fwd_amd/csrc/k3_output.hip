@@ -5,9 +5,12 @@
 // pair carries M_t to about 2^-17 relative, so O keeps float32 accuracy.
 //
 // One workgroup per frame (frame_output.h has the tiling and the access
-// patterns); frames [t0, t0 + nt) of every head per launch.
+// patterns), or per token part of a frame when a launch has only a few
+// frames; frames [t0, t0 + nt) of every head per launch.
 #include "frame_output.h"
 #include "gdn_launch.h"
+
+#include <algorithm>
 
 namespace gdn {
 namespace {
@@ -15,15 +18,18 @@ namespace {
 template <bool kPackedM, bool kOutBf16>
 __global__ __launch_bounds__(256, 2) void k3_output_bf16_d128(
     const uint16_t* __restrict__ Q, const void* __restrict__ M_all, void* __restrict__ out, int S,
-    int64_t T, int t0, int nt) {
+    int64_t T, int t0, int nt, int nsplit) {
   constexpr int D = 128;
   __shared__ uint16_t Ml[2][D][kOutLdsW];
-  // workgroup i: frame t0 + i % nt of head i / nt (frames are [head][T])
-  const int64_t f = (int64_t)(blockIdx.x / nt) * T + t0 + blockIdx.x % nt;
-  const int64_t in_off = f * (int64_t)S * D;
+  // workgroup i: token part i % nsplit of frame t0 + j % nt of head j / nt,
+  // j = i / nsplit (frames are [head][T])
+  const int j = blockIdx.x / nsplit, part = blockIdx.x % nsplit;
+  const int64_t f = (int64_t)(j / nt) * T + t0 + j % nt;
+  const int s0 = (int)((int64_t)part * S / nsplit), s1 = (int)((int64_t)(part + 1) * S / nsplit);
+  const int64_t in_off = (f * (int64_t)S + s0) * D;
   const char* Mt = static_cast<const char*>(M_all) + f * packed::kFrameBytes;
   void* Of = static_cast<char*>(out) + in_off * (kOutBf16 ? 2 : 4);
-  output_frame<kPackedM, kOutBf16>(Q + in_off, Mt, Of, S, Ml, [] {});
+  output_frame<kPackedM, kOutBf16>(Q + in_off, Mt, Of, s1 - s0, Ml, [] {});
 }
 
 }  // namespace
@@ -32,13 +38,17 @@ template <bool kPackedM>
 hipError_t launch_out(const uint16_t* q, const void* M_all, void* out, bool out_bf16, int64_t heads,
                       int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st) {
   const int nt = (int)(t1 - t0);
-  const dim3 grid((unsigned)(heads * nt));
+  // A launch of a few frames splits each frame's tokens over up to 8
+  // workgroups (each token's arithmetic is unchanged).
+  const int64_t frames = heads * nt;
+  const int nsplit = frames <= kFewFrames ? (int)std::min<int64_t>({8, 512 / frames, S}) : 1;
+  const dim3 grid((unsigned)(frames * nsplit));
   if (out_bf16)
     hipLaunchKernelGGL((k3_output_bf16_d128<kPackedM, true>), grid, dim3(256), 0, st, q, M_all, out, S, T,
-                       (int)t0, nt);
+                       (int)t0, nt, nsplit);
   else
     hipLaunchKernelGGL((k3_output_bf16_d128<kPackedM, false>), grid, dim3(256), 0, st, q, M_all, out, S, T,
-                       (int)t0, nt);
+                       (int)t0, nt, nsplit);
   return hipGetLastError();
 }
 

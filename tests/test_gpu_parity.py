@@ -209,6 +209,28 @@ def test_segmented_forward_equals_stage_chain_bitwise():
     assert torch.equal(out, out2)
 
 
+def test_single_frame_calls_equal_one_call_bitwise():
+    """Launches of a few frames take the small-launch kernels (a build with
+    more loads in flight, an output split over token parts); 12 successive
+    T=1 calls must reproduce one T=12 call (16 x 12 frames, full-size
+    kernels) bit for bit, and match the oracle."""
+    w = CLIP_5S.with_(T=12, name="clip_t12", state_std=0.02)
+    x = device_inputs(w, DEV)
+    out1, st1 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    state = x["state"].clone()
+    outs = []
+    for t in range(w.T):
+        sl = slice(t, t + 1)
+        o, _ = F.frame_fwd(x["q"][:, :, sl].contiguous(), x["k"][:, :, sl].contiguous(),
+                           x["v"][:, :, sl].contiguous(), x["gamma"][:, :, sl].contiguous(),
+                           x["beta"][:, :, sl].contiguous(), state, state_out=state)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, dim=2), out1)
+    assert torch.equal(state, st1)
+    _forward_parity(w, frames=[0, 5, 11])
+
+
 def test_segmented_forward_is_ordered_on_a_user_stream():
     """Work queued on the caller's stream before the call is seen by every
     segment, and work queued after it runs after the last one."""
