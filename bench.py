@@ -35,6 +35,7 @@ PATH_KERNELS = {
     1: {0: ("build", "k1_build.hip", "k1_build_bf16_d128"),
         1: ("state", "k2_state.hip", "k2_state_d128"),
         2: ("output", "k3_output.hip", "k3_output_bf16_d128")},
+    2: {1: ("fused", "k_fused.hip", "k_fused")},
 }
 KERNELS = {n: (f, k) for d in PATH_KERNELS.values() for n, f, k in d.values()}
 
@@ -53,12 +54,13 @@ def per_head_frame_bytes(S, D, in_bytes=2, out_bytes=4):
         "state": 2 * dd + dd,           # read G, U; write M_t
         "output": qkv + dd + o,         # read Q, M_t; write O
         "step": 3 * qkv + o,            # q, k, v in; O out (state in/out per head is extra)
+        "fused": 3 * qkv + o,           # the fused kernel: G, U, M stay on chip
     }
 
 
 def per_head_frame_flops(S, D):
     f = {"build": 4 * S * D * D, "state": 2 * D ** 3, "output": 2 * S * D * D,
-         "step": 6 * S * D * D + 2 * D ** 3}
+         "step": 6 * S * D * D + 2 * D ** 3, "fused": 6 * S * D * D + 2 * D ** 3}
     return f
 
 
@@ -366,7 +368,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) q/k/v, keys scaled by 1/sqrt(D*S), gamma~U(0.95,1), "
                 "beta=sigmoid(N(0,1)), N(0,0.02) fp32 initial state)",
-        "path": "three MFMA kernels, overlapped over frame segments",
+        "path": {1: "three MFMA kernels, overlapped over frame segments",
+                 2: "fused persistent kernel"}.get(path, str(path)),
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "S": S, "D": D, "in_dtype": "bf16",
                    "out_dtype": "f32", "state_dtype": "f32", "parallelism": "single GPU"},
         "roofline": roofline,

@@ -50,7 +50,11 @@ __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, con
   // packed output so that it leaves in contiguous 4 KB rows of stores.
   u32x4 (*frag)[8][kWave] = reinterpret_cast<u32x4 (*)[8][kWave]>(lds);
 
-  const int tid = threadIdx.x;
+  // An opaque copy of the thread index: lane-dependent addresses are then
+  // computed at each call instead of being hoisted out of a caller's loop
+  // and kept live (in registers) across the whole call.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int w = tid >> 6, l = tid & 63;
   const int g = l >> 4, c = l & 15;
   const uint16_t* src = w < 2 ? Kf : Vf;

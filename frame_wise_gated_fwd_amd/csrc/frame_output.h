@@ -52,7 +52,11 @@ __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, co
                                              OnStaged on_staged) {
   constexpr int D = 128;
   constexpr int kTile = kOutTile;
-  const int tid = threadIdx.x;
+  // An opaque copy of the thread index: lane-dependent addresses are then
+  // computed at each call instead of being hoisted out of a caller's loop
+  // and kept live (in registers) across the whole call.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int w = tid >> 6, l = tid & 63;
   const int n = l & 15, g = l >> 4;
 

@@ -16,6 +16,7 @@ namespace {
 
 constexpr int64_t kMaxFrames = (int64_t{1} << 24) - 1;  // B*H*T: one workgroup per frame
 constexpr int64_t kSegmentFrames = 64;                   // frames per segment, overlapped schedule
+constexpr int64_t kFusedMinT = 64;                       // shorter sequences take the three-kernel path
 
 struct Dims {
   int64_t B, H, T, S, D;
@@ -93,6 +94,14 @@ bool aliasing_ok(const Range* outs, int nout, const Range* ins, int nin,
 
 bool fast_path(int in_dtype, int64_t D) { return in_dtype == GDN_BF16 && D == 128; }
 
+// The fused kernel takes bf16, D == 128 sequences longer than one segment
+// of the three-kernel schedule (GDN_FUSED=0 in the environment, read once,
+// turns it off).
+bool fused_path(int in_dtype, const Dims& d) {
+  static const bool off = [] { const char* e = std::getenv("GDN_FUSED"); return e && std::atoi(e) == 0; }();
+  return !off && fast_path(in_dtype, d.D) && d.T > kFusedMinT;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t{255}; }
@@ -149,6 +158,33 @@ hipError_t side_init(Side& sd) {
   for (hipEvent_t* ev : {&sd.fork, &sd.built, &sd.stated, &sd.state_done, &sd.out_done})
     if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
   sd.ready = true;
+  return hipSuccess;
+}
+
+// Per-device facts the fused path needs, queried once: the launch size of
+// the fused kernel (0 when the device cannot run it cooperatively).
+struct DevInfo {
+  int fused_grid[2];  // [out_bf16]
+  bool ready;
+};
+DevInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+hipError_t dev_info(DevInfo** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DevInfo& di = g_dev[dev];
+  if (!di.ready) {
+    int cus = 0, coop = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev)) != hipSuccess) return e;
+    for (int b = 0; b < 2; ++b) di.fused_grid[b] = coop ? gdn::fused_grid(b != 0, cus) : 0;
+    di.ready = true;
+  }
+  *out = &di;
   return hipSuccess;
 }
 
@@ -275,6 +311,18 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
   float* U = reinterpret_cast<float*>(ws + slot);
   void* M_all = ws + 2 * slot;
   const bool ob = out_dtype == GDN_BF16;
+  if (fused_path(in_dtype, d)) {
+    DevInfo* di = nullptr;
+    if (dev_info(&di) != hipSuccess) return GDN_E_HIP;
+    const int grid = di->fused_grid[ob ? 1 : 0];
+    if (grid > 0 && (size_t)gdn::fused_workspace_bytes(d.heads) <= workspace_bytes)
+      return hip_status(timed(rec, s, 1, [&] {
+        return gdn::launch_fused(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                 static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out,
+                                 workspace, d.heads, d.T, (int)d.S, grid, s);
+      }));
+    // this device cannot host the fused kernel: the three-kernel schedule
+  }
   if (fast_path(in_dtype, d.D))
     return hip_status(run_mfma(d, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out, G,
@@ -323,6 +371,7 @@ int gdn_supports_d(int64_t D) { return D >= 16 && D <= 128 && D % 16 == 0; }
 int gdn_path(const gdn_shape* shape, int in_dtype) {
   Dims d;
   if (!valid_dtype(in_dtype) || check_shape(shape, true, &d) != GDN_OK) return -1;
+  if (fused_path(in_dtype, d)) return GDN_PATH_FUSED;
   return fast_path(in_dtype, d.D) ? GDN_PATH_MFMA : GDN_PATH_PLAIN;
 }
 

@@ -34,6 +34,19 @@ hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool pa
                                    bool out_bf16, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
                                    hipStream_t st);
 
+// ---- fused MFMA path: the three stages in one persistent kernel -------------
+// bf16, D == 128.  Heads go in groups of at most 16, one cooperative launch
+// (plus a tiny flag reset) per group.  fused_grid returns the launch size
+// (workgroups resident at once on num_cus CUs) or 0 when the device cannot
+// host the kernel's roles.  The workspace holds a control block, per-head
+// flags and per-head rings (fused_workspace_bytes).
+int64_t fused_workspace_bytes(int64_t heads);
+int fused_grid(bool out_bf16, int num_cus);
+hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
+                        const float* beta, const float* state_in, void* out, bool out_bf16,
+                        float* state_out, void* workspace, int64_t heads, int64_t T, int S, int grid,
+                        hipStream_t st);
+
 // ---- plain float32 path: any supported D, f32 or bf16 inputs ---------------
 hipError_t launch_build_generic(const void* k, const void* v, bool in_bf16, float* G, float* U,
                                 int64_t frames, int S, int D, hipStream_t st);

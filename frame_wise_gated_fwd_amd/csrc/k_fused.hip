@@ -1,0 +1,579 @@
+// The whole frame-wise GDN forward (bf16 inputs, head dim 128) as one
+// persistent, cooperatively launched kernel that overlaps the three stages:
+//   build   G_t = K_t^T K_t, U_t = V_t^T K_t      (parallel over frames)
+//   state   M_t = M_{t-1} gamma_t (I - beta_t G_t) + beta_t U_t   (sequential)
+//   output  O_t = Q_t M_t^T                        (parallel over frames)
+// (the recurrence of "SANA-WM: NVIDIA puts a one-minute world model on a
+// single GPU", zhichai.net, section 1; one step per latent frame, bilibili
+// cv49203711, fourth key point).
+//
+// Why one kernel.  As separate kernels the per-frame maps G_t, U_t and the
+// states M_t make a round trip through HBM (384 KB per head-frame against
+// the 1,126 KB of q, k, v and O).  Here they pass between compute units
+// through the L2 of one XCD and, as long as the rings below stay resident
+// there, never reach HBM.
+//
+// Layout of the work.  MI355X has 8 XCDs, each with its own 4 MB L2.  Head h
+// is handled entirely by XCD h % 8.  A workgroup learns its XCD from the
+// XCC_ID hardware register and takes a ticket from that XCD's counter: the
+// first tickets become state-pass workgroups (kParts per head, each owning
+// kRows rows of M; rows of M evolve independently), the rest become
+// workers that pull build and output items from the XCD's queue.  Two
+// workgroups fit on a CU (every role stays within 256 registers per lane
+// and 80 KB of LDS), and the launch is cooperative, so every workgroup is
+// resident at once; state-pass waves raise their issue priority so that a
+// worker sharing their CU does not stretch the sequential chain.
+//
+// Hand-off between CUs of one XCD.  The L2 is shared by the XCD's CUs and
+// the vector L1 is write-through, so a producer makes data visible by
+// waiting for its stores to be acknowledged (s_waitcnt vmcnt(0)) and then
+// setting a flag; a consumer reads the flag from L2 (device-scope relaxed
+// atomic load), invalidates its own L1 (buffer_inv sc0) and reads the data.
+// Device-scope acquire/release would write back or invalidate whole L2s and
+// is not needed within one XCD.
+//
+// Rings.  Per head: kWG slots for G_t/U_t and kWM slots for M_t, with
+// monotonic per-slot flags (frame index + 1).  The queue of an XCD lists,
+// per head, the builds of frames 0 .. kLag-1, then output(f) and
+// build(f + kLag) alternately, then the last outputs.  Every wait of an item
+// depends only on items earlier in the queue, or on state-pass progress that
+// needs only such items (kLag > kPrefetch + 1, rings large enough), and all
+// workgroups are resident, so the lowest unfinished item can always proceed.
+// Every wait is still bounded: one that runs out sets an error word, every
+// other wait then gives up, the state pass writes NaN to state_out, and the
+// kernel ends.
+#include "frame_build.h"
+#include "frame_output.h"
+#include "gdn_common.h"
+#include "gdn_launch.h"
+#include "gdn_packed.h"
+
+#include <cstdio>
+#include <cstdlib>
+#include <type_traits>
+#include <utility>
+
+namespace gdn {
+namespace {
+
+constexpr int D = 128;
+constexpr int kXcd = 8;
+constexpr int kPrefetch = 1;          // frames the state pass loads ahead
+constexpr int kMaxWG = 96;            // G/U ring slots per head (at most)
+constexpr int kMaxWM = 64;            // M ring slots per head (at most)
+constexpr int kMaxHeadsPerXcd = 2;
+constexpr int kMaxParts = 8;          // kRows >= 16
+constexpr int kLdsW = D + 8;
+constexpr int kChainWaves = 4;
+constexpr uint32_t kSpinLimit = 1u << 22;  // polls (a few seconds) before a wait gives up
+
+
+// Control block (zeroed before every launch) followed by per-head flags.
+struct Ctrl {
+  uint32_t error;
+  uint32_t pad0[31];
+  uint32_t ticket[kXcd];
+  uint32_t pad1[24];
+  uint32_t queue[kXcd];
+  uint32_t pad2[24];
+};
+// Per-head flag block.  The state pass publishes per wave, so no extra
+// workgroup barrier is needed to publish.
+constexpr int kFlagGReady = 0;                                         // [wg]  frame + 1 of the G/U in the slot
+constexpr int kFlagConsumed = kMaxWG;                                  // [parts][waves] frames loaded by the wave
+constexpr int kFlagMReady = kFlagConsumed + kMaxParts * kChainWaves;   // [wm][parts][waves] frame + 1 of M rows
+constexpr int kFlagOutDone = kFlagMReady + kMaxWM * kMaxParts * kChainWaves;  // [wm] frame + 1 staged by the output
+constexpr int kFlagWords = (kFlagOutDone + kMaxWM + 63) / 64 * 64;  // whole cache lines per head
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  // HW_REG_XCC_ID, bits [3:0]
+  return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 0xfu;
+}
+__device__ __forceinline__ uint32_t flag_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void invalidate_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
+
+// Spin (one thread) until pred() holds; false if it never did or another
+// wait already failed.
+template <typename Pred>
+__device__ bool spin_until(Ctrl* ctrl, Pred pred) {
+  for (uint32_t i = 0; i < kSpinLimit; ++i) {
+    if (pred()) return true;
+    if ((i & 63) == 63 && flag_load(&ctrl->error)) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __hip_atomic_store(&ctrl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
+}
+
+struct Args {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* gamma;
+  const float* beta;
+  const float* state_in;
+  void* out;
+  float* state_out;
+  char* ring;       // per head: wg x (Gp, Up) then wm x Mp, 64 KB each
+  Ctrl* ctrl;
+  uint32_t* flags;  // per head kFlagWords
+  int heads, T, S;
+  int wg, wm, lag;  // ring slots for G/U and for M; queue distance from build(t) to output(t)
+  int prio;
+};
+
+__host__ __device__ constexpr int64_t ring_head_bytes(int wg, int wm) {
+  return int64_t{2 * wg + wm} * packed::kFrameBytes;
+}
+
+struct Item {
+  int kind;  // 0 build, 1 output
+  int hl;    // head index within the XCD
+  int t;     // frame
+};
+
+// Item i of an XCD with nh heads.  Slot k = i / nh holds one item per head:
+// builds of frames 0..L-1, then alternately output(f) and build(f + L), then
+// the last L outputs.
+__device__ Item decode_item(int i, int nh, int T, int lag) {
+  const int L = T < lag ? T : lag;
+  const int k = i / nh, hl = i % nh;
+  if (k < L) return {0, hl, k};
+  const int j = k - L;
+  if (j < 2 * (T - L)) return (j & 1) ? Item{0, hl, L + (j >> 1)} : Item{1, hl, j >> 1};
+  return {1, hl, T - L + (j - 2 * (T - L))};
+}
+
+template <int kRows>
+union __attribute__((aligned(16))) Lds {
+  u32x4 build[build_lds_bytes<true>() / 16];
+  uint16_t out[2][D][kOutLdsW];
+  uint16_t chain[2][2][kRows][kLdsW];
+};
+
+// ---------------------------------------------------------------------------
+// state pass: one workgroup owns rows [r0, r0 + kRows) of one head's M
+// ---------------------------------------------------------------------------
+// X = M G on bf16 MFMA in three passes (Ghi*Mhi + Glo*Mhi + Ghi*Mlo), as the
+// stand-alone state pass: computed transposed, X^T = G M^T (G is symmetric),
+// wave w owning G rows 32w .. 32w+31; each lane ends with 4 consecutive
+// columns of kRows/16 rows of M.  Each wave keeps its own flags: at the top
+// of step t it waits only for memory operations it issued during step t-1
+// (M_{t-1} stores, the loads of frame t, the flag loads for this step),
+// publishes M_{t-1} and its progress, and checks the flags it loaded a step
+// ahead.  The only barrier per step is the LDS hand-off of M between the
+// waves.  A wave whose wait fails sets `abort` in LDS; after the barrier
+// every wave sees it and all leave together.
+template <int kRows>
+__device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int head, int part) {
+  constexpr int kParts = D / kRows;
+  constexpr int kRB = kRows / 16;
+  uint16_t (*Ml)[2][kRows][kLdsW] = lds.chain;
+  const int T = a.T;
+  const int r0 = part * kRows;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63;
+  const int n = l & 15, g = l >> 4;
+  uint32_t* fl = a.flags + (int64_t)head * kFlagWords;
+  const int kWG = a.wg, kWM = a.wm;
+  char* ring = a.ring + head * ring_head_bytes(kWG, kWM);
+  auto gp_slot = [&](int t) { return ring + (int64_t)(2 * (t % kWG)) * packed::kFrameBytes; };
+  auto up_slot = [&](int t) { return ring + (int64_t)(2 * (t % kWG) + 1) * packed::kFrameBytes; };
+  auto mp_slot = [&](int t) { return ring + (int64_t)(2 * kWG + t % kWM) * packed::kFrameBytes; };
+  uint32_t* my_consumed = fl + kFlagConsumed + part * kChainWaves + w;
+  auto my_mready = [&](int t) { return fl + kFlagMReady + ((t % kWM) * kParts + part) * kChainWaves + w; };
+
+  auto row_of = [&](int rb) { return r0 + 16 * rb + n; };
+  auto col_of = [&](int cb) { return 32 * w + 16 * cb + 4 * g; };
+  const int64_t hoff = (int64_t)head * D * D;
+
+  f32x4 Mreg[2][kRB];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+      Mreg[cb][rb] = a.state_in ? *reinterpret_cast<const f32x4*>(a.state_in + hoff + row_of(rb) * D + col_of(cb))
+                                : (f32x4){0.f, 0.f, 0.f, 0.f};
+  u32x2 mh[2][kRB], ml[2][kRB];
+  auto split_m = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const u32x2 p0 = split2(Mreg[cb][rb][0], Mreg[cb][rb][1]);
+        const u32x2 p1 = split2(Mreg[cb][rb][2], Mreg[cb][rb][3]);
+        mh[cb][rb] = (u32x2){p0.x, p1.x};
+        ml[cb][rb] = (u32x2){p0.y, p1.y};
+      }
+  };
+  auto put_lds = [&](int buf) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        *reinterpret_cast<u32x2*>(&Ml[buf][0][16 * rb + n][col_of(cb)]) = mh[cb][rb];
+        *reinterpret_cast<u32x2*>(&Ml[buf][1][16 * rb + n][col_of(cb)]) = ml[cb][rb];
+      }
+  };
+  split_m();
+  put_lds(0);
+  // bcast[0] is the abort word: zeroed by the kernel entry before its
+  // barrier, set to 1 by any wave whose wait fails, and read by every wave
+  // only after the next barrier, so all waves leave the loop together.
+
+  // gamma/beta: 64-frame windows per lane, read with readlane (scalar loads
+  // would share the LDS wait counter)
+  const float* gh = a.gamma + (int64_t)head * T;
+  const float* bh = a.beta + (int64_t)head * T;
+  auto win_load = [&](int t0, float& gv, float& bv) {
+    const int tt = t0 + l;
+    gv = tt < T ? gh[tt] : 0.f;
+    bv = tt < T ? bh[tt] : 0.f;
+  };
+  float gwin, bwin, gnxt, bnxt;
+  win_load(0, gwin, bwin);
+  win_load(64, gnxt, bnxt);
+
+  // one-frame register ring: this wave's G_t rows (hi/lo) and U_t elements
+  u32x4 rgh[2][4], rgl[2][4];
+  f32x4 ru[2][kRB];
+  auto load_frame = [&](int t) {
+    if (t >= T) return;
+    const char* Gp = gp_slot(t);
+    const char* Up = up_slot(t);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int unit = ((2 * w + cb) * 4 + kb) * 2;
+        rgh[cb][kb] = *reinterpret_cast<const u32x4*>(Gp + (unit << 10) + 16 * l);
+        rgl[cb][kb] = *reinterpret_cast<const u32x4*>(Gp + ((unit + 1) << 10) + 16 * l);
+      }
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+        ru[cb][rb] = *reinterpret_cast<const f32x4*>(Up + ((((r0 >> 4) + rb) * 8 + 2 * w + cb) << 10) + 16 * l);
+  };
+
+  // Prologue: wait for build(0) (every wave for itself) and load frame 0.
+  bool ok = true;
+  if (l == 0) ok = spin_until(a.ctrl, [&] { return flag_load(fl + kFlagGReady) >= 1u; });
+  ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+  if (!ok && l == 0) bcast[0] = 1;
+  invalidate_l1();
+  if (ok) load_frame(0);
+  uint32_t gflag = 0, oflag = 0;  // flags for the next step, loaded a step ahead (lane 0)
+  if (l == 0 && kPrefetch < T) gflag = flag_load(fl + kFlagGReady + kPrefetch % kWG);
+  lds_barrier();
+  ok = bcast[0] == 0;  // the same on every wave
+
+  for (int t = 0; t < T && ok; ++t) {
+    // Everything this wave issued in step t-1 is complete after this wait.
+    wait_stores();
+    bool good = true;
+    if (l == 0) {
+      if (t > 0) flag_store(my_mready(t - 1), (uint32_t)t);
+      flag_store(my_consumed, (uint32_t)(t + kPrefetch < T ? t + kPrefetch : T));
+      const int tn = t + kPrefetch;
+      if (tn < T && gflag < (uint32_t)(tn + 1))
+        good = spin_until(a.ctrl, [&] { return flag_load(fl + kFlagGReady + tn % kWG) >= (uint32_t)(tn + 1); });
+      if (good && t >= kWM && oflag < (uint32_t)(t - kWM + 1))
+        good = spin_until(a.ctrl, [&] { return flag_load(fl + kFlagOutDone + t % kWM) >= (uint32_t)(t - kWM + 1); });
+      // flags for step t + 1, in flight during this step
+      if (t + 1 + kPrefetch < T) gflag = flag_load(fl + kFlagGReady + (t + 1 + kPrefetch) % kWG);
+      if (t + 1 >= kWM) oflag = flag_load(fl + kFlagOutDone + (t + 1) % kWM);
+    }
+    good = __builtin_amdgcn_readfirstlane((int)good) != 0;
+    if (good) {
+      const int buf = t & 1;
+      const int tw = t & 63;
+      const float gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwin), tw));
+      const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwin), tw));
+      if (tw == 63) {
+        gwin = gnxt;
+        bwin = bnxt;
+        win_load(t + 65, gnxt, bnxt);
+      }
+      u32x4 ahi[2][4], alo[2][4];
+      f32x4 ureg[2][kRB];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          ahi[cb][kb] = rgh[cb][kb];
+          alo[cb][kb] = rgl[cb][kb];
+        }
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) ureg[cb][rb] = ru[cb][rb];
+      }
+      // refill the ring with frame t + 1 (its build is done)
+      invalidate_l1();
+      load_frame(t + kPrefetch);
+
+      f32x4 acc[2][kRB];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) acc[cb][rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        u32x4 bhi[kRB], blo[kRB];
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          bhi[rb] = *reinterpret_cast<const u32x4*>(&Ml[buf][0][16 * rb + n][32 * kb + 8 * g]);
+          blo[rb] = *reinterpret_cast<const u32x4*>(&Ml[buf][1][16 * rb + n][32 * kb + 8 * g]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(ahi[cb][kb], bhi[rb], acc[cb][rb]);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(alo[cb][kb], bhi[rb], acc[cb][rb]);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(ahi[cb][kb], blo[rb], acc[cb][rb]);
+      }
+      const float gb = gm * bt;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Mreg[cb][rb][i] = fmaf(gm, Mreg[cb][rb][i], fmaf(-gb, acc[cb][rb][i], bt * ureg[cb][rb][i]));
+      split_m();
+      put_lds(buf ^ 1);
+      // this wave's rows of M_t into the ring (the slot's previous frame is staged)
+      char* Mp = mp_slot(t);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          *reinterpret_cast<u32x2*>(Mp + packed::m_chunk(row_of(rb), col_of(cb), 0)) = mh[cb][rb];
+          *reinterpret_cast<u32x2*>(Mp + packed::m_chunk(row_of(rb), col_of(cb), 1)) = ml[cb][rb];
+        }
+    } else if (l == 0) {
+      bcast[0] = 1;
+    }
+    lds_barrier();
+    ok = bcast[0] == 0;
+  }
+  wait_stores();
+  if (ok && l == 0) {
+    flag_store(my_mready(T - 1), (uint32_t)T);
+    flag_store(my_consumed, (uint32_t)T);
+  }
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+      *reinterpret_cast<f32x4*>(a.state_out + hoff + row_of(rb) * D + col_of(cb)) =
+          ok ? Mreg[cb][rb] : (f32x4){nan, nan, nan, nan};
+}
+
+// ---------------------------------------------------------------------------
+// workers
+// ---------------------------------------------------------------------------
+template <bool kOutBf16, int kRows>
+__device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int xcd, int nh) {
+  constexpr int kParts = D / kRows;
+  const int T = a.T, S = a.S;
+  const int kWG = a.wg, kWM = a.wm;
+  const int total = 2 * nh * T;
+  const int tid = threadIdx.x;
+  for (;;) {
+    if (tid == 0) bcast[2] = atomicAdd(&a.ctrl->queue[xcd], 1u);
+    __syncthreads();
+    const int i = (int)bcast[2];
+    __syncthreads();  // everyone has read the item before thread 0 overwrites it
+    if (i >= total) return;
+    const Item it = decode_item(i, nh, T, a.lag);
+    const int head = it.hl * kXcd + xcd;
+    uint32_t* fl = a.flags + (int64_t)head * kFlagWords;
+    char* ring = a.ring + head * ring_head_bytes(kWG, kWM);
+    const int64_t fr = (int64_t)head * T + it.t;
+    if (it.kind == 0) {
+      // build(t): every state-pass wave must have loaded the slot's previous frame
+      if (tid == 0) {
+        const uint32_t need = it.t >= kWG ? (uint32_t)(it.t - kWG + 1) : 0u;
+        bcast[3] = spin_until(a.ctrl, [&] {
+          uint32_t m = 0xffffffffu;
+#pragma unroll
+          for (int p = 0; p < kParts * kChainWaves; ++p) {
+            const uint32_t c = flag_load(fl + kFlagConsumed + p);
+            m = c < m ? c : m;
+          }
+          return m >= need;
+        });
+      }
+      __syncthreads();
+      if (!bcast[3]) return;
+      char* gp = ring + (int64_t)(2 * (it.t % kWG)) * packed::kFrameBytes;
+      float* up = reinterpret_cast<float*>(ring + (int64_t)(2 * (it.t % kWG) + 1) * packed::kFrameBytes);
+      build_frame<true, 1>(a.k + fr * S * D, a.v + fr * S * D, S, lds.build, gp, up);
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) flag_store(fl + kFlagGReady + it.t % kWG, (uint32_t)(it.t + 1));
+    } else {
+      // output(t): every state-pass wave's rows of M_t must be in the ring
+      if (tid == 0) {
+        bcast[3] = spin_until(a.ctrl, [&] {
+          uint32_t m = 0xffffffffu;
+#pragma unroll
+          for (int p = 0; p < kParts * kChainWaves; ++p) {
+            const uint32_t c = flag_load(fl + kFlagMReady + (it.t % kWM) * kParts * kChainWaves + p);
+            m = c < m ? c : m;
+          }
+          return m >= (uint32_t)(it.t + 1);
+        });
+      }
+      __syncthreads();
+      if (!bcast[3]) return;
+      invalidate_l1();
+      const char* mp = ring + (int64_t)(2 * kWG + it.t % kWM) * packed::kFrameBytes;
+      void* of = static_cast<char*>(a.out) + fr * S * D * (kOutBf16 ? 2 : 4);
+      output_frame<true, kOutBf16, 1>(a.q + fr * S * D, mp, of, S, lds.out, [&] {
+        if (tid == 0) flag_store(fl + kFlagOutDone + it.t % kWM, (uint32_t)(it.t + 1));
+      });
+    }
+  }
+}
+
+template <bool kOutBf16, int kRows>
+__global__ __launch_bounds__(256, 2) void k_fused(Args a) {
+  constexpr int kParts = D / kRows;
+  __shared__ Lds<kRows> lds;
+  __shared__ uint32_t bcast[4];
+  const uint32_t xcd = xcc_id();
+  if (xcd >= (uint32_t)kXcd) return;  // not an MI355X XCD id: take no part
+  const int nh = (int)xcd < a.heads ? (a.heads - (int)xcd + kXcd - 1) / kXcd : 0;
+  if (threadIdx.x == 0) {
+    bcast[0] = 0;
+    bcast[1] = atomicAdd(&a.ctrl->ticket[xcd], 1u);
+  }
+  __syncthreads();
+  const int ticket = (int)bcast[1];
+  __syncthreads();
+  if (nh == 0) return;
+  if (ticket < nh * kParts) {
+    if (a.prio) __builtin_amdgcn_s_setprio(3);
+    state_role<kRows>(a, lds, bcast, (ticket / kParts) * kXcd + (int)xcd, ticket % kParts);
+  } else {
+    worker_role<kOutBf16, kRows>(a, lds, bcast, (int)xcd, nh);
+  }
+}
+
+__global__ void k_fused_init(uint32_t* words, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) words[i] = 0;
+}
+
+int fused_rows() {
+  static const int r = [] { const char* e = std::getenv("GDN_FUSED_ROWS"); return e && std::atoi(e) == 32 ? 32 : 16; }();
+  return r;
+}
+
+template <bool kOutBf16>
+const void* fused_kernel() {
+  return fused_rows() == 32 ? reinterpret_cast<const void*>(&k_fused<kOutBf16, 32>)
+                            : reinterpret_cast<const void*>(&k_fused<kOutBf16, 16>);
+}
+
+// Ring shape: G/U slots, M slots and the queue distance from build(t) to
+// output(t).  The queue distance must cover a build's duration in chain
+// steps; every wait then depends only on earlier items as long as
+// lag > kPrefetch + 1 and lag <= wg + wm (see the ring notes above).
+struct RingShape {
+  int wg, wm, lag;
+};
+RingShape ring_shape() {
+  static const RingShape r = [] {
+    RingShape x{40, 16, 32};
+    if (const char* e = std::getenv("GDN_FUSED_RING")) {
+      RingShape y{};
+      if (std::sscanf(e, "%d,%d,%d", &y.wg, &y.wm, &y.lag) == 3 && y.wg >= kPrefetch + 2 && y.wg <= kMaxWG &&
+          y.wm >= 2 && y.wm <= kMaxWM && y.lag > kPrefetch + 1 && y.lag <= y.wg + y.wm)
+        x = y;
+    }
+    return x;
+  }();
+  return r;
+}
+
+}  // namespace
+
+int64_t fused_workspace_bytes(int64_t heads) {
+  const int64_t h = heads < kXcd * kMaxHeadsPerXcd ? heads : kXcd * kMaxHeadsPerXcd;
+  const int64_t ctrl = ((int64_t)sizeof(Ctrl) + kXcd * kMaxHeadsPerXcd * kFlagWords * 4 + 255) & ~int64_t{255};
+  const RingShape r = ring_shape();
+  return ctrl + h * ring_head_bytes(r.wg, r.wm);
+}
+
+int fused_grid(bool out_bf16, int num_cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<false>(), 256, 0) != hipSuccess)
+    return 0;
+  int per_cu16 = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu16, fused_kernel<true>(), 256, 0) != hipSuccess)
+    return 0;
+  const int pc = out_bf16 ? per_cu16 : per_cu;
+  // every XCD needs its state-pass workgroups and at least as many workers
+  const int grid = pc * num_cus;
+  return grid / kXcd >= 2 * kMaxHeadsPerXcd * (D / fused_rows()) ? grid : 0;
+}
+
+hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
+                        const float* beta, const float* state_in, void* out, bool out_bf16,
+                        float* state_out, void* workspace, int64_t heads, int64_t T, int S, int grid,
+                        hipStream_t st) {
+  char* ws = static_cast<char*>(workspace);
+  const int64_t group = kXcd * kMaxHeadsPerXcd;
+  const int64_t ctrl_bytes = (int64_t)sizeof(Ctrl) + group * kFlagWords * 4;
+  const int nwords = (int)(ctrl_bytes / 4);
+  // heads are independent: groups of at most 16 heads, one launch each
+  for (int64_t h0 = 0; h0 < heads; h0 += group) {
+    const int64_t nh = heads - h0 < group ? heads - h0 : group;
+    Args a;
+    a.q = q + h0 * T * S * D;
+    a.k = k + h0 * T * S * D;
+    a.v = v + h0 * T * S * D;
+    a.gamma = gamma + h0 * T;
+    a.beta = beta + h0 * T;
+    a.state_in = state_in ? state_in + h0 * D * D : nullptr;
+    a.out = static_cast<char*>(out) + h0 * T * S * D * (out_bf16 ? 2 : 4);
+    a.state_out = state_out + h0 * D * D;
+    a.ctrl = reinterpret_cast<Ctrl*>(ws);
+    a.flags = reinterpret_cast<uint32_t*>(ws + sizeof(Ctrl));
+    a.ring = ws + ((ctrl_bytes + 255) & ~int64_t{255});
+    a.heads = (int)nh;
+    a.T = (int)T;
+    a.S = S;
+    const RingShape r = ring_shape();
+    a.wg = r.wg;
+    a.wm = r.wm;
+    a.lag = r.lag;
+    static const int prio = [] { const char* e = std::getenv("GDN_FUSED_PRIO"); return e ? std::atoi(e) : 1; }();
+    a.prio = prio;
+    hipLaunchKernelGGL(k_fused_init, dim3((nwords + 255) / 256), dim3(256), 0, st,
+                       reinterpret_cast<uint32_t*>(ws), nwords);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    void* params[] = {&a};
+    e = hipLaunchCooperativeKernel(out_bf16 ? fused_kernel<true>() : fused_kernel<false>(), dim3((unsigned)grid),
+                                   dim3(256), params, 0, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace gdn

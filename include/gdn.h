@@ -83,9 +83,10 @@ int gdn_supports_d(int64_t D);
 /*
  * Which implementation gdn_frame_fwd uses for this shape and input dtype (a
  * pure function of its arguments):
- *   GDN_PATH_MFMA   bf16, D == 128: three bf16-MFMA kernels (build, state
- *                   pass, output) with the per-frame intermediates in the
- *                   workspace.  When T > 64 the frames are cut into
+ *   GDN_PATH_MFMA   bf16, D == 128, T <= 64 (and longer sequences when the
+ *                   fused kernel below is unavailable): three bf16-MFMA
+ *                   kernels (build, state pass, output) with the per-frame
+ *                   intermediates in the workspace.  When T > 64 the frames are cut into
  *                   ceil(T / 64) segments of nearly equal length and the
  *                   build of segment i+1, the state pass of segment i and
  *                   the output of segment i-1 overlap: builds run on
@@ -96,13 +97,25 @@ int gdn_supports_d(int64_t D);
  *                   on `stream` like a single kernel.  The environment
  *                   variable GDN_SEGMENT_FRAMES (read once per process)
  *                   replaces the 64.  Otherwise all three run on `stream`;
+ *   GDN_PATH_FUSED  bf16, D == 128, T > 64: build, state pass and output in
+ *                   one persistent kernel per group of at most 16 heads,
+ *                   launched cooperatively on `stream` (every workgroup
+ *                   resident at once) after a tiny flag-reset kernel.  Each
+ *                   head runs on one XCD and its per-frame G_t, U_t, M_t
+ *                   pass between compute units through that XCD's L2 instead
+ *                   of HBM.  Every internal wait is bounded: if one runs out
+ *                   (it cannot while all workgroups are resident), state_out
+ *                   of the affected heads is NaN.  On a device that cannot
+ *                   launch it cooperatively at full size, or with the
+ *                   environment variable GDN_FUSED=0 (read once), these
+ *                   shapes take GDN_PATH_MFMA;
  *   GDN_PATH_PLAIN  every other supported case: three float32 kernels on
  *                   `stream`;
  *   -1              invalid arguments.
  * Results do not depend on the segmentation: the state pass carries the
  * float32 state exactly from one segment to the next.
  */
-enum { GDN_PATH_PLAIN = 0, GDN_PATH_MFMA = 1 };
+enum { GDN_PATH_PLAIN = 0, GDN_PATH_MFMA = 1, GDN_PATH_FUSED = 2 };
 int gdn_path(const gdn_shape* shape, int in_dtype);
 
 /*
@@ -131,7 +144,8 @@ int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype,
  * gdn_frame_fwd, plus per-kernel durations: a pair of HIP events is recorded
  * around every kernel launch of the call, on the stream that launch uses;
  * the call waits for `stream` (which the call joins back to) and writes,
- * for kernel kinds 0 = build, 1 = state pass, 2 = output, the summed
+ * for kernel kinds 0 = build, 1 = state pass (the whole fused kernel on the
+ * fused path, flag reset included), 2 = output, the summed
  * elapsed milliseconds to
  * kernel_ms[kind] and the number of launches to launches[kind] (both host
  * arrays of 3).  Launches of different kinds may overlap in time, so the
