@@ -36,6 +36,7 @@ SIGNATURES = {
     "gdn_status_str": (ctypes.c_char_p, [_i]),
     "gdn_supports_d": (_i, [ctypes.c_int64]),
     "gdn_path": (_i, [_PS, _i]),
+    "gdn_set_fused": (_i, [_i]),
     "gdn_workspace_bytes": (_sz, [_PS, _i]),
     "gdn_frame_fwd": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp]),
     "gdn_frame_fwd_timed": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp,

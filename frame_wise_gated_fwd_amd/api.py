@@ -53,6 +53,12 @@ def shape_of(q: torch.Tensor) -> Shape:
     return Shape(B, H, T, S, D)
 
 
+def set_fused(enabled: bool) -> bool:
+    """gdn_set_fused: enable or disable the fused kernel for later calls
+    (process-wide); returns the previous setting."""
+    return bool(lib().gdn_set_fused(1 if enabled else 0))
+
+
 def workspace_bytes(B: int, H: int, T: int, S: int, D: int, in_dtype: torch.dtype) -> int:
     shp = Shape(B, H, T, S, D)
     return int(lib().gdn_workspace_bytes(ctypes.byref(shp), _dtype_code(in_dtype)))

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdlib>
 #include <limits>
 #include <mutex>
@@ -97,9 +98,16 @@ bool fast_path(int in_dtype, int64_t D) { return in_dtype == GDN_BF16 && D == 12
 // The fused kernel takes bf16, D == 128 sequences longer than one segment
 // of the three-kernel schedule (GDN_FUSED=0 in the environment, read once,
 // turns it off).
+std::atomic<int>& fused_enabled() {
+  static std::atomic<int> on{[] {
+    const char* e = std::getenv("GDN_FUSED");
+    return e && std::atoi(e) == 0 ? 0 : 1;
+  }()};
+  return on;
+}
+
 bool fused_path(int in_dtype, const Dims& d) {
-  static const bool off = [] { const char* e = std::getenv("GDN_FUSED"); return e && std::atoi(e) == 0; }();
-  return !off && fast_path(in_dtype, d.D) && d.T > kFusedMinT;
+  return fused_enabled().load() && fast_path(in_dtype, d.D) && d.T > kFusedMinT;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
@@ -365,6 +373,8 @@ const char* gdn_status_str(int s) {
     default: return "unknown status";
   }
 }
+
+int gdn_set_fused(int enabled) { return fused_enabled().exchange(enabled ? 1 : 0); }
 
 int gdn_supports_d(int64_t D) { return D >= 16 && D <= 128 && D % 16 == 0; }
 

@@ -81,6 +81,15 @@ const char* gdn_status_str(int status);
 int gdn_supports_d(int64_t D);
 
 /*
+ * Enables (nonzero) or disables (0) the fused kernel (GDN_PATH_FUSED below)
+ * for calls made after it returns, process-wide; returns the previous
+ * setting.  The default is enabled unless the environment variable
+ * GDN_FUSED is 0 when the library first needs the setting.  Both paths give
+ * bit-identical results; the switch exists for comparison and testing.
+ */
+int gdn_set_fused(int enabled);
+
+/*
  * Which implementation gdn_frame_fwd uses for this shape and input dtype (a
  * pure function of its arguments):
  *   GDN_PATH_MFMA   bf16, D == 128, T <= 64 (and longer sequences when the
@@ -106,9 +115,9 @@ int gdn_supports_d(int64_t D);
  *                   of HBM.  Every internal wait is bounded: if one runs out
  *                   (it cannot while all workgroups are resident), state_out
  *                   of the affected heads is NaN.  On a device that cannot
- *                   launch it cooperatively at full size, or with the
- *                   environment variable GDN_FUSED=0 (read once), these
- *                   shapes take GDN_PATH_MFMA;
+ *                   launch it cooperatively at full size, or while the
+ *                   fused kernel is disabled (gdn_set_fused), these shapes
+ *                   take GDN_PATH_MFMA;
  *   GDN_PATH_PLAIN  every other supported case: three float32 kernels on
  *                   `stream`;
  *   -1              invalid arguments.

@@ -61,6 +61,20 @@ def test_path_selection():
     assert L.gdn_path(None, BF16) == -1
 
 
+def test_fused_switch_selects_path():
+    L = F.lib()
+    s = _shape(1, 16, 961, 880, 128)
+    prev = L.gdn_set_fused(0)
+    try:
+        assert L.gdn_path(ctypes.byref(s), BF16) == 1
+        assert L.gdn_set_fused(1) == 0
+        assert L.gdn_path(ctypes.byref(s), BF16) == 2
+        assert F.set_fused(False) is True
+        assert L.gdn_path(ctypes.byref(s), BF16) == 1
+    finally:
+        L.gdn_set_fused(prev)
+
+
 def test_workspace_bytes():
     L = F.lib()
     for s in (_shape(4, 16, 961, 880, 128), _shape(1, 16, 961, 880, 128)):

@@ -193,12 +193,20 @@ def test_forward_stress_b4_sampled():
 # ---------------------------------------------------------------------------
 # the segmented, multi-stream schedule of the MFMA path
 # ---------------------------------------------------------------------------
-def test_segmented_forward_equals_stage_chain_bitwise():
-    """T = 70 runs as 3 overlapped segments on three streams; the stage entry
+@pytest.fixture
+def three_kernel_path():
+    """Route long sequences through the three-kernel segmented schedule."""
+    prev = F.set_fused(False)
+    yield
+    F.set_fused(prev)
+
+
+def test_segmented_forward_equals_stage_chain_bitwise(three_kernel_path):
+    """T = 140 runs as 3 overlapped segments on three streams; the stage entry
     points run each kernel once over all frames on one stream, exchanging
     float32 row-major maps.  Both feed the MFMAs the same bf16 hi/lo operands,
     so the results agree bit for bit."""
-    w = CLIP_5S.with_(T=70, H=3, S=200, name="clip_t70_s200", state_std=0.02)
+    w = CLIP_5S.with_(T=140, H=3, S=200, name="clip_t140_s200", state_std=0.02)
     x = device_inputs(w, DEV)
     out, st = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
     G, U = F.build_maps(x["k"], x["v"])
@@ -207,6 +215,27 @@ def test_segmented_forward_equals_stage_chain_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(st, st2)
     assert torch.equal(out, out2)
+
+
+def test_fused_kernel_equals_three_kernel_path_bitwise():
+    """The fused kernel (one cooperative launch, rings on chip) and the
+    three-kernel schedule run the same per-element arithmetic: identical
+    results on the 5 s workload (16 heads, 81 frames) and on 20 heads (two
+    head groups, the second partial) with a bf16 output."""
+    import ctypes
+    from frame_wise_gated_fwd_amd._lib import Shape, lib, GDN_BF16
+    for w, odt in ((CLIP_5S.with_(state_std=0.02, name="clip5s_state"), torch.float32),
+                   (CLIP_5S.with_(H=20, T=70, S=300, name="clip_h20", state_std=0.02), torch.bfloat16)):
+        assert lib().gdn_path(ctypes.byref(Shape(w.B, w.H, w.T, w.S, w.D)), GDN_BF16) == 2
+        x = device_inputs(w, DEV)
+        o1, s1 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"], out_dtype=odt)
+        prev = F.set_fused(False)
+        try:
+            o2, s2 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"], out_dtype=odt)
+        finally:
+            F.set_fused(prev)
+        torch.cuda.synchronize()
+        assert torch.equal(s1, s2) and torch.equal(o1, o2), w.name
 
 
 def test_single_frame_calls_equal_one_call_bitwise():
@@ -231,10 +260,20 @@ def test_single_frame_calls_equal_one_call_bitwise():
     _forward_parity(w, frames=[0, 5, 11])
 
 
-def test_segmented_forward_is_ordered_on_a_user_stream():
-    """Work queued on the caller's stream before the call is seen by every
-    segment, and work queued after it runs after the last one."""
-    w = CLIP_5S.with_(T=70, H=3, S=200, name="clip_t70_s200", state_std=0.02)
+@pytest.mark.parametrize("fused", [True, False])
+def test_forward_is_ordered_on_a_user_stream(fused):
+    """Work queued on the caller's stream before the call is seen by the
+    whole call (every segment, or the fused kernel), and work queued after
+    it runs after the call's last kernel."""
+    prev = F.set_fused(fused)
+    try:
+        _ordered_on_user_stream()
+    finally:
+        F.set_fused(prev)
+
+
+def _ordered_on_user_stream():
+    w = CLIP_5S.with_(T=140, H=3, S=200, name="clip_t140_s200", state_std=0.02)
     x = device_inputs(w, DEV)
     ref_o, ref_s = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
     torch.cuda.synchronize()
