@@ -1,6 +1,10 @@
 // C ABI of the frame-wise GDN forward: argument validation, workspace layout
 // and dispatch to the HIP kernels.  Declarations and the contract are in
 // include/gdn.h.
+//
+// Layout of this file: argument checks; per-device state (timing events,
+// the side streams of the segmented schedule, fused-kernel launch sizes);
+// the two schedules of the MFMA path; the extern "C" entry points.
 #include "gdn.h"
 
 #include <hip/hip_runtime.h>
@@ -96,8 +100,8 @@ bool aliasing_ok(const Range* outs, int nout, const Range* ins, int nin,
 bool fast_path(int in_dtype, int64_t D) { return in_dtype == GDN_BF16 && D == 128; }
 
 // The fused kernel takes bf16, D == 128 sequences longer than one segment
-// of the three-kernel schedule (GDN_FUSED=0 in the environment, read once,
-// turns it off).
+// of the three-kernel schedule while it is enabled: gdn_set_fused switches
+// it; GDN_FUSED=0 in the environment makes the default "disabled".
 std::atomic<int>& fused_enabled() {
   static std::atomic<int> on{[] {
     const char* e = std::getenv("GDN_FUSED");
@@ -114,10 +118,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t{255}; }
 
-}  // namespace
-
-namespace {
-
+// ---------------------------------------------------------------------------
+// per-device state, created on first use and kept for the life of the process
+// ---------------------------------------------------------------------------
 constexpr int kMaxDevices = 64;
 
 // Per-launch HIP events of gdn_frame_fwd_timed: a pair around every kernel,
@@ -207,15 +210,9 @@ int64_t segment_frames() {
   return f;
 }
 
-int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
-                   const void* v, const float* gamma, const float* beta, const float* state_in,
-                   void* out, float* state_out, void* workspace, size_t workspace_bytes,
-                   void* stream, Recorder* rec);
-
-}  // namespace
-
-namespace {
-
+// ---------------------------------------------------------------------------
+// schedules
+// ---------------------------------------------------------------------------
 // One kernel launch, bracketed by timing events when rec is set.
 template <typename F>
 hipError_t timed(Recorder* rec, hipStream_t st, int kind, F&& launch) {
@@ -356,6 +353,9 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// entry points
+// ---------------------------------------------------------------------------
 extern "C" {
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
@@ -449,7 +449,6 @@ int gdn_output(const gdn_shape* shape, int in_dtype, int out_dtype, const void* 
   return hip_status(gdn::launch_output_generic(q, in_dtype == GDN_BF16, M_all, out, ob, d.frames,
                                                (int)d.S, (int)d.D, s));
 }
-
 
 int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
                   const void* v, const float* gamma, const float* beta, const float* state_in,

@@ -10,8 +10,8 @@
 // Why one kernel.  As separate kernels the per-frame maps G_t, U_t and the
 // states M_t make a round trip through HBM (384 KB per head-frame against
 // the 1,126 KB of q, k, v and O).  Here they pass between compute units
-// through the L2 of one XCD and, as long as the rings below stay resident
-// there, never reach HBM.
+// through the L2 of one XCD and the memory-side cache behind it instead of
+// making a round trip to HBM between kernels.
 //
 // Layout of the work.  MI355X has 8 XCDs, each with its own 4 MB L2.  Head h
 // is handled entirely by XCD h % 8.  A workgroup learns its XCD from the
@@ -32,12 +32,12 @@
 // Device-scope acquire/release would write back or invalidate whole L2s and
 // is not needed within one XCD.
 //
-// Rings.  Per head: kWG slots for G_t/U_t and kWM slots for M_t, with
-// monotonic per-slot flags (frame index + 1).  The queue of an XCD lists,
-// per head, the builds of frames 0 .. kLag-1, then output(f) and
-// build(f + kLag) alternately, then the last outputs.  Every wait of an item
+// Rings.  Per head: kRing.wg slots for G_t/U_t and kRing.wm slots for M_t,
+// with monotonic per-slot flags (frame index + 1).  The queue of an XCD
+// lists, per head, the builds of frames 0 .. lag-1, then output(f) and
+// build(f + lag) alternately, then the last outputs.  Every wait of an item
 // depends only on items earlier in the queue, or on state-pass progress that
-// needs only such items (kLag > kPrefetch + 1, rings large enough), and all
+// needs only such items (lag > kPrefetch + 1, lag <= wg + wm), and all
 // workgroups are resident, so the lowest unfinished item can always proceed.
 // Every wait is still bounded: one that runs out sets an error word, every
 // other wait then gives up, the state pass writes NaN to state_out, and the
@@ -48,8 +48,6 @@
 #include "gdn_launch.h"
 #include "gdn_packed.h"
 
-#include <cstdio>
-#include <cstdlib>
 #include <type_traits>
 #include <utility>
 
@@ -59,14 +57,26 @@ namespace {
 constexpr int D = 128;
 constexpr int kXcd = 8;
 constexpr int kPrefetch = 1;          // frames the state pass loads ahead
-constexpr int kMaxWG = 96;            // G/U ring slots per head (at most)
-constexpr int kMaxWM = 64;            // M ring slots per head (at most)
 constexpr int kMaxHeadsPerXcd = 2;
 constexpr int kMaxParts = 8;          // kRows >= 16
 constexpr int kLdsW = D + 8;
 constexpr int kChainWaves = 4;
 constexpr uint32_t kSpinLimit = 1u << 22;  // polls (a few seconds) before a wait gives up
 
+// Ring shape: G/U slots, M slots and the queue distance from build(t) to
+// output(t).  The queue distance must cover a build's duration in state-pass
+// steps (a build takes ~45 us, a step ~4 us); every wait then depends only
+// on earlier items as long as lag > kPrefetch + 1 and lag <= wg + wm (see
+// the ring notes above).  Measured on the 60 s workload: 32-64 G/U slots all
+// run within 2 %; 8 slots starve the state pass (8-10 ms); 96 overflow the
+// memory-side cache (4.8 ms).
+struct RingShape {
+  int wg, wm, lag;
+};
+constexpr RingShape kRing{40, 16, 32};
+static_assert(kRing.wg >= kPrefetch + 2 && kRing.wm >= 2 &&
+                  kRing.lag > kPrefetch + 1 && kRing.lag <= kRing.wg + kRing.wm,
+              "ring shape could stall the queue");
 
 // Control block (zeroed before every launch) followed by per-head flags.
 struct Ctrl {
@@ -80,10 +90,10 @@ struct Ctrl {
 // Per-head flag block.  The state pass publishes per wave, so no extra
 // workgroup barrier is needed to publish.
 constexpr int kFlagGReady = 0;                                         // [wg]  frame + 1 of the G/U in the slot
-constexpr int kFlagConsumed = kMaxWG;                                  // [parts][waves] frames loaded by the wave
+constexpr int kFlagConsumed = kRing.wg;                                 // [parts][waves] frames loaded by the wave
 constexpr int kFlagMReady = kFlagConsumed + kMaxParts * kChainWaves;   // [wm][parts][waves] frame + 1 of M rows
-constexpr int kFlagOutDone = kFlagMReady + kMaxWM * kMaxParts * kChainWaves;  // [wm] frame + 1 staged by the output
-constexpr int kFlagWords = (kFlagOutDone + kMaxWM + 63) / 64 * 64;  // whole cache lines per head
+constexpr int kFlagOutDone = kFlagMReady + kRing.wm * kMaxParts * kChainWaves;  // [wm] frame + 1 staged by the output
+constexpr int kFlagWords = (kFlagOutDone + kRing.wm + 63) / 64 * 64;  // whole cache lines per head
 
 __device__ __forceinline__ uint32_t xcc_id() {
   // HW_REG_XCC_ID, bits [3:0]
@@ -120,12 +130,10 @@ struct Args {
   const float* state_in;
   void* out;
   float* state_out;
-  char* ring;       // per head: wg x (Gp, Up) then wm x Mp, 64 KB each
+  char* ring;       // per head: kRing.wg x (Gp, Up) then kRing.wm x Mp, 64 KB each
   Ctrl* ctrl;
   uint32_t* flags;  // per head kFlagWords
   int heads, T, S;
-  int wg, wm, lag;  // ring slots for G/U and for M; queue distance from build(t) to output(t)
-  int prio;
 };
 
 __host__ __device__ constexpr int64_t ring_head_bytes(int wg, int wm) {
@@ -181,7 +189,7 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
   const int w = tid >> 6, l = tid & 63;
   const int n = l & 15, g = l >> 4;
   uint32_t* fl = a.flags + (int64_t)head * kFlagWords;
-  const int kWG = a.wg, kWM = a.wm;
+  constexpr int kWG = kRing.wg, kWM = kRing.wm;
   char* ring = a.ring + head * ring_head_bytes(kWG, kWM);
   auto gp_slot = [&](int t) { return ring + (int64_t)(2 * (t % kWG)) * packed::kFrameBytes; };
   auto up_slot = [&](int t) { return ring + (int64_t)(2 * (t % kWG) + 1) * packed::kFrameBytes; };
@@ -389,7 +397,7 @@ template <bool kOutBf16, int kRows>
 __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int xcd, int nh) {
   constexpr int kParts = D / kRows;
   const int T = a.T, S = a.S;
-  const int kWG = a.wg, kWM = a.wm;
+  constexpr int kWG = kRing.wg, kWM = kRing.wm;
   const int total = 2 * nh * T;
   const int tid = threadIdx.x;
   for (;;) {
@@ -398,7 +406,7 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
     const int i = (int)bcast[2];
     __syncthreads();  // everyone has read the item before thread 0 overwrites it
     if (i >= total) return;
-    const Item it = decode_item(i, nh, T, a.lag);
+    const Item it = decode_item(i, nh, T, kRing.lag);
     const int head = it.hl * kXcd + xcd;
     uint32_t* fl = a.flags + (int64_t)head * kFlagWords;
     char* ring = a.ring + head * ring_head_bytes(kWG, kWM);
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void k_fused(Args a) {
   __syncthreads();
   if (nh == 0) return;
   if (ticket < nh * kParts) {
-    if (a.prio) __builtin_amdgcn_s_setprio(3);
+    __builtin_amdgcn_s_setprio(3);
     state_role<kRows>(a, lds, bcast, (ticket / kParts) * kXcd + (int)xcd, ticket % kParts);
   } else {
     worker_role<kOutBf16, kRows>(a, lds, bcast, (int)xcd, nh);
@@ -478,45 +486,24 @@ __global__ void k_fused_init(uint32_t* words, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) words[i] = 0;
 }
 
-int fused_rows() {
-  static const int r = [] { const char* e = std::getenv("GDN_FUSED_ROWS"); return e && std::atoi(e) == 32 ? 32 : 16; }();
-  return r;
-}
+// State-pass rows per workgroup: 16 (8 workgroups per head) keeps each
+// sequential step short enough; 32 halves the state-pass workgroups but the
+// longer step then limits the kernel (5.4 ms against 4.2 ms for the 60 s
+// workload).
+constexpr int kFusedRows = 16;
 
 template <bool kOutBf16>
 const void* fused_kernel() {
-  return fused_rows() == 32 ? reinterpret_cast<const void*>(&k_fused<kOutBf16, 32>)
-                            : reinterpret_cast<const void*>(&k_fused<kOutBf16, 16>);
+  return reinterpret_cast<const void*>(&k_fused<kOutBf16, kFusedRows>);
 }
 
-// Ring shape: G/U slots, M slots and the queue distance from build(t) to
-// output(t).  The queue distance must cover a build's duration in chain
-// steps; every wait then depends only on earlier items as long as
-// lag > kPrefetch + 1 and lag <= wg + wm (see the ring notes above).
-struct RingShape {
-  int wg, wm, lag;
-};
-RingShape ring_shape() {
-  static const RingShape r = [] {
-    RingShape x{40, 16, 32};
-    if (const char* e = std::getenv("GDN_FUSED_RING")) {
-      RingShape y{};
-      if (std::sscanf(e, "%d,%d,%d", &y.wg, &y.wm, &y.lag) == 3 && y.wg >= kPrefetch + 2 && y.wg <= kMaxWG &&
-          y.wm >= 2 && y.wm <= kMaxWM && y.lag > kPrefetch + 1 && y.lag <= y.wg + y.wm)
-        x = y;
-    }
-    return x;
-  }();
-  return r;
-}
 
 }  // namespace
 
 int64_t fused_workspace_bytes(int64_t heads) {
   const int64_t h = heads < kXcd * kMaxHeadsPerXcd ? heads : kXcd * kMaxHeadsPerXcd;
   const int64_t ctrl = ((int64_t)sizeof(Ctrl) + kXcd * kMaxHeadsPerXcd * kFlagWords * 4 + 255) & ~int64_t{255};
-  const RingShape r = ring_shape();
-  return ctrl + h * ring_head_bytes(r.wg, r.wm);
+  return ctrl + h * ring_head_bytes(kRing.wg, kRing.wm);
 }
 
 int fused_grid(bool out_bf16, int num_cus) {
@@ -529,7 +516,7 @@ int fused_grid(bool out_bf16, int num_cus) {
   const int pc = out_bf16 ? per_cu16 : per_cu;
   // every XCD needs its state-pass workgroups and at least as many workers
   const int grid = pc * num_cus;
-  return grid / kXcd >= 2 * kMaxHeadsPerXcd * (D / fused_rows()) ? grid : 0;
+  return grid / kXcd >= 2 * kMaxHeadsPerXcd * (D / kFusedRows) ? grid : 0;
 }
 
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
@@ -558,12 +545,6 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     a.heads = (int)nh;
     a.T = (int)T;
     a.S = S;
-    const RingShape r = ring_shape();
-    a.wg = r.wg;
-    a.wm = r.wm;
-    a.lag = r.lag;
-    static const int prio = [] { const char* e = std::getenv("GDN_FUSED_PRIO"); return e ? std::atoi(e) : 1; }();
-    a.prio = prio;
     hipLaunchKernelGGL(k_fused_init, dim3((nwords + 255) / 256), dim3(256), 0, st,
                        reinterpret_cast<uint32_t*>(ws), nwords);
     hipError_t e = hipGetLastError();
@@ -571,7 +552,10 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     void* params[] = {&a};
     e = hipLaunchCooperativeKernel(out_bf16 ? fused_kernel<true>() : fused_kernel<false>(), dim3((unsigned)grid),
                                    dim3(256), params, 0, st);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+      (void)hipGetLastError();  // do not leave the error for a later, unrelated check
+      return e;
+    }
   }
   return hipSuccess;
 }
