@@ -302,6 +302,32 @@ def test_forward_edge_shapes(T, S, D, dt):
     _forward_parity(w)
 
 
+@pytest.mark.parametrize("B,H,T,S,state", [
+    (1, 3, 65, 880, True),     # just long enough for the fused kernel; 5 of 8 XCDs without a head
+    (1, 17, 70, 100, True),    # two launch groups, the second with one head; ragged tokens (64 + 36)
+    (2, 4, 67, 1, False),      # one token per frame, zero initial state
+    (1, 8, 66, 17, True),      # one head per XCD, 17 tokens
+])
+def test_fused_kernel_edge_shapes(B, H, T, S, state):
+    import ctypes
+    from frame_wise_gated_fwd_amd._lib import Shape, lib, GDN_BF16
+    assert lib().gdn_path(ctypes.byref(Shape(B, H, T, S, 128)), GDN_BF16) == 2
+    w = Workload(name=f"fused_{B}_{H}_{T}_{S}", B=B, H=H, T=T, S=S, D=128, in_dtype="bf16",
+                 seed=60 + H + T + S, gamma_range=(0.9, 1.0), beta_kind="sigmoid_normal",
+                 state_std=0.05 if state else None)
+    _forward_parity(w, frames=sample_frames(T, seed=T))
+
+
+def test_fused_kernel_bf16_output_matches_rounded_f32():
+    w = CLIP_5S.with_(T=66, H=5, S=300, name="clip_t66_h5", state_std=0.02)
+    x = device_inputs(w, DEV)
+    o32, s32 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    o16, s16 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(s32, s16)
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
 def test_forward_bf16_output():
     w = CLIP_5S.with_(T=7, name="clip_t7")
     x = device_inputs(w, DEV)
