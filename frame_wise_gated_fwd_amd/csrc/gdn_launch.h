@@ -13,6 +13,7 @@ namespace gdn {
 // G_t and M_t as bf16 hi/lo pairs, all three in the order the consumer's
 // waves read them), which is what gdn_frame_fwd uses.  Every per-frame array
 // is laid out [head][T]; each launcher covers frames [t0, t1) of every head.
+//
 // Launches of at most this many frames (heads x frames in the range) take the
 // small-launch variants: a build with more loads in flight per workgroup and
 // an output that splits each frame's tokens over several workgroups.  Both

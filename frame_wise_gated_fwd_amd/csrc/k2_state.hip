@@ -28,6 +28,12 @@
 // for LDS traffic, so those loads stay in flight across it.  Workgroups of
 // one head are placed on one XCD (dispatch is round-robin over the 8 XCDs),
 // so the G_t they all read comes from one L2.
+//
+// A launch covers frames [tb, te) of every head (a segment of the
+// overlapped schedule, or all frames), starting from the state after frame
+// tb - 1 in state_in and leaving the state after frame te - 1 in
+// state_out; the float32 state is carried exactly, so a sequence cut into
+// segments gives the same bits as one launch.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 #include "gdn_packed.h"
