@@ -1,4 +1,4 @@
-"""CPU oracle for the frame-wise Gated DeltaNet forward.
+"""CPU oracle for the frame-wise Gated DeltaNet forward and its backward pass.
 
 TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's CPU
 baseline may import this package.  It shares no code with the GPU library.
@@ -7,3 +7,4 @@ from .gdn_ref import (as_f64, frame_maps, transition, gdn_head, gdn_head_residua
                       build_maps_head, state_pass_head, output_head, compose,
                       state_pass_chunked, tokenwise_gated_delta, gdn_forward,
                       gdn_forward_streamed, flops_per_head_frame)
+from .gdn_bwd import gdn_head_backward, scalar_loss
