@@ -4,7 +4,9 @@
 A step is one gdn_frame_fwd call over the whole 60 s, 720p workload
 (B=1, H=16, T=961 latent frames, S=880 tokens per frame, D=128, bf16 q/k/v,
 float32 state and output) with every input already resident in HBM.
-value = frame-steps/s = B*T / seconds per step.  One JSON line is printed.
+value = frame-steps/s = B*T / seconds per step.  One JSON line is printed;
+besides the forward it carries the backward pass (gdn_frame_bwd) on the same
+workload, the same frames as streamed calls, and single-frame latency.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --copy-calibration     # plain copy of a known size, for counters
@@ -55,6 +57,11 @@ def per_head_frame_bytes(S, D, in_bytes=2, out_bytes=4):
         "output": qkv + dd + o,         # read Q, M_t; write O
         "step": 3 * qkv + o,            # q, k, v in; O out (state in/out per head is extra)
         "fused": 3 * qkv + o,           # the fused kernel: G, U, M stay on chip
+        # backward: q, k, v, d_out in; dq, dk, dv out (f32)
+        "backward": 4 * qkv + 3 * o,
+        # what its ten launches move: eight token-tensor reads, four f32
+        # gradient writes and one read back (dk += K S), nineteen D x D maps
+        "backward_design": 8 * qkv + 5 * o + 19 * dd,
     }
 
 
@@ -211,6 +218,52 @@ def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
            {"isolated_us_median": round(float(np.median(iso)), 2), "back_to_back_us": round(back_to_back, 2)}
 
 
+def backward_leg(x, L, w, stream, steps=5, warmup=1):
+    """gdn_frame_bwd over the whole workload: seeded N(0,1) bf16 d_out and
+    N(0, 0.01) f32 d_state_out, outputs and workspace allocated once."""
+    import torch
+    from frame_wise_gated_fwd_amd._lib import Shape, check, GDN_BF16
+    B, H, T, S, D = w.B, w.H, w.T, w.S, w.D
+    dev = x["q"].device
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    d_out = torch.randn((B, H, T, S, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    d_state = torch.randn((B, H, D, D), generator=gen, device=dev, dtype=torch.float32) * 0.1
+    grads = [torch.empty((B, H, T, S, D), dtype=torch.float32, device=dev) for _ in range(3)]
+    dg = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    db = torch.empty_like(dg)
+    dst = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    shp = Shape(B, H, T, S, D)
+    wsb = L.gdn_bwd_workspace_bytes(ctypes.byref(shp), GDN_BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    def call():
+        check(L.gdn_frame_bwd(ctypes.byref(shp), GDN_BF16, P(x["q"]), P(x["k"]), P(x["v"]), P(x["gamma"]),
+                              P(x["beta"]), P(x["state"]), P(d_out), P(d_state), P(grads[0]), P(grads[1]),
+                              P(grads[2]), P(dg), P(db), P(dst), P(ws), wsb, stream), "gdn_frame_bwd")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    hf = B * H * T
+    by = per_head_frame_bytes(S, D)
+    alg = by["backward"] * hf
+    des = by["backward_design"] * hf
+    del grads, ws, d_out
+    return {"ms": round(ms, 4), "frame_steps_per_s": round(B * T / (ms * 1e-3), 1),
+            "algorithmic_bytes": alg, "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "design_bytes": des, "design_GBps": round(des / (ms * 1e-3) / 1e9, 1),
+            "steps": steps, "launches_per_call": 10}
+
+
 def copy_calibration(gib=1.0, reps=5):
     import torch
     n = int(gib * (1 << 30)) // 4
@@ -242,6 +295,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the streamed-calls and single-frame latency measurements")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--backward-steps", type=int, default=5)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -339,6 +394,12 @@ def main():
                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                       "TFLOPs": round(flops_hf[k] * hf / (v * 1e-3) / 1e12, 2) if v > 0 else 0.0}
 
+    backward = None
+    if not args.no_backward:
+        log("backward pass")
+        backward = backward_leg(x, L, w, stream, steps=args.backward_steps)
+        log(f"backward: {backward}")
+
     streamed = t1 = None
     if not args.no_extras:
         log("streaming calls and T=1 latency")
@@ -380,6 +441,7 @@ def main():
                           "mfma_frac": round(step_tflops / BF16_PEAK_TFLOPS, 4)},
         "kernels": kernels,
         "head_frame_steps_per_s": round(hf / (ms * 1e-3), 1),
+        "backward": backward,
         "streamed_calls": streamed,
         "t1_call": t1,
     }

@@ -3,8 +3,8 @@
 The computation lives in libgdn.so (HIP kernels behind the C ABI in
 include/gdn.h); this package only marshals torch tensors into it.
 """
-from .api import frame_fwd, build_maps, state_pass, output, workspace_bytes, set_fused
+from .api import frame_fwd, frame_bwd, build_maps, state_pass, output, workspace_bytes, set_fused
 from ._lib import lib, GDNError, LIB_PATH
 
-__all__ = ["frame_fwd", "build_maps", "state_pass", "output", "workspace_bytes", "set_fused", "lib",
+__all__ = ["frame_fwd", "frame_bwd", "build_maps", "state_pass", "output", "workspace_bytes", "set_fused", "lib",
            "GDNError", "LIB_PATH"]

@@ -41,6 +41,9 @@ SIGNATURES = {
     "gdn_frame_fwd": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp]),
     "gdn_frame_fwd_timed": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp,
                                  ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
+    "gdn_bwd_workspace_bytes": (_sz, [_PS, _i]),
+    "gdn_frame_bwd": (_i, [_PS, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _vp, _vp,
+                           _vp, _vp, _sz, _vp]),
     "gdn_build_maps": (_i, [_PS, _i, _cvp, _cvp, _vp, _vp, _vp]),
     "gdn_state_pass": (_i, [_PS, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp]),
     "gdn_output": (_i, [_PS, _i, _i, _cvp, _cvp, _vp, _vp]),

@@ -103,6 +103,44 @@ def frame_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Te
     return out, state_out
 
 
+def frame_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
+              d_out: torch.Tensor, state: Optional[torch.Tensor] = None,
+              d_state_out: Optional[torch.Tensor] = None, *,
+              d_state_in: Optional[torch.Tensor] = None):
+    """Backward pass of frame_fwd (gdn_frame_bwd): gradients of
+    <d_out, out> + <d_state_out, state_out>.
+
+    q, k, v, d_out: [B, H, T, S, 128] bf16; gamma, beta: [B, H, T] f32;
+    state, d_state_out: [B, H, 128, 128] f32 or None (zeros).  Returns
+    (dq, dk, dv [B, H, T, S, 128] f32, dgamma, dbeta [B, H, T] f32,
+    d_state_in [B, H, 128, 128] f32); d_state_in may be d_state_out."""
+    shp = shape_of(q)
+    B, H, T, S, D = q.shape
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (d_out, "d_out")):
+        _need(t, name, (B, H, T, S, D), torch.bfloat16, dev)
+    _need(gamma, "gamma", (B, H, T), torch.float32, dev)
+    _need(beta, "beta", (B, H, T), torch.float32, dev)
+    for t, name in ((state, "state"), (d_state_out, "d_state_out")):
+        if t is not None:
+            _need(t, name, (B, H, D, D), torch.float32, dev)
+    grads = [torch.empty((B, H, T, S, D), dtype=torch.float32, device=dev) for _ in range(3)]
+    dgamma = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dbeta = torch.empty_like(dgamma)
+    if d_state_in is None:
+        d_state_in = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    _need(d_state_in, "d_state_in", (B, H, D, D), torch.float32, dev)
+    L = lib()
+    wsb = int(L.gdn_bwd_workspace_bytes(ctypes.byref(shp), GDN_BF16))
+    workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = L.gdn_frame_bwd(ctypes.byref(shp), GDN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta),
+                         _ptr(state), _ptr(d_out), _ptr(d_state_out), _ptr(grads[0]), _ptr(grads[1]),
+                         _ptr(grads[2]), _ptr(dgamma), _ptr(dbeta), _ptr(d_state_in), _ptr(workspace), wsb,
+                         _stream(dev))
+    check(st, "gdn_frame_bwd")
+    return grads[0], grads[1], grads[2], dgamma, dbeta, d_state_in
+
+
 def build_maps(k: torch.Tensor, v: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """Stage 1 (gdn_build_maps): G_t = K_t^T K_t and U_t = V_t^T K_t, [B,H,T,D,D] f32."""
     shp = shape_of(k)

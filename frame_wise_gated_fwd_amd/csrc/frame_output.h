@@ -46,12 +46,17 @@ __device__ __forceinline__ int lds_row(int r) {
 // output_lds_bytes().  on_staged() runs on every thread once M_t has been
 // copied into LDS (the caller may then release M_t's buffer).  kDepth: token
 // tiles each wave loads ahead.  All 256 threads of the workgroup must call it.
-template <bool kPackedM, bool kOutBf16, int kDepth = 1, typename OnStaged>
+// Two options of the float32 form of M_t (used by the backward pass):
+// kTransM stages M_t^T instead of M_t (so the frame gets Q_t M_t), and
+// kAccum adds the result to the float32 output already in Of.
+template <bool kPackedM, bool kOutBf16, int kDepth = 1, bool kTransM = false, bool kAccum = false,
+          typename OnStaged>
 __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, const void* __restrict__ Mt_in,
                                              void* __restrict__ Of, int S, uint16_t (*Ml)[128][kOutLdsW],
                                              OnStaged on_staged) {
   constexpr int D = 128;
   constexpr int kTile = kOutTile;
+  static_assert(!(kPackedM && kTransM) && !(kOutBf16 && kAccum), "option not available for this form");
   // An opaque copy of the thread index: lane-dependent addresses are then
   // computed at each call instead of being hoisted out of a caller's loop
   // and kept live (in registers) across the whole call.
@@ -76,6 +81,17 @@ __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, co
       const int r = idx >> 5, c4 = (idx & 31) * 4;
       const f32x4 mv = *reinterpret_cast<const f32x4*>(Mt + r * D + c4);
       const u32x2 p0 = split2(mv[0], mv[1]), p1 = split2(mv[2], mv[3]);
+      if constexpr (kTransM) {
+        // element (r, c4 + e) of M is element (c4 + e, r) of the staged matrix
+        const uint32_t hi[2] = {p0.x, p1.x}, lo[2] = {p0.y, p1.y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rho = lds_row<kOutBf16>(c4 + e);
+          Ml[0][rho][r] = (uint16_t)(hi[e >> 1] >> (16 * (e & 1)));
+          Ml[1][rho][r] = (uint16_t)(lo[e >> 1] >> (16 * (e & 1)));
+        }
+        continue;
+      }
       const int rho = lds_row<kOutBf16>(r);
       *reinterpret_cast<u32x2*>(&Ml[0][rho][c4]) = (u32x2){p0.x, p1.x};
       *reinterpret_cast<u32x2*>(&Ml[1][rho][c4]) = (u32x2){p0.y, p1.y};
@@ -147,8 +163,14 @@ __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, co
           st_nt(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(Of) + row + 8 * n), pk);
         } else {
           float* o = static_cast<float*>(Of) + row + 4 * n;
-          st_nt(reinterpret_cast<f32x4*>(o), (f32x4){acc[rb][0][i], acc[rb][1][i], acc[rb][2][i], acc[rb][3][i]});
-          st_nt(reinterpret_cast<f32x4*>(o + 64), (f32x4){acc[rb][4][i], acc[rb][5][i], acc[rb][6][i], acc[rb][7][i]});
+          f32x4 v0 = {acc[rb][0][i], acc[rb][1][i], acc[rb][2][i], acc[rb][3][i]};
+          f32x4 v1 = {acc[rb][4][i], acc[rb][5][i], acc[rb][6][i], acc[rb][7][i]};
+          if constexpr (kAccum) {
+            v0 = *reinterpret_cast<const f32x4*>(o) + v0;
+            v1 = *reinterpret_cast<const f32x4*>(o + 64) + v1;
+          }
+          st_nt(reinterpret_cast<f32x4*>(o), v0);
+          st_nt(reinterpret_cast<f32x4*>(o + 64), v1);
         }
       }
   };

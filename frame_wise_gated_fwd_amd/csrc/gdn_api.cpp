@@ -484,4 +484,83 @@ int gdn_frame_fwd_timed(const gdn_shape* shape, int in_dtype, int out_dtype, con
   return GDN_OK;
 }
 
+size_t gdn_bwd_workspace_bytes(const gdn_shape* shape, int in_dtype) {
+  Dims d;
+  if (!valid_dtype(in_dtype) || check_shape(shape, true, &d) != GDN_OK) return 0;
+  // G, U, M_all, P, LB and S (the last also holds Q^T Q while P is built),
+  // then the dgamma/dbeta partial sums and the recomputed final state
+  return 6 * round256(d.map_elems * sizeof(float)) +
+         round256((size_t)d.frames * gdn::kBwdParts * 2 * sizeof(float)) +
+         round256(d.state_elems * sizeof(float));
+}
+
+int gdn_frame_bwd(const gdn_shape* shape, int in_dtype, const void* q, const void* k, const void* v,
+                  const float* gamma, const float* beta, const float* state_in, const void* d_out,
+                  const float* d_state_out, float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
+                  float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int st = check_shape(shape, true, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(in_dtype)) return GDN_E_DTYPE;
+  if (in_dtype != GDN_BF16) return GDN_E_DTYPE;
+  if (d.D != 128) return GDN_E_UNSUPPORTED_D;
+  if (!q || !k || !v || !gamma || !beta || !d_out || !dq || !dk || !dv || !dgamma || !dbeta || !d_state_in)
+    return GDN_E_NULLPTR;
+  const size_t need = gdn_bwd_workspace_bytes(shape, in_dtype);
+  if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0) return GDN_E_WORKSPACE;
+  const size_t inb = d.in_elems * 2, gradb = d.in_elems * 4;
+  const size_t stb = d.state_elems * 4, gb = (size_t)d.frames * 4;
+  const Range outs[] = {{dq, gradb}, {dk, gradb}, {dv, gradb}, {dgamma, gb}, {dbeta, gb},
+                        {d_state_in, stb}, {workspace, need}};
+  const Range ins[] = {{q, inb}, {k, inb}, {v, inb}, {gamma, gb}, {beta, gb}, {state_in, state_in ? stb : 0},
+                       {d_out, inb}, {d_state_out, d_state_out ? stb : 0}};
+  if (!aliasing_ok(outs, 7, ins, 8, d_state_in, d_state_out)) return GDN_E_ALIAS;
+
+  const size_t slot = round256(d.map_elems * sizeof(float));
+  char* ws = static_cast<char*>(workspace);
+  float* G = reinterpret_cast<float*>(ws);
+  float* U = reinterpret_cast<float*>(ws + slot);
+  float* M_all = reinterpret_cast<float*>(ws + 2 * slot);
+  float* P = reinterpret_cast<float*>(ws + 3 * slot);
+  float* LB = reinterpret_cast<float*>(ws + 4 * slot);
+  float* Sb = reinterpret_cast<float*>(ws + 5 * slot);
+  float* partials = reinterpret_cast<float*>(ws + 6 * slot);
+  float* fstate = reinterpret_cast<float*>(ws + 6 * slot +
+                                           round256((size_t)d.frames * gdn::kBwdParts * 2 * sizeof(float)));
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kb = static_cast<const uint16_t*>(k);
+  const auto* vb = static_cast<const uint16_t*>(v);
+  const auto* ob = static_cast<const uint16_t*>(d_out);
+  const int S = (int)d.S;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  // forward recomputation: G_t, U_t and every state M_t (float32 forms)
+  if ((e = gdn::launch_build_bf16_d128(kb, vb, G, false, U, d.heads, d.T, 0, d.T, S, s)) != hipSuccess)
+    return GDN_E_HIP;
+  if ((e = gdn::launch_state_d128(G, false, U, gamma, beta, state_in, M_all, fstate, d.heads, d.T, 0, d.T, s)) !=
+      hipSuccess)
+    return GDN_E_HIP;
+  // P_t = d_out_t^T Q_t: the build's second map with (K, V) = (Q, d_out); its
+  // first map (Q^T Q) lands in the S buffer and is overwritten below
+  if ((e = gdn::launch_build_bf16_d128(qb, ob, Sb, false, P, d.heads, d.T, 0, d.T, S, s)) != hipSuccess)
+    return GDN_E_HIP;
+  // reverse-time state pass: LB_t = beta_t Lambda_t, dgamma/dbeta partials, d_state_in
+  if ((e = gdn::launch_state_bwd_d128(G, U, P, M_all, state_in, gamma, beta, d_state_out, LB, partials,
+                                      d_state_in, d.heads, d.T, s)) != hipSuccess)
+    return GDN_E_HIP;
+  if ((e = gdn::launch_bwd_reduce(partials, dgamma, dbeta, d.frames, s)) != hipSuccess) return GDN_E_HIP;
+  if ((e = gdn::launch_sym_bwd_d128(M_all, state_in, LB, gamma, Sb, d.heads, d.T, s)) != hipSuccess)
+    return GDN_E_HIP;
+  // contractions over tokens, on the output kernel (out = X_t Y_t^T form)
+  if ((e = gdn::launch_output_bwd_d128(ob, M_all, dq, true, false, d.heads, d.T, S, s)) != hipSuccess)
+    return GDN_E_HIP;  // dq = d_out M
+  if ((e = gdn::launch_output_bwd_d128(kb, LB, dv, false, false, d.heads, d.T, S, s)) != hipSuccess)
+    return GDN_E_HIP;  // dv = K LB^T
+  if ((e = gdn::launch_output_bwd_d128(vb, LB, dk, true, false, d.heads, d.T, S, s)) != hipSuccess)
+    return GDN_E_HIP;  // dk = V LB
+  if ((e = gdn::launch_output_bwd_d128(kb, Sb, dk, false, true, d.heads, d.T, S, s)) != hipSuccess)
+    return GDN_E_HIP;  // dk += K S
+  return GDN_OK;
+}
+
 }  // extern "C"

@@ -193,6 +193,36 @@ int gdn_state_pass(const gdn_shape* shape, const float* G, const float* U,
 int gdn_output(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q,
                const float* M_all, void* out, void* stream);
 
+/*
+ * Backward pass (vector-Jacobian product) of gdn_frame_fwd.  The pages train
+ * the model ("SANA-WM: NVIDIA puts a one-minute world model on a single
+ * GPU", zhichai.net, training pipeline) without stating the gradients; these
+ * are the exact derivative of the forward above.  With Lambda_t the total
+ * gradient reaching M_t (d_out_t^T Q_t plus what flows back from M_{t+1}):
+ *   dq_t = d_out_t M_t,   dv_t = beta_t K_t Lambda_t^T,
+ *   dk_t = beta_t V_t Lambda_t + K_t (dG_t + dG_t^T),
+ *          dG_t = -gamma_t beta_t M_{t-1}^T Lambda_t,
+ *   dgamma_t = < Lambda_t, M_{t-1} (I - beta_t G_t) >,
+ *   dbeta_t  = < Lambda_t, U_t - gamma_t M_{t-1} G_t >,
+ *   d_state_in = gradient of M_0 (written even when state_in is NULL).
+ * Supported: in_dtype GDN_BF16 with D == 128 (otherwise GDN_E_DTYPE or
+ * GDN_E_UNSUPPORTED_D).  d_out has in_dtype; d_state_out is [B,H,D,D] f32 or
+ * NULL (zero).  dq, dk, dv: [B,H,T,S,D] f32; dgamma, dbeta: [B,H,T] f32;
+ * d_state_in: [B,H,D,D] f32 (may equal d_state_out, for chunked backward
+ * passes that carry the state gradient).  The forward states are recomputed
+ * from q, k, v, gamma, beta and state_in.  Asynchronous on `stream`;
+ * argument errors return before any launch.  workspace: at least
+ * gdn_bwd_workspace_bytes(shape, in_dtype) bytes of device memory,
+ * 256-byte aligned.
+ */
+size_t gdn_bwd_workspace_bytes(const gdn_shape* shape, int in_dtype);
+int gdn_frame_bwd(const gdn_shape* shape, int in_dtype,
+                  const void* q, const void* k, const void* v,
+                  const float* gamma, const float* beta, const float* state_in,
+                  const void* d_out, const float* d_state_out,
+                  float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
+                  float* d_state_in, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

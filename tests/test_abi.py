@@ -140,6 +140,32 @@ def test_timed_needs_output_array():
                                  P[6], P[7], wsb, None, ms, None) == NULLPTR
 
 
+def test_backward_argument_errors():
+    L = F.lib()
+    s = _shape()
+    wsb = L.gdn_bwd_workspace_bytes(ctypes.byref(s), BF16)
+    per = 2 * 3 * 128 * 128 * 4
+    partials = 6 * 8 * 2 * 4  # frames x 8 parts x (dgamma, dbeta) floats
+    assert wsb == 6 * ((per + 255) // 256 * 256) + (partials + 255) // 256 * 256 + 2 * 128 * 128 * 4
+
+    def bwd(shape=s, dt=BF16, d_state_out=None, d_state_in=P[11], ws=P[10], wsb=wsb, **kw):
+        a = dict(q=P[0], k=P[1], v=P[2], gamma=P[3], beta=P[4], state=None, d_out=P[5], dq=P[6], dk=P[7],
+                 dv=P[8], dgamma=P[9] + (1 << 30), dbeta=P[9] + (2 << 30))
+        a.update(kw)
+        return L.gdn_frame_bwd(ctypes.byref(shape) if shape else None, dt, a["q"], a["k"], a["v"], a["gamma"],
+                               a["beta"], a["state"], a["d_out"], d_state_out, a["dq"], a["dk"], a["dv"],
+                               a["dgamma"], a["dbeta"], d_state_in, ws, wsb, None)
+    assert bwd(shape=None) == NULLPTR
+    assert bwd(dt=F32) == DTYPE
+    assert bwd(shape=_shape(D=64), wsb=L.gdn_bwd_workspace_bytes(ctypes.byref(_shape(D=64)), BF16)) == UNSUP_D
+    assert bwd(d_out=None) == NULLPTR
+    assert bwd(d_state_in=None) == NULLPTR
+    assert bwd(wsb=wsb - 1) == WORKSPACE
+    assert bwd(dq=P[0]) == ALIAS                       # a gradient over q
+    assert bwd(dk=P[6]) == ALIAS                       # two gradients in one buffer
+    assert bwd(d_state_out=P[11] + 4) == ALIAS         # partial overlap of the state gradients
+
+
 def test_stage_argument_errors():
     L = F.lib()
     s = _shape()

@@ -1,0 +1,117 @@
+"""GPU parity of the backward pass (gdn_frame_bwd, through the C ABI) against
+the fp64 backward oracle on the same seeded inputs, plus consistency checks
+that hold bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import frame_wise_gated_fwd_amd as F
+from synth import CLIP_5S, Workload, head_inputs
+from gpu_util import device_inputs, RelL2, log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+KEYS = ("dq", "dk", "dv", "dgamma", "dbeta", "dstate")
+
+
+def _upstream(w, seed, with_dstate):
+    """Seeded incoming gradients: d_out bf16 (as the inputs), d_state_out f32."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    d_out = rng.standard_normal((w.B, w.H, w.T, w.S, w.D), dtype=np.float32)
+    d_out_t = torch.from_numpy(d_out).to(torch.bfloat16)
+    d_state = (rng.standard_normal((w.B, w.H, w.D, w.D), dtype=np.float32) * 0.1) if with_dstate else None
+    return d_out_t, d_state
+
+
+def _gpu_backward(x, d_out_t, d_state):
+    ds = None if d_state is None else torch.from_numpy(d_state).to(DEV)
+    return dict(zip(KEYS, F.frame_bwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], d_out_t.to(DEV),
+                                      x["state"], ds)))
+
+
+def _backward_parity(w, seed=1, with_dstate=True, heads=None, tol=2e-3):
+    log(f"backward {w.name}: B={w.B} H={w.H} T={w.T} S={w.S} D={w.D} d_state={with_dstate}")
+    x = device_inputs(w, DEV)
+    d_out_t, d_state = _upstream(w, seed, with_dstate)
+    got = _gpu_backward(x, d_out_t, d_state)
+    torch.cuda.synchronize()
+    d_out_bits = d_out_t.view(torch.int16).numpy().view(np.uint16)
+    hs = heads or [(b, h) for b in range(w.B) for h in range(w.H)]
+    err = {k: RelL2() for k in KEYS}
+    for b, h in hs:
+        d = head_inputs(w, b, h)
+        ref = oracle.gdn_head_backward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], d.get("state"),
+                                       d_out_bits[b, h], None if d_state is None else d_state[b, h])
+        for key in KEYS:
+            err[key].add(got[key][b, h].cpu().numpy(), ref[key])
+    log("  relL2 " + ", ".join(f"{k}={err[k].value:.2e}" for k in KEYS))
+    for key in KEYS:
+        assert np.isfinite(err[key].value) and err[key].value <= tol, (key, err[key].value)
+    return x, d_out_t, d_state, got
+
+
+def test_backward_small_ragged():
+    w = Workload(name="bwd_small", B=1, H=3, T=7, S=100, D=128, in_dtype="bf16", seed=71,
+                 gamma_range=(0.9, 1.0), beta_kind="sigmoid_normal", state_std=0.05)
+    _backward_parity(w)
+
+
+def test_backward_zero_state_no_state_gradient():
+    w = Workload(name="bwd_zero", B=2, H=2, T=5, S=37, D=128, in_dtype="bf16", seed=72,
+                 gamma_range=(0.9, 1.0), beta_kind="sigmoid_normal")
+    _backward_parity(w, with_dstate=False)
+
+
+def test_backward_clip_frames_sampled_heads():
+    w = CLIP_5S.with_(T=12, name="bwd_clip_t12", state_std=0.02)
+    _backward_parity(w, heads=[(0, 0), (0, 5), (0, 10), (0, 15)])
+
+
+def test_backward_in_place_state_gradient_and_determinism():
+    w = Workload(name="bwd_inplace", B=1, H=4, T=6, S=64, D=128, in_dtype="bf16", seed=73,
+                 gamma_range=(0.9, 1.0), beta_kind="sigmoid_normal", state_std=0.05)
+    x = device_inputs(w, DEV)
+    d_out_t, d_state = _upstream(w, 5, True)
+    a = _gpu_backward(x, d_out_t, d_state)
+    b = _gpu_backward(x, d_out_t, d_state)
+    ds = torch.from_numpy(d_state).to(DEV)
+    res = F.frame_bwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], d_out_t.to(DEV), x["state"], ds,
+                      d_state_in=ds)
+    torch.cuda.synchronize()
+    for key in KEYS:
+        assert torch.equal(a[key], b[key]), key
+    assert res[5] is ds and torch.equal(ds, a["dstate"])
+    for i, key in enumerate(KEYS[:5]):
+        assert torch.equal(res[i], a[key]), key
+
+
+def test_chunked_backward_equals_one_call_bitwise():
+    """Frames [t0, T) then [0, t0), carrying the forward state forwards and the
+    state gradient backwards, reproduce the one-call backward bit for bit."""
+    w = Workload(name="bwd_chunks", B=1, H=3, T=9, S=120, D=128, in_dtype="bf16", seed=74,
+                 gamma_range=(0.9, 1.0), beta_kind="sigmoid_normal", state_std=0.05)
+    x = device_inputs(w, DEV)
+    d_out_t, d_state = _upstream(w, 6, True)
+    one = _gpu_backward(x, d_out_t, d_state)
+    t0 = 4
+    sl1, sl2 = slice(0, t0), slice(t0, w.T)
+    part = lambda key, sl: x[key][:, :, sl].contiguous()
+    _, mid = F.frame_fwd(part("q", sl1), part("k", sl1), part("v", sl1), part("gamma", sl1),
+                         part("beta", sl1), x["state"])
+    d_out = d_out_t.to(DEV)
+    g2 = F.frame_bwd(part("q", sl2), part("k", sl2), part("v", sl2), part("gamma", sl2), part("beta", sl2),
+                     d_out[:, :, sl2].contiguous(), mid, torch.from_numpy(d_state).to(DEV))
+    g1 = F.frame_bwd(part("q", sl1), part("k", sl1), part("v", sl1), part("gamma", sl1), part("beta", sl1),
+                     d_out[:, :, sl1].contiguous(), x["state"], g2[5])
+    torch.cuda.synchronize()
+    for i, key in enumerate(("dq", "dk", "dv", "dgamma", "dbeta")):
+        assert torch.equal(torch.cat([g1[i], g2[i]], dim=2), one[key]), key
+    assert torch.equal(g1[5], one["dstate"])
+
+
+def test_backward_rejects_unsupported():
+    q = torch.zeros((1, 1, 2, 8, 64), dtype=torch.bfloat16, device=DEV)
+    g = torch.ones((1, 1, 2), device=DEV)
+    with pytest.raises(F.GDNError):
+        F.frame_bwd(q, q, q, g, g, q)
