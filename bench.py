@@ -59,9 +59,10 @@ def per_head_frame_bytes(S, D, in_bytes=2, out_bytes=4):
         "fused": 3 * qkv + o,           # the fused kernel: G, U, M stay on chip
         # backward: q, k, v, d_out in; dq, dk, dv out (f32)
         "backward": 4 * qkv + 3 * o,
-        # what its ten launches move: eight token-tensor reads, four f32
-        # gradient writes and one read back (dk += K S), nineteen D x D maps
-        "backward_design": 8 * qkv + 5 * o + 19 * dd,
+        # what its kernels move: eight bf16 token-tensor reads (K, V twice
+        # each; Q, dO in the P build; dO for dq; K for dv), three f32
+        # gradient writes and nineteen D x D float32 maps written or read
+        "backward_design": 8 * qkv + 3 * o + 19 * dd,
     }
 
 
@@ -261,7 +262,7 @@ def backward_leg(x, L, w, stream, steps=5, warmup=1):
             "algorithmic_bytes": alg, "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "design_bytes": des, "design_GBps": round(des / (ms * 1e-3) / 1e9, 1),
-            "steps": steps, "launches_per_call": 10}
+            "steps": steps}
 
 
 def copy_calibration(gib=1.0, reps=5):

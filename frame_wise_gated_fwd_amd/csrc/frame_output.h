@@ -46,17 +46,15 @@ __device__ __forceinline__ int lds_row(int r) {
 // output_lds_bytes().  on_staged() runs on every thread once M_t has been
 // copied into LDS (the caller may then release M_t's buffer).  kDepth: token
 // tiles each wave loads ahead.  All 256 threads of the workgroup must call it.
-// Two options of the float32 form of M_t (used by the backward pass):
-// kTransM stages M_t^T instead of M_t (so the frame gets Q_t M_t), and
-// kAccum adds the result to the float32 output already in Of.
-template <bool kPackedM, bool kOutBf16, int kDepth = 1, bool kTransM = false, bool kAccum = false,
-          typename OnStaged>
+// With the float32 form of M_t, kTransM stages M_t^T instead of M_t (so the
+// frame gets Q_t M_t; used by the backward pass).
+template <bool kPackedM, bool kOutBf16, int kDepth = 1, bool kTransM = false, typename OnStaged>
 __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, const void* __restrict__ Mt_in,
                                              void* __restrict__ Of, int S, uint16_t (*Ml)[128][kOutLdsW],
                                              OnStaged on_staged) {
   constexpr int D = 128;
   constexpr int kTile = kOutTile;
-  static_assert(!(kPackedM && kTransM) && !(kOutBf16 && kAccum), "option not available for this form");
+  static_assert(!(kPackedM && kTransM), "option not available for this form");
   // An opaque copy of the thread index: lane-dependent addresses are then
   // computed at each call instead of being hoisted out of a caller's loop
   // and kept live (in registers) across the whole call.
@@ -163,12 +161,8 @@ __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, co
           st_nt(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(Of) + row + 8 * n), pk);
         } else {
           float* o = static_cast<float*>(Of) + row + 4 * n;
-          f32x4 v0 = {acc[rb][0][i], acc[rb][1][i], acc[rb][2][i], acc[rb][3][i]};
-          f32x4 v1 = {acc[rb][4][i], acc[rb][5][i], acc[rb][6][i], acc[rb][7][i]};
-          if constexpr (kAccum) {
-            v0 = *reinterpret_cast<const f32x4*>(o) + v0;
-            v1 = *reinterpret_cast<const f32x4*>(o + 64) + v1;
-          }
+          const f32x4 v0 = {acc[rb][0][i], acc[rb][1][i], acc[rb][2][i], acc[rb][3][i]};
+          const f32x4 v1 = {acc[rb][4][i], acc[rb][5][i], acc[rb][6][i], acc[rb][7][i]};
           st_nt(reinterpret_cast<f32x4*>(o), v0);
           st_nt(reinterpret_cast<f32x4*>(o + 64), v1);
         }

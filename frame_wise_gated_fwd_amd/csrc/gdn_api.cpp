@@ -13,6 +13,7 @@
 #include <cstdlib>
 #include <limits>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "gdn_launch.h"
@@ -289,6 +290,108 @@ hipError_t run_mfma(const Dims& d, const uint16_t* q, const uint16_t* k, const u
   return err;
 }
 
+// ---------------------------------------------------------------------------
+// the backward schedule
+// ---------------------------------------------------------------------------
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *d_out;
+  const float *gamma, *beta, *state_in, *d_state_out;
+  float *dq, *dk, *dv, *dgamma, *dbeta, *d_state_in;
+};
+struct BwdBuffers {
+  float *G, *U, *M_all, *P, *LB, *Sb, *partials, *fstate;
+};
+
+// gdn_frame_bwd over ceil(T / F) segments, on the side streams of the
+// overlapped forward schedule.  First the forward is recomputed in float32
+// forms: (K, V) builds on the caller's stream, the state pass (a chain)
+// segment by segment on the state stream, and dq = dO M per segment on the
+// output stream as its states appear; the P_t = dO_t^T Q_t build follows
+// the (K, V) builds on the caller's stream.  Then the reverse-time state pass
+// walks the segments from the last to the first on the state stream, the
+// state gradient carried through d_state_in, and each segment's S, dv and dk
+// follow on the output stream.  The chains run on a few CUs while the
+// builds and token contractions stream from HBM on the rest.  No kernel's
+// arithmetic depends on the segmentation.  With one segment everything runs
+// on the caller's stream.
+hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStream_t s) {
+  const int64_t F = segment_frames();
+  const int64_t nseg = (d.T + F - 1) / F;
+  const int S = (int)d.S;
+  const int64_t H = d.heads, T = d.T;
+  auto seg = [&](int64_t i) { return std::make_pair(i * T / nseg, (i + 1) * T / nseg); };
+  auto build_kv = [&](hipStream_t st, int64_t t0, int64_t t1) {
+    return gdn::launch_build_bf16_d128(a.k, a.v, b.G, false, b.U, H, T, t0, t1, S, st);
+  };
+  // the build's first map (Q^T Q) lands in the S buffer; S overwrites it later
+  auto build_p = [&](hipStream_t st) { return gdn::launch_build_bf16_d128(a.q, a.d_out, b.Sb, false, b.P, H, T, 0, T, S, st); };
+  auto state_fwd = [&](hipStream_t st, int64_t t0, int64_t t1) {
+    return gdn::launch_state_d128(b.G, false, b.U, a.gamma, a.beta, t0 ? b.fstate : a.state_in, b.M_all, b.fstate,
+                                  H, T, t0, t1, st);
+  };
+  auto dq = [&](hipStream_t st, int64_t t0, int64_t t1) {
+    return gdn::launch_output_bwd_d128(a.d_out, b.M_all, a.dq, true, H, T, t0, t1, S, st);  // dq = dO M
+  };
+  auto state_bwd = [&](hipStream_t st, int64_t t0, int64_t t1) {
+    const float* carry = t1 == T ? a.d_state_out : a.d_state_in;
+    return gdn::launch_state_bwd_d128(b.G, b.U, b.P, b.M_all, a.state_in, a.gamma, a.beta, carry, b.LB,
+                                      b.partials, a.d_state_in, H, T, t0, t1, st);
+  };
+  auto grads = [&](hipStream_t st, int64_t t0, int64_t t1) {
+    hipError_t e;
+    if ((e = gdn::launch_sym_bwd_d128(b.M_all, a.state_in, b.LB, a.gamma, b.Sb, H, T, t0, t1, st)) != hipSuccess)
+      return e;
+    if ((e = gdn::launch_output_bwd_d128(a.k, b.LB, a.dv, false, H, T, t0, t1, S, st)) != hipSuccess)
+      return e;  // dv = K LB^T
+    return gdn::launch_dk_bwd_d128(a.v, a.k, b.LB, b.Sb, a.dk, H, T, t0, t1, S, st);  // dk = V LB + K S
+  };
+  auto reduce = [&]() { return gdn::launch_bwd_reduce(b.partials, a.dgamma, a.dbeta, d.frames, s); };
+  hipError_t e;
+  if (nseg == 1) {
+    if ((e = build_kv(s, 0, T)) != hipSuccess || (e = state_fwd(s, 0, T)) != hipSuccess ||
+        (e = dq(s, 0, T)) != hipSuccess || (e = build_p(s)) != hipSuccess || (e = state_bwd(s, 0, T)) != hipSuccess ||
+        (e = grads(s, 0, T)) != hipSuccess)
+      return e;
+    return reduce();
+  }
+  int dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  Side& sd = g_side[dev];
+  if ((e = side_init(sd)) != hipSuccess) return e;
+  if ((e = hipEventRecord(sd.fork, s)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sd.state_st, sd.fork, 0)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sd.out_st, sd.fork, 0)) != hipSuccess) return e;
+  // each wait is enqueued right after the record it refers to, so the events are reused
+  auto hand_off = [&](hipStream_t from, hipEvent_t ev, hipStream_t to) {
+    hipError_t err = hipEventRecord(ev, from);
+    return err == hipSuccess ? hipStreamWaitEvent(to, ev, 0) : err;
+  };
+  hipError_t err = hipSuccess;
+  for (int64_t i = 0; i < nseg && err == hipSuccess; ++i) {
+    const auto [t0, t1] = seg(i);
+    if ((err = build_kv(s, t0, t1)) != hipSuccess) break;
+    if ((err = hand_off(s, sd.built, sd.state_st)) != hipSuccess) break;
+    if ((err = state_fwd(sd.state_st, t0, t1)) != hipSuccess) break;
+    if ((err = hand_off(sd.state_st, sd.stated, sd.out_st)) != hipSuccess) break;
+    err = dq(sd.out_st, t0, t1);
+  }
+  if (err == hipSuccess && (err = build_p(s)) == hipSuccess) err = hand_off(s, sd.built, sd.state_st);
+  for (int64_t i = nseg - 1; i >= 0 && err == hipSuccess; --i) {
+    const auto [t0, t1] = seg(i);
+    if ((err = state_bwd(sd.state_st, t0, t1)) != hipSuccess) break;
+    if ((err = hand_off(sd.state_st, sd.stated, sd.out_st)) != hipSuccess) break;
+    err = grads(sd.out_st, t0, t1);
+  }
+  // join, also after a failed launch, so the caller's stream stays ordered
+  if ((e = hipEventRecord(sd.state_done, sd.state_st)) != hipSuccess) return e;
+  if ((e = hipEventRecord(sd.out_done, sd.out_st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(s, sd.state_done, 0)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(s, sd.out_done, 0)) != hipSuccess) return e;
+  return err == hipSuccess ? reduce() : err;
+}
+
 int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
                    const void* v, const float* gamma, const float* beta, const float* state_in,
                    void* out, float* state_out, void* workspace, size_t workspace_bytes,
@@ -518,49 +621,20 @@ int gdn_frame_bwd(const gdn_shape* shape, int in_dtype, const void* q, const voi
 
   const size_t slot = round256(d.map_elems * sizeof(float));
   char* ws = static_cast<char*>(workspace);
-  float* G = reinterpret_cast<float*>(ws);
-  float* U = reinterpret_cast<float*>(ws + slot);
-  float* M_all = reinterpret_cast<float*>(ws + 2 * slot);
-  float* P = reinterpret_cast<float*>(ws + 3 * slot);
-  float* LB = reinterpret_cast<float*>(ws + 4 * slot);
-  float* Sb = reinterpret_cast<float*>(ws + 5 * slot);
-  float* partials = reinterpret_cast<float*>(ws + 6 * slot);
-  float* fstate = reinterpret_cast<float*>(ws + 6 * slot +
-                                           round256((size_t)d.frames * gdn::kBwdParts * 2 * sizeof(float)));
-  const auto* qb = static_cast<const uint16_t*>(q);
-  const auto* kb = static_cast<const uint16_t*>(k);
-  const auto* vb = static_cast<const uint16_t*>(v);
-  const auto* ob = static_cast<const uint16_t*>(d_out);
-  const int S = (int)d.S;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  // forward recomputation: G_t, U_t and every state M_t (float32 forms)
-  if ((e = gdn::launch_build_bf16_d128(kb, vb, G, false, U, d.heads, d.T, 0, d.T, S, s)) != hipSuccess)
-    return GDN_E_HIP;
-  if ((e = gdn::launch_state_d128(G, false, U, gamma, beta, state_in, M_all, fstate, d.heads, d.T, 0, d.T, s)) !=
-      hipSuccess)
-    return GDN_E_HIP;
-  // P_t = d_out_t^T Q_t: the build's second map with (K, V) = (Q, d_out); its
-  // first map (Q^T Q) lands in the S buffer and is overwritten below
-  if ((e = gdn::launch_build_bf16_d128(qb, ob, Sb, false, P, d.heads, d.T, 0, d.T, S, s)) != hipSuccess)
-    return GDN_E_HIP;
-  // reverse-time state pass: LB_t = beta_t Lambda_t, dgamma/dbeta partials, d_state_in
-  if ((e = gdn::launch_state_bwd_d128(G, U, P, M_all, state_in, gamma, beta, d_state_out, LB, partials,
-                                      d_state_in, d.heads, d.T, s)) != hipSuccess)
-    return GDN_E_HIP;
-  if ((e = gdn::launch_bwd_reduce(partials, dgamma, dbeta, d.frames, s)) != hipSuccess) return GDN_E_HIP;
-  if ((e = gdn::launch_sym_bwd_d128(M_all, state_in, LB, gamma, Sb, d.heads, d.T, s)) != hipSuccess)
-    return GDN_E_HIP;
-  // contractions over tokens, on the output kernel (out = X_t Y_t^T form)
-  if ((e = gdn::launch_output_bwd_d128(ob, M_all, dq, true, false, d.heads, d.T, S, s)) != hipSuccess)
-    return GDN_E_HIP;  // dq = d_out M
-  if ((e = gdn::launch_output_bwd_d128(kb, LB, dv, false, false, d.heads, d.T, S, s)) != hipSuccess)
-    return GDN_E_HIP;  // dv = K LB^T
-  if ((e = gdn::launch_output_bwd_d128(vb, LB, dk, true, false, d.heads, d.T, S, s)) != hipSuccess)
-    return GDN_E_HIP;  // dk = V LB
-  if ((e = gdn::launch_output_bwd_d128(kb, Sb, dk, false, true, d.heads, d.T, S, s)) != hipSuccess)
-    return GDN_E_HIP;  // dk += K S
-  return GDN_OK;
+  BwdBuffers b;
+  b.G = reinterpret_cast<float*>(ws);
+  b.U = reinterpret_cast<float*>(ws + slot);
+  b.M_all = reinterpret_cast<float*>(ws + 2 * slot);
+  b.P = reinterpret_cast<float*>(ws + 3 * slot);
+  b.LB = reinterpret_cast<float*>(ws + 4 * slot);
+  b.Sb = reinterpret_cast<float*>(ws + 5 * slot);
+  b.partials = reinterpret_cast<float*>(ws + 6 * slot);
+  b.fstate = reinterpret_cast<float*>(ws + 6 * slot +
+                                      round256((size_t)d.frames * gdn::kBwdParts * 2 * sizeof(float)));
+  const BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                  static_cast<const uint16_t*>(d_out), gamma, beta, state_in, d_state_out,
+                  dq, dk, dv, dgamma, dbeta, d_state_in};
+  return hip_status(run_bwd(d, a, b, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -7,8 +7,8 @@
 // One workgroup per frame (frame_output.h has the tiling and the access
 // patterns), or per token part of a frame when a launch has only a few
 // frames; frames [t0, t0 + nt) of every head per launch.  The backward pass
-// uses it as well, with M_t given as float32 and optionally transposed or
-// added to the output (see output_frame).
+// uses it as well, with M_t given as float32 and optionally transposed (see
+// output_frame).
 #include "frame_output.h"
 #include "gdn_launch.h"
 
@@ -17,7 +17,7 @@
 namespace gdn {
 namespace {
 
-template <bool kPackedM, bool kOutBf16, bool kTransM = false, bool kAccum = false>
+template <bool kPackedM, bool kOutBf16, bool kTransM = false>
 __global__ __launch_bounds__(256, 2) void k3_output_bf16_d128(
     const uint16_t* __restrict__ Q, const void* __restrict__ M_all, void* __restrict__ out, int S,
     int64_t T, int t0, int nt, int nsplit) {
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256, 2) void k3_output_bf16_d128(
   const int64_t in_off = (f * (int64_t)S + s0) * D;
   const char* Mt = static_cast<const char*>(M_all) + f * packed::kFrameBytes;
   void* Of = static_cast<char*>(out) + in_off * (kOutBf16 ? 2 : 4);
-  output_frame<kPackedM, kOutBf16, 1, kTransM, kAccum>(Q + in_off, Mt, Of, s1 - s0, Ml, [] {});
+  output_frame<kPackedM, kOutBf16, 1, kTransM>(Q + in_off, Mt, Of, s1 - s0, Ml, [] {});
 }
 
 }  // namespace
@@ -58,23 +58,21 @@ hipError_t launch_out(const uint16_t* q, const void* M_all, void* out, bool out_
   return hipGetLastError();
 }
 
-template <bool kTransM, bool kAccum>
-hipError_t launch_out_bwd(const uint16_t* q, const float* M_all, float* out, int64_t heads, int64_t T, int S,
-                          hipStream_t st) {
-  const int64_t frames = heads * T;
+template <bool kTransM>
+hipError_t launch_out_bwd(const uint16_t* q, const float* M_all, float* out, int64_t heads, int64_t T, int64_t t0,
+                          int64_t t1, int S, hipStream_t st) {
+  const int nt = (int)(t1 - t0);
+  const int64_t frames = heads * nt;
   const int nsplit = token_split(frames, S);
-  hipLaunchKernelGGL((k3_output_bf16_d128<false, false, kTransM, kAccum>), dim3((unsigned)(frames * nsplit)),
-                     dim3(256), 0, st, q, M_all, out, S, T, 0, (int)T, nsplit);
+  hipLaunchKernelGGL((k3_output_bf16_d128<false, false, kTransM>), dim3((unsigned)(frames * nsplit)), dim3(256),
+                     0, st, q, M_all, out, S, T, (int)t0, nt, nsplit);
   return hipGetLastError();
 }
 
-hipError_t launch_output_bwd_d128(const uint16_t* q, const float* M_all, float* out, bool trans_m,
-                                  bool accumulate, int64_t heads, int64_t T, int S, hipStream_t st) {
-  if (trans_m)
-    return accumulate ? launch_out_bwd<true, true>(q, M_all, out, heads, T, S, st)
-                      : launch_out_bwd<true, false>(q, M_all, out, heads, T, S, st);
-  return accumulate ? launch_out_bwd<false, true>(q, M_all, out, heads, T, S, st)
-                    : launch_out_bwd<false, false>(q, M_all, out, heads, T, S, st);
+hipError_t launch_output_bwd_d128(const uint16_t* q, const float* M_all, float* out, bool trans_m, int64_t heads,
+                                  int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st) {
+  return trans_m ? launch_out_bwd<true>(q, M_all, out, heads, T, t0, t1, S, st)
+                 : launch_out_bwd<false>(q, M_all, out, heads, T, t0, t1, S, st);
 }
 
 hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool packed_m, void* out,

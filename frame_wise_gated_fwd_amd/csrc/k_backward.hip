@@ -1,7 +1,9 @@
 // Backward pass of the frame-wise GDN, head dim 128: the reverse-time state
-// pass, the reduction of its dgamma/dbeta partial sums, and the symmetric
-// G-gradient term.  (The contractions over tokens reuse the forward's build
-// and output kernels; see gdn_api.cpp.)
+// pass, the reduction of its dgamma/dbeta partial sums, the symmetric
+// G-gradient term and the key gradient.  (dq, dv and P_t = dO_t^T Q_t reuse
+// the forward's output and build kernels; gdn_api.cpp orders the launches.)
+// Every launcher covers frames [t0, t1) of every head, so the schedule can
+// cut the sequence into segments; results do not depend on the cut.
 //
 // Reverse-time state pass.
 //
@@ -12,7 +14,10 @@
 //   Lambda_t = L_t + P_t,          P_t = dO_t^T Q_t,  L_{T-1} = dM_T,
 //   X_t      = Lambda_t G_t,
 //   L_{t-1}  = gamma_t (Lambda_t - beta_t X_t)      (G_t is symmetric),
-// and the gradient of the initial state is L_{-1}.  Per frame this kernel
+// and the gradient of the initial state is L_{-1}.  A launch over frames
+// [tb, te) starts from L_{te-1} in d_state_out and leaves L_{tb-1} in
+// d_state_in (P_{tb-1} not yet added, as the next launch adds it).  Per
+// frame this kernel
 // also writes LB_t = beta_t Lambda_t (the frame's dU_t, which the gradient
 // kernels use) and, over its rows, partial sums of
 //   dgamma_t = < Lambda_t - beta_t X_t, M_{t-1} >,
@@ -27,6 +32,7 @@
 // M_{t-1} and P_{t-1}) stream through a two-frame register ring.  The
 // partial sums are reduced in a fixed order (lanes, then waves), so the
 // results are deterministic.
+#include "frame_output.h"
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -59,7 +65,7 @@ __global__ __launch_bounds__(256, 1) void k2_state_bwd_d128(
     const float* __restrict__ G, const float* __restrict__ U, const float* __restrict__ P,
     const float* __restrict__ M_all, const float* m0, const float* __restrict__ gamma,
     const float* __restrict__ beta, const float* d_state_out, float* __restrict__ LB,
-    float* __restrict__ partials, float* d_state_in, int heads, int T) {
+    float* __restrict__ partials, float* d_state_in, int heads, int T, int tb, int te) {
   __shared__ uint16_t Ml[2][2][kRows][kLdsW];  // [buffer][hi|lo][row][col]
   __shared__ float red[2][4][2];              // [buffer][wave][dgamma, dbeta]
 
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(256, 1) void k2_state_bwd_d128(
   for (int cb = 0; cb < 2; ++cb) {
     const f32x4 d0 = d_state_out ? *reinterpret_cast<const f32x4*>(d_state_out + hoff + row * D + col_of(cb))
                                  : (f32x4){0.f, 0.f, 0.f, 0.f};
-    Lr[cb] = d0 + *reinterpret_cast<const f32x4*>(P + frame(T - 1) + row * D + col_of(cb));  // Lambda_{T-1}
+    Lr[cb] = d0 + *reinterpret_cast<const f32x4*>(P + frame(te - 1) + row * D + col_of(cb));  // Lambda_{te-1}
   }
   auto put_lds = [&](int buf) {
 #pragma unroll
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(256, 1) void k2_state_bwd_d128(
   f32x4 ru[kDepth][2], rm[kDepth][2], rp[kDepth][2];
   auto load_frame = [&](auto jc, int t) {
     constexpr int j = decltype(jc)::value;
-    if (t < 0) return;
+    if (t < tb) return;
     const float* Gt = G + frame(t);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
@@ -119,31 +125,31 @@ __global__ __launch_bounds__(256, 1) void k2_state_bwd_d128(
       const int e = row * D + col_of(cb);
       ru[j][cb] = *reinterpret_cast<const f32x4*>(U + frame(t) + e);
       rm[j][cb] = Mp ? *reinterpret_cast<const f32x4*>(Mp + e) : zero;
-      rp[j][cb] = t > 0 ? *reinterpret_cast<const f32x4*>(P + frame(t - 1) + e) : zero;
+      rp[j][cb] = t > tb ? *reinterpret_cast<const f32x4*>(P + frame(t - 1) + e) : zero;
     }
   };
 
-  // gamma/beta: lane i holds frame T-1-(64k+i) of window k (vector loads,
+  // gamma/beta: lane i holds frame te-1-(64k+i) of window k (vector loads,
   // read with readlane; scalar loads would share the LDS wait counter)
   const float* gh = gamma + (int64_t)head * T;
   const float* bh = beta + (int64_t)head * T;
   auto win_load = [&](int i0, float& gv, float& bv) {
-    const int t = T - 1 - (i0 + l);
-    gv = t >= 0 ? gh[t] : 0.f;
-    bv = t >= 0 ? bh[t] : 0.f;
+    const int t = te - 1 - (i0 + l);
+    gv = t >= tb ? gh[t] : 0.f;
+    bv = t >= tb ? bh[t] : 0.f;
   };
   float gwin, bwin, gnxt, bnxt;
   win_load(0, gwin, bwin);
   win_load(64, gnxt, bnxt);
 
   [&]<int... js>(std::integer_sequence<int, js...>) {
-    (load_frame(std::integral_constant<int, js>{}, T - 1 - js), ...);
+    (load_frame(std::integral_constant<int, js>{}, te - 1 - js), ...);
   }(std::make_integer_sequence<int, kDepth>{});
   lds_barrier();
 
   auto step = [&](auto jc, int i) {
     constexpr int j = decltype(jc)::value;
-    const int t = T - 1 - i;
+    const int t = te - 1 - i;
     const int buf = i & 1;
     const int iw = i & 63;
     const float gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwin), iw));
@@ -201,8 +207,8 @@ __global__ __launch_bounds__(256, 1) void k2_state_bwd_d128(
         dg = fmaf(fmaf(-bt, x, lam), mm[cb][e], dg);
         db = fmaf(lam, uu[cb][e], fmaf(-gm * x, mm[cb][e], db));
         // L_{t-1} = gamma (Lambda - beta X), rounded, then + P_{t-1} (zero at
-        // t = 0): the same two roundings as when a sequence is cut here and
-        // the next call adds P_{t-1} to the state gradient it is given
+        // t = tb): the same two roundings as when a sequence is cut here and
+        // the next launch or call adds P_{t-1} to the state gradient it is given
         Lr[cb][e] = mul_then_add(gm, fmaf(-bt, x, lam), pp[cb][e]);
       }
       *reinterpret_cast<f32x4*>(LBt + row * D + col_of(cb)) = lb;
@@ -222,12 +228,14 @@ __global__ __launch_bounds__(256, 1) void k2_state_bwd_d128(
     }
   };
 
-  for (int i0 = 0; i0 < T; i0 += kDepth) {
+  const int nf = te - tb;
+  for (int i0 = 0; i0 < nf; i0 += kDepth) {
     [&]<int... js>(std::integer_sequence<int, js...>) {
-      ((i0 + js < T ? step(std::integral_constant<int, js>{}, i0 + js) : void()), ...);
+      ((i0 + js < nf ? step(std::integral_constant<int, js>{}, i0 + js) : void()), ...);
     }(std::make_integer_sequence<int, kDepth>{});
   }
-  // after frame 0 the running value is the gradient of the initial state
+  // after frame tb the running value is L_{tb-1} (the gradient of the
+  // initial state when tb = 0)
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
     *reinterpret_cast<f32x4*>(d_state_in + hoff + row * D + col_of(cb)) = Lr[cb];
@@ -247,94 +255,263 @@ __global__ void k_bwd_reduce(const float* __restrict__ partials, float* __restri
   dbeta[f] = sb;
 }
 
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // S_t = -gamma_t (A + A^T), A = M_{t-1}^T LB_t (both float32 row-major), one
 // workgroup per frame.  The gradient of G_t = K_t^T K_t is
 // dG_t = -gamma_t beta_t M_{t-1}^T Lambda_t, and K_t receives K_t (dG + dG^T);
-// LB_t = beta_t Lambda_t already carries beta.  Thread (ta, tb) accumulates
-// the 8 x 8 block A[8ta .. 8ta+7][8tb .. 8tb+7] over 32-row chunks of M and
-// LB staged in LDS; A then goes through LDS once more to be symmetrized.
-__global__ __launch_bounds__(256, 1) void k_sym_bwd_d128(const float* __restrict__ M_all, const float* m0,
+// LB_t = beta_t Lambda_t already carries beta.  A runs on float32 MFMA
+// (v_mfma_f32_16x16x4_f32: exact products, float32 accumulation): wave w
+// computes rows 32w .. 32w+31 of A, 2 x 8 blocks of 16 x 16, reducing over the
+// 128 rows of M and LB in chunks of 32 rows staged through LDS (the next
+// chunk is loaded into registers meanwhile).  Both operands are read along
+// rows: for A[m][k] = M[i][m] and B[k][n] = LB[i][n] (k = i), 16 lanes read
+// 16 consecutive floats of one row.  A then goes through LDS once to be
+// symmetrized; S is exactly symmetric (the two sums are the same float
+// addition), so each lane stores the value for (a, b) at (b, a), four
+// consecutive columns at once.
+__global__ __launch_bounds__(256, 2) void k_sym_bwd_d128(const float* __restrict__ M_all, const float* m0,
                                                        const float* __restrict__ LB,
                                                        const float* __restrict__ gamma,
-                                                       float* __restrict__ Sout, int T) {
+                                                       float* __restrict__ Sout, int T, int t0, int nt) {
   constexpr int kChunk = 32;
-  __shared__ float Ms[kChunk][D];
-  __shared__ float Ls[kChunk][D];
-  __shared__ float As[D][D + 1];
-  const int64_t f = blockIdx.x;
-  const int head = (int)(f / T), t = (int)(f % T);
+  constexpr int kCw = D + 16;  // chunk row (floats): consecutive rows start 16 banks apart, so the
+                               // 4 rows x 16 columns of an operand read hit 64 distinct banks
+  constexpr int kAw = D + 4;   // row of A (floats): 16-byte rows, transposed reads without conflicts
+  constexpr int kLds = 2 * kChunk * kCw > D * kAw ? 2 * kChunk * kCw : D * kAw;
+  __shared__ __attribute__((aligned(16))) float lds[kLds];
+  const int j = blockIdx.x;
+  const int head = j / nt, t = t0 + j % nt;
+  const int64_t f = (int64_t)head * T + t;
   const float* Mp = t > 0 ? M_all + (f - 1) * D * D : (m0 ? m0 + (int64_t)head * D * D : nullptr);
   const float* Lt = LB + f * D * D;
   float* St = Sout + f * D * D;
   const int tid = threadIdx.x;
-  const int ta = tid >> 4, tb = tid & 15;
   if (!Mp) {  // zero initial state: M_{-1} = 0, so S_0 = 0
     for (int i = tid; i < D * D / 4; i += 256) reinterpret_cast<f32x4*>(St)[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     return;
   }
-  float acc[8][8];
+  const int w = tid >> 6, l = tid & 63;
+  const int n = l & 15, g = l >> 4;
+  float (*Ms)[kCw] = reinterpret_cast<float (*)[kCw]>(lds);
+  float (*Ls)[kCw] = reinterpret_cast<float (*)[kCw]>(lds + kChunk * kCw);
+
+  // a chunk is 32 rows x 32 float4 of each matrix: 4 float4 of each per thread
+  f32x4 pm[4], pl[4];
+  auto load_chunk = [&](int c) {
 #pragma unroll
-  for (int x = 0; x < 8; ++x)
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + 256 * k, r = idx >> 5, c4 = (idx & 31) * 4;
+      pm[k] = *reinterpret_cast<const f32x4*>(Mp + (kChunk * c + r) * D + c4);
+      pl[k] = *reinterpret_cast<const f32x4*>(Lt + (kChunk * c + r) * D + c4);
+    }
+  };
+  f32x4 acc[2][8];
 #pragma unroll
-    for (int y = 0; y < 8; ++y) acc[x][y] = 0.f;
-  for (int i0 = 0; i0 < D; i0 += kChunk) {
-    __syncthreads();
-    for (int e = tid; e < kChunk * D / 4; e += 256) {
-      const int r = e / (D / 4), c = (e % (D / 4)) * 4;
-      *reinterpret_cast<f32x4*>(&Ms[r][c]) = *reinterpret_cast<const f32x4*>(Mp + (i0 + r) * D + c);
-      *reinterpret_cast<f32x4*>(&Ls[r][c]) = *reinterpret_cast<const f32x4*>(Lt + (i0 + r) * D + c);
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[rb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  load_chunk(0);
+  for (int c = 0; c < D / kChunk; ++c) {
+    if (c) __syncthreads();  // every wave is done with the previous chunk
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + 256 * k, r = idx >> 5, c4 = (idx & 31) * 4;
+      *reinterpret_cast<f32x4*>(&Ms[r][c4]) = pm[k];
+      *reinterpret_cast<f32x4*>(&Ls[r][c4]) = pl[k];
     }
     __syncthreads();
-    for (int i = 0; i < kChunk; ++i) {
-      const f32x4 m0v = *reinterpret_cast<const f32x4*>(&Ms[i][8 * ta]);
-      const f32x4 m1v = *reinterpret_cast<const f32x4*>(&Ms[i][8 * ta + 4]);
-      const f32x4 l0v = *reinterpret_cast<const f32x4*>(&Ls[i][8 * tb]);
-      const f32x4 l1v = *reinterpret_cast<const f32x4*>(&Ls[i][8 * tb + 4]);
-      const float mv[8] = {m0v[0], m0v[1], m0v[2], m0v[3], m1v[0], m1v[1], m1v[2], m1v[3]};
-      const float lv[8] = {l0v[0], l0v[1], l0v[2], l0v[3], l1v[0], l1v[1], l1v[2], l1v[3]};
+    if (c + 1 < D / kChunk) load_chunk(c + 1);
 #pragma unroll
-      for (int x = 0; x < 8; ++x)
+    for (int k0 = 0; k0 < kChunk; k0 += 4) {
+      // A operand: lane (n, g) holds A[n][g] = M[i][32w + 16rb + n]; B: LB[i][16nb + n]
+      const int i = k0 + g;
+      float a[2], b[8];
 #pragma unroll
-        for (int y = 0; y < 8; ++y) acc[x][y] = fmaf(mv[x], lv[y], acc[x][y]);
+      for (int rb = 0; rb < 2; ++rb) a[rb] = Ms[i][32 * w + 16 * rb + n];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) b[nb] = Ls[i][16 * nb + n];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) acc[rb][nb] = mfma16x16x4f32(a[rb], b[nb], acc[rb][nb]);
     }
   }
+  __syncthreads();  // the chunks are dead: A takes their LDS
+  float (*As)[kAw] = reinterpret_cast<float (*)[kAw]>(lds);
+  // lane (n, g) holds A[32w + 16rb + 4g + i][16nb + n] in acc[rb][nb][i]
 #pragma unroll
-  for (int x = 0; x < 8; ++x)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int y = 0; y < 8; ++y) As[8 * ta + x][8 * tb + y] = acc[x][y];
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) As[32 * w + 16 * rb + 4 * g + i][16 * nb + n] = acc[rb][nb][i];
   __syncthreads();
   const float ng = -gamma[f];
 #pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const int a = 8 * ta + x;
-    f32x4 s0, s1;
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      s0[y] = ng * (acc[x][y] + As[8 * tb + y][a]);
-      s1[y] = ng * (acc[x][y + 4] + As[8 * tb + y + 4][a]);
+    for (int nb = 0; nb < 8; ++nb) {
+      const int b = 16 * nb + n, a0 = 32 * w + 16 * rb + 4 * g;
+      const f32x4 at = *reinterpret_cast<const f32x4*>(&As[b][a0]);  // A[b][a0 .. a0+3]
+      f32x4 sv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = ng * (acc[rb][nb][i] + at[i]);
+      *reinterpret_cast<f32x4*>(St + b * D + a0) = sv;  // S[b][a0 + i] = S[a0 + i][b]
     }
-    *reinterpret_cast<f32x4*>(St + a * D + 8 * tb) = s0;
-    *reinterpret_cast<f32x4*>(St + a * D + 8 * tb + 4) = s1;
+}
+
+// dk_t = V_t LB_t + K_t S_t for the tokens of one frame (or one token part
+// of it, in launches of a few frames): per output element one 256-term
+// reduction, 128 terms over the rows of LB_t and then 128 over those of S_t
+// (symmetric), in one accumulator; dk is written once.  Tiling and global
+// access patterns are the output kernel's (frame_output.h), with two A
+// operands per 32-token tile (V rows and K rows) and two staged matrices:
+// LB_t^T and S_t, each as bf16 hi/lo planes in LDS (2 x 69.6 KB, so one
+// workgroup per CU), which carry them to about 2^-17 relative.
+template <int kDepth>
+__global__ __launch_bounds__(256, 1) void k_dk_d128(const uint16_t* __restrict__ V, const uint16_t* __restrict__ K,
+                                                  const float* __restrict__ LB, const float* __restrict__ Sm,
+                                                  float* __restrict__ dk, int S, int64_t T, int t0, int nt,
+                                                  int nsplit) {
+  __shared__ uint16_t Ml[2][2][D][kOutLdsW];  // [LB^T | S][hi | lo][LDS row][column]
+  const int jf = blockIdx.x / nsplit, part = blockIdx.x % nsplit;
+  const int64_t f = (int64_t)(jf / nt) * T + t0 + jf % nt;
+  const int s0 = (int)((int64_t)part * S / nsplit), s1 = (int)((int64_t)(part + 1) * S / nsplit);
+  const int ns = s1 - s0;
+  const int64_t in_off = (f * (int64_t)S + s0) * D;
+  const uint16_t* Vf = V + in_off;
+  const uint16_t* Kf = K + in_off;
+  float* Of = dk + in_off;
+  const float* LBt = LB + f * D * D;
+  const float* St = Sm + f * D * D;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63;
+  const int n = l & 15, g = l >> 4;
+
+  // LDS row lds_row(r) of a staged matrix holds its row r (output column
+  // sigma, as in the output kernel): staged LB^T row c is column c of LB
+  for (int idx = tid; idx < D * D / 4; idx += 256) {
+    const int r = idx >> 5, c4 = (idx & 31) * 4;
+    const f32x4 lv = *reinterpret_cast<const f32x4*>(LBt + r * D + c4);
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(St + r * D + c4);
+    const u32x2 p0 = split2(lv[0], lv[1]), p1 = split2(lv[2], lv[3]);
+    const uint32_t hi[2] = {p0.x, p1.x}, lo[2] = {p0.y, p1.y};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rho = lds_row<false>(c4 + e);
+      Ml[0][0][rho][r] = (uint16_t)(hi[e >> 1] >> (16 * (e & 1)));
+      Ml[0][1][rho][r] = (uint16_t)(lo[e >> 1] >> (16 * (e & 1)));
+    }
+    const u32x2 q0 = split2(sv[0], sv[1]), q1 = split2(sv[2], sv[3]);
+    const int rs = lds_row<false>(r);
+    *reinterpret_cast<u32x2*>(&Ml[1][0][rs][c4]) = (u32x2){q0.x, q1.x};
+    *reinterpret_cast<u32x2*>(&Ml[1][1][rs][c4]) = (u32x2){q0.y, q1.y};
+  }
+  __syncthreads();
+
+  constexpr int kTile = kOutTile;
+  const int ntiles = (ns + kTile - 1) / kTile;
+  // A operands of a 32-token tile: lane (m, g) holds tokens tok0 + 16rb + m,
+  // dims 32kb + 8g .. +7 of V (av) and of K (ak)
+  auto load_a = [&](int tile, u32x4 (&av)[2][4], u32x4 (&ak)[2][4]) {
+    const int tok0 = tile * kTile;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int s = tok0 + 16 * rb + n;
+      const bool in = tile < ntiles && s < ns;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int64_t o = (int64_t)s * D + 32 * kb + 8 * g;
+        av[rb][kb] = in ? *reinterpret_cast<const u32x4*>(Vf + o) : (u32x4){0u, 0u, 0u, 0u};
+        ak[rb][kb] = in ? *reinterpret_cast<const u32x4*>(Kf + o) : (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  constexpr int kRing = kDepth + 1;
+  u32x4 rv[kRing][2][4], rk[kRing][2][4];
+  auto tile_body = [&](auto jc, int tile) {
+    constexpr int jb = decltype(jc)::value;
+    const int tok0 = tile * kTile;
+    load_a(tile + 4 * kDepth, rv[(jb + kDepth) % kRing], rk[(jb + kDepth) % kRing]);
+    f32x4 acc[2][8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) acc[rb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        u32x4(&a)[2][4] = m == 0 ? rv[jb] : rk[jb];
+        u32x4 bh[4], bl[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          bh[kb] = *reinterpret_cast<const u32x4*>(&Ml[m][0][nb * 16 + n][32 * kb + 8 * g]);
+          bl[kb] = *reinterpret_cast<const u32x4*>(&Ml[m][1][nb * 16 + n][32 * kb + 8 * g]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            acc[rb][nb] = mfma16x16x32(a[rb][kb], bh[kb], acc[rb][nb]);
+            acc[rb][nb] = mfma16x16x32(a[rb][kb], bl[kb], acc[rb][nb]);
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane (n, g), register i of block nb: dk[tok0 + 16rb + 4g + i][sigma(nb, n)]
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = tok0 + 16 * rb + 4 * g + i;
+        if (s >= ns) continue;
+        float* o = Of + (int64_t)s * D + 4 * n;
+        st_nt(reinterpret_cast<f32x4*>(o), (f32x4){acc[rb][0][i], acc[rb][1][i], acc[rb][2][i], acc[rb][3][i]});
+        st_nt(reinterpret_cast<f32x4*>(o + 64),
+              (f32x4){acc[rb][4][i], acc[rb][5][i], acc[rb][6][i], acc[rb][7][i]});
+      }
+  };
+  [&]<int... js>(std::integer_sequence<int, js...>) {
+    (load_a(w + 4 * js, rv[js], rk[js]), ...);
+  }(std::make_integer_sequence<int, kDepth>{});
+  for (int tile0 = w; tile0 < ntiles; tile0 += 4 * kRing) {
+    [&]<int... js>(std::integer_sequence<int, js...>) {
+      ((tile0 + 4 * js < ntiles ? tile_body(std::integral_constant<int, js>{}, tile0 + 4 * js) : void()), ...);
+    }(std::make_integer_sequence<int, kRing>{});
   }
 }
 
 }  // namespace
 
 hipError_t launch_sym_bwd_d128(const float* M_all, const float* m0, const float* LB, const float* gamma,
-                               float* Sout, int64_t heads, int64_t T, hipStream_t st) {
-  hipLaunchKernelGGL(k_sym_bwd_d128, dim3((unsigned)(heads * T)), dim3(256), 0, st, M_all, m0, LB, gamma, Sout,
-                     (int)T);
+                               float* Sout, int64_t heads, int64_t T, int64_t t0, int64_t t1, hipStream_t st) {
+  const int64_t nt = t1 - t0;
+  hipLaunchKernelGGL(k_sym_bwd_d128, dim3((unsigned)(heads * nt)), dim3(256), 0, st, M_all, m0, LB, gamma, Sout,
+                     (int)T, (int)t0, (int)nt);
+  return hipGetLastError();
+}
+
+hipError_t launch_dk_bwd_d128(const uint16_t* v, const uint16_t* k, const float* LB, const float* Sm, float* dk,
+                              int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st) {
+  const int64_t nt = t1 - t0, frames = heads * nt;
+  const int nsplit = token_split(frames, S);
+  hipLaunchKernelGGL(k_dk_d128<1>, dim3((unsigned)(frames * nsplit)), dim3(256), 0, st, v, k, LB, Sm, dk, S, T,
+                     (int)t0, (int)nt, nsplit);
   return hipGetLastError();
 }
 
 hipError_t launch_state_bwd_d128(const float* G, const float* U, const float* P, const float* M_all,
                                  const float* m0, const float* gamma, const float* beta,
                                  const float* d_state_out, float* LB, float* partials, float* d_state_in,
-                                 int64_t heads, int64_t T, hipStream_t st) {
+                                 int64_t heads, int64_t T, int64_t t0, int64_t t1, hipStream_t st) {
   // workgroup ids grouped so that the parts of a head share id % 8 (one XCD)
   const unsigned grid = (unsigned)((heads + 7) / 8 * 8 * kBwdParts);
   hipLaunchKernelGGL(k2_state_bwd_d128, dim3(grid), dim3(256), 0, st, G, U, P, M_all, m0, gamma, beta,
-                     d_state_out, LB, partials, d_state_in, (int)heads, (int)T);
+                     d_state_out, LB, partials, d_state_in, (int)heads, (int)T, (int)t0, (int)t1);
   return hipGetLastError();
 }
 

@@ -86,15 +86,25 @@ def test_backward_in_place_state_gradient_and_determinism():
         assert torch.equal(res[i], a[key]), key
 
 
-def test_chunked_backward_equals_one_call_bitwise():
+def test_backward_segmented_schedule():
+    """T = 150 is cut into segments (the forward recomputation and the
+    reverse-time pass run segment by segment on the side streams)."""
+    w = Workload(name="bwd_segments", B=1, H=3, T=150, S=48, D=128, in_dtype="bf16", seed=75,
+                 gamma_range=(0.95, 1.0), beta_kind="sigmoid_normal", state_std=0.05)
+    _backward_parity(w)
+
+
+@pytest.mark.parametrize("T,t0,S", [(9, 4, 120), (150, 70, 40)])
+def test_chunked_backward_equals_one_call_bitwise(T, t0, S):
     """Frames [t0, T) then [0, t0), carrying the forward state forwards and the
-    state gradient backwards, reproduce the one-call backward bit for bit."""
-    w = Workload(name="bwd_chunks", B=1, H=3, T=9, S=120, D=128, in_dtype="bf16", seed=74,
+    state gradient backwards, reproduce the one-call backward bit for bit
+    (the calls also differ in how many segments their schedules use)."""
+    w = Workload(name="bwd_chunks", B=1, H=3, T=T, S=S, D=128, in_dtype="bf16", seed=74,
                  gamma_range=(0.9, 1.0), beta_kind="sigmoid_normal", state_std=0.05)
+    log(f"chunked backward: T={T} t0={t0} S={S}")
     x = device_inputs(w, DEV)
     d_out_t, d_state = _upstream(w, 6, True)
     one = _gpu_backward(x, d_out_t, d_state)
-    t0 = 4
     sl1, sl2 = slice(0, t0), slice(t0, w.T)
     part = lambda key, sl: x[key][:, :, sl].contiguous()
     _, mid = F.frame_fwd(part("q", sl1), part("k", sl1), part("v", sl1), part("gamma", sl1),
