@@ -59,10 +59,11 @@ def per_head_frame_bytes(S, D, in_bytes=2, out_bytes=4):
         "fused": 3 * qkv + o,           # the fused kernel: G, U, M stay on chip
         # backward: q, k, v, d_out in; dq, dk, dv out (f32)
         "backward": 4 * qkv + 3 * o,
-        # what its kernels move: eight bf16 token-tensor reads (K, V twice
-        # each; Q, dO in the P build; dO for dq; K for dv), three f32
-        # gradient writes and nineteen D x D float32 maps written or read
-        "backward_design": 8 * qkv + 3 * o + 19 * dd,
+        # what its kernels move: seven bf16 token-tensor reads (K, V twice
+        # each; Q, dO in the P build; dO for dq), three f32 gradient writes
+        # and seventeen D x D float32 maps written or read (G, U: 3 each;
+        # M: 4; P: 2; LB: 3; S: 2)
+        "backward_design": 7 * qkv + 3 * o + 17 * dd,
     }
 
 

@@ -35,7 +35,8 @@ constexpr int build_lds_bytes() { return kPacked ? 65536 : 32768; }
 // G_t = K_t^T K_t and U_t = V_t^T K_t of one frame.  Kf, Vf: the frame's
 // [S, 128] bf16 rows.  kPacked: Gout receives the packed bf16 hi/lo form
 // and Uout the packed float32 form (gdn_packed.h); otherwise both are
-// float32 row-major 128 x 128.  `lds` must hold build_lds_bytes<kPacked>().
+// float32 row-major 128 x 128, and Gout may be null (only U_t is written).
+// `lds` must hold build_lds_bytes<kPacked>().
 // kDepth: token iterations loaded ahead (register buffers of 32 VGPRs each).
 // All 256 threads of the workgroup must call it.  On return this thread's
 // stores are issued, not necessarily complete.
@@ -167,8 +168,10 @@ __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, con
         const int row = 32 * g + 8 * i + j;
         f32x4* gp = reinterpret_cast<f32x4*>(static_cast<float*>(Gout) + row * D + 8 * c);
         f32x4* up = reinterpret_cast<f32x4*>(Uout + row * D + 8 * c);
-        gp[0] = (f32x4){accG[jj][0][i], accG[jj][1][i], accG[jj][2][i], accG[jj][3][i]};
-        gp[1] = (f32x4){accG[jj][4][i], accG[jj][5][i], accG[jj][6][i], accG[jj][7][i]};
+        if (Gout) {
+          gp[0] = (f32x4){accG[jj][0][i], accG[jj][1][i], accG[jj][2][i], accG[jj][3][i]};
+          gp[1] = (f32x4){accG[jj][4][i], accG[jj][5][i], accG[jj][6][i], accG[jj][7][i]};
+        }
         up[0] = (f32x4){accU[jj][0][i], accU[jj][1][i], accU[jj][2][i], accU[jj][3][i]};
         up[1] = (f32x4){accU[jj][4][i], accU[jj][5][i], accU[jj][6][i], accU[jj][7][i]};
       }

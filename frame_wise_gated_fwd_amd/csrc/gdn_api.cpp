@@ -323,8 +323,10 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
   auto build_kv = [&](hipStream_t st, int64_t t0, int64_t t1) {
     return gdn::launch_build_bf16_d128(a.k, a.v, b.G, false, b.U, H, T, t0, t1, S, st);
   };
-  // the build's first map (Q^T Q) lands in the S buffer; S overwrites it later
-  auto build_p = [&](hipStream_t st) { return gdn::launch_build_bf16_d128(a.q, a.d_out, b.Sb, false, b.P, H, T, 0, T, S, st); };
+  // P_t = dO_t^T Q_t: the build's second map with (K, V) = (Q, dO); its first (Q^T Q) is not stored
+  auto build_p = [&](hipStream_t st) {
+    return gdn::launch_build_bf16_d128(a.q, a.d_out, nullptr, false, b.P, H, T, 0, T, S, st);
+  };
   auto state_fwd = [&](hipStream_t st, int64_t t0, int64_t t1) {
     return gdn::launch_state_d128(b.G, false, b.U, a.gamma, a.beta, t0 ? b.fstate : a.state_in, b.M_all, b.fstate,
                                   H, T, t0, t1, st);
@@ -341,9 +343,8 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
     hipError_t e;
     if ((e = gdn::launch_sym_bwd_d128(b.M_all, a.state_in, b.LB, a.gamma, b.Sb, H, T, t0, t1, st)) != hipSuccess)
       return e;
-    if ((e = gdn::launch_output_bwd_d128(a.k, b.LB, a.dv, false, H, T, t0, t1, S, st)) != hipSuccess)
-      return e;  // dv = K LB^T
-    return gdn::launch_dk_bwd_d128(a.v, a.k, b.LB, b.Sb, a.dk, H, T, t0, t1, S, st);  // dk = V LB + K S
+    // dk = V LB + K S, dv = K LB^T
+    return gdn::launch_dkv_bwd_d128(a.v, a.k, b.LB, b.Sb, a.dk, a.dv, H, T, t0, t1, S, st);
   };
   auto reduce = [&]() { return gdn::launch_bwd_reduce(b.partials, a.dgamma, a.dbeta, d.frames, s); };
   hipError_t e;

@@ -20,6 +20,8 @@ namespace gdn {
 // give bit-identical results to the full-size variants.
 constexpr int64_t kFewFrames = 128;
 
+// G_t = K_t^T K_t and U_t = V_t^T K_t for frames [t0, t1); packed_out
+// selects the packed forms, else float32 row-major, where G may be null.
 hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
                                   float* U, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
                                   hipStream_t st);
@@ -39,7 +41,7 @@ hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool pa
 // Each launcher covers frames [t0, t1) of every head; per-frame matrices are
 // float32 row-major [head][T][D][D].
 //
-// out_t = Q_t X_t^T, X_t = M_t (or M_t^T when trans_m).
+// out_t = Q_t X_t^T, X_t = M_t (or M_t^T when trans_m).  (dq = dO M uses it.)
 hipError_t launch_output_bwd_d128(const uint16_t* q, const float* M_all, float* out, bool trans_m,
                                   int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st);
 // Reverse-time state pass of the backward: from G_t, U_t, P_t = dO_t^T Q_t,
@@ -60,9 +62,9 @@ hipError_t launch_bwd_reduce(const float* partials, float* dgamma, float* dbeta,
 // (null = zero).
 hipError_t launch_sym_bwd_d128(const float* M_all, const float* m0, const float* LB, const float* gamma,
                                float* Sout, int64_t heads, int64_t T, int64_t t0, int64_t t1, hipStream_t st);
-// dk_t = V_t LB_t + K_t S_t (S_t symmetric), float32 out.
-hipError_t launch_dk_bwd_d128(const uint16_t* v, const uint16_t* k, const float* LB, const float* Sm, float* dk,
-                              int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st);
+// dk_t = V_t LB_t + K_t S_t (S_t symmetric) and dv_t = K_t LB_t^T, float32 out.
+hipError_t launch_dkv_bwd_d128(const uint16_t* v, const uint16_t* k, const float* LB, const float* Sm, float* dk,
+                               float* dv, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st);
 // Token parts per frame for a launch of `frames` frames (1 unless the launch
 // is small); the parts only split the tokens, not any reduction.
 int token_split(int64_t frames, int S);

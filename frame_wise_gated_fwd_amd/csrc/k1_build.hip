@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
   // workgroup i: frame t0 + i % nt of head i / nt (frames are [head][T])
   const int64_t f = (int64_t)(blockIdx.x / nt) * T + t0 + blockIdx.x % nt;
   const int64_t in_off = f * (int64_t)S * D, mat_off = f * (int64_t)D * D;
-  build_frame<kPacked>(K + in_off, V + in_off, S, lds, static_cast<char*>(Gout) + mat_off * 4,
+  build_frame<kPacked>(K + in_off, V + in_off, S, lds, Gout ? static_cast<char*>(Gout) + mat_off * 4 : nullptr,
                        Uout + mat_off);
 }
 
@@ -56,6 +56,7 @@ hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G,
                                   hipStream_t st) {
   const int nt = (int)(t1 - t0);
   const dim3 grid((unsigned)(heads * nt));
+  if (packed_out && !G) return hipErrorInvalidValue;  // the packed form always writes G
   if (packed_out && heads * nt <= kFewFrames)
     hipLaunchKernelGGL(k1_build_bf16_d128_deep, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt);
   else if (packed_out)

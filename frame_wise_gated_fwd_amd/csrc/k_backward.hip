@@ -1,7 +1,8 @@
 // Backward pass of the frame-wise GDN, head dim 128: the reverse-time state
 // pass, the reduction of its dgamma/dbeta partial sums, the symmetric
-// G-gradient term and the key gradient.  (dq, dv and P_t = dO_t^T Q_t reuse
-// the forward's output and build kernels; gdn_api.cpp orders the launches.)
+// G-gradient term and the key and value gradients.  (dq and P_t = dO_t^T Q_t
+// reuse the forward's output and build kernels; gdn_api.cpp orders the
+// launches.)
 // Every launcher covers frames [t0, t1) of every head, so the schedule can
 // cut the sequence into segments; results do not depend on the cut.
 //
@@ -363,20 +364,37 @@ __global__ __launch_bounds__(256, 2) void k_sym_bwd_d128(const float* __restrict
     }
 }
 
-// dk_t = V_t LB_t + K_t S_t for the tokens of one frame (or one token part
-// of it, in launches of a few frames): per output element one 256-term
-// reduction, 128 terms over the rows of LB_t and then 128 over those of S_t
-// (symmetric), in one accumulator; dk is written once.  Tiling and global
-// access patterns are the output kernel's (frame_output.h), with two A
-// operands per 32-token tile (V rows and K rows) and two staged matrices:
-// LB_t^T and S_t, each as bf16 hi/lo planes in LDS (2 x 69.6 KB, so one
-// workgroup per CU), which carry them to about 2^-17 relative.
+// ds_read_b64_tr_b16 (gfx950): each lane names an 8-byte-aligned LDS
+// address; within every 16-lane group, lane i receives as its element e
+// (e = 0..3) element i % 4 of the 8 bytes named by lane 4e + i / 4.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Key and value gradients for the tokens of one frame (or one token part of
+// it, in launches of a few frames):
+//   dk_t = V_t LB_t + K_t S_t   (S_t symmetric),   dv_t = K_t LB_t^T,
+// with LB_t^T and S_t staged once in LDS as bf16 hi/lo planes (2 x 69.6 KB,
+// so one workgroup per CU), which carry them to about 2^-17 relative.
+// Tiling and global access patterns are the output kernel's (frame_output.h):
+// a wave takes 32-token tiles of V and K rows as MFMA operands.
+//  * dk: one 256-term reduction per element, 128 terms over the rows of LB_t
+//    (A = V tile, B = staged LB^T rows) and then 128 over those of S_t
+//    (A = K tile, B = staged S rows), in one accumulator; output column
+//    sigma(nb, n) as in the output kernel, 16-byte stores.
+//  * dv, computed transposed as dv^T = LB_t K_t^T: A = rows of LB_t, which
+//    are columns of the staged LB^T, fetched with transposed LDS reads (two
+//    per fragment), and B = the K tile already in registers for dk.  A lane
+//    then holds 4 consecutive value dims of one token: 16-byte stores.
 template <int kDepth>
-__global__ __launch_bounds__(256, 1) void k_dk_d128(const uint16_t* __restrict__ V, const uint16_t* __restrict__ K,
-                                                  const float* __restrict__ LB, const float* __restrict__ Sm,
-                                                  float* __restrict__ dk, int S, int64_t T, int t0, int nt,
-                                                  int nsplit) {
-  __shared__ uint16_t Ml[2][2][D][kOutLdsW];  // [LB^T | S][hi | lo][LDS row][column]
+__global__ __launch_bounds__(256, 1) void k_dkv_d128(const uint16_t* __restrict__ V,
+                                                   const uint16_t* __restrict__ K, const float* __restrict__ LB,
+                                                   const float* __restrict__ Sm, float* __restrict__ dk,
+                                                   float* __restrict__ dv, int S, int64_t T, int t0, int nt,
+                                                   int nsplit) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ml[2][2][D][kOutLdsW];  // [LB^T | S][hi | lo][row][column]
   const int jf = blockIdx.x / nsplit, part = blockIdx.x % nsplit;
   const int64_t f = (int64_t)(jf / nt) * T + t0 + jf % nt;
   const int s0 = (int)((int64_t)part * S / nsplit), s1 = (int)((int64_t)(part + 1) * S / nsplit);
@@ -384,7 +402,8 @@ __global__ __launch_bounds__(256, 1) void k_dk_d128(const uint16_t* __restrict__
   const int64_t in_off = (f * (int64_t)S + s0) * D;
   const uint16_t* Vf = V + in_off;
   const uint16_t* Kf = K + in_off;
-  float* Of = dk + in_off;
+  float* dkf = dk + in_off;
+  float* dvf = dv + in_off;
   const float* LBt = LB + f * D * D;
   const float* St = Sm + f * D * D;
   const int tid = threadIdx.x;
@@ -436,44 +455,88 @@ __global__ __launch_bounds__(256, 1) void k_dk_d128(const uint16_t* __restrict__
     constexpr int jb = decltype(jc)::value;
     const int tok0 = tile * kTile;
     load_a(tile + 4 * kDepth, rv[(jb + kDepth) % kRing], rk[(jb + kDepth) % kRing]);
-    f32x4 acc[2][8];
+    {  // dk = V LB + K S
+      f32x4 acc[2][8];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) acc[rb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < 8; ++nb) acc[rb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
+      for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        u32x4(&a)[2][4] = m == 0 ? rv[jb] : rk[jb];
-        u32x4 bh[4], bl[4];
+        for (int m = 0; m < 2; ++m) {
+          u32x4(&a)[2][4] = m == 0 ? rv[jb] : rk[jb];
+          u32x4 bh[4], bl[4];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            bh[kb] = *reinterpret_cast<const u32x4*>(&Ml[m][0][nb * 16 + n][32 * kb + 8 * g]);
+            bl[kb] = *reinterpret_cast<const u32x4*>(&Ml[m][1][nb * 16 + n][32 * kb + 8 * g]);
+          }
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+              acc[rb][nb] = mfma16x16x32(a[rb][kb], bh[kb], acc[rb][nb]);
+              acc[rb][nb] = mfma16x16x32(a[rb][kb], bl[kb], acc[rb][nb]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // lane (n, g), register i of block nb: dk[tok0 + 16rb + 4g + i][sigma(nb, n)]
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = tok0 + 16 * rb + 4 * g + i;
+          if (s >= ns) continue;
+          float* o = dkf + (int64_t)s * D + 4 * n;
+          st_nt(reinterpret_cast<f32x4*>(o), (f32x4){acc[rb][0][i], acc[rb][1][i], acc[rb][2][i], acc[rb][3][i]});
+          st_nt(reinterpret_cast<f32x4*>(o + 64),
+                (f32x4){acc[rb][4][i], acc[rb][5][i], acc[rb][6][i], acc[rb][7][i]});
+        }
+    }
+    {  // dv^T = LB K^T
+      f32x4 acc[2][8];  // [token block rb][value-dim block ib]
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib) acc[rb][ib] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ib = 0; ib < 8; ++ib) {
+        // A fragment (ib, kb): lane (m, g) needs LB[16ib + m][32kb + 8g + j],
+        // j = 0..7, i.e. staged LB^T rows 32kb + 8g + j at column 16ib + m.
+        // As a source of the transposed read, lane (n, g) names row
+        // 32kb + 8g + 4h + n/4 at columns 16ib + 4(n%4) .. +3 (h: j = 4h .. 4h+3).
+        u32x4 ah[4], al[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          bh[kb] = *reinterpret_cast<const u32x4*>(&Ml[m][0][nb * 16 + n][32 * kb + 8 * g]);
-          bl[kb] = *reinterpret_cast<const u32x4*>(&Ml[m][1][nb * 16 + n][32 * kb + 8 * g]);
+          const int r0 = lds_row<false>(32 * kb + 8 * g + (n >> 2));
+          const int r1 = lds_row<false>(32 * kb + 8 * g + 4 + (n >> 2));
+          const int c = 16 * ib + 4 * (n & 3);
+          const u32x2 h0 = lds_read_tr16(&Ml[0][0][r0][c]), h1 = lds_read_tr16(&Ml[0][0][r1][c]);
+          const u32x2 l0 = lds_read_tr16(&Ml[0][1][r0][c]), l1 = lds_read_tr16(&Ml[0][1][r1][c]);
+          ah[kb] = (u32x4){h0.x, h0.y, h1.x, h1.y};
+          al[kb] = (u32x4){l0.x, l0.y, l1.x, l1.y};
         }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
-            acc[rb][nb] = mfma16x16x32(a[rb][kb], bh[kb], acc[rb][nb]);
-            acc[rb][nb] = mfma16x16x32(a[rb][kb], bl[kb], acc[rb][nb]);
+            acc[rb][ib] = mfma16x16x32(ah[kb], rk[jb][rb][kb], acc[rb][ib]);
+            acc[rb][ib] = mfma16x16x32(al[kb], rk[jb][rb][kb], acc[rb][ib]);
           }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // lane (n, g), register i of block nb: dk[tok0 + 16rb + 4g + i][sigma(nb, n)]
+      // lane (n, g) holds dv^T[16ib + 4g + i][tok0 + 16rb + n] in acc[rb][ib][i]
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = tok0 + 16 * rb + 4 * g + i;
+      for (int rb = 0; rb < 2; ++rb) {
+        const int s = tok0 + 16 * rb + n;
         if (s >= ns) continue;
-        float* o = Of + (int64_t)s * D + 4 * n;
-        st_nt(reinterpret_cast<f32x4*>(o), (f32x4){acc[rb][0][i], acc[rb][1][i], acc[rb][2][i], acc[rb][3][i]});
-        st_nt(reinterpret_cast<f32x4*>(o + 64),
-              (f32x4){acc[rb][4][i], acc[rb][5][i], acc[rb][6][i], acc[rb][7][i]});
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib)
+          st_nt(reinterpret_cast<f32x4*>(dvf + (int64_t)s * D + 16 * ib + 4 * g), acc[rb][ib]);
       }
+    }
   };
   [&]<int... js>(std::integer_sequence<int, js...>) {
     (load_a(w + 4 * js, rv[js], rk[js]), ...);
@@ -495,12 +558,12 @@ hipError_t launch_sym_bwd_d128(const float* M_all, const float* m0, const float*
   return hipGetLastError();
 }
 
-hipError_t launch_dk_bwd_d128(const uint16_t* v, const uint16_t* k, const float* LB, const float* Sm, float* dk,
-                              int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st) {
+hipError_t launch_dkv_bwd_d128(const uint16_t* v, const uint16_t* k, const float* LB, const float* Sm, float* dk,
+                               float* dv, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st) {
   const int64_t nt = t1 - t0, frames = heads * nt;
   const int nsplit = token_split(frames, S);
-  hipLaunchKernelGGL(k_dk_d128<1>, dim3((unsigned)(frames * nsplit)), dim3(256), 0, st, v, k, LB, Sm, dk, S, T,
-                     (int)t0, (int)nt, nsplit);
+  hipLaunchKernelGGL(k_dkv_d128<1>, dim3((unsigned)(frames * nsplit)), dim3(256), 0, st, v, k, LB, Sm, dk, dv, S,
+                     T, (int)t0, (int)nt, nsplit);
   return hipGetLastError();
 }
 
