@@ -245,7 +245,7 @@ hipError_t run_mfma(const Dims& d, const uint16_t* q, const uint16_t* k, const u
   };
   auto state = [&](hipStream_t st, int64_t t0, int64_t t1) {
     return timed(rec, st, 1, [&] {
-      return gdn::launch_state_d128(G, true, U, gamma, beta, t0 ? state_out : state_in, M_all, state_out,
+      return gdn::launch_state_d128(G, true, U, gamma, beta, t0 ? state_out : state_in, M_all, false, state_out,
                                     d.heads, d.T, t0, t1, st);
     });
   };
@@ -303,8 +303,9 @@ struct BwdBuffers {
 };
 
 // gdn_frame_bwd over ceil(T / F) segments, on the side streams of the
-// overlapped forward schedule.  First the forward is recomputed in float32
-// forms: (K, V) builds on the caller's stream, the state pass (a chain)
+// overlapped forward schedule.  First the forward is recomputed (G_t, U_t in
+// the packed forms of the forward, every M_t in float32): (K, V) builds on
+// the caller's stream, the state pass (a chain)
 // segment by segment on the state stream, and dq = dO M per segment on the
 // output stream as its states appear; the P_t = dO_t^T Q_t build follows
 // the (K, V) builds on the caller's stream.  Then the reverse-time state pass
@@ -321,15 +322,15 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
   const int64_t H = d.heads, T = d.T;
   auto seg = [&](int64_t i) { return std::make_pair(i * T / nseg, (i + 1) * T / nseg); };
   auto build_kv = [&](hipStream_t st, int64_t t0, int64_t t1) {
-    return gdn::launch_build_bf16_d128(a.k, a.v, b.G, false, b.U, H, T, t0, t1, S, st);
+    return gdn::launch_build_bf16_d128(a.k, a.v, b.G, true, b.U, H, T, t0, t1, S, st);
   };
   // P_t = dO_t^T Q_t: the build's second map with (K, V) = (Q, dO); its first (Q^T Q) is not stored
   auto build_p = [&](hipStream_t st) {
     return gdn::launch_build_bf16_d128(a.q, a.d_out, nullptr, false, b.P, H, T, 0, T, S, st);
   };
   auto state_fwd = [&](hipStream_t st, int64_t t0, int64_t t1) {
-    return gdn::launch_state_d128(b.G, false, b.U, a.gamma, a.beta, t0 ? b.fstate : a.state_in, b.M_all, b.fstate,
-                                  H, T, t0, t1, st);
+    return gdn::launch_state_d128(b.G, true, b.U, a.gamma, a.beta, t0 ? b.fstate : a.state_in, b.M_all, true,
+                                  b.fstate, H, T, t0, t1, st);
   };
   auto dq = [&](hipStream_t st, int64_t t0, int64_t t1) {
     return gdn::launch_output_bwd_d128(a.d_out, b.M_all, a.dq, true, H, T, t0, t1, S, st);  // dq = dO M
@@ -528,7 +529,7 @@ int gdn_state_pass(const gdn_shape* shape, const float* G, const float* U, const
   if (!aliasing_ok(outs, 2, ins, 5, state_out, state_in)) return GDN_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.D == 128)
-    return hip_status(gdn::launch_state_d128(G, false, U, gamma, beta, state_in, M_all, state_out,
+    return hip_status(gdn::launch_state_d128(G, false, U, gamma, beta, state_in, M_all, true, state_out,
                                              d.heads, d.T, 0, d.T, s));
   return hip_status(gdn::launch_state_generic(G, U, gamma, beta, state_in, M_all, state_out,
                                               d.heads, d.T, (int)d.D, s));

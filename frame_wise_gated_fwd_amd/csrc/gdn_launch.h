@@ -27,9 +27,10 @@ hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G,
                                   hipStream_t st);
 // State pass over frames [t0, t1) for `heads` heads, starting from state_in
 // (M_{t0-1}; null = zero) and leaving M_{t1-1} in state_out (which may equal
-// state_in).  G, U and M_out are all packed or all float32; M_out may be null.
+// state_in).  G and U are both packed or both float32; M_out (may be null)
+// is float32 when m_f32, else packed (only with packed G and U).
 hipError_t launch_state_d128(const void* G, bool packed, const float* U, const float* gamma,
-                             const float* beta, const float* state_in, void* M_out,
+                             const float* beta, const float* state_in, void* M_out, bool m_f32,
                              float* state_out, int64_t heads, int64_t T, int64_t t0, int64_t t1,
                              hipStream_t st);
 // O_t = Q_t M_t^T for frames [t0, t1); out_bf16 selects the output dtype.
@@ -44,11 +45,13 @@ hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool pa
 // out_t = Q_t X_t^T, X_t = M_t (or M_t^T when trans_m).  (dq = dO M uses it.)
 hipError_t launch_output_bwd_d128(const uint16_t* q, const float* M_all, float* out, bool trans_m,
                                   int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st);
-// Reverse-time state pass of the backward: from G_t, U_t, P_t = dO_t^T Q_t,
+// Reverse-time state pass of the backward: from G_t, U_t (packed forms),
+// P_t = dO_t^T Q_t,
 // the forward states M_all and the forward initial state m0 (null = zero),
 // starting from the gradient reaching M_{t1-1} from later frames in
 // d_state_out (null = zero), writes LB_t = beta_t Lambda_t, per-workgroup
-// partial sums of dgamma_t and dbeta_t (partials[head][T][kBwdParts][2]) and
+// partial sums of dgamma_t and dbeta_t per 16-row block of the state
+// (partials[head][T][kBwdParts][2]) and
 // the gradient reaching M_{t0-1} in d_state_in (may equal d_state_out).
 constexpr int kBwdParts = 8;
 hipError_t launch_state_bwd_d128(const float* G, const float* U, const float* P, const float* M_all,

@@ -20,7 +20,8 @@
 // Two data forms.  Packed (gdn_packed.h): G_t, U_t and M_t in the order
 // the waves read or write them, each wave access one contiguous block; this
 // is what gdn_frame_fwd uses.  Plain: float32 row-major (the stage entry
-// point); the bf16 split of G_t then happens here.
+// point); the bf16 split of G_t then happens here.  The backward pass reads
+// packed G_t, U_t and writes M_t as float32 (kMf32).
 //
 // The per-frame data (this wave's G_t rows and U_t elements) streams
 // through a ring of kDepth register buffers: frame t + kDepth is requested
@@ -47,7 +48,7 @@ namespace {
 constexpr int D = 128;
 constexpr int kLdsW = D + 8;  // padded LDS row (bf16 elements)
 
-template <int kRows, bool kPacked, int kDepth>
+template <int kRows, bool kPacked, int kDepth, bool kMf32>
 __global__ __launch_bounds__(256, 1) void k2_state_d128(
     const void* __restrict__ Gin, const float* __restrict__ U, const float* __restrict__ gamma,
     const float* __restrict__ beta, const float* state_in, void* __restrict__ Mout,
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void k2_state_d128(
 
     if (Mout) {
       const int64_t fo = ((int64_t)head * T + t) * D * D;
-      if constexpr (kPacked) {
+      if constexpr (!kMf32) {
         char* Mp = static_cast<char*>(Mout) + fo * 4;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
@@ -283,14 +284,14 @@ __global__ __launch_bounds__(256, 1) void k2_state_d128(
       *reinterpret_cast<f32x4*>(state_out + hoff + row_of(rb) * D + col_of(cb)) = Mreg[cb][rb];
 }
 
-template <int kRows, bool kPacked, int kDepth>
+template <int kRows, bool kPacked, int kDepth, bool kMf32>
 hipError_t launch_rows(const void* G, const float* U, const float* gamma, const float* beta,
                        const float* state_in, void* M_out, float* state_out, int64_t heads,
                        int64_t T, int64_t tb, int64_t te, hipStream_t st) {
   // Workgroup ids are grouped so that the workgroups of a head share id % 8.
   const int64_t groups = (heads + 7) / 8;
   const unsigned grid = (unsigned)(groups * 8 * (D / kRows));
-  hipLaunchKernelGGL((k2_state_d128<kRows, kPacked, kDepth>), dim3(grid), dim3(256), 0, st, G, U, gamma,
+  hipLaunchKernelGGL((k2_state_d128<kRows, kPacked, kDepth, kMf32>), dim3(grid), dim3(256), 0, st, G, U, gamma,
                      beta, state_in, M_out, state_out, (int)heads, (int)T, (int)tb, (int)te);
   return hipGetLastError();
 }
@@ -298,12 +299,14 @@ hipError_t launch_rows(const void* G, const float* U, const float* gamma, const 
 }  // namespace
 
 hipError_t launch_state_d128(const void* G, bool packed, const float* U, const float* gamma,
-                             const float* beta, const float* state_in, void* M_out,
+                             const float* beta, const float* state_in, void* M_out, bool m_f32,
                              float* state_out, int64_t heads, int64_t T, int64_t tb, int64_t te,
                              hipStream_t st) {
-  if (packed)
-    return launch_rows<16, true, 2>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, st);
-  return launch_rows<32, false, 2>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, st);
+  if (!packed)
+    return launch_rows<32, false, 2, true>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, st);
+  if (m_f32)
+    return launch_rows<16, true, 2, true>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, st);
+  return launch_rows<16, true, 2, false>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, st);
 }
 
 }  // namespace gdn

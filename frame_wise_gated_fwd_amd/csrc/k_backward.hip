@@ -26,16 +26,19 @@
 //
 // It runs like the forward state pass, frames in reverse: rows of Lambda
 // evolve independently (row i of L_{t-1} needs only row i of Lambda_t), so
-// each head's 128 rows are split over 8 workgroups of 16 rows; X = Lambda G
-// runs on bf16 MFMA in three passes (Ghi*Lhi + Glo*Lhi + Ghi*Llo) with the
+// each head's 128 rows are split over workgroups of kBwdRows rows; X = Lambda G
+// runs on bf16 MFMA in three passes (Ghi*Lhi + Glo*Lhi + Ghi*Llo, G_t and
+// U_t in the forward's packed forms) with the
 // float32 running value in registers and its hi/lo pair in LDS; the
 // per-frame inputs (this wave's G_t rows, and the workgroup's rows of U_t,
 // M_{t-1} and P_{t-1}) stream through a two-frame register ring.  The
-// partial sums are reduced in a fixed order (lanes, then waves), so the
-// results are deterministic.
+// partial sums are kept per 16-row block (whatever kBwdRows is) and
+// reduced in a fixed order (lanes, then waves, then blocks), so the results
+// are deterministic and do not depend on kBwdRows.
 #include "frame_output.h"
 #include "gdn_common.h"
 #include "gdn_launch.h"
+#include "gdn_packed.h"
 
 #include <type_traits>
 #include <utility>
@@ -45,10 +48,10 @@ namespace {
 
 constexpr int D = 128;
 constexpr int kLdsW = D + 8;
-constexpr int kRows = D / kBwdParts;  // 16
 constexpr int kDepth = 2;
-
-static_assert(kRows == 16, "one 16-row MFMA block per workgroup");
+// rows of the state gradient per workgroup of the reverse-time pass
+constexpr int kBwdRows = 16;
+static_assert(kBwdParts == D / 16, "partial sums are kept per 16-row block");
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -62,72 +65,84 @@ __device__ __forceinline__ float mul_then_add(float a, float b, float c) {
   return a * b + c;
 }
 
+template <int kRows>
 __global__ __launch_bounds__(256, 1) void k2_state_bwd_d128(
     const float* __restrict__ G, const float* __restrict__ U, const float* __restrict__ P,
     const float* __restrict__ M_all, const float* m0, const float* __restrict__ gamma,
     const float* __restrict__ beta, const float* d_state_out, float* __restrict__ LB,
     float* __restrict__ partials, float* d_state_in, int heads, int T, int tb, int te) {
+  constexpr int kRB = kRows / 16;    // 16-row blocks per workgroup
+  constexpr int kParts = D / kRows;  // workgroups per head
   __shared__ uint16_t Ml[2][2][kRows][kLdsW];  // [buffer][hi|lo][row][col]
-  __shared__ float red[2][4][2];              // [buffer][wave][dgamma, dbeta]
+  __shared__ float red[2][4][kRB][2];         // [buffer][wave][row block][dgamma, dbeta]
 
   const int id = blockIdx.x;
   const int xcd = id & 7, slot = id >> 3;
-  const int part = slot % kBwdParts;
-  const int head = (slot / kBwdParts) * 8 + xcd;
+  const int part = slot % kParts;
+  const int head = (slot / kParts) * 8 + xcd;
   if (head >= heads) return;
   const int r0 = part * kRows;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   const int n = l & 15, g = l >> 4;
-  const int row = r0 + n;
+  // this lane's elements: rows row_of(rb), columns col_of(cb) .. +3
+  auto row_of = [&](int rb) { return r0 + 16 * rb + n; };
   auto col_of = [&](int cb) { return 32 * w + 16 * cb + 4 * g; };
   const int64_t hoff = (int64_t)head * D * D;
   auto frame = [&](int t) { return ((int64_t)head * T + t) * D * D; };
 
-  // running gradient, this lane's 8 elements: row `row`, columns col_of(cb) .. +3
-  f32x4 Lr[2];
+  f32x4 Lr[2][kRB];  // the running gradient
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const f32x4 d0 = d_state_out ? *reinterpret_cast<const f32x4*>(d_state_out + hoff + row * D + col_of(cb))
-                                 : (f32x4){0.f, 0.f, 0.f, 0.f};
-    Lr[cb] = d0 + *reinterpret_cast<const f32x4*>(P + frame(te - 1) + row * D + col_of(cb));  // Lambda_{te-1}
-  }
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const int e = row_of(rb) * D + col_of(cb);
+      const f32x4 d0 = d_state_out ? *reinterpret_cast<const f32x4*>(d_state_out + hoff + e)
+                                   : (f32x4){0.f, 0.f, 0.f, 0.f};
+      Lr[cb][rb] = d0 + *reinterpret_cast<const f32x4*>(P + frame(te - 1) + e);  // Lambda_{te-1}
+    }
   auto put_lds = [&](int buf) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const u32x2 p0 = split2(Lr[cb][0], Lr[cb][1]), p1 = split2(Lr[cb][2], Lr[cb][3]);
-      *reinterpret_cast<u32x2*>(&Ml[buf][0][n][col_of(cb)]) = (u32x2){p0.x, p1.x};
-      *reinterpret_cast<u32x2*>(&Ml[buf][1][n][col_of(cb)]) = (u32x2){p0.y, p1.y};
-    }
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const u32x2 p0 = split2(Lr[cb][rb][0], Lr[cb][rb][1]), p1 = split2(Lr[cb][rb][2], Lr[cb][rb][3]);
+        *reinterpret_cast<u32x2*>(&Ml[buf][0][16 * rb + n][col_of(cb)]) = (u32x2){p0.x, p1.x};
+        *reinterpret_cast<u32x2*>(&Ml[buf][1][16 * rb + n][col_of(cb)]) = (u32x2){p0.y, p1.y};
+      }
   };
   put_lds(0);
 
-  // Ring: this wave's G_t rows 32w .. 32w+31 (the A operand, float32) and
-  // the workgroup's rows of U_t, M_{t-1} and P_{t-1} (this lane's elements).
-  f32x4 rg[kDepth][2][4][2];
-  f32x4 ru[kDepth][2], rm[kDepth][2], rp[kDepth][2];
+  // Ring: this wave's G_t rows 32w .. 32w+31 (the A operand, hi/lo words of
+  // the packed form) and the workgroup's rows of U_t (packed form), M_{t-1}
+  // and P_{t-1} (this lane's elements; gdn_packed.h gives the packed units).
+  u32x4 rgh[kDepth][2][4], rgl[kDepth][2][4];
+  f32x4 ru[kDepth][2][kRB], rm[kDepth][2][kRB], rp[kDepth][2][kRB];
   auto load_frame = [&](auto jc, int t) {
     constexpr int j = decltype(jc)::value;
     if (t < tb) return;
-    const float* Gt = G + frame(t);
+    const char* Gp = reinterpret_cast<const char*>(G + frame(t));
+    const char* Up = reinterpret_cast<const char*>(U + frame(t));
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const float* p = Gt + (32 * w + 16 * cb + n) * D + 32 * kb + 8 * g;
-        rg[j][cb][kb][0] = *reinterpret_cast<const f32x4*>(p);
-        rg[j][cb][kb][1] = *reinterpret_cast<const f32x4*>(p + 4);
+        const int unit = ((2 * w + cb) * 4 + kb) * 2;
+        rgh[j][cb][kb] = *reinterpret_cast<const u32x4*>(Gp + (unit << 10) + 16 * l);
+        rgl[j][cb][kb] = *reinterpret_cast<const u32x4*>(Gp + ((unit + 1) << 10) + 16 * l);
       }
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const float* Mp = t > 0 ? M_all + frame(t - 1) : (m0 ? m0 + hoff : nullptr);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int e = row * D + col_of(cb);
-      ru[j][cb] = *reinterpret_cast<const f32x4*>(U + frame(t) + e);
-      rm[j][cb] = Mp ? *reinterpret_cast<const f32x4*>(Mp + e) : zero;
-      rp[j][cb] = t > tb ? *reinterpret_cast<const f32x4*>(P + frame(t - 1) + e) : zero;
-    }
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const int e = row_of(rb) * D + col_of(cb);
+        ru[j][cb][rb] = *reinterpret_cast<const f32x4*>(Up + ((((r0 >> 4) + rb) * 8 + 2 * w + cb) << 10) + 16 * l);
+        rm[j][cb][rb] = Mp ? *reinterpret_cast<const f32x4*>(Mp + e) : zero;
+        rp[j][cb][rb] = t > tb ? *reinterpret_cast<const f32x4*>(P + frame(t - 1) + e) : zero;
+      }
   };
 
   // gamma/beta: lane i holds frame te-1-(64k+i) of window k (vector loads,
@@ -166,66 +181,87 @@ __global__ __launch_bounds__(256, 1) void k2_state_bwd_d128(
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const u32x2 p0 = split2(rg[j][cb][kb][0][0], rg[j][cb][kb][0][1]);
-        const u32x2 p1 = split2(rg[j][cb][kb][0][2], rg[j][cb][kb][0][3]);
-        const u32x2 p2 = split2(rg[j][cb][kb][1][0], rg[j][cb][kb][1][1]);
-        const u32x2 p3 = split2(rg[j][cb][kb][1][2], rg[j][cb][kb][1][3]);
-        ahi[cb][kb] = (u32x4){p0.x, p1.x, p2.x, p3.x};
-        alo[cb][kb] = (u32x4){p0.y, p1.y, p2.y, p3.y};
+        ahi[cb][kb] = rgh[j][cb][kb];
+        alo[cb][kb] = rgl[j][cb][kb];
       }
-    f32x4 uu[2], mm[2], pp[2];
+    f32x4 uu[2][kRB], mm[2][kRB], pp[2][kRB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      uu[cb] = ru[j][cb];
-      mm[cb] = rm[j][cb];
-      pp[cb] = rp[j][cb];
-    }
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        uu[cb][rb] = ru[j][cb][rb];
+        mm[cb][rb] = rm[j][cb][rb];
+        pp[cb][rb] = rp[j][cb][rb];
+      }
     load_frame(jc, t - kDepth);  // refill this ring slot kDepth frames ahead
 
-    // X^T = G Lambda^T: acc[cb][i] = X[row][col_of(cb) + i]
-    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // X^T = G Lambda^T: acc[cb][rb][i] = X[row_of(rb)][col_of(cb) + i]
+    f32x4 acc[2][kRB];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) acc[cb][rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const u32x4 bhi = *reinterpret_cast<const u32x4*>(&Ml[buf][0][n][32 * kb + 8 * g]);
-      const u32x4 blo = *reinterpret_cast<const u32x4*>(&Ml[buf][1][n][32 * kb + 8 * g]);
+      u32x4 bhi[kRB], blo[kRB];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[cb] = mfma16x16x32(ahi[cb][kb], bhi, acc[cb]);
+      for (int rb = 0; rb < kRB; ++rb) {
+        bhi[rb] = *reinterpret_cast<const u32x4*>(&Ml[buf][0][16 * rb + n][32 * kb + 8 * g]);
+        blo[rb] = *reinterpret_cast<const u32x4*>(&Ml[buf][1][16 * rb + n][32 * kb + 8 * g]);
+      }
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[cb] = mfma16x16x32(alo[cb][kb], bhi, acc[cb]);
+      for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[cb] = mfma16x16x32(ahi[cb][kb], blo, acc[cb]);
+        for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(ahi[cb][kb], bhi[rb], acc[cb][rb]);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(alo[cb][kb], bhi[rb], acc[cb][rb]);
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(ahi[cb][kb], blo[rb], acc[cb][rb]);
     }
 
-    float dg = 0.f, db = 0.f;
     float* LBt = LB + frame(t);
+    float dg[kRB], db[kRB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      f32x4 lb;
+    for (int rb = 0; rb < kRB; ++rb) {
+      dg[rb] = 0.f;
+      db[rb] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lam = Lr[cb][e], x = acc[cb][e];
-        lb[e] = bt * lam;
-        dg = fmaf(fmaf(-bt, x, lam), mm[cb][e], dg);
-        db = fmaf(lam, uu[cb][e], fmaf(-gm * x, mm[cb][e], db));
-        // L_{t-1} = gamma (Lambda - beta X), rounded, then + P_{t-1} (zero at
-        // t = tb): the same two roundings as when a sequence is cut here and
-        // the next launch or call adds P_{t-1} to the state gradient it is given
-        Lr[cb][e] = mul_then_add(gm, fmaf(-bt, x, lam), pp[cb][e]);
+      for (int cb = 0; cb < 2; ++cb) {
+        f32x4 lb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lam = Lr[cb][rb][e], x = acc[cb][rb][e];
+          lb[e] = bt * lam;
+          dg[rb] = fmaf(fmaf(-bt, x, lam), mm[cb][rb][e], dg[rb]);
+          db[rb] = fmaf(lam, uu[cb][rb][e], fmaf(-gm * x, mm[cb][rb][e], db[rb]));
+          // L_{t-1} = gamma (Lambda - beta X), rounded, then + P_{t-1} (zero at
+          // t = tb): the same two roundings as when a sequence is cut here and
+          // the next launch or call adds P_{t-1} to the state gradient it is given
+          Lr[cb][rb][e] = mul_then_add(gm, fmaf(-bt, x, lam), pp[cb][rb][e]);
+        }
+        *reinterpret_cast<f32x4*>(LBt + row_of(rb) * D + col_of(cb)) = lb;
       }
-      *reinterpret_cast<f32x4*>(LBt + row * D + col_of(cb)) = lb;
+      dg[rb] = wave_sum(dg[rb]);
+      db[rb] = wave_sum(db[rb]);
     }
-    dg = wave_sum(dg);
-    db = wave_sum(db);
     if (l == 0) {
-      red[buf][w][0] = dg;
-      red[buf][w][1] = db;
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        red[buf][w][rb][0] = dg[rb];
+        red[buf][w][rb][1] = db[rb];
+      }
     }
     put_lds(buf ^ 1);
     lds_barrier();
-    if (tid == 0) {
-      float* pr = partials + (((int64_t)head * T + t) * kBwdParts + part) * 2;
-      pr[0] = ((red[buf][0][0] + red[buf][1][0]) + red[buf][2][0]) + red[buf][3][0];
-      pr[1] = ((red[buf][0][1] + red[buf][1][1]) + red[buf][2][1]) + red[buf][3][1];
+    if (tid < kRB) {  // one partial pair per 16-row block, whatever the workgroup size
+      const int rb = tid;
+      float* pr = partials + (((int64_t)head * T + t) * kBwdParts + (r0 >> 4) + rb) * 2;
+      pr[0] = ((red[buf][0][rb][0] + red[buf][1][rb][0]) + red[buf][2][rb][0]) + red[buf][3][rb][0];
+      pr[1] = ((red[buf][0][rb][1] + red[buf][1][rb][1]) + red[buf][2][rb][1]) + red[buf][3][rb][1];
     }
   };
 
@@ -239,7 +275,9 @@ __global__ __launch_bounds__(256, 1) void k2_state_bwd_d128(
   // initial state when tb = 0)
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
-    *reinterpret_cast<f32x4*>(d_state_in + hoff + row * D + col_of(cb)) = Lr[cb];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb)
+      *reinterpret_cast<f32x4*>(d_state_in + hoff + row_of(rb) * D + col_of(cb)) = Lr[cb][rb];
 }
 
 __global__ void k_bwd_reduce(const float* __restrict__ partials, float* __restrict__ dgamma,
@@ -572,8 +610,8 @@ hipError_t launch_state_bwd_d128(const float* G, const float* U, const float* P,
                                  const float* d_state_out, float* LB, float* partials, float* d_state_in,
                                  int64_t heads, int64_t T, int64_t t0, int64_t t1, hipStream_t st) {
   // workgroup ids grouped so that the parts of a head share id % 8 (one XCD)
-  const unsigned grid = (unsigned)((heads + 7) / 8 * 8 * kBwdParts);
-  hipLaunchKernelGGL(k2_state_bwd_d128, dim3(grid), dim3(256), 0, st, G, U, P, M_all, m0, gamma, beta,
+  const unsigned grid = (unsigned)((heads + 7) / 8 * 8 * (D / kBwdRows));
+  hipLaunchKernelGGL(k2_state_bwd_d128<kBwdRows>, dim3(grid), dim3(256), 0, st, G, U, P, M_all, m0, gamma, beta,
                      d_state_out, LB, partials, d_state_in, (int)heads, (int)T, (int)t0, (int)t1);
   return hipGetLastError();
 }
