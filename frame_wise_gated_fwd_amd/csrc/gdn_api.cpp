@@ -307,11 +307,14 @@ struct BwdBuffers {
 // the packed forms of the forward, every M_t in float32): (K, V) builds on
 // the caller's stream, the state pass (a chain)
 // segment by segment on the state stream, and dq = dO M per segment on the
-// output stream as its states appear; the P_t = dO_t^T Q_t build follows
-// the (K, V) builds on the caller's stream.  Then the reverse-time state pass
+// output stream as its states appear.  Then the reverse-time state pass
 // walks the segments from the last to the first on the state stream, the
-// state gradient carried through d_state_in, and each segment's S, dv and dk
-// follow on the output stream.  The chains run on a few CUs while the
+// state gradient carried through d_state_in; each segment waits for its
+// P_t = dO_t^T Q_t, built on the caller's stream right after the (K, V)
+// builds in the same reverse order (so the pass can start as soon as the
+// forward chain ends), and its S and then dk, dv (one kernel) follow on the
+// output stream, behind the last dq.  (A third stream for them, measured,
+// lets them take bandwidth from the P builds the chain waits for.)  The chains run on a few CUs while the
 // builds and token contractions stream from HBM on the rest.  No kernel's
 // arithmetic depends on the segmentation.  With one segment everything runs
 // on the caller's stream.
@@ -325,8 +328,8 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
     return gdn::launch_build_bf16_d128(a.k, a.v, b.G, true, b.U, H, T, t0, t1, S, st);
   };
   // P_t = dO_t^T Q_t: the build's second map with (K, V) = (Q, dO); its first (Q^T Q) is not stored
-  auto build_p = [&](hipStream_t st) {
-    return gdn::launch_build_bf16_d128(a.q, a.d_out, nullptr, false, b.P, H, T, 0, T, S, st);
+  auto build_p = [&](hipStream_t st, int64_t t0, int64_t t1) {
+    return gdn::launch_build_bf16_d128(a.q, a.d_out, nullptr, false, b.P, H, T, t0, t1, S, st);
   };
   auto state_fwd = [&](hipStream_t st, int64_t t0, int64_t t1) {
     return gdn::launch_state_d128(b.G, true, b.U, a.gamma, a.beta, t0 ? b.fstate : a.state_in, b.M_all, true,
@@ -351,7 +354,7 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
   hipError_t e;
   if (nseg == 1) {
     if ((e = build_kv(s, 0, T)) != hipSuccess || (e = state_fwd(s, 0, T)) != hipSuccess ||
-        (e = dq(s, 0, T)) != hipSuccess || (e = build_p(s)) != hipSuccess || (e = state_bwd(s, 0, T)) != hipSuccess ||
+        (e = dq(s, 0, T)) != hipSuccess || (e = build_p(s, 0, T)) != hipSuccess || (e = state_bwd(s, 0, T)) != hipSuccess ||
         (e = grads(s, 0, T)) != hipSuccess)
       return e;
     return reduce();
@@ -379,9 +382,10 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
     if ((err = hand_off(sd.state_st, sd.stated, sd.out_st)) != hipSuccess) break;
     err = dq(sd.out_st, t0, t1);
   }
-  if (err == hipSuccess && (err = build_p(s)) == hipSuccess) err = hand_off(s, sd.built, sd.state_st);
   for (int64_t i = nseg - 1; i >= 0 && err == hipSuccess; --i) {
     const auto [t0, t1] = seg(i);
+    if ((err = build_p(s, t0, t1)) != hipSuccess) break;
+    if ((err = hand_off(s, sd.built, sd.state_st)) != hipSuccess) break;
     if ((err = state_bwd(sd.state_st, t0, t1)) != hipSuccess) break;
     if ((err = hand_off(sd.state_st, sd.stated, sd.out_st)) != hipSuccess) break;
     err = grads(sd.out_st, t0, t1);
