@@ -18,6 +18,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -92,11 +93,21 @@ def device_inputs(w, dev):
     return x
 
 
-def source_hash(fname=None):
-    """Hash of the HIP sources the measured kernel is built from (all of csrc,
-    so that a change to any shared header invalidates old counter figures)."""
+def source_hash(fname):
+    """Hash of the HIP sources a kernel is built from: its file and every
+    header of csrc it includes, transitively (a change to any of them
+    invalidates old counter figures)."""
+    seen, todo = set(), [fname]
+    while todo:
+        name = todo.pop()
+        if name in seen or not os.path.exists(os.path.join(CSRC, name)):
+            continue
+        seen.add(name)
+        with open(os.path.join(CSRC, name), "rb") as f:
+            text = f.read()
+        todo.extend(m.decode() for m in re.findall(rb'#include "([^"]+)"', text))
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(seen):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -113,7 +124,7 @@ def measured_traffic(kernel, workload_name):
         if "=" in line and not line.lstrip().startswith("#"):
             k_, v_ = line.split("=", 1)
             kv[k_.strip()] = v_.strip()
-    if kv.get("source_sha256_16") != source_hash():
+    if kv.get("source_sha256_16") != source_hash(KERNELS[kernel][0]):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
