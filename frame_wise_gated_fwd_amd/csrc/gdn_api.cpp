@@ -16,6 +16,7 @@
 #include <utility>
 #include <vector>
 
+#include "gdn_backward.h"
 #include "gdn_launch.h"
 
 namespace {

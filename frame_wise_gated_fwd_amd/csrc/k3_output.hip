@@ -10,6 +10,7 @@
 // uses it as well, with M_t given as float32 and optionally transposed (see
 // output_frame).
 #include "frame_output.h"
+#include "gdn_backward.h"
 #include "gdn_launch.h"
 
 #include <algorithm>

@@ -37,6 +37,7 @@
 // are deterministic and do not depend on kBwdRows.
 #include "frame_output.h"
 #include "gdn_common.h"
+#include "gdn_backward.h"
 #include "gdn_launch.h"
 #include "gdn_packed.h"
 
