@@ -300,7 +300,7 @@ struct BwdArgs {
   float *dq, *dk, *dv, *dgamma, *dbeta, *d_state_in;
 };
 struct BwdBuffers {
-  float *G, *U, *M_all, *P, *LB, *Sb, *partials, *fstate;
+  float *G, *U, *M_all, *P, *LB, *partials, *fstate;
 };
 
 // gdn_frame_bwd over ceil(T / F) segments, on the side streams of the
@@ -313,8 +313,8 @@ struct BwdBuffers {
 // state gradient carried through d_state_in; each segment waits for its
 // P_t = dO_t^T Q_t, built on the caller's stream right after the (K, V)
 // builds in the same reverse order (so the pass can start as soon as the
-// forward chain ends), and its S and then dk, dv (one kernel) follow on the
-// output stream, behind the last dq.  (A third stream for them, measured,
+// forward chain ends), and its dk, dv (one kernel) follow on the output
+// stream, behind the last dq.  (A third stream for them, measured,
 // lets them take bandwidth from the P builds the chain waits for.)  The chains run on a few CUs while the
 // builds and token contractions stream from HBM on the rest.  No kernel's
 // arithmetic depends on the segmentation.  With one segment everything runs
@@ -344,12 +344,8 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
     return gdn::launch_state_bwd_d128(b.G, b.U, b.P, b.M_all, a.state_in, a.gamma, a.beta, carry, b.LB,
                                       b.partials, a.d_state_in, H, T, t0, t1, st);
   };
-  auto grads = [&](hipStream_t st, int64_t t0, int64_t t1) {
-    hipError_t e;
-    if ((e = gdn::launch_sym_bwd_d128(b.M_all, a.state_in, b.LB, a.gamma, b.Sb, H, T, t0, t1, st)) != hipSuccess)
-      return e;
-    // dk = V LB + K S, dv = K LB^T
-    return gdn::launch_dkv_bwd_d128(a.v, a.k, b.LB, b.Sb, a.dk, a.dv, H, T, t0, t1, S, st);
+  auto grads = [&](hipStream_t st, int64_t t0, int64_t t1) {  // dk = V LB + K S, dv = K LB^T
+    return gdn::launch_dkv_bwd_d128(a.v, a.k, b.LB, b.M_all, a.state_in, a.gamma, a.dk, a.dv, H, T, t0, t1, S, st);
   };
   auto reduce = [&]() { return gdn::launch_bwd_reduce(b.partials, a.dgamma, a.dbeta, d.frames, s); };
   hipError_t e;
@@ -597,9 +593,9 @@ int gdn_frame_fwd_timed(const gdn_shape* shape, int in_dtype, int out_dtype, con
 size_t gdn_bwd_workspace_bytes(const gdn_shape* shape, int in_dtype) {
   Dims d;
   if (!valid_dtype(in_dtype) || check_shape(shape, true, &d) != GDN_OK) return 0;
-  // G, U, M_all, P, LB and S (the last also holds Q^T Q while P is built),
-  // then the dgamma/dbeta partial sums and the recomputed final state
-  return 6 * round256(d.map_elems * sizeof(float)) +
+  // G, U (packed forms), M_all, P and LB (float32), then the dgamma/dbeta
+  // partial sums and the recomputed final state
+  return 5 * round256(d.map_elems * sizeof(float)) +
          round256((size_t)d.frames * gdn::kBwdParts * 2 * sizeof(float)) +
          round256(d.state_elems * sizeof(float));
 }
@@ -634,9 +630,8 @@ int gdn_frame_bwd(const gdn_shape* shape, int in_dtype, const void* q, const voi
   b.M_all = reinterpret_cast<float*>(ws + 2 * slot);
   b.P = reinterpret_cast<float*>(ws + 3 * slot);
   b.LB = reinterpret_cast<float*>(ws + 4 * slot);
-  b.Sb = reinterpret_cast<float*>(ws + 5 * slot);
-  b.partials = reinterpret_cast<float*>(ws + 6 * slot);
-  b.fstate = reinterpret_cast<float*>(ws + 6 * slot +
+  b.partials = reinterpret_cast<float*>(ws + 5 * slot);
+  b.fstate = reinterpret_cast<float*>(ws + 5 * slot +
                                       round256((size_t)d.frames * gdn::kBwdParts * 2 * sizeof(float)));
   const BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                   static_cast<const uint16_t*>(d_out), gamma, beta, state_in, d_state_out,

@@ -1,6 +1,6 @@
 // Backward pass of the frame-wise GDN, head dim 128: the reverse-time state
-// pass, the reduction of its dgamma/dbeta partial sums, the symmetric
-// G-gradient term and the key and value gradients.  (dq and P_t = dO_t^T Q_t
+// pass, the reduction of its dgamma/dbeta partial sums, and the key and value
+// gradients (with the symmetric G-gradient term).  (dq and P_t = dO_t^T Q_t
 // reuse the forward's output and build kernels; gdn_api.cpp orders the
 // launches.)
 // Every launcher covers frames [t0, t1) of every head, so the schedule can
@@ -52,6 +52,9 @@ constexpr int kLdsW = D + 8;
 constexpr int kDepth = 2;
 // rows of the state gradient per workgroup of the reverse-time pass
 constexpr int kBwdRows = 16;
+// waves per workgroup of the key/value-gradient kernel (its LDS allows one
+// workgroup per CU)
+constexpr int kDkvWaves = 4;
 static_assert(kBwdParts == D / 16, "partial sums are kept per 16-row block");
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -295,114 +298,6 @@ __global__ void k_bwd_reduce(const float* __restrict__ partials, float* __restri
   dbeta[f] = sb;
 }
 
-__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// S_t = -gamma_t (A + A^T), A = M_{t-1}^T LB_t (both float32 row-major), one
-// workgroup per frame.  The gradient of G_t = K_t^T K_t is
-// dG_t = -gamma_t beta_t M_{t-1}^T Lambda_t, and K_t receives K_t (dG + dG^T);
-// LB_t = beta_t Lambda_t already carries beta.  A runs on float32 MFMA
-// (v_mfma_f32_16x16x4_f32: exact products, float32 accumulation): wave w
-// computes rows 32w .. 32w+31 of A, 2 x 8 blocks of 16 x 16, reducing over the
-// 128 rows of M and LB in chunks of 32 rows staged through LDS (the next
-// chunk is loaded into registers meanwhile).  Both operands are read along
-// rows: for A[m][k] = M[i][m] and B[k][n] = LB[i][n] (k = i), 16 lanes read
-// 16 consecutive floats of one row.  A then goes through LDS once to be
-// symmetrized; S is exactly symmetric (the two sums are the same float
-// addition), so each lane stores the value for (a, b) at (b, a), four
-// consecutive columns at once.
-__global__ __launch_bounds__(256, 2) void k_sym_bwd_d128(const float* __restrict__ M_all, const float* m0,
-                                                       const float* __restrict__ LB,
-                                                       const float* __restrict__ gamma,
-                                                       float* __restrict__ Sout, int T, int t0, int nt) {
-  constexpr int kChunk = 32;
-  constexpr int kCw = D + 16;  // chunk row (floats): consecutive rows start 16 banks apart, so the
-                               // 4 rows x 16 columns of an operand read hit 64 distinct banks
-  constexpr int kAw = D + 4;   // row of A (floats): 16-byte rows, transposed reads without conflicts
-  constexpr int kLds = 2 * kChunk * kCw > D * kAw ? 2 * kChunk * kCw : D * kAw;
-  __shared__ __attribute__((aligned(16))) float lds[kLds];
-  const int j = blockIdx.x;
-  const int head = j / nt, t = t0 + j % nt;
-  const int64_t f = (int64_t)head * T + t;
-  const float* Mp = t > 0 ? M_all + (f - 1) * D * D : (m0 ? m0 + (int64_t)head * D * D : nullptr);
-  const float* Lt = LB + f * D * D;
-  float* St = Sout + f * D * D;
-  const int tid = threadIdx.x;
-  if (!Mp) {  // zero initial state: M_{-1} = 0, so S_0 = 0
-    for (int i = tid; i < D * D / 4; i += 256) reinterpret_cast<f32x4*>(St)[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    return;
-  }
-  const int w = tid >> 6, l = tid & 63;
-  const int n = l & 15, g = l >> 4;
-  float (*Ms)[kCw] = reinterpret_cast<float (*)[kCw]>(lds);
-  float (*Ls)[kCw] = reinterpret_cast<float (*)[kCw]>(lds + kChunk * kCw);
-
-  // a chunk is 32 rows x 32 float4 of each matrix: 4 float4 of each per thread
-  f32x4 pm[4], pl[4];
-  auto load_chunk = [&](int c) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int idx = tid + 256 * k, r = idx >> 5, c4 = (idx & 31) * 4;
-      pm[k] = *reinterpret_cast<const f32x4*>(Mp + (kChunk * c + r) * D + c4);
-      pl[k] = *reinterpret_cast<const f32x4*>(Lt + (kChunk * c + r) * D + c4);
-    }
-  };
-  f32x4 acc[2][8];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[rb][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  load_chunk(0);
-  for (int c = 0; c < D / kChunk; ++c) {
-    if (c) __syncthreads();  // every wave is done with the previous chunk
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int idx = tid + 256 * k, r = idx >> 5, c4 = (idx & 31) * 4;
-      *reinterpret_cast<f32x4*>(&Ms[r][c4]) = pm[k];
-      *reinterpret_cast<f32x4*>(&Ls[r][c4]) = pl[k];
-    }
-    __syncthreads();
-    if (c + 1 < D / kChunk) load_chunk(c + 1);
-#pragma unroll
-    for (int k0 = 0; k0 < kChunk; k0 += 4) {
-      // A operand: lane (n, g) holds A[n][g] = M[i][32w + 16rb + n]; B: LB[i][16nb + n]
-      const int i = k0 + g;
-      float a[2], b[8];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) a[rb] = Ms[i][32 * w + 16 * rb + n];
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) b[nb] = Ls[i][16 * nb + n];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) acc[rb][nb] = mfma16x16x4f32(a[rb], b[nb], acc[rb][nb]);
-    }
-  }
-  __syncthreads();  // the chunks are dead: A takes their LDS
-  float (*As)[kAw] = reinterpret_cast<float (*)[kAw]>(lds);
-  // lane (n, g) holds A[32w + 16rb + 4g + i][16nb + n] in acc[rb][nb][i]
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) As[32 * w + 16 * rb + 4 * g + i][16 * nb + n] = acc[rb][nb][i];
-  __syncthreads();
-  const float ng = -gamma[f];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const int b = 16 * nb + n, a0 = 32 * w + 16 * rb + 4 * g;
-      const f32x4 at = *reinterpret_cast<const f32x4*>(&As[b][a0]);  // A[b][a0 .. a0+3]
-      f32x4 sv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = ng * (acc[rb][nb][i] + at[i]);
-      *reinterpret_cast<f32x4*>(St + b * D + a0) = sv;  // S[b][a0 + i] = S[a0 + i][b]
-    }
-}
-
 // ds_read_b64_tr_b16 (gfx950): each lane names an 8-byte-aligned LDS
 // address; within every 16-lane group, lane i receives as its element e
 // (e = 0..3) element i % 4 of the 8 bytes named by lane 4e + i / 4.
@@ -414,28 +309,44 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 
 // Key and value gradients for the tokens of one frame (or one token part of
 // it, in launches of a few frames):
-//   dk_t = V_t LB_t + K_t S_t   (S_t symmetric),   dv_t = K_t LB_t^T,
-// with LB_t^T and S_t staged once in LDS as bf16 hi/lo planes (2 x 69.6 KB,
-// so one workgroup per CU), which carry them to about 2^-17 relative.
-// Tiling and global access patterns are the output kernel's (frame_output.h):
-// a wave takes 32-token tiles of V and K rows as MFMA operands.
+//   dk_t = V_t LB_t + K_t S_t,   dv_t = K_t LB_t^T,
+//   S_t = -gamma_t (A + A^T),    A = M_{t-1}^T LB_t
+// (K_t S_t is K_t (dG_t + dG_t^T) with dG_t = -gamma_t beta_t M_{t-1}^T Lambda_t;
+// LB_t = beta_t Lambda_t carries beta).  LDS holds two 128 x 128 matrices as
+// bf16 hi/lo planes (2 x 69.6 KB, so one workgroup per CU), which carry them
+// to about 2^-17 relative: LB_t^T throughout, and in the second slot first
+// M_{t-1}, then S_t.
+//  * A on bf16 MFMA in three passes (Mhi*LBhi + Mlo*LBhi + Mhi*LBlo), each
+//    wave taking 128 / kWaves rows: its A operand (M_{t-1} read down columns)
+//    comes from transposed LDS reads of the row-major staged M, its B operand
+//    from rows of the staged LB^T.  A then goes through LDS (as float32, in
+//    the slot of M) for A + A^T, and S_t is split and staged.  With a zero
+//    initial state, S_0 = 0.
 //  * dk: one 256-term reduction per element, 128 terms over the rows of LB_t
 //    (A = V tile, B = staged LB^T rows) and then 128 over those of S_t
 //    (A = K tile, B = staged S rows), in one accumulator; output column
-//    sigma(nb, n) as in the output kernel, 16-byte stores.
+//    sigma(nb, n) as in the output kernel (frame_output.h), 16-byte stores.
 //  * dv, computed transposed as dv^T = LB_t K_t^T: A = rows of LB_t, which
 //    are columns of the staged LB^T, fetched with transposed LDS reads (two
 //    per fragment), and B = the K tile already in registers for dk.  A lane
 //    then holds 4 consecutive value dims of one token: 16-byte stores.
-template <int kDepth>
-__global__ __launch_bounds__(256, 1) void k_dkv_d128(const uint16_t* __restrict__ V,
+// The token tiling and global access patterns are the output kernel's: a
+// wave takes 32-token tiles of V and K rows as MFMA operands.
+template <int kDepth, int kWaves>
+__global__ __launch_bounds__(64 * kWaves, 1) void k_dkv_d128(const uint16_t* __restrict__ V,
                                                    const uint16_t* __restrict__ K, const float* __restrict__ LB,
-                                                   const float* __restrict__ Sm, float* __restrict__ dk,
+                                                   const float* __restrict__ M_all, const float* m0,
+                                                   const float* __restrict__ gamma, float* __restrict__ dk,
                                                    float* __restrict__ dv, int S, int64_t T, int t0, int nt,
                                                    int nsplit) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ml[2][2][D][kOutLdsW];  // [LB^T | S][hi | lo][row][column]
+  // [LB^T | M_{t-1}, then S][hi | lo][LDS row][column]
+  __shared__ __attribute__((aligned(16))) uint16_t Ml[2][2][D][kOutLdsW];
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kAB = 8 / kWaves;  // 16-row blocks of A per wave
+  static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
   const int jf = blockIdx.x / nsplit, part = blockIdx.x % nsplit;
-  const int64_t f = (int64_t)(jf / nt) * T + t0 + jf % nt;
+  const int head = jf / nt, t = t0 + jf % nt;
+  const int64_t f = (int64_t)head * T + t;
   const int s0 = (int)((int64_t)part * S / nsplit), s1 = (int)((int64_t)(part + 1) * S / nsplit);
   const int ns = s1 - s0;
   const int64_t in_off = (f * (int64_t)S + s0) * D;
@@ -444,17 +355,28 @@ __global__ __launch_bounds__(256, 1) void k_dkv_d128(const uint16_t* __restrict_
   float* dkf = dk + in_off;
   float* dvf = dv + in_off;
   const float* LBt = LB + f * D * D;
-  const float* St = Sm + f * D * D;
+  const float* Mp = t > 0 ? M_all + (f - 1) * D * D : (m0 ? m0 + (int64_t)head * D * D : nullptr);
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63;
   const int n = l & 15, g = l >> 4;
 
   // LDS row lds_row(r) of a staged matrix holds its row r (output column
-  // sigma, as in the output kernel): staged LB^T row c is column c of LB
-  for (int idx = tid; idx < D * D / 4; idx += 256) {
+  // sigma, as in the output kernel): staged LB^T row c is column c of LB.
+  // M_{t-1} is staged row-major with natural rows.  All 16-byte loads of
+  // LB_t and M_{t-1} are issued before the first is used.
+  constexpr int kLoads = D * D / 4 / kThreads;
+  f32x4 lvs[kLoads], mvs[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) lvs[i] = *reinterpret_cast<const f32x4*>(LBt + 4 * (tid + kThreads * i));
+  if (Mp) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) mvs[i] = *reinterpret_cast<const f32x4*>(Mp + 4 * (tid + kThreads * i));
+  }
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int idx = tid + kThreads * i;
     const int r = idx >> 5, c4 = (idx & 31) * 4;
-    const f32x4 lv = *reinterpret_cast<const f32x4*>(LBt + r * D + c4);
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(St + r * D + c4);
+    const f32x4 lv = lvs[i];
     const u32x2 p0 = split2(lv[0], lv[1]), p1 = split2(lv[2], lv[3]);
     const uint32_t hi[2] = {p0.x, p1.x}, lo[2] = {p0.y, p1.y};
 #pragma unroll
@@ -463,12 +385,87 @@ __global__ __launch_bounds__(256, 1) void k_dkv_d128(const uint16_t* __restrict_
       Ml[0][0][rho][r] = (uint16_t)(hi[e >> 1] >> (16 * (e & 1)));
       Ml[0][1][rho][r] = (uint16_t)(lo[e >> 1] >> (16 * (e & 1)));
     }
-    const u32x2 q0 = split2(sv[0], sv[1]), q1 = split2(sv[2], sv[3]);
-    const int rs = lds_row<false>(r);
-    *reinterpret_cast<u32x2*>(&Ml[1][0][rs][c4]) = (u32x2){q0.x, q1.x};
-    *reinterpret_cast<u32x2*>(&Ml[1][1][rs][c4]) = (u32x2){q0.y, q1.y};
+    if (Mp) {
+      const f32x4 mv = mvs[i];
+      const u32x2 q0 = split2(mv[0], mv[1]), q1 = split2(mv[2], mv[3]);
+      *reinterpret_cast<u32x2*>(&Ml[1][0][r][c4]) = (u32x2){q0.x, q1.x};
+      *reinterpret_cast<u32x2*>(&Ml[1][1][r][c4]) = (u32x2){q0.y, q1.y};
+    } else {
+      const int rs = lds_row<false>(r);  // S_0 = 0
+      *reinterpret_cast<u32x2*>(&Ml[1][0][rs][c4]) = (u32x2){0u, 0u};
+      *reinterpret_cast<u32x2*>(&Ml[1][1][rs][c4]) = (u32x2){0u, 0u};
+    }
   }
   __syncthreads();
+  if (Mp) {
+    // A = M^T LB: wave w takes the row blocks kAB w .. kAB w + kAB - 1; lane
+    // (n, g) of block (ab, bb) ends with A[16(kAB w + ab) + 4g + i][16bb + n]
+    f32x4 acc[kAB][8];
+#pragma unroll
+    for (int ab = 0; ab < kAB; ++ab)
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) acc[ab][bb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      // A operand (ab, kb): lane (m, g) needs M[32kb + 8g + j][16(kAB w + ab) + m],
+      // j = 0..7; as a source of the transposed read, lane (n, g) names row
+      // 32kb + 8g + 4h + n/4 at columns 16(kAB w + ab) + 4(n%4) .. +3.
+      u32x4 ah[kAB], al[kAB];
+#pragma unroll
+      for (int ab = 0; ab < kAB; ++ab) {
+        const int r0 = 32 * kb + 8 * g + (n >> 2), c = 16 * (kAB * w + ab) + 4 * (n & 3);
+        const u32x2 h0 = lds_read_tr16(&Ml[1][0][r0][c]), h1 = lds_read_tr16(&Ml[1][0][r0 + 4][c]);
+        const u32x2 l0 = lds_read_tr16(&Ml[1][1][r0][c]), l1 = lds_read_tr16(&Ml[1][1][r0 + 4][c]);
+        ah[ab] = (u32x4){h0.x, h0.y, h1.x, h1.y};
+        al[ab] = (u32x4){l0.x, l0.y, l1.x, l1.y};
+      }
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb) {
+        // B operand (kb, bb): lane (n, g) needs LB[32kb + 8g + j][16bb + n], a row of LB^T
+        const int rho = lds_row<false>(16 * bb + n);
+        const u32x4 bh = *reinterpret_cast<const u32x4*>(&Ml[0][0][rho][32 * kb + 8 * g]);
+        const u32x4 bl = *reinterpret_cast<const u32x4*>(&Ml[0][1][rho][32 * kb + 8 * g]);
+#pragma unroll
+        for (int ab = 0; ab < kAB; ++ab) {
+          acc[ab][bb] = mfma16x16x32(ah[ab], bh, acc[ab][bb]);
+          acc[ab][bb] = mfma16x16x32(al[ab], bh, acc[ab][bb]);
+          acc[ab][bb] = mfma16x16x32(ah[ab], bl, acc[ab][bb]);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with M: A takes its slot as float32
+    constexpr int kAw = D + 4;  // 16-byte rows (128 x 528 B fit in the 69.6 KB slot)
+    float (*As)[kAw] = reinterpret_cast<float (*)[kAw]>(&Ml[1][0][0][0]);
+#pragma unroll
+    for (int ab = 0; ab < kAB; ++ab)
+#pragma unroll
+      for (int bb = 0; bb < 8; ++bb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) As[16 * (kAB * w + ab) + 4 * g + i][16 * bb + n] = acc[ab][bb][i];
+    __syncthreads();
+    const float ng = -gamma[f];
+    u32x2 sh[D * D / 4 / kThreads], sl[D * D / 4 / kThreads];
+#pragma unroll
+    for (int jj = 0; jj < D * D / 4 / kThreads; ++jj) {
+      const int idx = tid + kThreads * jj, r = idx >> 5, c4 = (idx & 31) * 4;
+      const f32x4 ar = *reinterpret_cast<const f32x4*>(&As[r][c4]);
+      float sv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[e] = ng * (ar[e] + As[c4 + e][r]);
+      const u32x2 q0 = split2(sv[0], sv[1]), q1 = split2(sv[2], sv[3]);
+      sh[jj] = (u32x2){q0.x, q1.x};
+      sl[jj] = (u32x2){q0.y, q1.y};
+    }
+    __syncthreads();  // A is read: S takes the slot
+#pragma unroll
+    for (int jj = 0; jj < D * D / 4 / kThreads; ++jj) {
+      const int idx = tid + kThreads * jj, r = idx >> 5, c4 = (idx & 31) * 4;
+      const int rs = lds_row<false>(r);
+      *reinterpret_cast<u32x2*>(&Ml[1][0][rs][c4]) = sh[jj];
+      *reinterpret_cast<u32x2*>(&Ml[1][1][rs][c4]) = sl[jj];
+    }
+    __syncthreads();
+  }
 
   constexpr int kTile = kOutTile;
   const int ntiles = (ns + kTile - 1) / kTile;
@@ -493,7 +490,7 @@ __global__ __launch_bounds__(256, 1) void k_dkv_d128(const uint16_t* __restrict_
   auto tile_body = [&](auto jc, int tile) {
     constexpr int jb = decltype(jc)::value;
     const int tok0 = tile * kTile;
-    load_a(tile + 4 * kDepth, rv[(jb + kDepth) % kRing], rk[(jb + kDepth) % kRing]);
+    load_a(tile + kWaves * kDepth, rv[(jb + kDepth) % kRing], rk[(jb + kDepth) % kRing]);
     {  // dk = V LB + K S
       f32x4 acc[2][8];
 #pragma unroll
@@ -578,31 +575,24 @@ __global__ __launch_bounds__(256, 1) void k_dkv_d128(const uint16_t* __restrict_
     }
   };
   [&]<int... js>(std::integer_sequence<int, js...>) {
-    (load_a(w + 4 * js, rv[js], rk[js]), ...);
+    (load_a(w + kWaves * js, rv[js], rk[js]), ...);
   }(std::make_integer_sequence<int, kDepth>{});
-  for (int tile0 = w; tile0 < ntiles; tile0 += 4 * kRing) {
+  for (int tile0 = w; tile0 < ntiles; tile0 += kWaves * kRing) {
     [&]<int... js>(std::integer_sequence<int, js...>) {
-      ((tile0 + 4 * js < ntiles ? tile_body(std::integral_constant<int, js>{}, tile0 + 4 * js) : void()), ...);
+      ((tile0 + kWaves * js < ntiles ? tile_body(std::integral_constant<int, js>{}, tile0 + kWaves * js) : void()), ...);
     }(std::make_integer_sequence<int, kRing>{});
   }
 }
 
 }  // namespace
 
-hipError_t launch_sym_bwd_d128(const float* M_all, const float* m0, const float* LB, const float* gamma,
-                               float* Sout, int64_t heads, int64_t T, int64_t t0, int64_t t1, hipStream_t st) {
-  const int64_t nt = t1 - t0;
-  hipLaunchKernelGGL(k_sym_bwd_d128, dim3((unsigned)(heads * nt)), dim3(256), 0, st, M_all, m0, LB, gamma, Sout,
-                     (int)T, (int)t0, (int)nt);
-  return hipGetLastError();
-}
-
-hipError_t launch_dkv_bwd_d128(const uint16_t* v, const uint16_t* k, const float* LB, const float* Sm, float* dk,
-                               float* dv, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st) {
+hipError_t launch_dkv_bwd_d128(const uint16_t* v, const uint16_t* k, const float* LB, const float* M_all,
+                               const float* m0, const float* gamma, float* dk, float* dv, int64_t heads, int64_t T,
+                               int64_t t0, int64_t t1, int S, hipStream_t st) {
   const int64_t nt = t1 - t0, frames = heads * nt;
   const int nsplit = token_split(frames, S);
-  hipLaunchKernelGGL(k_dkv_d128<1>, dim3((unsigned)(frames * nsplit)), dim3(256), 0, st, v, k, LB, Sm, dk, dv, S,
-                     T, (int)t0, (int)nt, nsplit);
+  hipLaunchKernelGGL((k_dkv_d128<1, kDkvWaves>), dim3((unsigned)(frames * nsplit)), dim3(64 * kDkvWaves), 0, st, v, k,
+                     LB, M_all, m0, gamma, dk, dv, S, T, (int)t0, (int)nt, nsplit);
   return hipGetLastError();
 }
 

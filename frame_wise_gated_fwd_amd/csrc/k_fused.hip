@@ -451,7 +451,7 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
       invalidate_l1();
       const char* mp = ring + (int64_t)(2 * kWG + it.t % kWM) * packed::kFrameBytes;
       void* of = static_cast<char*>(a.out) + fr * S * D * (kOutBf16 ? 2 : 4);
-      output_frame<true, kOutBf16, 1>(a.q + fr * S * D, mp, of, S, lds.out, [&] {
+      output_frame<true, kOutBf16, 1, false, false>(a.q + fr * S * D, mp, of, S, lds.out, [&] {
         if (tid == 0) flag_store(fl + kFlagOutDone + it.t % kWM, (uint32_t)(it.t + 1));
       });
     }

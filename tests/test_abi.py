@@ -146,7 +146,7 @@ def test_backward_argument_errors():
     wsb = L.gdn_bwd_workspace_bytes(ctypes.byref(s), BF16)
     per = 2 * 3 * 128 * 128 * 4
     partials = 6 * 8 * 2 * 4  # frames x 8 parts x (dgamma, dbeta) floats
-    assert wsb == 6 * ((per + 255) // 256 * 256) + (partials + 255) // 256 * 256 + 2 * 128 * 128 * 4
+    assert wsb == 5 * ((per + 255) // 256 * 256) + (partials + 255) // 256 * 256 + 2 * 128 * 128 * 4
 
     def bwd(shape=s, dt=BF16, d_state_out=None, d_state_in=P[11], ws=P[10], wsb=wsb, **kw):
         a = dict(q=P[0], k=P[1], v=P[2], gamma=P[3], beta=P[4], state=None, d_out=P[5], dq=P[6], dk=P[7],

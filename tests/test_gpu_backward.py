@@ -86,6 +86,14 @@ def test_backward_in_place_state_gradient_and_determinism():
         assert torch.equal(res[i], a[key]), key
 
 
+def test_backward_stress_slice():
+    """Two heads of the stress workload (gamma ~ U(0.999, 1), beta ~ U(0.9, 1),
+    a tenth of the key rows x4), 70 frames: two segments, zero initial state."""
+    from synth import STRESS_B4
+    w = STRESS_B4.with_(name="bwd_stress_slice", B=1, H=2, T=70)
+    _backward_parity(w)
+
+
 def test_backward_segmented_schedule():
     """T = 150 is cut into segments (the forward recomputation and the
     reverse-time pass run segment by segment on the side streams)."""
