@@ -62,9 +62,9 @@ def per_head_frame_bytes(S, D, in_bytes=2, out_bytes=4):
         "backward": 4 * qkv + 3 * o,
         # what its kernels move: seven bf16 token-tensor reads (K, V twice
         # each; Q, dO in the P build; dO for dq), three f32 gradient writes
-        # and seventeen D x D float32 maps written or read (G, U: 3 each;
-        # M: 4; P: 2; LB: 3; S: 2)
-        "backward_design": 7 * qkv + 3 * o + 17 * dd,
+        # and fourteen D x D maps written or read (G, U: 3 each; M: 4;
+        # P: 2; LB: 2)
+        "backward_design": 7 * qkv + 3 * o + 14 * dd,
     }
 
 

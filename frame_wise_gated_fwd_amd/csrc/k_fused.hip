@@ -67,13 +67,16 @@ constexpr uint32_t kSpinLimit = 1u << 22;  // polls (a few seconds) before a wai
 // output(t).  The queue distance must cover a build's duration in state-pass
 // steps (a build takes ~45 us, a step ~4 us); every wait then depends only
 // on earlier items as long as lag > kPrefetch + 1 and lag <= wg + wm (see
-// the ring notes above).  Measured on the 60 s workload: 32-64 G/U slots all
-// run within 2 %; 8 slots starve the state pass (8-10 ms); 96 overflow the
-// memory-side cache (4.8 ms).
+// the ring notes above).  Measured on the 60 s workload (same box, same
+// inputs): {32, 12, 20} and {32, 12, 24} beat {40, 16, 32} by 1.5-4 % on
+// three boxes; more M slots ({40, 24, 32}: +6 %), faster M staging in the
+// output items (+18 %) and {30, 12, 22} (+7 %) are slower; 8 G/U slots
+// starve the state pass (8-10 ms); 96 overflow the memory-side cache
+// (4.8 ms).
 struct RingShape {
   int wg, wm, lag;
 };
-constexpr RingShape kRing{40, 16, 32};
+constexpr RingShape kRing{32, 12, 20};
 static_assert(kRing.wg >= kPrefetch + 2 && kRing.wm >= 2 &&
                   kRing.lag > kPrefetch + 1 && kRing.lag <= kRing.wg + kRing.wm,
               "ring shape could stall the queue");
