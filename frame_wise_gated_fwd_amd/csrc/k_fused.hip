@@ -57,6 +57,7 @@ namespace {
 constexpr int D = 128;
 constexpr int kXcd = 8;
 constexpr int kPrefetch = 1;          // frames the state pass loads ahead
+static_assert(kPrefetch == 1, "the state pass holds exactly one frame ahead in registers");
 constexpr int kMaxHeadsPerXcd = 2;
 constexpr int kMaxParts = 8;          // kRows >= 16
 constexpr int kLdsW = D + 8;
