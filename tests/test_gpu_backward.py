@@ -94,6 +94,33 @@ def test_backward_stress_slice():
     _backward_parity(w)
 
 
+def test_backward_seq60s_full_size_sampled_heads():
+    """The 60 s workload at full size, in the configuration bench.py times
+    (one call over all 16 heads and 961 frames, 16 segments); two heads are
+    checked whole against the oracle.  d_out and d_state_out are drawn on the
+    device (seeded) and the checked heads' values copied back for the oracle."""
+    from synth import SEQ_60S
+    w = SEQ_60S
+    log(f"backward {w.name}: B={w.B} H={w.H} T={w.T} S={w.S} D={w.D} (full size, 2 heads checked)")
+    x = device_inputs(w, DEV)
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    d_out = torch.randn((w.B, w.H, w.T, w.S, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+    d_state = torch.randn((w.B, w.H, w.D, w.D), generator=gen, device=DEV) * 0.1
+    got = dict(zip(KEYS, F.frame_bwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], d_out, x["state"], d_state)))
+    torch.cuda.synchronize()
+    err = {k: RelL2() for k in KEYS}
+    for b, h in [(0, 3), (0, 12)]:
+        d = head_inputs(w, b, h)
+        dob = d_out[b, h].cpu().view(torch.int16).numpy().view(np.uint16)
+        ref = oracle.gdn_head_backward(d["q"], d["k"], d["v"], d["gamma"], d["beta"], d.get("state"), dob,
+                                       d_state[b, h].cpu().numpy())
+        for key in KEYS:
+            err[key].add(got[key][b, h].cpu().numpy(), ref[key])
+    log("  relL2 " + ", ".join(f"{k}={err[k].value:.2e}" for k in KEYS))
+    for key in KEYS:
+        assert np.isfinite(err[key].value) and err[key].value <= 2e-3, (key, err[key].value)
+
+
 def test_backward_segmented_schedule():
     """T = 150 is cut into segments (the forward recomputation and the
     reverse-time pass run segment by segment on the side streams)."""
