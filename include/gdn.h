@@ -1,6 +1,6 @@
 /*
- * gdn.h -- C ABI of the frame-wise Gated DeltaNet forward on AMD Instinct
- * MI355X (gfx950).
+ * gdn.h -- C ABI of the frame-wise Gated DeltaNet forward (and its backward
+ * pass) on AMD Instinct MI355X (gfx950).
  *
  * What is computed.  The SANA-WM pages ("SANA-WM: NVIDIA puts a one-minute
  * world model on a single GPU", zhichai.net, section "1. Hybrid Linear
@@ -37,8 +37,9 @@
  * launch returns GDN_E_HIP.  Faults during execution surface at the caller's
  * next synchronisation.  Non-finite inputs are not checked: they propagate.
  *
- * Aliasing.  state_out may equal state_in exactly (in-place streaming).  Any
- * other overlap between an output and any other buffer is GDN_E_ALIAS.
+ * Aliasing.  state_out may equal state_in exactly (in-place streaming), and
+ * in gdn_frame_bwd d_state_in may equal d_state_out.  Any other overlap
+ * between an output and any other buffer is GDN_E_ALIAS.
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -95,7 +96,8 @@ int gdn_set_fused(int enabled);
  *   GDN_PATH_MFMA   bf16, D == 128, T <= 64 (and longer sequences when the
  *                   fused kernel below is unavailable): three bf16-MFMA
  *                   kernels (build, state pass, output) with the per-frame
- *                   intermediates in the workspace.  When T > 64 the frames are cut into
+ *                   intermediates in the workspace.  When T > 64 the
+ *                   frames are cut into
  *                   ceil(T / 64) segments of nearly equal length and the
  *                   build of segment i+1, the state pass of segment i and
  *                   the output of segment i-1 overlap: builds run on
@@ -154,10 +156,9 @@ int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype,
  * around every kernel launch of the call, on the stream that launch uses;
  * the call waits for `stream` (which the call joins back to) and writes,
  * for kernel kinds 0 = build, 1 = state pass (the whole fused kernel on the
- * fused path, flag reset included), 2 = output, the summed
- * elapsed milliseconds to
- * kernel_ms[kind] and the number of launches to launches[kind] (both host
- * arrays of 3).  Launches of different kinds may overlap in time, so the
+ * fused path, flag reset included), 2 = output, the summed elapsed
+ * milliseconds to kernel_ms[kind] and the number of launches to
+ * launches[kind] (both host arrays of 3).  Launches of different kinds may overlap in time, so the
  * three sums can add up to more than the call.  Results are identical to
  * gdn_frame_fwd.  The events are created as needed and kept for the life of
  * the process; this entry point is for profiling and is not meant for graph
@@ -209,11 +210,19 @@ int gdn_output(const gdn_shape* shape, int in_dtype, int out_dtype, const void* 
  * GDN_E_UNSUPPORTED_D).  d_out has in_dtype; d_state_out is [B,H,D,D] f32 or
  * NULL (zero).  dq, dk, dv: [B,H,T,S,D] f32; dgamma, dbeta: [B,H,T] f32;
  * d_state_in: [B,H,D,D] f32 (may equal d_state_out, for chunked backward
- * passes that carry the state gradient).  The forward states are recomputed
- * from q, k, v, gamma, beta and state_in.  Asynchronous on `stream`;
- * argument errors return before any launch.  workspace: at least
- * gdn_bwd_workspace_bytes(shape, in_dtype) bytes of device memory,
- * 256-byte aligned.
+ * passes that carry the state gradient: cutting a sequence into calls made
+ * last chunk first, each given the next chunk's d_state_in as d_state_out
+ * and its own forward state_in, gives the one-call result bit for bit).
+ * The forward states are recomputed from q, k, v, gamma, beta and state_in.
+ * Asynchronous on `stream`; for T > 64 the work runs in 64-frame segments on
+ * the same library-owned side streams as gdn_frame_fwd, forked from and
+ * joined back to `stream`, and results do not depend on the segmentation.
+ * Argument errors return before any launch.  workspace: at least
+ * gdn_bwd_workspace_bytes(shape, in_dtype) bytes of device memory
+ * (5 * B*H*T*D*D*4 bytes for the per-frame maps, plus 64 bytes per frame of
+ * partial sums and one state, each rounded up to 256), 256-byte aligned; its
+ * contents on return are unspecified.  gdn_bwd_workspace_bytes returns 0
+ * for an invalid shape.
  */
 size_t gdn_bwd_workspace_bytes(const gdn_shape* shape, int in_dtype);
 int gdn_frame_bwd(const gdn_shape* shape, int in_dtype,
