@@ -57,6 +57,14 @@ def test_backward_small_ragged():
     _backward_parity(w)
 
 
+@pytest.mark.parametrize("T", [1, 64, 65])
+def test_backward_segment_boundaries(T):
+    """A single frame; 64 frames (one segment); 65 frames (two segments)."""
+    w = Workload(name=f"bwd_t{T}", B=1, H=4, T=T, S=24, D=128, in_dtype="bf16", seed=76 + T,
+                 gamma_range=(0.9, 1.0), beta_kind="sigmoid_normal", state_std=0.05)
+    _backward_parity(w)
+
+
 def test_backward_zero_state_no_state_gradient():
     w = Workload(name="bwd_zero", B=2, H=2, T=5, S=37, D=128, in_dtype="bf16", seed=72,
                  gamma_range=(0.9, 1.0), beta_kind="sigmoid_normal")
