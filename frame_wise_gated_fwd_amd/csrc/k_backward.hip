@@ -1,40 +1,37 @@
 // Backward pass of the frame-wise GDN, head dim 128: the reverse-time state
-// pass, the reduction of its dgamma/dbeta partial sums, and the key and value
-// gradients (with the symmetric G-gradient term).  (dq and P_t = dO_t^T Q_t
-// reuse the forward's output and build kernels; gdn_api.cpp orders the
-// launches.)
-// Every launcher covers frames [t0, t1) of every head, so the schedule can
-// cut the sequence into segments; results do not depend on the cut.
+// pass, the reduction of its dgamma/dbeta partial sums, and the key and
+// value gradients (with the symmetric G-gradient term).  dq and
+// P_t = dO_t^T Q_t reuse the forward's output and build kernels;
+// gdn_api.cpp orders the launches.  Every launcher covers frames [t0, t1)
+// of every head, so the schedule can cut the sequence into segments; results
+// do not depend on the cut.
 //
-// Reverse-time state pass.
-//
-// The forward M_t = gamma_t (M_{t-1} - beta_t M_{t-1} G_t) + beta_t U_t with
-// O_t = Q_t M_t^T (the recurrence of "SANA-WM: NVIDIA puts a one-minute world
-// model on a single GPU", zhichai.net, section 1) has, for the total gradient
-// Lambda_t reaching M_t,
+// Reverse-time state pass.  The forward
+// M_t = gamma_t (M_{t-1} - beta_t M_{t-1} G_t) + beta_t U_t, O_t = Q_t M_t^T
+// (the recurrence of "SANA-WM: NVIDIA puts a one-minute world model on a
+// single GPU", zhichai.net, section 1) has, for the total gradient Lambda_t
+// reaching M_t,
 //   Lambda_t = L_t + P_t,          P_t = dO_t^T Q_t,  L_{T-1} = dM_T,
 //   X_t      = Lambda_t G_t,
 //   L_{t-1}  = gamma_t (Lambda_t - beta_t X_t)      (G_t is symmetric),
 // and the gradient of the initial state is L_{-1}.  A launch over frames
 // [tb, te) starts from L_{te-1} in d_state_out and leaves L_{tb-1} in
-// d_state_in (P_{tb-1} not yet added, as the next launch adds it).  Per
-// frame this kernel
+// d_state_in (P_{tb-1} not yet added: the next launch adds it).  Per frame it
 // also writes LB_t = beta_t Lambda_t (the frame's dU_t, which the gradient
-// kernels use) and, over its rows, partial sums of
+// kernel uses) and, over its rows, partial sums of
 //   dgamma_t = < Lambda_t - beta_t X_t, M_{t-1} >,
 //   dbeta_t  = < Lambda_t, U_t > - gamma_t < X_t, M_{t-1} >.
-//
 // It runs like the forward state pass, frames in reverse: rows of Lambda
 // evolve independently (row i of L_{t-1} needs only row i of Lambda_t), so
-// each head's 128 rows are split over workgroups of kBwdRows rows; X = Lambda G
-// runs on bf16 MFMA in three passes (Ghi*Lhi + Glo*Lhi + Ghi*Llo, G_t and
-// U_t in the forward's packed forms) with the
-// float32 running value in registers and its hi/lo pair in LDS; the
-// per-frame inputs (this wave's G_t rows, and the workgroup's rows of U_t,
-// M_{t-1} and P_{t-1}) stream through a two-frame register ring.  The
-// partial sums are kept per 16-row block (whatever kBwdRows is) and
-// reduced in a fixed order (lanes, then waves, then blocks), so the results
-// are deterministic and do not depend on kBwdRows.
+// each head's 128 rows are split over workgroups of kBwdRows rows.
+// X = Lambda G runs on bf16 MFMA in three passes (Ghi*Lhi + Glo*Lhi +
+// Ghi*Llo; G_t and U_t in the forward's packed forms) with the float32
+// running value in registers and its hi/lo pair in LDS; the per-frame inputs
+// (this wave's G_t rows, and the workgroup's rows of U_t, M_{t-1} and
+// P_{t-1}) stream through a two-frame register ring.  The partial sums are
+// kept per 16-row block and reduced in a fixed order (lanes, then waves,
+// then blocks), so the results are deterministic and do not depend on
+// kBwdRows.
 #include "frame_output.h"
 #include "gdn_common.h"
 #include "gdn_backward.h"
@@ -50,10 +47,11 @@ namespace {
 constexpr int D = 128;
 constexpr int kLdsW = D + 8;
 constexpr int kDepth = 2;
-// rows of the state gradient per workgroup of the reverse-time pass
+// rows of the state gradient per workgroup of the reverse-time pass (32 rows,
+// half the workgroups, measured slower: the pass is on the critical path)
 constexpr int kBwdRows = 16;
 // waves per workgroup of the key/value-gradient kernel (its LDS allows one
-// workgroup per CU)
+// workgroup per CU; 8 waves must fit 256 registers, spill and are slower)
 constexpr int kDkvWaves = 4;
 static_assert(kBwdParts == D / 16, "partial sums are kept per 16-row block");
 
