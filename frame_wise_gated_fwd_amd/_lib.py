@@ -17,11 +17,12 @@ GDN_BF16 = 1
 GDN_PATH_PLAIN, GDN_PATH_MFMA, GDN_PATH_FUSED = 0, 1, 2
 
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_E_NULLPTR", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE",
-                4: "GDN_E_UNSUPPORTED_D", 5: "GDN_E_WORKSPACE", 6: "GDN_E_ALIAS", 7: "GDN_E_HIP"}
+                4: "GDN_E_UNSUPPORTED_D", 5: "GDN_E_WORKSPACE", 6: "GDN_E_ALIAS", 7: "GDN_E_HIP",
+                8: "GDN_E_VALUE"}
 
 # Every symbol include/gdn.h declares, with (restype, argtypes).
 _vp, _cvp = ctypes.c_void_p, ctypes.c_void_p
-_sz, _i = ctypes.c_size_t, ctypes.c_int
+_sz, _i, _f = ctypes.c_size_t, ctypes.c_int, ctypes.c_float
 
 
 class Shape(ctypes.Structure):
@@ -39,11 +40,14 @@ SIGNATURES = {
     "gdn_set_fused": (_i, [_i]),
     "gdn_workspace_bytes": (_sz, [_PS, _i]),
     "gdn_frame_fwd": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp]),
+    "gdn_frame_fwd_ks": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _f, _vp, _vp, _vp, _sz, _vp]),
     "gdn_frame_fwd_timed": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp,
                                  ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
     "gdn_bwd_workspace_bytes": (_sz, [_PS, _i]),
     "gdn_frame_bwd": (_i, [_PS, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _sz, _vp]),
+    "gdn_frame_bwd_ks": (_i, [_PS, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _f, _cvp, _cvp, _vp, _vp, _vp, _vp,
+                              _vp, _vp, _vp, _sz, _vp]),
     "gdn_build_maps": (_i, [_PS, _i, _cvp, _cvp, _vp, _vp, _vp]),
     "gdn_state_pass": (_i, [_PS, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp]),
     "gdn_output": (_i, [_PS, _i, _i, _cvp, _cvp, _vp, _vp]),

@@ -67,12 +67,15 @@ def workspace_bytes(B: int, H: int, T: int, S: int, D: int, in_dtype: torch.dtyp
 def frame_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
               beta: torch.Tensor, state: Optional[torch.Tensor] = None,
               out_dtype: torch.dtype = torch.float32, *, out: Optional[torch.Tensor] = None,
-              state_out: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Frame-wise GDN forward (gdn_frame_fwd).
+              state_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              key_scale: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Frame-wise GDN forward (gdn_frame_fwd; gdn_frame_fwd_ks when key_scale
+    is given).
 
-    q, k, v: [B, H, T, S, D] bf16 or f32 (k already scaled by 1/sqrt(D*S));
-    gamma, beta: [B, H, T] f32; state: [B, H, D, D] f32 or None (zeros).
+    q, k, v: [B, H, T, S, D] bf16 or f32; gamma, beta: [B, H, T] f32;
+    state: [B, H, D, D] f32 or None (zeros).  Without key_scale, k is already
+    scaled (by 1/sqrt(D*S) in the pages' setting); with it, the build runs on
+    key_scale * k.
     Returns (out [B, H, T, S, D] out_dtype, state_out [B, H, D, D] f32).
     state_out may be the same tensor as state (in-place streaming)."""
     shp = shape_of(q)
@@ -96,19 +99,26 @@ def frame_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Te
     wsb = int(L.gdn_workspace_bytes(ctypes.byref(shp), in_code))
     if workspace is None:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    st = L.gdn_frame_fwd(ctypes.byref(shp), in_code, out_code, _ptr(q), _ptr(k), _ptr(v),
-                         _ptr(gamma), _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out),
-                         _ptr(workspace), workspace.numel(), _stream(dev))
-    check(st, "gdn_frame_fwd")
+    if key_scale is None:
+        st = L.gdn_frame_fwd(ctypes.byref(shp), in_code, out_code, _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(gamma), _ptr(beta), _ptr(state), _ptr(out), _ptr(state_out),
+                             _ptr(workspace), workspace.numel(), _stream(dev))
+        check(st, "gdn_frame_fwd")
+    else:
+        st = L.gdn_frame_fwd_ks(ctypes.byref(shp), in_code, out_code, _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(gamma), _ptr(beta), _ptr(state), float(key_scale), _ptr(out),
+                                _ptr(state_out), _ptr(workspace), workspace.numel(), _stream(dev))
+        check(st, "gdn_frame_fwd_ks")
     return out, state_out
 
 
 def frame_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
               d_out: torch.Tensor, state: Optional[torch.Tensor] = None,
               d_state_out: Optional[torch.Tensor] = None, *,
-              d_state_in: Optional[torch.Tensor] = None):
-    """Backward pass of frame_fwd (gdn_frame_bwd): gradients of
-    <d_out, out> + <d_state_out, state_out>.
+              d_state_in: Optional[torch.Tensor] = None, key_scale: Optional[float] = None):
+    """Backward pass of frame_fwd (gdn_frame_bwd; gdn_frame_bwd_ks when
+    key_scale is given, dk then being the gradient with respect to the
+    unscaled keys): gradients of <d_out, out> + <d_state_out, state_out>.
 
     q, k, v, d_out: [B, H, T, S, 128] bf16; gamma, beta: [B, H, T] f32;
     state, d_state_out: [B, H, 128, 128] f32 or None (zeros).  Returns
@@ -133,11 +143,13 @@ def frame_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Te
     L = lib()
     wsb = int(L.gdn_bwd_workspace_bytes(ctypes.byref(shp), GDN_BF16))
     workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    st = L.gdn_frame_bwd(ctypes.byref(shp), GDN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta),
-                         _ptr(state), _ptr(d_out), _ptr(d_state_out), _ptr(grads[0]), _ptr(grads[1]),
-                         _ptr(grads[2]), _ptr(dgamma), _ptr(dbeta), _ptr(d_state_in), _ptr(workspace), wsb,
-                         _stream(dev))
-    check(st, "gdn_frame_bwd")
+    tail = (_ptr(d_out), _ptr(d_state_out), _ptr(grads[0]), _ptr(grads[1]), _ptr(grads[2]), _ptr(dgamma),
+            _ptr(dbeta), _ptr(d_state_in), _ptr(workspace), wsb, _stream(dev))
+    head = (ctypes.byref(shp), GDN_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(state))
+    if key_scale is None:
+        check(L.gdn_frame_bwd(*head, *tail), "gdn_frame_bwd")
+    else:
+        check(L.gdn_frame_bwd_ks(*head, float(key_scale), *tail), "gdn_frame_bwd_ks")
     return grads[0], grads[1], grads[2], dgamma, dbeta, d_state_in
 
 

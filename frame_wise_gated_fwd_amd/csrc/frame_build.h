@@ -33,7 +33,9 @@ template <bool kPacked>
 constexpr int build_lds_bytes() { return kPacked ? 65536 : 32768; }
 
 // G_t = K_t^T K_t and U_t = V_t^T K_t of one frame.  Kf, Vf: the frame's
-// [S, 128] bf16 rows.  kPacked: Gout receives the packed bf16 hi/lo form
+// [S, 128] bf16 rows.  ks scales the keys: the maps are written as
+// ks^2 G_t and ks U_t (the float32 sums times ks^2 or ks, one rounding;
+// ks = 1 leaves them unchanged).  kPacked: Gout receives the packed bf16 hi/lo form
 // and Uout the packed float32 form (gdn_packed.h); otherwise both are
 // float32 row-major 128 x 128, and Gout may be null (only U_t is written).
 // `lds` must hold build_lds_bytes<kPacked>().
@@ -43,7 +45,7 @@ constexpr int build_lds_bytes() { return kPacked ? 65536 : 32768; }
 template <bool kPacked, int kDepth = 1>
 __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, const uint16_t* __restrict__ Vf,
                                             int S, u32x4* __restrict__ lds, void* __restrict__ Gout,
-                                            float* __restrict__ Uout) {
+                                            float* __restrict__ Uout, float ks) {
   constexpr int D = 128;
   constexpr int kIterTok = kBuildIterTok;
   // During the token loop: frag[unit][j][lane] (32 KB); unit 0,1 = K slab 0,1;
@@ -127,6 +129,16 @@ __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, con
       ((it0 + js < iters ? iteration(std::integral_constant<int, js>{}, it0 + js) : void()), ...);
     }(std::make_integer_sequence<int, kDepth>{});
   }
+
+  // the key scale: G_t picks up ks twice, U_t once
+  const float ks2 = ks * ks;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      accG[a][b] *= ks2;
+      accU[a][b] *= ks;
+    }
 
   // Lane (g, c), register i of block (j, jp) holds X[32g + 8i + j][8c + jp].
   if constexpr (kPacked) {

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdlib>
 #include <limits>
 #include <mutex>
@@ -233,7 +234,7 @@ hipError_t timed(Recorder* rec, hipStream_t st, int kind, F&& launch) {
 // from HBM on the rest.  With one segment everything runs on the caller's
 // stream.
 hipError_t run_mfma(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                    const float* gamma, const float* beta, const float* state_in, void* out,
+                    const float* gamma, const float* beta, const float* state_in, float ks, void* out,
                     bool out_bf16, float* state_out, void* G, float* U, void* M_all, hipStream_t s,
                     Recorder* rec) {
   const int64_t F = segment_frames();
@@ -241,7 +242,7 @@ hipError_t run_mfma(const Dims& d, const uint16_t* q, const uint16_t* k, const u
   const int S = (int)d.S;
   auto build = [&](hipStream_t st, int64_t t0, int64_t t1) {
     return timed(rec, st, 0, [&] {
-      return gdn::launch_build_bf16_d128(k, v, G, true, U, d.heads, d.T, t0, t1, S, st);
+      return gdn::launch_build_bf16_d128(k, v, G, true, U, d.heads, d.T, t0, t1, S, ks, st);
     });
   };
   auto state = [&](hipStream_t st, int64_t t0, int64_t t1) {
@@ -298,6 +299,7 @@ struct BwdArgs {
   const uint16_t *q, *k, *v, *d_out;
   const float *gamma, *beta, *state_in, *d_state_out;
   float *dq, *dk, *dv, *dgamma, *dbeta, *d_state_in;
+  float ks;  // key scale of the forward
 };
 struct BwdBuffers {
   float *G, *U, *M_all, *P, *LB, *partials, *fstate;
@@ -326,11 +328,11 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
   const int64_t H = d.heads, T = d.T;
   auto seg = [&](int64_t i) { return std::make_pair(i * T / nseg, (i + 1) * T / nseg); };
   auto build_kv = [&](hipStream_t st, int64_t t0, int64_t t1) {
-    return gdn::launch_build_bf16_d128(a.k, a.v, b.G, true, b.U, H, T, t0, t1, S, st);
+    return gdn::launch_build_bf16_d128(a.k, a.v, b.G, true, b.U, H, T, t0, t1, S, a.ks, st);
   };
   // P_t = dO_t^T Q_t: the build's second map with (K, V) = (Q, dO); its first (Q^T Q) is not stored
   auto build_p = [&](hipStream_t st, int64_t t0, int64_t t1) {
-    return gdn::launch_build_bf16_d128(a.q, a.d_out, nullptr, false, b.P, H, T, t0, t1, S, st);
+    return gdn::launch_build_bf16_d128(a.q, a.d_out, nullptr, false, b.P, H, T, t0, t1, S, 1.f, st);
   };
   auto state_fwd = [&](hipStream_t st, int64_t t0, int64_t t1) {
     return gdn::launch_state_d128(b.G, true, b.U, a.gamma, a.beta, t0 ? b.fstate : a.state_in, b.M_all, true,
@@ -345,7 +347,8 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
                                       b.partials, a.d_state_in, H, T, t0, t1, st);
   };
   auto grads = [&](hipStream_t st, int64_t t0, int64_t t1) {  // dk = V LB + K S, dv = K LB^T
-    return gdn::launch_dkv_bwd_d128(a.v, a.k, b.LB, b.M_all, a.state_in, a.gamma, a.dk, a.dv, H, T, t0, t1, S, st);
+    return gdn::launch_dkv_bwd_d128(a.v, a.k, b.LB, b.M_all, a.state_in, a.gamma, a.ks, a.dk, a.dv, H, T, t0, t1, S,
+                                    st);
   };
   auto reduce = [&]() { return gdn::launch_bwd_reduce(b.partials, a.dgamma, a.dbeta, d.frames, s); };
   hipError_t e;
@@ -396,12 +399,13 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
 }
 
 int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
-                   const void* v, const float* gamma, const float* beta, const float* state_in,
+                   const void* v, const float* gamma, const float* beta, const float* state_in, float ks,
                    void* out, float* state_out, void* workspace, size_t workspace_bytes,
                    void* stream, Recorder* rec) {
   Dims d;
   int st = check_shape(shape, true, &d);
   if (st != GDN_OK) return st;
+  if (!std::isfinite(ks)) return GDN_E_VALUE;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GDN_E_DTYPE;
   if (!q || !k || !v || !gamma || !beta || !out || !state_out) return GDN_E_NULLPTR;
   const size_t need = gdn_workspace_bytes(shape, in_dtype);
@@ -430,18 +434,18 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
       return hip_status(timed(rec, s, 1, [&] {
         return gdn::launch_fused(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                  static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out,
-                                 workspace, d.heads, d.T, (int)d.S, grid, s);
+                                 workspace, d.heads, d.T, (int)d.S, ks, grid, s);
       }));
     // this device cannot host the fused kernel: the three-kernel schedule
   }
   if (fast_path(in_dtype, d.D))
     return hip_status(run_mfma(d, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                               static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out, G,
-                               U, M_all, s, rec));
+                               static_cast<const uint16_t*>(v), gamma, beta, state_in, ks, out, ob, state_out,
+                               G, U, M_all, s, rec));
   hipError_t e;
   if ((e = timed(rec, s, 0, [&] {
          return gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, static_cast<float*>(G), U, d.frames,
-                                          (int)d.S, (int)d.D, s);
+                                          (int)d.S, (int)d.D, ks, s);
        })) != hipSuccess)
     return GDN_E_HIP;
   if ((e = timed(rec, s, 1, [&] {
@@ -455,6 +459,46 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
        })) != hipSuccess)
     return GDN_E_HIP;
   return GDN_OK;
+}
+
+int frame_bwd_impl(const gdn_shape* shape, int in_dtype, const void* q, const void* k, const void* v,
+                   const float* gamma, const float* beta, const float* state_in, float ks, const void* d_out,
+                   const float* d_state_out, float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
+                   float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int st = check_shape(shape, true, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(in_dtype)) return GDN_E_DTYPE;
+  if (in_dtype != GDN_BF16) return GDN_E_DTYPE;
+  if (d.D != 128) return GDN_E_UNSUPPORTED_D;
+  if (!std::isfinite(ks)) return GDN_E_VALUE;
+  if (!q || !k || !v || !gamma || !beta || !d_out || !dq || !dk || !dv || !dgamma || !dbeta || !d_state_in)
+    return GDN_E_NULLPTR;
+  const size_t need = gdn_bwd_workspace_bytes(shape, in_dtype);
+  if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0) return GDN_E_WORKSPACE;
+  const size_t inb = d.in_elems * 2, gradb = d.in_elems * 4;
+  const size_t stb = d.state_elems * 4, gb = (size_t)d.frames * 4;
+  const Range outs[] = {{dq, gradb}, {dk, gradb}, {dv, gradb}, {dgamma, gb}, {dbeta, gb},
+                        {d_state_in, stb}, {workspace, need}};
+  const Range ins[] = {{q, inb}, {k, inb}, {v, inb}, {gamma, gb}, {beta, gb}, {state_in, state_in ? stb : 0},
+                       {d_out, inb}, {d_state_out, d_state_out ? stb : 0}};
+  if (!aliasing_ok(outs, 7, ins, 8, d_state_in, d_state_out)) return GDN_E_ALIAS;
+
+  const size_t slot = round256(d.map_elems * sizeof(float));
+  char* ws = static_cast<char*>(workspace);
+  BwdBuffers b;
+  b.G = reinterpret_cast<float*>(ws);
+  b.U = reinterpret_cast<float*>(ws + slot);
+  b.M_all = reinterpret_cast<float*>(ws + 2 * slot);
+  b.P = reinterpret_cast<float*>(ws + 3 * slot);
+  b.LB = reinterpret_cast<float*>(ws + 4 * slot);
+  b.partials = reinterpret_cast<float*>(ws + 5 * slot);
+  b.fstate = reinterpret_cast<float*>(ws + 5 * slot +
+                                      round256((size_t)d.frames * gdn::kBwdParts * 2 * sizeof(float)));
+  const BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                  static_cast<const uint16_t*>(d_out), gamma, beta, state_in, d_state_out,
+                  dq, dk, dv, dgamma, dbeta, d_state_in, ks};
+  return hip_status(run_bwd(d, a, b, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -476,6 +520,7 @@ const char* gdn_status_str(int s) {
     case GDN_E_WORKSPACE: return "workspace missing or too small";
     case GDN_E_ALIAS: return "an output overlaps another buffer";
     case GDN_E_HIP: return "HIP runtime or launch error";
+    case GDN_E_VALUE: return "an argument value is outside its domain (a non-finite key scale)";
     default: return "unknown status";
   }
 }
@@ -512,9 +557,9 @@ int gdn_build_maps(const gdn_shape* shape, int in_dtype, const void* k, const vo
   if (fast_path(in_dtype, d.D))
     return hip_status(gdn::launch_build_bf16_d128(static_cast<const uint16_t*>(k),
                                                   static_cast<const uint16_t*>(v), G, false, U,
-                                                  d.heads, d.T, 0, d.T, (int)d.S, s));
+                                                  d.heads, d.T, 0, d.T, (int)d.S, 1.f, s));
   return hip_status(gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, G, U, d.frames, (int)d.S,
-                                              (int)d.D, s));
+                                              (int)d.D, 1.f, s));
 }
 
 int gdn_state_pass(const gdn_shape* shape, const float* G, const float* U, const float* gamma,
@@ -560,7 +605,14 @@ int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype, const voi
                   const void* v, const float* gamma, const float* beta, const float* state_in,
                   void* out, float* state_out, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  return frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, gamma, beta, state_in, out, state_out,
+  return frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, gamma, beta, state_in, 1.f, out, state_out,
+                        workspace, workspace_bytes, stream, nullptr);
+}
+
+int gdn_frame_fwd_ks(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
+                     const void* v, const float* gamma, const float* beta, const float* state_in, float key_scale,
+                     void* out, float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, gamma, beta, state_in, key_scale, out, state_out,
                         workspace, workspace_bytes, stream, nullptr);
 }
 
@@ -573,7 +625,7 @@ int gdn_frame_fwd_timed(const gdn_shape* shape, int in_dtype, int out_dtype, con
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_E_HIP;
   std::lock_guard<std::mutex> lock(g_timing_mu);
   Recorder rec{&g_timing_pool[dev], {}};
-  const int st = frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, gamma, beta, state_in, out,
+  const int st = frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, gamma, beta, state_in, 1.f, out,
                                 state_out, workspace, workspace_bytes, stream, &rec);
   if (st != GDN_OK) return st;
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return GDN_E_HIP;
@@ -600,43 +652,21 @@ size_t gdn_bwd_workspace_bytes(const gdn_shape* shape, int in_dtype) {
          round256(d.state_elems * sizeof(float));
 }
 
+
 int gdn_frame_bwd(const gdn_shape* shape, int in_dtype, const void* q, const void* k, const void* v,
                   const float* gamma, const float* beta, const float* state_in, const void* d_out,
                   const float* d_state_out, float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
                   float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
-  Dims d;
-  int st = check_shape(shape, true, &d);
-  if (st != GDN_OK) return st;
-  if (!valid_dtype(in_dtype)) return GDN_E_DTYPE;
-  if (in_dtype != GDN_BF16) return GDN_E_DTYPE;
-  if (d.D != 128) return GDN_E_UNSUPPORTED_D;
-  if (!q || !k || !v || !gamma || !beta || !d_out || !dq || !dk || !dv || !dgamma || !dbeta || !d_state_in)
-    return GDN_E_NULLPTR;
-  const size_t need = gdn_bwd_workspace_bytes(shape, in_dtype);
-  if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0) return GDN_E_WORKSPACE;
-  const size_t inb = d.in_elems * 2, gradb = d.in_elems * 4;
-  const size_t stb = d.state_elems * 4, gb = (size_t)d.frames * 4;
-  const Range outs[] = {{dq, gradb}, {dk, gradb}, {dv, gradb}, {dgamma, gb}, {dbeta, gb},
-                        {d_state_in, stb}, {workspace, need}};
-  const Range ins[] = {{q, inb}, {k, inb}, {v, inb}, {gamma, gb}, {beta, gb}, {state_in, state_in ? stb : 0},
-                       {d_out, inb}, {d_state_out, d_state_out ? stb : 0}};
-  if (!aliasing_ok(outs, 7, ins, 8, d_state_in, d_state_out)) return GDN_E_ALIAS;
+  return frame_bwd_impl(shape, in_dtype, q, k, v, gamma, beta, state_in, 1.f, d_out, d_state_out, dq, dk, dv,
+                        dgamma, dbeta, d_state_in, workspace, workspace_bytes, stream);
+}
 
-  const size_t slot = round256(d.map_elems * sizeof(float));
-  char* ws = static_cast<char*>(workspace);
-  BwdBuffers b;
-  b.G = reinterpret_cast<float*>(ws);
-  b.U = reinterpret_cast<float*>(ws + slot);
-  b.M_all = reinterpret_cast<float*>(ws + 2 * slot);
-  b.P = reinterpret_cast<float*>(ws + 3 * slot);
-  b.LB = reinterpret_cast<float*>(ws + 4 * slot);
-  b.partials = reinterpret_cast<float*>(ws + 5 * slot);
-  b.fstate = reinterpret_cast<float*>(ws + 5 * slot +
-                                      round256((size_t)d.frames * gdn::kBwdParts * 2 * sizeof(float)));
-  const BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                  static_cast<const uint16_t*>(d_out), gamma, beta, state_in, d_state_out,
-                  dq, dk, dv, dgamma, dbeta, d_state_in};
-  return hip_status(run_bwd(d, a, b, static_cast<hipStream_t>(stream)));
+int gdn_frame_bwd_ks(const gdn_shape* shape, int in_dtype, const void* q, const void* k, const void* v,
+                     const float* gamma, const float* beta, const float* state_in, float key_scale,
+                     const void* d_out, const float* d_state_out, float* dq, float* dk, float* dv, float* dgamma,
+                     float* dbeta, float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
+  return frame_bwd_impl(shape, in_dtype, q, k, v, gamma, beta, state_in, key_scale, d_out, d_state_out, dq, dk,
+                        dv, dgamma, dbeta, d_state_in, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

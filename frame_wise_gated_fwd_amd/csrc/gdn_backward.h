@@ -28,11 +28,11 @@ hipError_t launch_state_bwd_d128(const float* G, const float* U, const float* P,
 // dgamma, dbeta [head][T] from the partial sums (fixed summation order).
 hipError_t launch_bwd_reduce(const float* partials, float* dgamma, float* dbeta, int64_t frames,
                              hipStream_t st);
-// dk_t = V_t LB_t + K_t S_t and dv_t = K_t LB_t^T, float32 out, with
-// S_t = -gamma_t (M_{t-1}^T LB_t + LB_t^T M_{t-1}) formed in the kernel
-// (M_{-1} = m0, null = zero).
+// dk_t = ks V_t LB_t + ks^2 K_t S_t and dv_t = ks K_t LB_t^T, float32 out,
+// with S_t = -gamma_t (M_{t-1}^T LB_t + LB_t^T M_{t-1}) formed in the kernel
+// (M_{-1} = m0, null = zero) and ks the forward's key scale (1 for none).
 hipError_t launch_dkv_bwd_d128(const uint16_t* v, const uint16_t* k, const float* LB, const float* M_all,
-                               const float* m0, const float* gamma, float* dk, float* dv, int64_t heads, int64_t T,
-                               int64_t t0, int64_t t1, int S, hipStream_t st);
+                               const float* m0, const float* gamma, float ks, float* dk, float* dv, int64_t heads,
+                               int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st);
 
 }  // namespace gdn

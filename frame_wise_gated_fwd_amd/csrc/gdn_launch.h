@@ -20,10 +20,11 @@ namespace gdn {
 // give bit-identical results to the full-size variants.
 constexpr int64_t kFewFrames = 128;
 
-// G_t = K_t^T K_t and U_t = V_t^T K_t for frames [t0, t1); packed_out
-// selects the packed forms, else float32 row-major, where G may be null.
+// ks^2 K_t^T K_t and ks V_t^T K_t for frames [t0, t1) (ks: the key scale,
+// 1 for none); packed_out selects the packed forms, else float32 row-major,
+// where G may be null.
 hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
-                                  float* U, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
+                                  float* U, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, float ks,
                                   hipStream_t st);
 // State pass over frames [t0, t1) for `heads` heads, starting from state_in
 // (M_{t0-1}; null = zero) and leaving M_{t1-1} in state_out (which may equal
@@ -52,12 +53,12 @@ int64_t fused_workspace_bytes(int64_t heads);
 int fused_grid(bool out_bf16, int num_cus);
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                         const float* beta, const float* state_in, void* out, bool out_bf16,
-                        float* state_out, void* workspace, int64_t heads, int64_t T, int S, int grid,
+                        float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks, int grid,
                         hipStream_t st);
 
 // ---- plain float32 path: any supported D, f32 or bf16 inputs ---------------
 hipError_t launch_build_generic(const void* k, const void* v, bool in_bf16, float* G, float* U,
-                                int64_t frames, int S, int D, hipStream_t st);
+                                int64_t frames, int S, int D, float ks, hipStream_t st);
 hipError_t launch_state_generic(const float* G, const float* U, const float* gamma,
                                 const float* beta, const float* state_in, float* M_all,
                                 float* state_out, int64_t heads, int64_t T, int D,

@@ -25,14 +25,14 @@ namespace {
 template <bool kPacked>
 __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, void* __restrict__ Gout,
-    float* __restrict__ Uout, int S, int64_t T, int t0, int nt) {
+    float* __restrict__ Uout, int S, int64_t T, int t0, int nt, float ks) {
   constexpr int D = 128;
   __shared__ u32x4 lds[build_lds_bytes<kPacked>() / 16];
   // workgroup i: frame t0 + i % nt of head i / nt (frames are [head][T])
   const int64_t f = (int64_t)(blockIdx.x / nt) * T + t0 + blockIdx.x % nt;
   const int64_t in_off = f * (int64_t)S * D, mat_off = f * (int64_t)D * D;
   build_frame<kPacked>(K + in_off, V + in_off, S, lds, Gout ? static_cast<char*>(Gout) + mat_off * 4 : nullptr,
-                       Uout + mat_off);
+                       Uout + mat_off, ks);
 }
 
 // The same work for launches too small to fill the GPU (a few frames):
@@ -41,28 +41,29 @@ __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
 // order is the same as above, so results are bit-identical.
 __global__ __launch_bounds__(256, 1) void k1_build_bf16_d128_deep(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, void* __restrict__ Gout,
-    float* __restrict__ Uout, int S, int64_t T, int t0, int nt) {
+    float* __restrict__ Uout, int S, int64_t T, int t0, int nt, float ks) {
   constexpr int D = 128;
   __shared__ u32x4 lds[build_lds_bytes<true>() / 16];
   const int64_t f = (int64_t)(blockIdx.x / nt) * T + t0 + blockIdx.x % nt;
   const int64_t in_off = f * (int64_t)S * D, mat_off = f * (int64_t)D * D;
-  build_frame<true, 4>(K + in_off, V + in_off, S, lds, static_cast<char*>(Gout) + mat_off * 4, Uout + mat_off);
+  build_frame<true, 4>(K + in_off, V + in_off, S, lds, static_cast<char*>(Gout) + mat_off * 4, Uout + mat_off,
+                       ks);
 }
 
 }  // namespace
 
 hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
-                                  float* U, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
+                                  float* U, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, float ks,
                                   hipStream_t st) {
   const int nt = (int)(t1 - t0);
   const dim3 grid((unsigned)(heads * nt));
   if (packed_out && !G) return hipErrorInvalidValue;  // the packed form always writes G
   if (packed_out && heads * nt <= kFewFrames)
-    hipLaunchKernelGGL(k1_build_bf16_d128_deep, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt);
+    hipLaunchKernelGGL(k1_build_bf16_d128_deep, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks);
   else if (packed_out)
-    hipLaunchKernelGGL(k1_build_bf16_d128<true>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt);
+    hipLaunchKernelGGL(k1_build_bf16_d128<true>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks);
   else
-    hipLaunchKernelGGL(k1_build_bf16_d128<false>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt);
+    hipLaunchKernelGGL(k1_build_bf16_d128<false>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks);
   return hipGetLastError();
 }
 

@@ -309,6 +309,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 // it, in launches of a few frames):
 //   dk_t = V_t LB_t + K_t S_t,   dv_t = K_t LB_t^T,
 //   S_t = -gamma_t (A + A^T),    A = M_{t-1}^T LB_t
+// for keys used as given; when the forward scaled them by ks inside its
+// build, the gradients with respect to the unscaled keys are
+// dk_t = ks V_t LB_t + ks^2 K_t S_t and dv_t = ks K_t LB_t^T: ks LB_t is
+// staged in place of LB_t (so A and the S_t formed from it pick up one ks)
+// and S_t is multiplied by ks once more.
 // (K_t S_t is K_t (dG_t + dG_t^T) with dG_t = -gamma_t beta_t M_{t-1}^T Lambda_t;
 // LB_t = beta_t Lambda_t carries beta).  LDS holds two 128 x 128 matrices as
 // bf16 hi/lo planes (2 x 69.6 KB, so one workgroup per CU), which carry them
@@ -334,7 +339,7 @@ template <int kDepth, int kWaves>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_dkv_d128(const uint16_t* __restrict__ V,
                                                    const uint16_t* __restrict__ K, const float* __restrict__ LB,
                                                    const float* __restrict__ M_all, const float* m0,
-                                                   const float* __restrict__ gamma, float* __restrict__ dk,
+                                                   const float* __restrict__ gamma, float ks, float* __restrict__ dk,
                                                    float* __restrict__ dv, int S, int64_t T, int t0, int nt,
                                                    int nsplit) {
   // [LB^T | M_{t-1}, then S][hi | lo][LDS row][column]
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_dkv_d128(const uint16_t* __r
   for (int i = 0; i < kLoads; ++i) {
     const int idx = tid + kThreads * i;
     const int r = idx >> 5, c4 = (idx & 31) * 4;
-    const f32x4 lv = lvs[i];
+    const f32x4 lv = lvs[i] * ks;
     const u32x2 p0 = split2(lv[0], lv[1]), p1 = split2(lv[2], lv[3]);
     const uint32_t hi[2] = {p0.x, p1.x}, lo[2] = {p0.y, p1.y};
 #pragma unroll
@@ -441,7 +446,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_dkv_d128(const uint16_t* __r
 #pragma unroll
         for (int i = 0; i < 4; ++i) As[16 * (kAB * w + ab) + 4 * g + i][16 * bb + n] = acc[ab][bb][i];
     __syncthreads();
-    const float ng = -gamma[f];
+    const float ng = ks * -gamma[f];  // staged LB carries one ks already: S picks up ks^2
     u32x2 sh[D * D / 4 / kThreads], sl[D * D / 4 / kThreads];
 #pragma unroll
     for (int jj = 0; jj < D * D / 4 / kThreads; ++jj) {
@@ -585,12 +590,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_dkv_d128(const uint16_t* __r
 }  // namespace
 
 hipError_t launch_dkv_bwd_d128(const uint16_t* v, const uint16_t* k, const float* LB, const float* M_all,
-                               const float* m0, const float* gamma, float* dk, float* dv, int64_t heads, int64_t T,
-                               int64_t t0, int64_t t1, int S, hipStream_t st) {
+                               const float* m0, const float* gamma, float ks, float* dk, float* dv, int64_t heads,
+                               int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st) {
   const int64_t nt = t1 - t0, frames = heads * nt;
   const int nsplit = token_split(frames, S);
   hipLaunchKernelGGL((k_dkv_d128<1, kDkvWaves>), dim3((unsigned)(frames * nsplit)), dim3(64 * kDkvWaves), 0, st, v, k,
-                     LB, M_all, m0, gamma, dk, dv, S, T, (int)t0, (int)nt, nsplit);
+                     LB, M_all, m0, gamma, ks, dk, dv, S, T, (int)t0, (int)nt, nsplit);
   return hipGetLastError();
 }
 

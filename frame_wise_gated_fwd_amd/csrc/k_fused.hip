@@ -138,6 +138,7 @@ struct Args {
   Ctrl* ctrl;
   uint32_t* flags;  // per head kFlagWords
   int heads, T, S;
+  float ks;         // key scale: the build items write ks^2 G_t and ks U_t
 };
 
 __host__ __device__ constexpr int64_t ring_head_bytes(int wg, int wm) {
@@ -435,7 +436,7 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
       float* up = reinterpret_cast<float*>(ring + (int64_t)(2 * (it.t % kWG) + 1) * packed::kFrameBytes);
       // two token iterations loaded ahead: 1-2 % faster than one, and the
       // kernel then uses exactly its 256 registers (three spill)
-      build_frame<true, 2>(a.k + fr * S * D, a.v + fr * S * D, S, lds.build, gp, up);
+      build_frame<true, 2>(a.k + fr * S * D, a.v + fr * S * D, S, lds.build, gp, up, a.ks);
       wait_stores();
       __syncthreads();
       if (tid == 0) flag_store(fl + kFlagGReady + it.t % kWG, (uint32_t)(it.t + 1));
@@ -527,7 +528,7 @@ int fused_grid(bool out_bf16, int num_cus) {
 
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                         const float* beta, const float* state_in, void* out, bool out_bf16,
-                        float* state_out, void* workspace, int64_t heads, int64_t T, int S, int grid,
+                        float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks, int grid,
                         hipStream_t st) {
   char* ws = static_cast<char*>(workspace);
   const int64_t group = kXcd * kMaxHeadsPerXcd;
@@ -551,6 +552,7 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     a.heads = (int)nh;
     a.T = (int)T;
     a.S = S;
+    a.ks = ks;
     hipLaunchKernelGGL(k_fused_init, dim3((nwords + 255) / 256), dim3(256), 0, st,
                        reinterpret_cast<uint32_t*>(ws), nwords);
     hipError_t e = hipGetLastError();

@@ -1,7 +1,7 @@
 // Plain float32 path of the frame-wise GDN for every supported head dim
 // (multiples of 16 up to 128) and for float32 inputs: the same three stages
 // as the MFMA path, written with LDS tiles and register-blocked float32 FMA.
-//   build:  G_t = K_t^T K_t, U_t = V_t^T K_t
+//   build:  G_t = ks^2 K_t^T K_t, U_t = ks V_t^T K_t (ks: the key scale)
 //   state:  M_t = gamma_t (M_{t-1} - beta_t M_{t-1} G_t) + beta_t U_t
 //   output: O_t = Q_t M_t^T
 // A 256-thread workgroup is a 16 x 16 grid; thread (ty, tx) owns the entries
@@ -26,7 +26,8 @@ __device__ __forceinline__ float load_in(const void* p, int64_t i) {
 
 template <bool kBf16>
 __global__ __launch_bounds__(256) void g_build(const void* __restrict__ K, const void* __restrict__ V,
-                                               float* __restrict__ G, float* __restrict__ U, int S, int D) {
+                                               float* __restrict__ G, float* __restrict__ U, int S, int D,
+                                               float ks) {
   __shared__ float Ks[kTokTile][kMaxD + 1];
   __shared__ float Vs[kTokTile][kMaxD + 1];
   const int64_t f = blockIdx.x;
@@ -76,8 +77,8 @@ __global__ __launch_bounds__(256) void g_build(const void* __restrict__ K, const
     for (int q = 0; q < kMaxB; ++q)
       if (p < nb && q < nb) {
         const int i = ty + 16 * p, j = tx + 16 * q;
-        Gf[i * D + j] = ag[p][q];
-        Uf[i * D + j] = au[p][q];
+        Gf[i * D + j] = ag[p][q] * (ks * ks);  // the key scale: twice in G, once in U
+        Uf[i * D + j] = au[p][q] * ks;
       }
 }
 
@@ -211,11 +212,11 @@ __global__ __launch_bounds__(256) void g_output(const void* __restrict__ Q, cons
 }  // namespace
 
 hipError_t launch_build_generic(const void* k, const void* v, bool in_bf16, float* G, float* U,
-                                int64_t frames, int S, int D, hipStream_t st) {
+                                int64_t frames, int S, int D, float ks, hipStream_t st) {
   if (in_bf16)
-    hipLaunchKernelGGL(g_build<true>, dim3((unsigned)frames), dim3(256), 0, st, k, v, G, U, S, D);
+    hipLaunchKernelGGL(g_build<true>, dim3((unsigned)frames), dim3(256), 0, st, k, v, G, U, S, D, ks);
   else
-    hipLaunchKernelGGL(g_build<false>, dim3((unsigned)frames), dim3(256), 0, st, k, v, G, U, S, D);
+    hipLaunchKernelGGL(g_build<false>, dim3((unsigned)frames), dim3(256), 0, st, k, v, G, U, S, D, ks);
   return hipGetLastError();
 }
 

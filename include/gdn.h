@@ -17,9 +17,10 @@
  *     M_t = M_{t-1} gamma_t (I - beta_t G_t) + beta_t U_t
  *     O_t = Q_t M_t^T
  *
- * with M_0 = state_in (zeros when NULL) and state_out = M_T.  The library
+ * with M_0 = state_in (zeros when NULL) and state_out = M_T.  gdn_frame_fwd
  * applies no key scaling: the caller passes keys already multiplied by
- * 1/sqrt(D*S).
+ * 1/sqrt(D*S).  gdn_frame_fwd_ks takes the scale as an argument instead and
+ * applies it inside the build of G_t and U_t (keys as given, unscaled).
  *
  * Layout.  All tensors are dense, row-major, innermost index last:
  *     q, k, v, out   [B, H, T, S, D]
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
   GDN_OK = 0,
@@ -61,7 +62,8 @@ typedef enum {
   GDN_E_UNSUPPORTED_D = 4,  /* head dim not one of the supported sizes        */
   GDN_E_WORKSPACE = 5,      /* workspace NULL or smaller than required        */
   GDN_E_ALIAS = 6,          /* an output overlaps another buffer              */
-  GDN_E_HIP = 7             /* a HIP runtime call or launch failed            */
+  GDN_E_HIP = 7,            /* a HIP runtime call or launch failed            */
+  GDN_E_VALUE = 8           /* an argument value is outside its domain        */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -152,6 +154,22 @@ int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_frame_fwd with the key scaling fused into the build: the keys K_t are
+ * used as given and the recurrence runs on key_scale * K_t, i.e.
+ *     G_t = key_scale^2 K_t^T K_t,    U_t = key_scale V_t^T K_t
+ * (the pages scale keys by 1/sqrt(D*S): pass that value with unscaled keys).
+ * Each map is its float32 sum times key_scale^2 or key_scale, one rounding,
+ * so key_scale = 1 gives gdn_frame_fwd's result bit for bit.  key_scale must
+ * be finite (else GDN_E_VALUE).  Everything else as gdn_frame_fwd.  The fused
+ * prologue saves the caller a separate pass over K (read and write).
+ */
+int gdn_frame_fwd_ks(const gdn_shape* shape, int in_dtype, int out_dtype,
+                     const void* q, const void* k, const void* v,
+                     const float* gamma, const float* beta,
+                     const float* state_in, float key_scale, void* out, float* state_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gdn_frame_fwd, plus per-kernel durations: a pair of HIP events is recorded
  * around every kernel launch of the call, on the stream that launch uses;
  * the call waits for `stream` (which the call joins back to) and writes,
@@ -231,6 +249,20 @@ int gdn_frame_bwd(const gdn_shape* shape, int in_dtype,
                   const void* d_out, const float* d_state_out,
                   float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
                   float* d_state_in, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward of gdn_frame_fwd_ks: gradients with respect to the unscaled
+ * keys given to it, dk = key_scale * (gradient with respect to
+ * key_scale * K); the other gradients as gdn_frame_bwd's.  key_scale = 1
+ * gives gdn_frame_bwd's result bit for bit; it must be finite (else
+ * GDN_E_VALUE).  Same workspace as gdn_frame_bwd.
+ */
+int gdn_frame_bwd_ks(const gdn_shape* shape, int in_dtype,
+                     const void* q, const void* k, const void* v,
+                     const float* gamma, const float* beta, const float* state_in, float key_scale,
+                     const void* d_out, const float* d_state_out,
+                     float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
+                     float* d_state_in, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -37,6 +37,7 @@ class Workload:
     # streaming partition (frames per successive call); empty -> one call
     stream_chunks: Tuple[int, ...] = field(default_factory=tuple)
     tol: float = 2e-3                  # relative L2 tolerance for O and the final state
+    keys_prescaled: bool = True        # False: raw keys, the library applies key_scale itself
 
     @property
     def heads(self) -> int:
@@ -44,7 +45,8 @@ class Workload:
 
     @property
     def key_scale(self) -> float:
-        """Keys are pre-scaled by 1/sqrt(D*S) before they reach the library."""
+        """1/sqrt(D*S): keys are pre-scaled by it before they reach the library,
+        unless keys_prescaled is False (then the caller passes it as key_scale)."""
         return 1.0 / (self.D * self.S) ** 0.5
 
     def with_(self, **kw) -> "Workload":

@@ -15,8 +15,8 @@ alone and in any process.  Draw order inside one head's stream:
   7. state : D*D float32 normals scaled by state_std, if the workload has one
 
 Keys are multiplied by the boost (exact in float32), then by the key scale
-1/sqrt(D*S) in float32, and only then rounded to bfloat16 when the workload
-is bf16.  Rounding is IEEE round-to-nearest-even, which is what
+1/sqrt(D*S) in float32 (skipped for workloads whose keys are not
+prescaled), and only then rounded to bfloat16 when the workload is bf16.  Rounding is IEEE round-to-nearest-even, which is what
 ``torch.Tensor.to(torch.bfloat16)`` does.
 
 bf16 tensors are returned as uint16 bit patterns.  This module holds no part
@@ -76,7 +76,8 @@ def head_inputs(w: Workload, b: int, h: int) -> Dict[str, np.ndarray]:
         for t in range(T):
             rows = rng.permutation(S)[:nb]
             k[t, rows, :] *= mult
-    k *= np.float32(w.key_scale)
+    if w.keys_prescaled:
+        k *= np.float32(w.key_scale)
     state = None
     if w.state_std is not None:
         state = (rng.standard_normal(D * D, dtype=np.float32)

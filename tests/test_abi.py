@@ -11,7 +11,7 @@ from frame_wise_gated_fwd_amd._lib import SIGNATURES, Shape
 
 HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "gdn.h")
 
-OK, NULLPTR, SHAPE, DTYPE, UNSUP_D, WORKSPACE, ALIAS, HIP = range(8)
+OK, NULLPTR, SHAPE, DTYPE, UNSUP_D, WORKSPACE, ALIAS, HIP, VALUE = range(9)
 F32, BF16 = 0, 1
 
 
@@ -29,13 +29,13 @@ def test_library_exports_every_declared_symbol():
     L = F.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.gdn_abi_version() == 1
+    assert L.gdn_abi_version() == 2
 
 
 def test_status_strings():
     L = F.lib()
-    for s in range(8):
-        assert L.gdn_status_str(s)
+    for s in range(9):
+        assert L.gdn_status_str(s) != b"unknown status"
     assert L.gdn_status_str(99) == b"unknown status"
 
 
@@ -118,6 +118,29 @@ def test_frame_fwd_argument_errors():
     assert fwd(s, ws=None) == WORKSPACE
     assert fwd(s, wsb=1000) == WORKSPACE
     assert fwd(s, ws=P[7] + 8) == WORKSPACE  # misaligned
+
+
+def test_key_scale_argument_errors():
+    L = F.lib()
+    s = _shape()
+    wsb = L.gdn_workspace_bytes(ctypes.byref(s), BF16)
+
+    def fks(ks, shape=s, k=P[1]):
+        return L.gdn_frame_fwd_ks(ctypes.byref(shape), BF16, F32, P[0], k, P[2], P[3], P[4], None, ks,
+                                  P[5], P[6], P[7], wsb, None)
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        assert fks(bad) == VALUE
+    assert fks(1.0, k=None) == NULLPTR     # other checks as gdn_frame_fwd's
+    assert fks(1.0, shape=_shape(D=100)) == UNSUP_D
+    bwsb = L.gdn_bwd_workspace_bytes(ctypes.byref(s), BF16)
+
+    def bks(ks, dt=BF16):
+        return L.gdn_frame_bwd_ks(ctypes.byref(s), dt, P[0], P[1], P[2], P[3], P[4], None, ks, P[5], None,
+                                  P[6], P[7], P[8], P[9] + (1 << 30), P[9] + (2 << 30), P[11], P[10], bwsb,
+                                  None)
+    assert bks(float("nan")) == VALUE
+    assert bks(float("inf")) == VALUE
+    assert bks(1.0, dt=F32) == DTYPE
 
 
 def test_frame_fwd_alias_errors():
