@@ -226,9 +226,22 @@ def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
         e1.record()
         e1.synchronize()
         iso.append(e0.elapsed_time(e1) * 1e3)
+    # cold: 1 GiB of other traffic between calls evicts the call's 20 MB of
+    # inputs from the 256 MB memory-side cache
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=x["q"].device)
+    cold = []
+    for _ in range(20):
+        flush.add_(1.0)
+        e0.record()
+        call(one, state)
+        e1.record()
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    del flush
     return {"calls": len(chunks), "ms": round(stream_ms, 4),
             "frame_steps_per_s": round(B * T / (stream_ms * 1e-3), 1)}, \
-           {"isolated_us_median": round(float(np.median(iso)), 2), "back_to_back_us": round(back_to_back, 2)}
+           {"isolated_us_median": round(float(np.median(iso)), 2), "back_to_back_us": round(back_to_back, 2),
+            "cold_us_median": round(float(np.median(cold)), 2)}
 
 
 def backward_leg(x, L, w, stream, steps=5, warmup=1):
