@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["gdn_api.cpp", "k1_build.hip", "k2_state.hip", "k3_output.hip", "k_fused.hip", "k_backward.hip", "k_generic.hip"]
+SOURCES = ["gdn_api.cpp", "k1_build.hip", "k2_state.hip", "k3_output.hip", "k_fused.hip", "k_backward.hip", "k_generic.hip", "k_empty.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

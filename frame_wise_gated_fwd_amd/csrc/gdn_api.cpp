@@ -32,9 +32,10 @@ struct Dims {
   size_t in_elems, state_elems, map_elems;  // per tensor
 };
 
+// a * b for a, b >= 0, false on overflow
 bool mul_ok(int64_t a, int64_t b, int64_t* r) {
-  if (a <= 0 || b <= 0) return false;
-  if (a > std::numeric_limits<int64_t>::max() / b) return false;
+  if (a < 0 || b < 0) return false;
+  if (b != 0 && a > std::numeric_limits<int64_t>::max() / b) return false;
   *r = a * b;
   return true;
 }
@@ -42,8 +43,10 @@ bool mul_ok(int64_t a, int64_t b, int64_t* r) {
 bool valid_dtype(int d) { return d == GDN_F32 || d == GDN_BF16; }
 size_t dsize(int d) { return d == GDN_BF16 ? 2 : 4; }
 
-// Validates the shape; use_s selects whether S takes part.
-int check_shape(const gdn_shape* s, bool use_s, Dims* out) {
+// Validates the shape; use_s selects whether S takes part.  allow_empty
+// admits B, H, T or S of 0 (the whole calls: nothing to do, or only the
+// state to set); the stage entry points need every size >= 1.
+int check_shape(const gdn_shape* s, bool use_s, Dims* out, bool allow_empty = false) {
   if (!s) return GDN_E_NULLPTR;
   Dims d{};
   d.B = s->B;
@@ -51,11 +54,12 @@ int check_shape(const gdn_shape* s, bool use_s, Dims* out) {
   d.T = s->T;
   d.S = use_s ? s->S : 1;
   d.D = s->D;
-  if (d.B < 1 || d.H < 1 || d.T < 1 || d.S < 1 || d.D < 1) return GDN_E_SHAPE;
+  const int64_t lo = allow_empty ? 0 : 1;
+  if (d.B < lo || d.H < lo || d.T < lo || d.S < lo || d.D < 1) return GDN_E_SHAPE;
   if (!gdn_supports_d(d.D)) return GDN_E_UNSUPPORTED_D;
   if (d.S > std::numeric_limits<int>::max() / 256) return GDN_E_SHAPE;
   int64_t heads, frames, tmp;
-  if (!mul_ok(d.B, d.H, &heads) || !mul_ok(heads, d.T, &frames)) return GDN_E_SHAPE;
+  if (!mul_ok(d.B, d.H, &heads) || heads > kMaxFrames || !mul_ok(heads, d.T, &frames)) return GDN_E_SHAPE;
   if (frames > kMaxFrames) return GDN_E_SHAPE;
   int64_t in_elems, map_elems;
   if (!mul_ok(frames, d.S, &tmp) || !mul_ok(tmp, d.D, &in_elems)) return GDN_E_SHAPE;
@@ -403,14 +407,17 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
                    void* out, float* state_out, void* workspace, size_t workspace_bytes,
                    void* stream, Recorder* rec) {
   Dims d;
-  int st = check_shape(shape, true, &d);
+  int st = check_shape(shape, true, &d, true);
   if (st != GDN_OK) return st;
   if (!std::isfinite(ks)) return GDN_E_VALUE;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GDN_E_DTYPE;
-  if (!q || !k || !v || !gamma || !beta || !out || !state_out) return GDN_E_NULLPTR;
+  // a pointer may be null exactly when its tensor has no elements
+  const bool has_in = d.in_elems > 0, has_fr = d.frames > 0, has_st = d.heads > 0;
+  if ((has_in && (!q || !k || !v || !out)) || (has_fr && (!gamma || !beta)) || (has_st && !state_out))
+    return GDN_E_NULLPTR;
   const size_t need = gdn_workspace_bytes(shape, in_dtype);
-  if (!workspace || workspace_bytes < need) return GDN_E_WORKSPACE;
-  if ((uintptr_t)workspace % 256 != 0) return GDN_E_WORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0))
+    return GDN_E_WORKSPACE;
   const size_t inb = d.in_elems * dsize(in_dtype), outb = d.in_elems * dsize(out_dtype);
   const size_t stb = d.state_elems * 4, gb = (size_t)d.frames * 4;
   const Range outs[] = {{out, outb}, {state_out, stb}, {workspace, need}};
@@ -418,6 +425,16 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
                        {state_in, state_in ? stb : 0}};
   if (!aliasing_ok(outs, 3, ins, 6, state_out, state_in)) return GDN_E_ALIAS;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!has_in) {
+    // no heads: nothing to do; no frames: state_out = state_in; frames
+    // without tokens: G_t = U_t = 0, each step only decays the state
+    if (!has_st) return GDN_OK;
+    if (!has_fr)
+      return hip_status(timed(rec, s, 1, [&] { return gdn::launch_state_fill(state_in, state_out, d.state_elems, s); }));
+    return hip_status(timed(rec, s, 1, [&] {
+      return gdn::launch_decay(gamma, state_in, state_out, d.heads, d.T, (int)d.D, s);
+    }));
+  }
 
   // Workspace: G_t, U_t, M_t of every frame (packed forms on the MFMA path).
   const size_t slot = round256(d.map_elems * sizeof(float));
@@ -466,16 +483,20 @@ int frame_bwd_impl(const gdn_shape* shape, int in_dtype, const void* q, const vo
                    const float* d_state_out, float* dq, float* dk, float* dv, float* dgamma, float* dbeta,
                    float* d_state_in, void* workspace, size_t workspace_bytes, void* stream) {
   Dims d;
-  int st = check_shape(shape, true, &d);
+  int st = check_shape(shape, true, &d, true);
   if (st != GDN_OK) return st;
   if (!valid_dtype(in_dtype)) return GDN_E_DTYPE;
   if (in_dtype != GDN_BF16) return GDN_E_DTYPE;
   if (d.D != 128) return GDN_E_UNSUPPORTED_D;
   if (!std::isfinite(ks)) return GDN_E_VALUE;
-  if (!q || !k || !v || !gamma || !beta || !d_out || !dq || !dk || !dv || !dgamma || !dbeta || !d_state_in)
+  // a pointer may be null exactly when its tensor has no elements
+  const bool has_in = d.in_elems > 0, has_fr = d.frames > 0, has_st = d.heads > 0;
+  if ((has_in && (!q || !k || !v || !d_out || !dq || !dk || !dv)) ||
+      (has_fr && (!gamma || !beta || !dgamma || !dbeta)) || (has_st && !d_state_in))
     return GDN_E_NULLPTR;
   const size_t need = gdn_bwd_workspace_bytes(shape, in_dtype);
-  if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0) return GDN_E_WORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0))
+    return GDN_E_WORKSPACE;
   const size_t inb = d.in_elems * 2, gradb = d.in_elems * 4;
   const size_t stb = d.state_elems * 4, gb = (size_t)d.frames * 4;
   const Range outs[] = {{dq, gradb}, {dk, gradb}, {dv, gradb}, {dgamma, gb}, {dbeta, gb},
@@ -483,6 +504,15 @@ int frame_bwd_impl(const gdn_shape* shape, int in_dtype, const void* q, const vo
   const Range ins[] = {{q, inb}, {k, inb}, {v, inb}, {gamma, gb}, {beta, gb}, {state_in, state_in ? stb : 0},
                        {d_out, inb}, {d_state_out, d_state_out ? stb : 0}};
   if (!aliasing_ok(outs, 7, ins, 8, d_state_in, d_state_out)) return GDN_E_ALIAS;
+  if (!has_in) {
+    // no heads: nothing to do; no frames: d_state_in = d_state_out; frames
+    // without tokens: the backward of the pure decay
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!has_st) return GDN_OK;
+    if (!has_fr) return hip_status(gdn::launch_state_fill(d_state_out, d_state_in, d.state_elems, s));
+    return hip_status(gdn::launch_decay_bwd(gamma, state_in, d_state_out, dgamma, dbeta, d_state_in, d.heads, d.T,
+                                            (int)d.D, s));
+  }
 
   const size_t slot = round256(d.map_elems * sizeof(float));
   char* ws = static_cast<char*>(workspace);
@@ -514,7 +544,7 @@ const char* gdn_status_str(int s) {
   switch (s) {
     case GDN_OK: return "ok";
     case GDN_E_NULLPTR: return "a required pointer is NULL";
-    case GDN_E_SHAPE: return "invalid shape (size < 1, too large, or overflow)";
+    case GDN_E_SHAPE: return "invalid shape (negative size, a stage call with a size of 0, too large, or overflow)";
     case GDN_E_DTYPE: return "unsupported dtype";
     case GDN_E_UNSUPPORTED_D: return "unsupported head dim (multiples of 16 up to 128)";
     case GDN_E_WORKSPACE: return "workspace missing or too small";
@@ -531,14 +561,15 @@ int gdn_supports_d(int64_t D) { return D >= 16 && D <= 128 && D % 16 == 0; }
 
 int gdn_path(const gdn_shape* shape, int in_dtype) {
   Dims d;
-  if (!valid_dtype(in_dtype) || check_shape(shape, true, &d) != GDN_OK) return -1;
+  if (!valid_dtype(in_dtype) || check_shape(shape, true, &d, true) != GDN_OK) return -1;
+  if (d.in_elems == 0) return GDN_PATH_PLAIN;
   if (fused_path(in_dtype, d)) return GDN_PATH_FUSED;
   return fast_path(in_dtype, d.D) ? GDN_PATH_MFMA : GDN_PATH_PLAIN;
 }
 
 size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype) {
   Dims d;
-  if (!valid_dtype(in_dtype) || check_shape(shape, true, &d) != GDN_OK) return 0;
+  if (!valid_dtype(in_dtype) || check_shape(shape, true, &d, true) != GDN_OK || d.in_elems == 0) return 0;
   return 3 * round256(d.map_elems * sizeof(float));
 }
 
@@ -644,7 +675,7 @@ int gdn_frame_fwd_timed(const gdn_shape* shape, int in_dtype, int out_dtype, con
 
 size_t gdn_bwd_workspace_bytes(const gdn_shape* shape, int in_dtype) {
   Dims d;
-  if (!valid_dtype(in_dtype) || check_shape(shape, true, &d) != GDN_OK) return 0;
+  if (!valid_dtype(in_dtype) || check_shape(shape, true, &d, true) != GDN_OK || d.in_elems == 0) return 0;
   // G, U (packed forms), M_all, P and LB (float32), then the dgamma/dbeta
   // partial sums and the recomputed final state
   return 5 * round256(d.map_elems * sizeof(float)) +

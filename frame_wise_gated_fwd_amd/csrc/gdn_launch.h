@@ -66,4 +66,16 @@ hipError_t launch_state_generic(const float* G, const float* U, const float* gam
 hipError_t launch_output_generic(const void* q, bool in_bf16, const float* M_all, void* out,
                                  bool out_bf16, int64_t frames, int S, int D, hipStream_t st);
 
+// ---- degenerate shapes (k_empty.hip), float32, any supported D ------------
+// dst = src (n floats), or zeros when src is null; nothing when src == dst.
+hipError_t launch_state_fill(const float* src, float* dst, int64_t n, hipStream_t st);
+// Frames without tokens (S = 0): M_t = gamma_t M_{t-1} over T frames per
+// head; state_out may equal state_in (null = zero).
+hipError_t launch_decay(const float* gamma, const float* state_in, float* state_out, int64_t heads, int64_t T,
+                        int D, hipStream_t st);
+// Its backward for the loss <d_state_out, state_out>: dgamma, dbeta [heads, T]
+// and d_state_in (may equal d_state_out; either state may be null = zero).
+hipError_t launch_decay_bwd(const float* gamma, const float* state_in, const float* d_state_out, float* dgamma,
+                            float* dbeta, float* d_state_in, int64_t heads, int64_t T, int D, hipStream_t st);
+
 }  // namespace gdn

@@ -41,6 +41,17 @@
  * Aliasing.  state_out may equal state_in exactly (in-place streaming), and
  * in gdn_frame_bwd d_state_in may equal d_state_out.  Any other overlap
  * between an output and any other buffer is GDN_E_ALIAS.
+ *
+ * Empty shapes.  gdn_frame_fwd, gdn_frame_bwd (and their _ks and _timed
+ * forms) accept B, H, T or S of 0; a pointer may then be NULL exactly when
+ * its tensor has no elements, and no workspace is needed (the workspace
+ * queries return 0).  With B*H = 0 nothing is done.  With T = 0 no step is
+ * taken: state_out = state_in (zeros when NULL), and in the backward
+ * d_state_in = d_state_out.  With S = 0 every frame has G_t = U_t = 0, so
+ * M_t = gamma_t M_{t-1} (one float32 product per frame); the backward then
+ * gives dbeta = 0, dgamma_t = (prod_{u != t} gamma_u) <d_state_out,
+ * state_in> and d_state_in = (prod_u gamma_u) d_state_out.  The stage entry
+ * points (gdn_build_maps, gdn_state_pass, gdn_output) need every size >= 1.
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -57,7 +68,8 @@ extern "C" {
 typedef enum {
   GDN_OK = 0,
   GDN_E_NULLPTR = 1,        /* a required pointer is NULL                     */
-  GDN_E_SHAPE = 2,          /* a size is < 1, too large, or overflows 64 bits */
+  GDN_E_SHAPE = 2,          /* a size is negative (or 0 in a stage call), too
+                               large, or overflows 64 bits                    */
   GDN_E_DTYPE = 3,          /* unknown or unsupported dtype                   */
   GDN_E_UNSUPPORTED_D = 4,  /* head dim not one of the supported sizes        */
   GDN_E_WORKSPACE = 5,      /* workspace NULL or smaller than required        */
@@ -123,7 +135,8 @@ int gdn_set_fused(int enabled);
  *                   fused kernel is disabled (gdn_set_fused), these shapes
  *                   take GDN_PATH_MFMA;
  *   GDN_PATH_PLAIN  every other supported case: three float32 kernels on
- *                   `stream`;
+ *                   `stream`; also empty shapes (one small float32 kernel
+ *                   or none, see "Empty shapes" above);
  *   -1              invalid arguments.
  * Results do not depend on the segmentation: the state pass carries the
  * float32 state exactly from one segment to the next.
@@ -133,8 +146,9 @@ int gdn_path(const gdn_shape* shape, int in_dtype);
 
 /*
  * Workspace bytes gdn_frame_fwd needs for this shape and input dtype, a pure
- * function of its arguments; 0 when the shape is invalid: G_t, U_t and M_t
- * of every frame, 3 * B*H*T*D*D*4 bytes, each of the three rounded up to 256.
+ * function of its arguments; 0 when the shape is invalid or empty: G_t, U_t
+ * and M_t of every frame, 3 * B*H*T*D*D*4 bytes, each of the three rounded
+ * up to 256.
  */
 size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype);
 
@@ -240,7 +254,7 @@ int gdn_output(const gdn_shape* shape, int in_dtype, int out_dtype, const void* 
  * (5 * B*H*T*D*D*4 bytes for the per-frame maps, plus 64 bytes per frame of
  * partial sums and one state, each rounded up to 256), 256-byte aligned; its
  * contents on return are unspecified.  gdn_bwd_workspace_bytes returns 0
- * for an invalid shape.
+ * for an invalid or empty shape.
  */
 size_t gdn_bwd_workspace_bytes(const gdn_shape* shape, int in_dtype);
 int gdn_frame_bwd(const gdn_shape* shape, int in_dtype,

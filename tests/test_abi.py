@@ -107,9 +107,9 @@ def test_frame_fwd_argument_errors():
     for bad in ({"q": None}, {"k": None}, {"v": None}, {"gamma": None}, {"beta": None},
                 {"out": None}, {"state_out": None}):
         assert fwd(s, **bad) == NULLPTR, bad
-    assert fwd(_shape(B=0)) == SHAPE
+    assert fwd(_shape(B=-1)) == SHAPE
     assert fwd(_shape(T=-1)) == SHAPE
-    assert fwd(_shape(S=0)) == SHAPE
+    assert fwd(_shape(S=-1)) == SHAPE
     assert fwd(_shape(D=100)) == UNSUP_D
     assert fwd(_shape(B=1 << 40, H=1 << 40)) == SHAPE
     assert fwd(_shape(B=1 << 12, H=1 << 12, T=2)) == SHAPE  # more frames than one launch can hold
@@ -141,6 +141,41 @@ def test_key_scale_argument_errors():
     assert bks(float("nan")) == VALUE
     assert bks(float("inf")) == VALUE
     assert bks(1.0, dt=F32) == DTYPE
+
+
+def test_empty_shapes_on_the_host():
+    """Sizes of 0 are accepted by the whole-call entry points; a pointer may
+    then be NULL exactly when its tensor is empty.  No heads: nothing to do
+    (returns before touching a device).  The calls that set a state need a
+    GPU and are tested there."""
+    L = F.lib()
+    none = dict(q=None, k=None, v=None, gamma=None, beta=None, out=None, state_out=None, ws=None, wsb=0)
+    assert fwd(_shape(B=0), **none) == OK
+    assert fwd(_shape(H=0, T=0, S=0), **none) == OK
+    assert fwd(_shape(T=0), **none) == NULLPTR                   # state_out is needed
+    assert fwd(_shape(S=0), **dict(none, state_out=P[6], beta=P[4])) == NULLPTR  # gamma is needed
+    assert fwd(_shape(S=0), **dict(none, state_out=P[6], gamma=P[3])) == NULLPTR  # beta too
+    assert fwd(_shape(T=0), **dict(none, state_out=P[6], state_in=P[6] + 4)) == ALIAS
+    for s in (_shape(B=0), _shape(T=0), _shape(S=0), _shape(H=0, T=0)):
+        assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == 0
+        assert L.gdn_bwd_workspace_bytes(ctypes.byref(s), BF16) == 0
+        assert L.gdn_path(ctypes.byref(s), BF16) == 0
+    assert L.gdn_frame_fwd_ks(ctypes.byref(_shape(B=0)), BF16, F32, None, None, None, None, None, None, 0.5,
+                              None, None, None, 0, None) == OK
+
+    def bwd(shape, **kw):
+        a = dict(q=None, k=None, v=None, gamma=None, beta=None, state=None, d_out=None, d_state_out=None,
+                 dq=None, dk=None, dv=None, dgamma=None, dbeta=None, d_state_in=None)
+        a.update(kw)
+        return L.gdn_frame_bwd(ctypes.byref(shape), BF16, a["q"], a["k"], a["v"], a["gamma"], a["beta"],
+                               a["state"], a["d_out"], a["d_state_out"], a["dq"], a["dk"], a["dv"], a["dgamma"],
+                               a["dbeta"], a["d_state_in"], None, 0, None)
+    assert bwd(_shape(B=0)) == OK
+    assert bwd(_shape(T=0)) == NULLPTR                                      # d_state_in is needed
+    assert bwd(_shape(S=0), gamma=P[3], beta=P[4], d_state_in=P[11], dbeta=P[9]) == NULLPTR   # dgamma
+    assert bwd(_shape(S=0, D=64)) == UNSUP_D                               # the backward is D = 128 only
+    assert L.gdn_build_maps(ctypes.byref(_shape(T=0)), BF16, P[0], P[1], P[2], P[3], None) == SHAPE
+    assert L.gdn_state_pass(ctypes.byref(_shape(H=0)), P[0], P[1], P[2], P[3], None, P[4], P[5], None) == SHAPE
 
 
 def test_frame_fwd_alias_errors():

@@ -8,7 +8,7 @@ import torch
 import oracle
 import frame_wise_gated_fwd_amd as F
 from synth import CLIP_5S, Workload, head_inputs
-from gpu_util import device_inputs, RelL2, log
+from gpu_util import device_inputs, RelL2, log, rel_l2
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -168,3 +168,42 @@ def test_backward_rejects_unsupported():
     g = torch.ones((1, 1, 2), device=DEV)
     with pytest.raises(F.GDNError):
         F.frame_bwd(q, q, q, g, g, q)
+
+
+@pytest.mark.parametrize("B,H,T,S", [(0, 2, 3, 8), (1, 3, 0, 8), (1, 3, 5, 0), (2, 1, 70, 0)])
+def test_backward_empty_shapes(B, H, T, S):
+    """No heads: nothing.  No frames: d_state_in = d_state_out.  Frames
+    without tokens: the backward of the pure decay (dbeta = 0) against the
+    backward oracle; also in place."""
+    D = 128
+    log(f"backward empty shape B={B} H={H} T={T} S={S}")
+    rng = np.random.Generator(np.random.PCG64(200 + T + S))
+    e = torch.empty((B, H, T, S, D), dtype=torch.bfloat16, device=DEV)
+    gamma = rng.uniform(0.5, 1.0, (B, H, T)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (B, H, T)).astype(np.float32)
+    st = (rng.standard_normal((B, H, D, D)) * 0.1).astype(np.float32)
+    ds = rng.standard_normal((B, H, D, D)).astype(np.float32)
+    g_t, b_t = torch.from_numpy(gamma).to(DEV), torch.from_numpy(beta).to(DEV)
+    for with_state, in_place in ((True, False), (False, False), (True, True)):
+        s_in = torch.from_numpy(st).to(DEV) if with_state else None
+        d_so = torch.from_numpy(ds).to(DEV)
+        kw = {"d_state_in": d_so} if in_place else {}
+        got = dict(zip(KEYS, F.frame_bwd(e, e, e, g_t, b_t, e, s_in, d_so, **kw)))
+        torch.cuda.synchronize()
+        assert got["dq"].shape == (B, H, T, S, D) and got["dstate"].shape == (B, H, D, D)
+        if B * H == 0:
+            continue
+        if T == 0:
+            assert torch.equal(got["dstate"].cpu(), torch.from_numpy(ds))
+            continue
+        assert torch.equal(got["dbeta"].cpu(), torch.zeros((B, H, T)))
+        for b in range(B):
+            for h in range(H):
+                z = np.zeros((T, S, D))
+                ref = oracle.gdn_head_backward(z, z, z, gamma[b, h], beta[b, h], st[b, h] if with_state else None,
+                                               z, ds[b, h])
+                assert rel_l2(got["dstate"][b, h].cpu().numpy(), ref["dstate"]) <= 1e-6
+                if with_state:
+                    assert rel_l2(got["dgamma"][b, h].cpu().numpy(), ref["dgamma"]) <= 1e-4
+                else:
+                    assert torch.equal(got["dgamma"][b, h].cpu(), torch.zeros(T))

@@ -408,3 +408,49 @@ def test_timed_entry_point_matches_and_reports():
     path = L.gdn_path(ctypes.byref(shp), GDN_BF16)
     assert path == 1
     assert list(nl) == [1, 1, 1] and all(m > 0 for m in ms)
+
+
+# ---------------------------------------------------------------------------
+# empty shapes: no heads, no frames, frames without tokens
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,H,T,S,D,dt", [(0, 2, 3, 8, 128, "bf16"), (1, 0, 3, 8, 64, "f32"),
+                                          (1, 3, 0, 8, 128, "bf16"), (2, 2, 0, 5, 32, "f32"),
+                                          (1, 3, 4, 0, 128, "bf16"), (2, 2, 5, 0, 48, "f32"),
+                                          (1, 2, 70, 0, 128, "bf16")])
+def test_empty_shapes(B, H, T, S, D, dt):
+    """T = 0 leaves the state; S = 0 decays it, M_t = gamma_t M_{t-1} (one
+    float32 product per frame, so it equals the same products in numpy bit
+    for bit); B*H = 0 does nothing.  Against the oracle as well."""
+    log(f"empty shape B={B} H={H} T={T} S={S} D={D} {dt}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    rng = np.random.Generator(np.random.PCG64(100 + T + S + D))
+    qkv = torch.empty((B, H, T, S, D), dtype=tdt, device=DEV)
+    gamma = rng.uniform(0.5, 1.0, (B, H, T)).astype(np.float32)
+    beta = rng.uniform(-0.5, 1.5, (B, H, T)).astype(np.float32)
+    st = rng.standard_normal((B, H, D, D)).astype(np.float32)
+    g_t, b_t = torch.from_numpy(gamma).to(DEV), torch.from_numpy(beta).to(DEV)
+    want = st.copy()
+    for t in range(T):
+        want = gamma[:, :, t, None, None] * want          # float32 products, frame by frame
+    for state in ("given", None, "in_place"):
+        s_in = None if state is None else torch.from_numpy(st).to(DEV)
+        kw = {"state_out": s_in} if state == "in_place" else {}
+        out, so = F.frame_fwd(qkv, qkv, qkv, g_t, b_t, s_in, **kw)
+        torch.cuda.synchronize()
+        assert out.shape == (B, H, T, S, D) and so.shape == (B, H, D, D)
+        if B * H == 0:
+            continue
+        ref = want if state is not None else np.zeros_like(st)
+        assert torch.equal(so.cpu(), torch.from_numpy(ref)), state
+        if state is None:
+            continue
+        for b in range(B):
+            for h in range(H):
+                e = np.zeros((T, S, D))
+                _, M = oracle.gdn_head(e, e, e, gamma[b, h], beta[b, h], st[b, h])
+                assert rel_l2(_to_np(so[b, h]), M) <= 1e-6
+    # the key-scale entry point takes the same route
+    if B * H > 0:
+        _, so = F.frame_fwd(qkv, qkv, qkv, g_t, b_t, torch.from_numpy(st).to(DEV), key_scale=0.25)
+        torch.cuda.synchronize()
+        assert torch.equal(so.cpu(), torch.from_numpy(want))

@@ -116,3 +116,53 @@ def test_key_scaling_bounds_transition_on_workloads(w):
 
 def test_oracle_counts():
     assert oracle.flops_per_head_frame(880, 128) == 90_701_824
+
+
+def test_no_frames_leaves_the_state():
+    """T = 0: no step is taken, so M_T = M_0 and O has no frames."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    D, S = 4, 3
+    M0 = rng.standard_normal((D, D))
+    empty = np.zeros((0, S, D))
+    O, M = oracle.gdn_head(empty, empty, empty, np.zeros(0), np.zeros(0), M0)
+    assert O.shape == (0, S, D) and np.array_equal(M, M0)
+    O, M = oracle.gdn_head(empty, empty, empty, np.zeros(0), np.zeros(0), None)
+    assert np.array_equal(M, np.zeros((D, D)))
+
+
+def test_frames_without_tokens_only_decay():
+    """S = 0: K_t has no rows, so G_t = U_t = 0 and M_t = gamma_t M_{t-1}
+    whatever beta is; the state after T frames is prod(gamma) M_0."""
+    rng = np.random.Generator(np.random.PCG64(32))
+    T, D = 6, 5
+    M0 = rng.standard_normal((D, D))
+    gamma = rng.uniform(0.5, 1.0, T)
+    beta = rng.uniform(-1.0, 2.0, T)
+    empty = np.zeros((T, 0, D))
+    O, M = oracle.gdn_head(empty, empty, empty, gamma, beta, M0)
+    assert O.shape == (T, 0, D)
+    assert np.allclose(M, np.prod(gamma) * M0, rtol=1e-14, atol=0)
+
+
+def test_backward_of_frames_without_tokens_closed_form():
+    """S = 0, loss <dM_T, M_T> with M_T = prod(gamma) M_0:
+    dgamma_t = prod_{u != t} gamma_u <dM_T, M_0>, dbeta = 0,
+    d(state_in) = prod(gamma) dM_T."""
+    rng = np.random.Generator(np.random.PCG64(33))
+    T, D = 5, 4
+    M0, dM = rng.standard_normal((D, D)), rng.standard_normal((D, D))
+    gamma = rng.uniform(0.5, 1.0, T)
+    beta = rng.uniform(0.0, 1.0, T)
+    empty = np.zeros((T, 0, D))
+    g = oracle.gdn_head_backward(empty, empty, empty, gamma, beta, M0, empty, dM)
+    dot = float(np.sum(dM * M0))
+    want = np.array([np.prod(np.delete(gamma, t)) * dot for t in range(T)])
+    assert np.allclose(g["dgamma"], want, rtol=1e-13, atol=0)
+    assert np.array_equal(g["dbeta"], np.zeros(T))
+    assert np.allclose(g["dstate"], np.prod(gamma) * dM, rtol=1e-14, atol=0)
+    for key in ("dq", "dk", "dv"):
+        assert g[key].shape == (T, 0, D)
+    # no frames: the incoming state gradient passes through unchanged
+    none = np.zeros((0, 0, D))
+    g0 = oracle.gdn_head_backward(none, none, none, np.zeros(0), np.zeros(0), M0, none, dM)
+    assert np.array_equal(g0["dstate"], dM)
