@@ -39,6 +39,7 @@ SIGNATURES = {
     "gdn_path": (_i, [_PS, _i]),
     "gdn_set_fused": (_i, [_i]),
     "gdn_workspace_bytes": (_sz, [_PS, _i]),
+    "gdn_set_spin_limit": (ctypes.c_uint, [ctypes.c_uint]),
     "gdn_frame_fwd": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp]),
     "gdn_frame_fwd_ks": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _f, _vp, _vp, _vp, _sz, _vp]),
     "gdn_frame_fwd_timed": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp,

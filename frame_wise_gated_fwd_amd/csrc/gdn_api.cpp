@@ -117,6 +117,13 @@ std::atomic<int>& fused_enabled() {
   return on;
 }
 
+// Polls before a wait of the fused kernel gives up (0: the kernel's default);
+// gdn_set_spin_limit sets it.
+std::atomic<uint32_t>& spin_limit() {
+  static std::atomic<uint32_t> polls{0};
+  return polls;
+}
+
 bool fused_path(int in_dtype, const Dims& d) {
   return fused_enabled().load() && fast_path(in_dtype, d.D) && d.T > kFusedMinT;
 }
@@ -451,7 +458,7 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
       return hip_status(timed(rec, s, 1, [&] {
         return gdn::launch_fused(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                  static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out,
-                                 workspace, d.heads, d.T, (int)d.S, ks, grid, s);
+                                 workspace, d.heads, d.T, (int)d.S, ks, spin_limit().load(), grid, s);
       }));
     // this device cannot host the fused kernel: the three-kernel schedule
   }
@@ -556,6 +563,8 @@ const char* gdn_status_str(int s) {
 }
 
 int gdn_set_fused(int enabled) { return fused_enabled().exchange(enabled ? 1 : 0); }
+
+unsigned gdn_set_spin_limit(unsigned polls) { return spin_limit().exchange(polls); }
 
 int gdn_supports_d(int64_t D) { return D >= 16 && D <= 128 && D % 16 == 0; }
 

@@ -48,13 +48,14 @@ int token_split(int64_t frames, int S);
 // (plus a tiny flag reset) per group.  fused_grid returns the launch size
 // (workgroups resident at once on num_cus CUs) or 0 when the device cannot
 // host the kernel's roles.  The workspace holds a control block, per-head
-// flags and per-head rings (fused_workspace_bytes).
+// flags and per-head rings (fused_workspace_bytes).  spin_limit: polls
+// before an internal wait gives up (0: the default, a few seconds).
 int64_t fused_workspace_bytes(int64_t heads);
 int fused_grid(bool out_bf16, int num_cus);
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                         const float* beta, const float* state_in, void* out, bool out_bf16,
-                        float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks, int grid,
-                        hipStream_t st);
+                        float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks,
+                        uint32_t spin_limit, int grid, hipStream_t st);
 
 // ---- plain float32 path: any supported D, f32 or bf16 inputs ---------------
 hipError_t launch_build_generic(const void* k, const void* v, bool in_bf16, float* G, float* U,

@@ -62,7 +62,7 @@ constexpr int kMaxHeadsPerXcd = 2;
 constexpr int kMaxParts = 8;          // kRows >= 16
 constexpr int kLdsW = D + 8;
 constexpr int kChainWaves = 4;
-constexpr uint32_t kSpinLimit = 1u << 22;  // polls (a few seconds) before a wait gives up
+constexpr uint32_t kSpinLimit = 1u << 22;  // default polls (a few seconds) before a wait gives up
 
 // Ring shape: G/U slots, M slots and the queue distance from build(t) to
 // output(t).  The queue distance must cover a build's duration in state-pass
@@ -112,11 +112,11 @@ __device__ __forceinline__ void flag_store(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void invalidate_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
 
-// Spin (one thread) until pred() holds; false if it never did or another
-// wait already failed.
+// Spin (one thread) until pred() holds, at most `limit` polls; false if it
+// never did or another wait already failed.
 template <typename Pred>
-__device__ bool spin_until(Ctrl* ctrl, Pred pred) {
-  for (uint32_t i = 0; i < kSpinLimit; ++i) {
+__device__ bool spin_until(Ctrl* ctrl, uint32_t limit, Pred pred) {
+  for (uint32_t i = 0; i < limit; ++i) {
     if (pred()) return true;
     if ((i & 63) == 63 && flag_load(&ctrl->error)) return false;
     __builtin_amdgcn_s_sleep(1);
@@ -138,7 +138,8 @@ struct Args {
   Ctrl* ctrl;
   uint32_t* flags;  // per head kFlagWords
   int heads, T, S;
-  float ks;         // key scale: the build items write ks^2 G_t and ks U_t
+  float ks;             // key scale: the build items write ks^2 G_t and ks U_t
+  uint32_t spin_limit;  // polls before a wait gives up
 };
 
 __host__ __device__ constexpr int64_t ring_head_bytes(int wg, int wm) {
@@ -277,7 +278,7 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
 
   // Prologue: wait for build(0) (every wave for itself) and load frame 0.
   bool ok = true;
-  if (l == 0) ok = spin_until(a.ctrl, [&] { return flag_load(fl + kFlagGReady) >= 1u; });
+  if (l == 0) ok = spin_until(a.ctrl, a.spin_limit, [&] { return flag_load(fl + kFlagGReady) >= 1u; });
   ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
   if (!ok && l == 0) bcast[0] = 1;
   invalidate_l1();
@@ -296,9 +297,9 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
       flag_store(my_consumed, (uint32_t)(t + kPrefetch < T ? t + kPrefetch : T));
       const int tn = t + kPrefetch;
       if (tn < T && gflag < (uint32_t)(tn + 1))
-        good = spin_until(a.ctrl, [&] { return flag_load(fl + kFlagGReady + tn % kWG) >= (uint32_t)(tn + 1); });
+        good = spin_until(a.ctrl, a.spin_limit, [&] { return flag_load(fl + kFlagGReady + tn % kWG) >= (uint32_t)(tn + 1); });
       if (good && t >= kWM && oflag < (uint32_t)(t - kWM + 1))
-        good = spin_until(a.ctrl, [&] { return flag_load(fl + kFlagOutDone + t % kWM) >= (uint32_t)(t - kWM + 1); });
+        good = spin_until(a.ctrl, a.spin_limit, [&] { return flag_load(fl + kFlagOutDone + t % kWM) >= (uint32_t)(t - kWM + 1); });
       // flags for step t + 1, in flight during this step
       if (t + 1 + kPrefetch < T) gflag = flag_load(fl + kFlagGReady + (t + 1 + kPrefetch) % kWG);
       if (t + 1 >= kWM) oflag = flag_load(fl + kFlagOutDone + (t + 1) % kWM);
@@ -420,7 +421,7 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
       // build(t): every state-pass wave must have loaded the slot's previous frame
       if (tid == 0) {
         const uint32_t need = it.t >= kWG ? (uint32_t)(it.t - kWG + 1) : 0u;
-        bcast[3] = spin_until(a.ctrl, [&] {
+        bcast[3] = spin_until(a.ctrl, a.spin_limit, [&] {
           uint32_t m = 0xffffffffu;
 #pragma unroll
           for (int p = 0; p < kParts * kChainWaves; ++p) {
@@ -443,7 +444,7 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
     } else {
       // output(t): every state-pass wave's rows of M_t must be in the ring
       if (tid == 0) {
-        bcast[3] = spin_until(a.ctrl, [&] {
+        bcast[3] = spin_until(a.ctrl, a.spin_limit, [&] {
           uint32_t m = 0xffffffffu;
 #pragma unroll
           for (int p = 0; p < kParts * kChainWaves; ++p) {
@@ -528,8 +529,8 @@ int fused_grid(bool out_bf16, int num_cus) {
 
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                         const float* beta, const float* state_in, void* out, bool out_bf16,
-                        float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks, int grid,
-                        hipStream_t st) {
+                        float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks,
+                        uint32_t spin_limit, int grid, hipStream_t st) {
   char* ws = static_cast<char*>(workspace);
   const int64_t group = kXcd * kMaxHeadsPerXcd;
   const int64_t ctrl_bytes = (int64_t)sizeof(Ctrl) + group * kFlagWords * 4;
@@ -553,6 +554,7 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     a.T = (int)T;
     a.S = S;
     a.ks = ks;
+    a.spin_limit = spin_limit ? spin_limit : kSpinLimit;
     hipLaunchKernelGGL(k_fused_init, dim3((nwords + 255) / 256), dim3(256), 0, st,
                        reinterpret_cast<uint32_t*>(ws), nwords);
     hipError_t e = hipGetLastError();

@@ -105,6 +105,20 @@ int gdn_supports_d(int64_t D);
 int gdn_set_fused(int enabled);
 
 /*
+ * Testing aid for the fused kernel's failure path: the number of polls after
+ * which one of its internal waits gives up, for launches made after it
+ * returns, process-wide; 0 restores the default (2^22 polls, a few
+ * seconds).  Returns the previous setting.  Every wait is bounded so that a
+ * failure ends the kernel instead of hanging it: the first wait that runs
+ * out sets an error word, every other wait then gives up at once, and the
+ * state pass writes NaN to the rows of state_out it had not finished (out
+ * is then unspecified).  A tiny limit makes the waits run out on purpose,
+ * with every workgroup still exiting normally.  The next launch starts from
+ * a fresh control block.
+ */
+unsigned gdn_set_spin_limit(unsigned polls);
+
+/*
  * Which implementation gdn_frame_fwd uses for this shape and input dtype (a
  * pure function of its arguments):
  *   GDN_PATH_MFMA   bf16, D == 128, T <= 64 (and longer sequences when the
