@@ -426,11 +426,34 @@ def main():
         backward = backward_leg(x, L, w, stream, steps=args.backward_steps)
         log(f"backward: {backward}")
 
-    streamed = t1 = None
+    streamed = t1 = bf16_out = None
     if not args.no_extras:
         log("streaming calls and T=1 latency")
         streamed, t1 = streaming_and_t1(x, L, w, stream)
         log(f"streamed: {streamed}; T=1: {t1}")
+        # the same call with a bf16 output (an option, not the headline): its
+        # algorithmic bytes per head-frame are q, k, v and O all in bf16
+        out16 = torch.empty((B, H, T, S, D), dtype=torch.bfloat16, device=dev)
+
+        def step16():
+            check(L.gdn_frame_fwd(ctypes.byref(shp), GDN_BF16, GDN_BF16, P(x["q"]), P(x["k"]), P(x["v"]),
+                                  P(x["gamma"]), P(x["beta"]), P(x["state"]), P(out16), P(st_out), P(ws),
+                                  wsb, stream), "gdn_frame_fwd")
+        for _ in range(args.warmup):
+            step16()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            step16()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms16 = ev0.elapsed_time(ev1) / args.steps
+        b16 = 4 * S * D * 2 * hf
+        bf16_out = {"ms": round(ms16, 4), "frame_steps_per_s": round(B * T / (ms16 * 1e-3), 1),
+                    "algorithmic_bytes": b16, "GBps": round(b16 / (ms16 * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(b16 / (ms16 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del out16
+        log(f"bf16 output: {bf16_out}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -468,6 +491,7 @@ def main():
         "kernels": kernels,
         "head_frame_steps_per_s": round(hf / (ms * 1e-3), 1),
         "backward": backward,
+        "bf16_output": bf16_out,
         "streamed_calls": streamed,
         "t1_call": t1,
     }
