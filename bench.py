@@ -17,6 +17,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -426,7 +427,7 @@ def main():
         backward = backward_leg(x, L, w, stream, steps=args.backward_steps)
         log(f"backward: {backward}")
 
-    streamed = t1 = bf16_out = None
+    streamed = t1 = bf16_out = key_scale_call = None
     if not args.no_extras:
         log("streaming calls and T=1 latency")
         streamed, t1 = streaming_and_t1(x, L, w, stream)
@@ -454,6 +455,26 @@ def main():
                     "hbm_frac": round(b16 / (ms16 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del out16
         log(f"bf16 output: {bf16_out}")
+        # the key scale applied inside the build (gdn_frame_fwd_ks), timed on
+        # the same tensors (already scaled, so the result is not used): the
+        # scale costs one multiply per map element
+        ks = 1.0 / math.sqrt(D * S)
+
+        def step_ks():
+            check(L.gdn_frame_fwd_ks(ctypes.byref(shp), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]), P(x["v"]),
+                                     P(x["gamma"]), P(x["beta"]), P(x["state"]), ks, P(out), P(st_out), P(ws),
+                                     wsb, stream), "gdn_frame_fwd_ks")
+        for _ in range(args.warmup):
+            step_ks()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            step_ks()
+        ev1.record()
+        torch.cuda.synchronize()
+        ks_ms = ev0.elapsed_time(ev1) / args.steps
+        key_scale_call = {"ms": round(ks_ms, 4), "frame_steps_per_s": round(B * T / (ks_ms * 1e-3), 1)}
+        log(f"key-scale call: {key_scale_call}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -492,6 +513,7 @@ def main():
         "head_frame_steps_per_s": round(hf / (ms * 1e-3), 1),
         "backward": backward,
         "bf16_output": bf16_out,
+        "key_scale_call": key_scale_call,
         "streamed_calls": streamed,
         "t1_call": t1,
     }
