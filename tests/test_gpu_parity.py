@@ -486,3 +486,12 @@ def test_fused_kernel_wait_failure_ends_without_hang():
     out2, st2 = F.frame_fwd(*args)
     torch.cuda.synchronize()
     assert torch.equal(out2, ref_out) and torch.equal(st2, ref_st)
+
+
+def test_fused_kernel_long_sequence():
+    """4,000 frames, four times the 60 s workload's chain: the fused kernel's
+    rings wrap 125 times and the state carries through 4,000 dependent steps;
+    output on sampled frames and the whole final state against the oracle."""
+    w = Workload(name="long4000", B=1, H=2, T=4000, S=40, D=128, in_dtype="bf16", seed=63,
+                 gamma_range=(0.99, 1.0), beta_kind="sigmoid_normal", state_std=0.02)
+    _forward_parity(w, frames=sample_frames(w.T, seed=6))
