@@ -1,8 +1,9 @@
 """Plain, slow fp64 CPU oracle for the backward pass (vector-Jacobian product)
 of the frame-wise Gated DeltaNet forward.
 
-TEST INFRASTRUCTURE.  Only the tests and the benchmark's CPU-baseline leg may
-import or run anything in this directory.  The GPU library never calls it.
+TEST INFRASTRUCTURE.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import or run anything in this directory.
+The GPU library never calls it.
 
 The pages describe training the model ("SANA-WM: NVIDIA puts a one-minute
 world model on a single GPU", zhichai.net, training pipeline, Stages 1-4)
