@@ -47,21 +47,16 @@ __device__ __forceinline__ int lds_row(int r) {
 // copied into LDS (the caller may then release M_t's buffer).  kDepth: token
 // tiles each wave loads ahead.  All 256 threads of the workgroup must call it.
 // With the float32 form of M_t, kTransM stages M_t^T instead of M_t (so the
-// frame gets Q_t M_t; used by the backward pass).  kBurst: M_t is read with
-// all sixteen 16-byte loads of a thread in flight at once (one memory round
-// trip); without it (packed form only), one 8-byte load per step, each used
-// before the next is issued.  The output kernel and the backward take the
-// burst; the persistent fused kernel measured faster with the serial form
-// (4.24 against 5.03 ms for the 60 s call, bit-identical results), so it
-// keeps it.
-template <bool kPackedM, bool kOutBf16, int kDepth = 1, bool kTransM = false, bool kBurst = true,
-          typename OnStaged>
+// frame gets Q_t M_t; used by the backward pass).  M_t is read with all
+// sixteen 16-byte loads of a thread in flight at once (one memory round trip,
+// not sixteen).
+template <bool kPackedM, bool kOutBf16, int kDepth = 1, bool kTransM = false, typename OnStaged>
 __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, const void* __restrict__ Mt_in,
                                              void* __restrict__ Of, int S, uint16_t (*Ml)[128][kOutLdsW],
                                              OnStaged on_staged) {
   constexpr int D = 128;
   constexpr int kTile = kOutTile;
-  static_assert(!(kPackedM && kTransM) && (kBurst || kPackedM), "option not available for this form");
+  static_assert(!(kPackedM && kTransM), "option not available for this form");
   // An opaque copy of the thread index: lane-dependent addresses are then
   // computed at each call instead of being hoisted out of a caller's loop
   // and kept live (in registers) across the whole call.
@@ -73,18 +68,9 @@ __device__ __forceinline__ void output_frame(const uint16_t* __restrict__ Qf, co
   // M_t is 64 KiB in either form: 16 loads of 16 bytes per thread, all
   // issued before the first is used (one memory round trip, not sixteen).
   constexpr int kLoads = D * D * 4 / 16 / 256;
-  if constexpr (kPackedM && !kBurst) {
-    // 8-byte chunk q: unit q / 64 = (row block, column block, plane), lane q % 64
-    const char* Mp = static_cast<const char*>(Mt_in);
-    for (int q = tid; q < D * D * 2 / 4; q += 256) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(Mp + 8 * q);
-      const int unit = q >> 6, ln = q & 63;
-      const int plane = unit & 1, rb = unit >> 4, cb = (unit >> 1) & 7;
-      const int r = 16 * rb + (ln & 15), c = 16 * cb + 4 * (ln >> 4);
-      *reinterpret_cast<u32x2*>(&Ml[plane][lds_row<kOutBf16>(r)][c]) = v;
-    }
-  } else if constexpr (kPackedM) {
-    // 8-byte chunk q as above; load i of this thread holds chunks 2j and
+  if constexpr (kPackedM) {
+    // 8-byte chunk q of the packed form: unit q / 64 = (row block, column
+    // block, plane), lane q % 64; load i of this thread holds chunks 2j and
     // 2j + 1, j = tid + 256 i
     const char* Mp = static_cast<const char*>(Mt_in);
     u32x4 mv[kLoads];

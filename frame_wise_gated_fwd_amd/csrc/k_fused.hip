@@ -62,22 +62,22 @@ constexpr int kMaxHeadsPerXcd = 2;
 constexpr int kMaxParts = 8;          // kRows >= 16
 constexpr int kLdsW = D + 8;
 constexpr int kChainWaves = 4;
-constexpr uint32_t kSpinLimit = 1u << 22;  // default polls (a few seconds) before a wait gives up
+constexpr uint32_t kSpinLimit = 1u << 22;  // default polls before a wait gives up (seconds)
 
 // Ring shape: G/U slots, M slots and the queue distance from build(t) to
 // output(t).  The queue distance must cover a build's duration in state-pass
-// steps (a build takes ~45 us, a step ~4 us); every wait then depends only
+// steps (a build takes ~40 us, a step ~4 us); every wait then depends only
 // on earlier items as long as lag > kPrefetch + 1 and lag <= wg + wm (see
 // the ring notes above).  Measured on the 60 s workload (same box, same
-// inputs): {32, 12, 20} and {32, 12, 24} beat {40, 16, 32} by 1.5-4 % on
-// three boxes; more M slots ({40, 24, 32}: +6 %), faster M staging in the
-// output items (+18 %) and {30, 12, 22} (+7 %) are slower; 8 G/U slots
-// starve the state pass (8-10 ms); 96 overflow the memory-side cache
-// (4.8 ms).
+// inputs): with the polling intervals above, the burst staging of M_t in
+// the output items and gamma/beta read before the flag loads, {32, 12, 24}
+// is 3-4 % faster than the earlier {32, 12, 20} with serial staging; more M
+// slots ({40, 24, 32}: +6 % earlier) and 8 G/U slots (starving the state
+// pass, 2x) are slower, 96 overflow the memory-side cache (+20 %).
 struct RingShape {
   int wg, wm, lag;
 };
-constexpr RingShape kRing{32, 12, 20};
+constexpr RingShape kRing{32, 12, 24};
 static_assert(kRing.wg >= kPrefetch + 2 && kRing.wm >= 2 &&
                   kRing.lag > kPrefetch + 1 && kRing.lag <= kRing.wg + kRing.wm,
               "ring shape could stall the queue");
@@ -112,14 +112,22 @@ __device__ __forceinline__ void flag_store(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void invalidate_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
 
-// Spin (one thread) until pred() holds, at most `limit` polls; false if it
-// never did or another wait already failed.
-template <typename Pred>
+// Spin (one thread) until pred() holds, at most `limit` polls kSleep x 64
+// clocks apart; false if it never did or another wait already failed.
+// Polls are flag loads from L2 by many workgroups at once, and that traffic
+// slows everything else on the XCD: the state pass polls every ~0.4 us,
+// the workers (whose items can wait longer) every ~3.4 us.  Measured on the
+// 60 s workload against polls every 64 clocks in both roles: 3-4 % faster
+// with a float32 output and 5-17 % with a bf16 one, where the tight polling
+// could double the call's time.
+constexpr int kStateSleep = 16;
+constexpr int kWorkerSleep = 127;  // the largest s_sleep
+template <int kSleep, typename Pred>
 __device__ bool spin_until(Ctrl* ctrl, uint32_t limit, Pred pred) {
   for (uint32_t i = 0; i < limit; ++i) {
     if (pred()) return true;
     if ((i & 63) == 63 && flag_load(&ctrl->error)) return false;
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(kSleep);
   }
   __hip_atomic_store(&ctrl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return false;
@@ -278,7 +286,7 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
 
   // Prologue: wait for build(0) (every wave for itself) and load frame 0.
   bool ok = true;
-  if (l == 0) ok = spin_until(a.ctrl, a.spin_limit, [&] { return flag_load(fl + kFlagGReady) >= 1u; });
+  if (l == 0) ok = spin_until<kStateSleep>(a.ctrl, a.spin_limit, [&] { return flag_load(fl + kFlagGReady) >= 1u; });
   ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
   if (!ok && l == 0) bcast[0] = 1;
   invalidate_l1();
@@ -291,15 +299,30 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
   for (int t = 0; t < T && ok; ++t) {
     // Everything this wave issued in step t-1 is complete after this wait.
     wait_stores();
+    // gamma_t and beta_t now, with nothing in flight: a readlane after the
+    // flag loads below would wait for those loads too (the compiler cannot
+    // count the loads in flight there, so it waits for all of them)
+    const int tw = t & 63;
+    const float gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwin), tw));
+    const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwin), tw));
+    if (tw == 63) {
+      gwin = gnxt;
+      bwin = bnxt;
+      win_load(t + 65, gnxt, bnxt);
+    }
     bool good = true;
     if (l == 0) {
       if (t > 0) flag_store(my_mready(t - 1), (uint32_t)t);
       flag_store(my_consumed, (uint32_t)(t + kPrefetch < T ? t + kPrefetch : T));
       const int tn = t + kPrefetch;
       if (tn < T && gflag < (uint32_t)(tn + 1))
-        good = spin_until(a.ctrl, a.spin_limit, [&] { return flag_load(fl + kFlagGReady + tn % kWG) >= (uint32_t)(tn + 1); });
+        good = spin_until<kStateSleep>(a.ctrl, a.spin_limit, [&] {
+          return flag_load(fl + kFlagGReady + tn % kWG) >= (uint32_t)(tn + 1);
+        });
       if (good && t >= kWM && oflag < (uint32_t)(t - kWM + 1))
-        good = spin_until(a.ctrl, a.spin_limit, [&] { return flag_load(fl + kFlagOutDone + t % kWM) >= (uint32_t)(t - kWM + 1); });
+        good = spin_until<kStateSleep>(a.ctrl, a.spin_limit, [&] {
+          return flag_load(fl + kFlagOutDone + t % kWM) >= (uint32_t)(t - kWM + 1);
+        });
       // flags for step t + 1, in flight during this step
       if (t + 1 + kPrefetch < T) gflag = flag_load(fl + kFlagGReady + (t + 1 + kPrefetch) % kWG);
       if (t + 1 >= kWM) oflag = flag_load(fl + kFlagOutDone + (t + 1) % kWM);
@@ -307,14 +330,6 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
     good = __builtin_amdgcn_readfirstlane((int)good) != 0;
     if (good) {
       const int buf = t & 1;
-      const int tw = t & 63;
-      const float gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwin), tw));
-      const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwin), tw));
-      if (tw == 63) {
-        gwin = gnxt;
-        bwin = bnxt;
-        win_load(t + 65, gnxt, bnxt);
-      }
       u32x4 ahi[2][4], alo[2][4];
       f32x4 ureg[2][kRB];
 #pragma unroll
@@ -421,7 +436,7 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
       // build(t): every state-pass wave must have loaded the slot's previous frame
       if (tid == 0) {
         const uint32_t need = it.t >= kWG ? (uint32_t)(it.t - kWG + 1) : 0u;
-        bcast[3] = spin_until(a.ctrl, a.spin_limit, [&] {
+        bcast[3] = spin_until<kWorkerSleep>(a.ctrl, a.spin_limit, [&] {
           uint32_t m = 0xffffffffu;
 #pragma unroll
           for (int p = 0; p < kParts * kChainWaves; ++p) {
@@ -444,7 +459,7 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
     } else {
       // output(t): every state-pass wave's rows of M_t must be in the ring
       if (tid == 0) {
-        bcast[3] = spin_until(a.ctrl, a.spin_limit, [&] {
+        bcast[3] = spin_until<kWorkerSleep>(a.ctrl, a.spin_limit, [&] {
           uint32_t m = 0xffffffffu;
 #pragma unroll
           for (int p = 0; p < kParts * kChainWaves; ++p) {
@@ -459,7 +474,7 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
       invalidate_l1();
       const char* mp = ring + (int64_t)(2 * kWG + it.t % kWM) * packed::kFrameBytes;
       void* of = static_cast<char*>(a.out) + fr * S * D * (kOutBf16 ? 2 : 4);
-      output_frame<true, kOutBf16, 1, false, false>(a.q + fr * S * D, mp, of, S, lds.out, [&] {
+      output_frame<true, kOutBf16>(a.q + fr * S * D, mp, of, S, lds.out, [&] {
         if (tid == 0) flag_store(fl + kFlagOutDone + it.t % kWM, (uint32_t)(it.t + 1));
       });
     }

@@ -107,8 +107,9 @@ int gdn_set_fused(int enabled);
 /*
  * Testing aid for the fused kernel's failure path: the number of polls after
  * which one of its internal waits gives up, for launches made after it
- * returns, process-wide; 0 restores the default (2^22 polls, a few
- * seconds).  Returns the previous setting.  Every wait is bounded so that a
+ * returns, process-wide; 0 restores the default (2^22 polls: seconds for a
+ * wait of the state pass, about 20 s for one of the other workgroups, which
+ * poll less often).  Returns the previous setting.  Every wait is bounded so that a
  * failure ends the kernel instead of hanging it: the first wait that runs
  * out sets an error word, every other wait then gives up at once, and the
  * state pass writes NaN to the rows of state_out it had not finished (out
