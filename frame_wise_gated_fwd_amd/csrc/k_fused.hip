@@ -69,15 +69,16 @@ constexpr uint32_t kSpinLimit = 1u << 22;  // default polls before a wait gives 
 // steps (a build takes ~40 us, a step ~4 us); every wait then depends only
 // on earlier items as long as lag > kPrefetch + 1 and lag <= wg + wm (see
 // the ring notes above).  Measured on the 60 s workload (same box, same
-// inputs): with the polling intervals above, the burst staging of M_t in
-// the output items and gamma/beta read before the flag loads, {32, 12, 24}
-// is 3-4 % faster than the earlier {32, 12, 20} with serial staging; more M
-// slots ({40, 24, 32}: +6 % earlier) and 8 G/U slots (starving the state
-// pass, 2x) are slower, 96 overflow the memory-side cache (+20 %).
+// inputs, with the polling intervals above): {32, 20, 24} is 2 % faster
+// than {32, 12, 24} with a float32 output and 3.5 % with a bf16 one, on two
+// boxes; {32, 16, 24}, {32, 20, 20} and {32, 20, 28} gain less, while
+// {32, 24, 24} (+4 %), {32, 28, 24}, {32, 14, 24}, {36 or 40, 12, 24-28}
+// (+2-5 %) lose; 8 G/U slots starve the state pass (2x) and 96 overflow the
+// memory-side cache (+20 %).
 struct RingShape {
   int wg, wm, lag;
 };
-constexpr RingShape kRing{32, 12, 24};
+constexpr RingShape kRing{32, 20, 24};
 static_assert(kRing.wg >= kPrefetch + 2 && kRing.wm >= 2 &&
                   kRing.lag > kPrefetch + 1 && kRing.lag <= kRing.wg + kRing.wm,
               "ring shape could stall the queue");
