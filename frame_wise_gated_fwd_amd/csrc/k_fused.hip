@@ -62,6 +62,7 @@ constexpr int kMaxHeadsPerXcd = 2;
 constexpr int kMaxParts = 8;          // kRows >= 16
 constexpr int kLdsW = D + 8;
 constexpr int kChainWaves = 4;
+static_assert(kMaxParts * kChainWaves <= 64, "a worker polls a head's per-wave flags from one wave");
 constexpr uint32_t kSpinLimit = 1u << 22;  // default polls before a wait gives up (seconds)
 
 // Ring shape: G/U slots, M slots and the queue distance from build(t) to
@@ -69,12 +70,11 @@ constexpr uint32_t kSpinLimit = 1u << 22;  // default polls before a wait gives 
 // steps (a build takes ~40 us, a step ~4 us); every wait then depends only
 // on earlier items as long as lag > kPrefetch + 1 and lag <= wg + wm (see
 // the ring notes above).  Measured on the 60 s workload (same box, same
-// inputs, with the polling intervals above): {32, 20, 24} is 2 % faster
-// than {32, 12, 24} with a float32 output and 3.5 % with a bf16 one, on two
-// boxes; {32, 16, 24}, {32, 20, 20} and {32, 20, 28} gain less, while
-// {32, 24, 24} (+4 %), {32, 28, 24}, {32, 14, 24}, {36 or 40, 12, 24-28}
-// (+2-5 %) lose; 8 G/U slots starve the state pass (2x) and 96 overflow the
-// memory-side cache (+20 %).
+// inputs): with the wave-wide polls above, {32, 12..28, 20..28} are all
+// within 1 % of each other; before them (one lane loading each flag),
+// {32, 20, 24} was 2-3.5 % faster than {32, 12, 24}, more G/U slots (36,
+// 40) lost 2-5 %, 8 G/U slots starved the state pass (2x) and 96
+// overflowed the memory-side cache (+20 %).
 struct RingShape {
   int wg, wm, lag;
 };
@@ -113,16 +113,19 @@ __device__ __forceinline__ void flag_store(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void invalidate_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
 
-// Spin (one thread) until pred() holds, at most `limit` polls kSleep x 64
-// clocks apart; false if it never did or another wait already failed.
-// Polls are flag loads from L2 by many workgroups at once, and that traffic
-// slows everything else on the XCD: the state pass polls every ~0.4 us,
-// the workers (whose items can wait longer) every ~3.4 us.  Measured on the
-// 60 s workload against polls every 64 clocks in both roles: 3-4 % faster
-// with a float32 output and 5-17 % with a bf16 one, where the tight polling
-// could double the call's time.
+// Spin until pred() holds, at most `limit` polls kSleep x 64 clocks apart;
+// false if it never did or another wait already failed.  A state-pass wave
+// polls one flag from one lane; a worker polls the 32 per-wave flags of a
+// head from the 32 lanes of its first wave, one load instruction that reads
+// the flags' one cache line once (pred must then give the same value in
+// every lane of the wave).  Polls from many workgroups land on those few
+// flag lines, and that traffic slows the whole XCD: with one lane loading
+// the 32 flags one by one every 64 clocks, a call took 5-17 % longer than
+// with a wave-wide load every ~0.4 us (more with a bf16 output, where it
+// could double the call's time); the poll interval matters little once each
+// poll is a single load.
 constexpr int kStateSleep = 16;
-constexpr int kWorkerSleep = 127;  // the largest s_sleep
+constexpr int kWorkerSleep = 32;
 template <int kSleep, typename Pred>
 __device__ bool spin_until(Ctrl* ctrl, uint32_t limit, Pred pred) {
   for (uint32_t i = 0; i < limit; ++i) {
@@ -130,9 +133,12 @@ __device__ bool spin_until(Ctrl* ctrl, uint32_t limit, Pred pred) {
     if ((i & 63) == 63 && flag_load(&ctrl->error)) return false;
     __builtin_amdgcn_s_sleep(kSleep);
   }
-  __hip_atomic_store(&ctrl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(&ctrl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return false;
 }
+
+// True in every lane when the condition holds in every lane of the wave.
+__device__ __forceinline__ bool wave_all(bool c) { return __builtin_amdgcn_ballot_w64(!c) == 0; }
 
 struct Args {
   const uint16_t* q;
@@ -435,17 +441,15 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
     const int64_t fr = (int64_t)head * T + it.t;
     if (it.kind == 0) {
       // build(t): every state-pass wave must have loaded the slot's previous frame
-      if (tid == 0) {
+      if (tid < 64) {
         const uint32_t need = it.t >= kWG ? (uint32_t)(it.t - kWG + 1) : 0u;
-        bcast[3] = spin_until<kWorkerSleep>(a.ctrl, a.spin_limit, [&] {
-          uint32_t m = 0xffffffffu;
-#pragma unroll
-          for (int p = 0; p < kParts * kChainWaves; ++p) {
-            const uint32_t c = flag_load(fl + kFlagConsumed + p);
-            m = c < m ? c : m;
-          }
-          return m >= need;
+        const bool ready = spin_until<kWorkerSleep>(a.ctrl, a.spin_limit, [&] {
+          int ln = threadIdx.x;  // opaque: the lane's flag address is formed here, not kept live
+          asm volatile("" : "+v"(ln));
+          const uint32_t c = ln < kParts * kChainWaves ? flag_load(fl + kFlagConsumed + ln) : 0xffffffffu;
+          return wave_all(c >= need);
         });
+        if (tid == 0) bcast[3] = ready;
       }
       __syncthreads();
       if (!bcast[3]) return;
@@ -459,16 +463,16 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
       if (tid == 0) flag_store(fl + kFlagGReady + it.t % kWG, (uint32_t)(it.t + 1));
     } else {
       // output(t): every state-pass wave's rows of M_t must be in the ring
-      if (tid == 0) {
-        bcast[3] = spin_until<kWorkerSleep>(a.ctrl, a.spin_limit, [&] {
-          uint32_t m = 0xffffffffu;
-#pragma unroll
-          for (int p = 0; p < kParts * kChainWaves; ++p) {
-            const uint32_t c = flag_load(fl + kFlagMReady + (it.t % kWM) * kParts * kChainWaves + p);
-            m = c < m ? c : m;
-          }
-          return m >= (uint32_t)(it.t + 1);
+      if (tid < 64) {
+        const bool ready = spin_until<kWorkerSleep>(a.ctrl, a.spin_limit, [&] {
+          int ln = threadIdx.x;  // opaque, as above
+          asm volatile("" : "+v"(ln));
+          const uint32_t c = ln < kParts * kChainWaves
+                                 ? flag_load(fl + kFlagMReady + (it.t % kWM) * kParts * kChainWaves + ln)
+                                 : 0xffffffffu;
+          return wave_all(c >= (uint32_t)(it.t + 1));
         });
+        if (tid == 0) bcast[3] = ready;
       }
       __syncthreads();
       if (!bcast[3]) return;
