@@ -70,15 +70,16 @@ constexpr uint32_t kSpinLimit = 1u << 22;  // default polls before a wait gives 
 // steps (a build takes ~40 us, a step ~4 us); every wait then depends only
 // on earlier items as long as lag > kPrefetch + 1 and lag <= wg + wm (see
 // the ring notes above).  Measured on the 60 s workload (same box, same
-// inputs): with the wave-wide polls above, {32, 12..28, 20..28} are all
-// within 1 % of each other; before them (one lane loading each flag),
-// {32, 20, 24} was 2-3.5 % faster than {32, 12, 24}, more G/U slots (36,
-// 40) lost 2-5 %, 8 G/U slots starved the state pass (2x) and 96
-// overflowed the memory-side cache (+20 %).
+// inputs): with the wave-wide polls above, 4-8 M slots are 1-2 % faster
+// than 12-28 (which are within 1 % of each other) on two boxes, 3 are 3 %
+// slower; 24, 20 or 16 G/U slots starve the state pass (+30-40 %), and
+// queue lags of 20-28 are within 1 %.  (Before those polls, with one lane
+// loading each flag, 20 M slots were 2-3.5 % faster than 12, 36-40 G/U
+// slots lost 2-5 %, and 96 overflowed the memory-side cache, +20 %.)
 struct RingShape {
   int wg, wm, lag;
 };
-constexpr RingShape kRing{32, 20, 24};
+constexpr RingShape kRing{32, 6, 24};
 static_assert(kRing.wg >= kPrefetch + 2 && kRing.wm >= 2 &&
                   kRing.lag > kPrefetch + 1 && kRing.lag <= kRing.wg + kRing.wm,
               "ring shape could stall the queue");
