@@ -40,9 +40,13 @@ constexpr int build_lds_bytes() { return kPacked ? 65536 : 32768; }
 // float32 row-major 128 x 128, and Gout may be null (only U_t is written).
 // `lds` must hold build_lds_bytes<kPacked>().
 // kDepth: token iterations loaded ahead (register buffers of 32 VGPRs each).
+// kUpperG (packed only): of G_t, only the halves of the packed units that
+// lie on or above the diagonal in 16 x 16 blocks are written (G_t is
+// symmetric bit for bit: both entries of a pair are the same products
+// summed in the same order).
 // All 256 threads of the workgroup must call it.  On return this thread's
 // stores are issued, not necessarily complete.
-template <bool kPacked, int kDepth = 1>
+template <bool kPacked, int kDepth = 1, bool kUpperG = false>
 __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, const uint16_t* __restrict__ Vf,
                                             int S, u32x4* __restrict__ lds, void* __restrict__ Gout,
                                             float* __restrict__ Uout, float ks) {
@@ -169,7 +173,12 @@ __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, con
       __syncthreads();
       u32x4* dst = reinterpret_cast<u32x4*>(pass == 0 ? static_cast<char*>(Gout) : reinterpret_cast<char*>(Uout));
 #pragma unroll
-      for (int k = 0; k < 16; ++k) dst[k * 256 + tid] = lds[k * 256 + tid];
+      for (int k = 0; k < 16; ++k) {
+        // chunk k * 256 + tid: packed unit 4k + tid / 64, half (tid % 64) / 32
+        const int unit = 4 * k + (tid >> 6), half = (tid & 63) >> 5;
+        const bool lower = (unit >> 3) > 2 * ((unit >> 1) & 3) + half;  // row block > column block
+        if (!(kUpperG && pass == 0 && lower)) dst[k * 256 + tid] = lds[k * 256 + tid];
+      }
     }
   } else {
 #pragma unroll

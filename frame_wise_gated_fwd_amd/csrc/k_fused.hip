@@ -33,7 +33,10 @@
 // is not needed within one XCD.
 //
 // Rings.  Per head: kRing.wg slots for G_t/U_t and kRing.wm slots for M_t,
-// with monotonic per-slot flags (frame index + 1).  The queue of an XCD
+// with monotonic per-slot flags (frame index + 1).  G_t is symmetric, so a
+// build writes only its upper triangle (36 of 64 16 x 16 blocks per plane,
+// 36 KB instead of 64) and the state pass reads the lower blocks as
+// transposes of the upper ones, out of LDS.  The queue of an XCD
 // lists, per head, the builds of frames 0 .. lag-1, then output(f) and
 // build(f + lag) alternately, then the last outputs.  Every wait of an item
 // depends only on items earlier in the queue, or on state-pass progress that
@@ -112,6 +115,13 @@ __device__ __forceinline__ void flag_store(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// gfx950 transposed LDS read: in every 16-lane group, lane i receives as its
+// element e element i % 4 of the 8 bytes that lane 4e + i / 4 addressed.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
 __device__ __forceinline__ void invalidate_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
 
 // Spin until pred() holds, at most `limit` polls kSleep x 64 clocks apart;
@@ -180,11 +190,22 @@ __device__ Item decode_item(int i, int nh, int T, int lag) {
   return {1, hl, T - L + (j - 2 * (T - L))};
 }
 
+// G_t as the state pass holds it in LDS: the 36 upper-triangle 16 x 16
+// blocks (row block rb <= column block cb) of each bf16 plane, 72 blocks of
+// 512 B in the order of sym_block(); inside a block, lane slot n + 16 h holds
+// the 8 bf16 of row n, columns 8h .. 8h+7 (one half of a packed Gp unit).
+constexpr int kSymBlocks = 36;
+constexpr int kSymChunks = kSymBlocks * 2 * 32;  // 16-byte chunks, both planes
+__host__ __device__ constexpr int sym_block(int rb, int cb) { return rb * 8 - rb * (rb - 1) / 2 + (cb - rb); }
+
 template <int kRows>
 union __attribute__((aligned(16))) Lds {
   u32x4 build[build_lds_bytes<true>() / 16];
   uint16_t out[2][D][kOutLdsW];
-  uint16_t chain[2][2][kRows][kLdsW];
+  struct {
+    uint16_t m[2][2][kRows][kLdsW];
+    u32x4 g[kSymChunks];
+  } chain;
 };
 
 // ---------------------------------------------------------------------------
@@ -193,18 +214,22 @@ union __attribute__((aligned(16))) Lds {
 // X = M G on bf16 MFMA in three passes (Ghi*Mhi + Glo*Mhi + Ghi*Mlo), as the
 // stand-alone state pass: computed transposed, X^T = G M^T (G is symmetric),
 // wave w owning G rows 32w .. 32w+31; each lane ends with 4 consecutive
-// columns of kRows/16 rows of M.  Each wave keeps its own flags: at the top
-// of step t it waits only for memory operations it issued during step t-1
+// columns of kRows/16 rows of M.  The workgroup loads G_t's upper triangle
+// a step ahead (9 chunks of 16 bytes per thread), puts it in LDS at the
+// start of the step and reads its MFMA operands from there, lower blocks
+// through transposed reads.  Each wave keeps its own flags: at the top of
+// step t it waits only for memory operations it issued during step t-1
 // (M_{t-1} stores, the loads of frame t, the flag loads for this step),
 // publishes M_{t-1} and its progress, and checks the flags it loaded a step
-// ahead.  The only barrier per step is the LDS hand-off of M between the
-// waves.  A wave whose wait fails sets `abort` in LDS; after the barrier
-// every wave sees it and all leave together.
+// ahead.  Two barriers per step: after G_t is in LDS, and for the LDS
+// hand-off of M between the waves.  A wave whose wait fails sets `abort` in
+// LDS; after the barrier every wave sees it and all leave together.
 template <int kRows>
 __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int head, int part) {
   constexpr int kParts = D / kRows;
   constexpr int kRB = kRows / 16;
-  uint16_t (*Ml)[2][kRows][kLdsW] = lds.chain;
+  uint16_t (*Ml)[2][kRows][kLdsW] = lds.chain.m;
+  u32x4* Gs = lds.chain.g;
   const int T = a.T;
   const int r0 = part * kRows;
   const int tid = threadIdx.x;
@@ -270,21 +295,32 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
   win_load(0, gwin, bwin);
   win_load(64, gnxt, bnxt);
 
-  // one-frame register ring: this wave's G_t rows (hi/lo) and U_t elements
-  u32x4 rgh[2][4], rgl[2][4];
+  // one-frame register ring: 9 of the 2304 16-byte chunks of G_t's upper
+  // triangle (the builders write only those halves of the packed units) and
+  // this wave's U_t elements.  Chunk c = tid + 256 i is LDS chunk c; its
+  // source in the packed slot is fixed per thread, computed once here.
+  constexpr int kChunks = kSymChunks / 256;
+  static_assert(kSymChunks % 256 == 0, "whole chunks per thread");
+  int goff[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int c = tid + 256 * i;
+    const int blk = c >> 5, plane = blk & 1, slot = c & 31;
+    int rb = 0, first = 0;
+#pragma unroll
+    for (int r = 1; r < 8; ++r)
+      if ((blk >> 1) >= sym_block(r, r)) rb = r, first = sym_block(r, r);
+    const int cbk = rb + ((blk >> 1) - first);  // column block of the 16 x 16 block
+    goff[i] = ((((rb * 4 + (cbk >> 1)) * 2 + plane) << 10) + ((cbk & 1) << 9) + (slot << 4));
+  }
+  u32x4 rg[kChunks];
   f32x4 ru[2][kRB];
   auto load_frame = [&](int t) {
     if (t >= T) return;
     const char* Gp = gp_slot(t);
     const char* Up = up_slot(t);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int unit = ((2 * w + cb) * 4 + kb) * 2;
-        rgh[cb][kb] = *reinterpret_cast<const u32x4*>(Gp + (unit << 10) + 16 * l);
-        rgl[cb][kb] = *reinterpret_cast<const u32x4*>(Gp + ((unit + 1) << 10) + 16 * l);
-      }
+    for (int i = 0; i < kChunks; ++i) rg[i] = *reinterpret_cast<const u32x4*>(Gp + goff[i]);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -336,20 +372,19 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
       if (t + 1 >= kWM) oflag = flag_load(fl + kFlagOutDone + (t + 1) % kWM);
     }
     good = __builtin_amdgcn_readfirstlane((int)good) != 0;
+    // G_t into LDS (every wave's reads of G_{t-1} ended at the last barrier)
+    if (good) {
+#pragma unroll
+      for (int i = 0; i < kChunks; ++i) Gs[tid + 256 * i] = rg[i];
+    }
+    lds_barrier();
     if (good) {
       const int buf = t & 1;
-      u32x4 ahi[2][4], alo[2][4];
       f32x4 ureg[2][kRB];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          ahi[cb][kb] = rgh[cb][kb];
-          alo[cb][kb] = rgl[cb][kb];
-        }
+      for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) ureg[cb][rb] = ru[cb][rb];
-      }
       // refill the ring with frame t + 1 (its build is done)
       invalidate_l1();
       load_frame(t + kPrefetch);
@@ -361,6 +396,30 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
         for (int rb = 0; rb < kRB; ++rb) acc[cb][rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
+        // A operand (cb, kb): lane (n, g) needs G[16(2w + cb) + n][32kb + 8g .. +7], in
+        // 16 x 16 block (2w + cb, 2kb + g/2).  An upper block is read as stored; a lower
+        // one is the transpose of block (2kb + g/2, 2w + cb): rows 8(g%2) + e, column n,
+        // e = 0..7, two transposed reads in which lane (n, g) names row 8(g%2) + 4h + n/4
+        // at columns 4(n%4) .. +3.
+        u32x4 ahi[2], alo[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const int rbk = 2 * w + cb, cbk = 2 * kb + (g >> 1);
+          if (rbk <= cbk) {
+            const int c = sym_block(rbk, cbk) * 64 + n + 16 * (g & 1);
+            ahi[cb] = Gs[c];
+            alo[cb] = Gs[c + 32];
+          } else {
+            const uint16_t* hb = reinterpret_cast<const uint16_t*>(Gs + sym_block(cbk, rbk) * 64);
+            const int r = 8 * (g & 1) + (n >> 2);
+            const int e0 = (r + 16 * ((n & 3) >> 1)) * 8 + 4 * (n & 1);      // bf16 index, rows r
+            const int e1 = (r + 4 + 16 * ((n & 3) >> 1)) * 8 + 4 * (n & 1);  // and r + 4
+            const u32x2 h0 = lds_read_tr16(hb + e0), h1 = lds_read_tr16(hb + e1);
+            const u32x2 l0 = lds_read_tr16(hb + 256 + e0), l1 = lds_read_tr16(hb + 256 + e1);
+            ahi[cb] = (u32x4){h0.x, h0.y, h1.x, h1.y};
+            alo[cb] = (u32x4){l0.x, l0.y, l1.x, l1.y};
+          }
+        }
         u32x4 bhi[kRB], blo[kRB];
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) {
@@ -370,15 +429,15 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(ahi[cb][kb], bhi[rb], acc[cb][rb]);
+          for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(ahi[cb], bhi[rb], acc[cb][rb]);
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(alo[cb][kb], bhi[rb], acc[cb][rb]);
+          for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(alo[cb], bhi[rb], acc[cb][rb]);
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(ahi[cb][kb], blo[rb], acc[cb][rb]);
+          for (int cb = 0; cb < 2; ++cb) acc[cb][rb] = mfma16x16x32(ahi[cb], blo[rb], acc[cb][rb]);
       }
       const float gb = gm * bt;
 #pragma unroll
@@ -458,7 +517,7 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
       float* up = reinterpret_cast<float*>(ring + (int64_t)(2 * (it.t % kWG) + 1) * packed::kFrameBytes);
       // two token iterations loaded ahead (one measured no faster); the
       // kernel fits its 256 registers per lane without spilling either way
-      build_frame<true, 2>(a.k + fr * S * D, a.v + fr * S * D, S, lds.build, gp, up, a.ks);
+      build_frame<true, 2, true>(a.k + fr * S * D, a.v + fr * S * D, S, lds.build, gp, up, a.ks);
       wait_stores();
       __syncthreads();
       if (tid == 0) flag_store(fl + kFlagGReady + it.t % kWG, (uint32_t)(it.t + 1));
