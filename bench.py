@@ -167,6 +167,40 @@ def _oracle_head_timed(args):
         return time.perf_counter() - t0
 
 
+def _oracle_parity_head(args):
+    """Untimed check beside the CPU baseline: the oracle's output at the
+    sampled frames and its final state for one head, against the GPU's."""
+    w, b, h, frames, o_gpu, m_gpu = args
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from synth import head_inputs
+    with threadpool_limits(1):
+        d = head_inputs(w, b, h)
+        O, M = oracle.gdn_head(d["q"], d["k"], d["v"], d["gamma"], d["beta"], d["state"], out_frames=frames)
+    per_frame = [float(np.linalg.norm(o_gpu[i] - O[i]) / np.linalg.norm(O[i])) for i in range(len(frames))]
+    num, den = float(np.sum((o_gpu - O) ** 2)), float(np.sum(O ** 2))
+    return b, h, per_frame, num, den, float(np.linalg.norm(m_gpu - M) / np.linalg.norm(M))
+
+
+def parity_sample(w, out, st_out, workers):
+    """Relative L2 errors of the timed call's output at 24 sampled frames
+    (every head) and of its final state, against the fp64 oracle."""
+    from concurrent.futures import ProcessPoolExecutor
+    rng = np.random.Generator(np.random.PCG64(11))
+    frames = sorted({0, 1, w.T // 4, w.T // 2, (3 * w.T) // 4, w.T - 2, w.T - 1}
+                    | {int(x) for x in rng.integers(0, w.T, size=17)})
+    idx = np.asarray(frames)
+    jobs = [(w, b, h, frames, out[b, h, idx].float().cpu().numpy().astype(np.float64),
+             st_out[b, h].cpu().numpy().astype(np.float64)) for b in range(w.B) for h in range(w.H)]
+    with ProcessPoolExecutor(max_workers=workers) as ex:
+        res = list(ex.map(_oracle_parity_head, jobs))
+    worst = max(max(r[2]) for r in res)
+    num, den = sum(r[3] for r in res), sum(r[4] for r in res)
+    return {"frames": len(frames), "heads": len(res), "out_relL2": round(math.sqrt(num / den), 9),
+            "max_frame_out_relL2": round(worst, 9), "max_head_state_relL2": round(max(r[5] for r in res), 9),
+            "tolerance": 2e-3}
+
+
 def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
     """The same tensors processed as successive calls that carry the float32
     state (24 calls of 40 frames and one of 1 frame for T = 961), and the
@@ -484,6 +518,12 @@ def main():
         log(f"cpu baseline: {frames} frames x {B * H} heads on {workers} processes")
         cpu = cpu_baseline(w, frames, workers)
         log(f"cpu baseline: {cpu['value']} frame-steps/s")
+        # untimed, beside it: the timed call's output and state against the same
+        # oracle (one more call first: the extras above reuse `out`)
+        step()
+        torch.cuda.synchronize()
+        cpu["parity"] = parity_sample(w, out, st_out, workers)
+        log(f"parity against the oracle: {cpu['parity']}")
 
     res = {
         "metric": "GDN frame-steps/s at H=16,D=128,S=880,T=961; % bf16 MFMA peak, HBM GB/s",
