@@ -24,7 +24,7 @@ namespace {
 
 constexpr int64_t kMaxFrames = (int64_t{1} << 24) - 1;  // B*H*T: one workgroup per frame
 constexpr int64_t kSegmentFrames = 64;                   // frames per segment, overlapped schedule
-constexpr int64_t kFusedMinT = 64;                       // shorter sequences take the three-kernel path
+constexpr int64_t kFusedMinT = 32;                       // shorter sequences take the three-kernel path
 
 struct Dims {
   int64_t B, H, T, S, D;

@@ -122,7 +122,7 @@ unsigned gdn_set_spin_limit(unsigned polls);
 /*
  * Which implementation gdn_frame_fwd uses for this shape and input dtype (a
  * pure function of its arguments):
- *   GDN_PATH_MFMA   bf16, D == 128, T <= 64 (and longer sequences when the
+ *   GDN_PATH_MFMA   bf16, D == 128, T <= 32 (and longer sequences when the
  *                   fused kernel below is unavailable): three bf16-MFMA
  *                   kernels (build, state pass, output) with the per-frame
  *                   intermediates in the workspace.  When T > 64 the
@@ -137,7 +137,7 @@ unsigned gdn_set_spin_limit(unsigned polls);
  *                   on `stream` like a single kernel.  The environment
  *                   variable GDN_SEGMENT_FRAMES (read once per process)
  *                   replaces the 64.  Otherwise all three run on `stream`;
- *   GDN_PATH_FUSED  bf16, D == 128, T > 64: build, state pass and output in
+ *   GDN_PATH_FUSED  bf16, D == 128, T > 32: build, state pass and output in
  *                   one persistent kernel per group of at most 16 heads,
  *                   launched cooperatively on `stream` (every workgroup
  *                   resident at once) after a tiny flag-reset kernel.  Each

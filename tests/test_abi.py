@@ -53,8 +53,9 @@ def test_path_selection():
     L = F.lib()
     assert L.gdn_path(ctypes.byref(_shape(1, 16, 961, 880, 128)), BF16) == 2
     assert L.gdn_path(ctypes.byref(_shape(4, 16, 961, 880, 128)), BF16) == 2
-    assert L.gdn_path(ctypes.byref(_shape(1, 16, 64, 880, 128)), BF16) == 1
-    assert L.gdn_path(ctypes.byref(_shape(1, 16, 65, 880, 128)), BF16) == 2
+    assert L.gdn_path(ctypes.byref(_shape(1, 16, 32, 880, 128)), BF16) == 1
+    assert L.gdn_path(ctypes.byref(_shape(1, 16, 33, 880, 128)), BF16) == 2
+    assert L.gdn_path(ctypes.byref(_shape(1, 16, 64, 880, 128)), BF16) == 2
     assert L.gdn_path(ctypes.byref(_shape(1, 16, 961, 880, 128)), F32) == 0
     assert L.gdn_path(ctypes.byref(_shape(1, 2, 8, 16, 64)), BF16) == 0
     assert L.gdn_path(ctypes.byref(_shape(D=100)), BF16) == -1
