@@ -296,15 +296,6 @@ __global__ void k_bwd_reduce(const float* __restrict__ partials, float* __restri
   dbeta[f] = sb;
 }
 
-// ds_read_b64_tr_b16 (gfx950): each lane names an 8-byte-aligned LDS
-// address; within every 16-lane group, lane i receives as its element e
-// (e = 0..3) element i % 4 of the 8 bytes named by lane 4e + i / 4.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-  return __builtin_bit_cast(u32x2, r);
-}
-
 // Key and value gradients for the tokens of one frame (or one token part of
 // it, in launches of a few frames):
 //   dk_t = V_t LB_t + K_t S_t,   dv_t = K_t LB_t^T,

@@ -115,13 +115,6 @@ __device__ __forceinline__ void flag_store(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// gfx950 transposed LDS read: in every 16-lane group, lane i receives as its
-// element e element i % 4 of the 8 bytes that lane 4e + i / 4 addressed.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-  return __builtin_bit_cast(u32x2, r);
-}
 __device__ __forceinline__ void invalidate_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
 
 // Spin until pred() holds, at most `limit` polls kSleep x 64 clocks apart;
