@@ -15,9 +15,9 @@ namespace gdn {
 // is laid out [head][T]; each launcher covers frames [t0, t1) of every head.
 //
 // Launches of at most this many frames (heads x frames in the range) take the
-// small-launch variants: a build with more loads in flight per workgroup and
-// an output that splits each frame's tokens over several workgroups.  Both
-// give bit-identical results to the full-size variants.
+// small-launch variants: a build that splits each frame's output rows over
+// four workgroups and an output that splits each frame's tokens over several
+// workgroups.  Both give bit-identical results to the full-size variants.
 constexpr int64_t kFewFrames = 128;
 
 // ks^2 K_t^T K_t and ks V_t^T K_t for frames [t0, t1) (ks: the key scale,
