@@ -200,4 +200,108 @@ __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, con
   }
 }
 
+// A quarter of build_frame's work (packed forms), for spreading one frame
+// over four workgroups: part q (0..3) computes the rows {8m + j : j in
+// {2q, 2q+1}} of G_t and U_t (the rows wave q owns in build_frame), its wave
+// w the 8 accumulators of G_t (w < 2) or U_t (w >= 2) at j = 2q + w % 2.
+// It loads and transposes all of the frame's K and V slabs as build_frame
+// does, so each accumulator receives the same MFMAs on the same operands in
+// the same order: every element it writes is bit-identical to build_frame's,
+// and a wave's serial MFMA chain is a quarter as long.  Gout and Uout
+// receive the part's whole rows of the packed forms (for G both triangles);
+// stores go straight from registers.  `frag` is 32 KB of LDS; kDepth token
+// iterations are loaded ahead.  All 256 threads must call it; on return this
+// thread's stores are issued, not necessarily complete.
+template <int kDepth>
+__device__ __forceinline__ void build_frame_part(const uint16_t* __restrict__ Kf, const uint16_t* __restrict__ Vf,
+                                                 int S, u32x4 (*__restrict__ frag)[8][kWave],
+                                                 char* __restrict__ Gout, char* __restrict__ Uout, float ks,
+                                                 int q) {
+  constexpr int D = 128;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // opaque, as in build_frame
+  const int w = tid >> 6, l = tid & 63;
+  const int g = l >> 4, c = l & 15;
+  const uint16_t* src = w < 2 ? Kf : Vf;
+  const int slab = w & 1;
+  const int j = 2 * q + (w & 1);   // the MFMA row fragment this wave accumulates
+  const int au = w < 2 ? 0 : 2;    // A operand from the K units (G) or the V units (U)
+
+  u32x4 x[kDepth][8];
+  auto load = [&](auto jc, int it) {
+    constexpr int jb = decltype(jc)::value;
+    const int base = it * kBuildIterTok + slab * 32 + 8 * g;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int s = base + r;
+      x[jb][r] = s < S ? *reinterpret_cast<const u32x4*>(src + (int64_t)s * D + 8 * c) : (u32x4){0u, 0u, 0u, 0u};
+    }
+  };
+  f32x4 acc[8];
+#pragma unroll
+  for (int jp = 0; jp < 8; ++jp) acc[jp] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int iters = (S + kBuildIterTok - 1) / kBuildIterTok;
+  auto iteration = [&](auto jc, int it) {
+    constexpr int jb = decltype(jc)::value;
+    __syncthreads();  // every wave is done reading the previous fragments
+#pragma unroll
+    for (int jf = 0; jf < 8; ++jf) {
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t lo = x[jb][2 * p][jf >> 1], hi = x[jb][2 * p + 1][jf >> 1];
+        o[p] = (jf & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      frag[w][jf][l] = o;
+    }
+    __syncthreads();
+    if (it + kDepth < iters) load(jc, it + kDepth);
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      u32x4 kf[8];
+#pragma unroll
+      for (int jp = 0; jp < 8; ++jp) kf[jp] = frag[sl][jp][l];
+      const u32x4 a = frag[au + sl][j][l];
+#pragma unroll
+      for (int jp = 0; jp < 8; ++jp) acc[jp] = mfma16x16x32(a, kf[jp], acc[jp]);
+    }
+  };
+  [&]<int... js>(std::integer_sequence<int, js...>) {
+    ((js < iters ? load(std::integral_constant<int, js>{}, js) : void()), ...);
+  }(std::make_integer_sequence<int, kDepth>{});
+  for (int it0 = 0; it0 < iters; it0 += kDepth) {
+    [&]<int... js>(std::integer_sequence<int, js...>) {
+      ((it0 + js < iters ? iteration(std::integral_constant<int, js>{}, it0 + js) : void()), ...);
+    }(std::make_integer_sequence<int, kDepth>{});
+  }
+
+  // lane (g, c), register r of accumulator jp holds X[32g + 8r + j][8c + jp];
+  // each lane's 8 columns are one 16-byte chunk of the packed form
+  if (w < 2) {
+    const float ks2 = ks * ks;
+#pragma unroll
+    for (int jp = 0; jp < 8; ++jp) acc[jp] *= ks2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 32 * g + 8 * r + j;
+      const u32x2 p0 = split2(acc[0][r], acc[1][r]), p1 = split2(acc[2][r], acc[3][r]);
+      const u32x2 p2 = split2(acc[4][r], acc[5][r]), p3 = split2(acc[6][r], acc[7][r]);
+      *reinterpret_cast<u32x4*>(Gout + packed::g_chunk(row, 8 * c, 0)) = (u32x4){p0.x, p1.x, p2.x, p3.x};
+      *reinterpret_cast<u32x4*>(Gout + packed::g_chunk(row, 8 * c, 1)) = (u32x4){p0.y, p1.y, p2.y, p3.y};
+    }
+  } else {
+#pragma unroll
+    for (int jp = 0; jp < 8; ++jp) acc[jp] *= ks;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 32 * g + 8 * r + j;
+      *reinterpret_cast<f32x4*>(Uout + packed::u_chunk(row, 8 * c)) =
+          (f32x4){acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+      *reinterpret_cast<f32x4*>(Uout + packed::u_chunk(row, 8 * c + 4)) =
+          (f32x4){acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+    }
+  }
+}
+
 }  // namespace gdn

@@ -305,7 +305,7 @@ def test_forward_edge_shapes(T, S, D, dt):
 @pytest.mark.parametrize("B,H,T,S,state", [
     (1, 3, 33, 880, True),     # just long enough for the fused kernel; 5 of 8 XCDs without a head
     (1, 17, 70, 100, True),    # two launch groups, the second with one head; ragged tokens (64 + 36)
-    (2, 4, 67, 1, False),      # one token per frame, zero initial state
+    (2, 4, 67, 1, False),      # one token per frame (3 of the 4 parts of a tail output empty), zero state
     (1, 8, 66, 17, True),      # one head per XCD, 17 tokens
 ])
 def test_fused_kernel_edge_shapes(B, H, T, S, state):
