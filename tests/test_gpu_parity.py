@@ -260,6 +260,19 @@ def test_single_frame_calls_equal_one_call_bitwise():
     _forward_parity(w, frames=[0, 5, 11])
 
 
+def test_small_launch_threshold_is_bitwise():
+    """128 head-frames take the small-launch kernels (each frame's build over
+    four workgroups, its output over token parts), 136 the full-size ones:
+    the 16 heads the two launches share agree bit for bit."""
+    w = CLIP_5S.with_(H=17, T=8, S=300, name="clip_h17_t8", state_std=0.02)
+    x = device_inputs(w, DEV)
+    full_out, full_st = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    sub = {n: x[n][:, :16].contiguous() for n in ("q", "k", "v", "gamma", "beta", "state")}
+    few_out, few_st = F.frame_fwd(sub["q"], sub["k"], sub["v"], sub["gamma"], sub["beta"], sub["state"])
+    torch.cuda.synchronize()
+    assert torch.equal(few_out, full_out[:, :16]) and torch.equal(few_st, full_st[:, :16])
+
+
 @pytest.mark.parametrize("fused", [True, False])
 def test_forward_is_ordered_on_a_user_stream(fused):
     """Work queued on the caller's stream before the call is seen by the
