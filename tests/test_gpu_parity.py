@@ -273,6 +273,23 @@ def test_small_launch_threshold_is_bitwise():
     assert torch.equal(few_out, full_out[:, :16]) and torch.equal(few_st, full_st[:, :16])
 
 
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_single_frame_launch_is_bitwise(odt):
+    """A single-frame call's output equals the first frame of a two-frame
+    call, for either output type, and its state equals the stage entry
+    points' (float32 maps, 32-row state pass)."""
+    w = CLIP_5S.with_(T=2, S=300, name="clip_t2_s300", state_std=0.02)
+    x = device_inputs(w, DEV)
+    two_out, _ = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"], out_dtype=odt)
+    one = {n: x[n][:, :, :1].contiguous() for n in ("q", "k", "v", "gamma", "beta")}
+    one_out, one_st = F.frame_fwd(one["q"], one["k"], one["v"], one["gamma"], one["beta"], x["state"],
+                                  out_dtype=odt)
+    st_ref = F.state_pass(*F.build_maps(one["k"], one["v"]), one["gamma"], one["beta"], x["state"])[1]
+    torch.cuda.synchronize()
+    assert torch.equal(one_out, two_out[:, :, :1])
+    assert torch.equal(one_st, st_ref)
+
+
 @pytest.mark.parametrize("fused", [True, False])
 def test_forward_is_ordered_on_a_user_stream(fused):
     """Work queued on the caller's stream before the call is seen by the
