@@ -25,6 +25,8 @@ namespace {
 constexpr int64_t kMaxFrames = (int64_t{1} << 24) - 1;  // B*H*T: one workgroup per frame
 constexpr int64_t kSegmentFrames = 64;                   // frames per segment, overlapped schedule
 constexpr int64_t kFusedMinT = 32;                       // shorter sequences take the three-kernel path
+constexpr int64_t kMapSlots = 3;                         // segments whose maps the MFMA path holds at once
+constexpr size_t kMapFrameBytes = 128 * 128 * 4;         // one packed G, U or M of one frame (D = 128)
 
 struct Dims {
   int64_t B, H, T, S, D;
@@ -137,6 +139,19 @@ size_t round256(size_t x) { return (x + 255) & ~size_t{255}; }
 // ---------------------------------------------------------------------------
 constexpr int kMaxDevices = 64;
 
+void teardown();
+
+// The library's own HIP objects (the timing events and the side streams
+// and events below) are destroyed by an exit handler registered right
+// after the first of them is created.  The HIP runtime registers its own
+// exit-time clean-up when it starts, which is before that, and exit
+// handlers run in reverse order of registration: this one runs first, while
+// the runtime is still whole, and the objects never outlive it.
+void register_teardown() {
+  static std::once_flag once;
+  std::call_once(once, [] { std::atexit(teardown); });
+}
+
 // Per-launch HIP events of gdn_frame_fwd_timed: a pair around every kernel,
 // on the stream that kernel is launched on.  One pool per device, grown on
 // demand and kept for the life of the process.
@@ -150,6 +165,7 @@ struct Recorder {
       hipError_t err = hipEventCreate(&e);
       if (err != hipSuccess) return err;
       pool->push_back(e);
+      register_teardown();
     }
     return hipEventRecord((*pool)[i], st);
   }
@@ -169,7 +185,8 @@ std::mutex g_timing_mu;
 // interleave their records and waits on these events.
 struct Side {
   hipStream_t state_st, out_st;
-  hipEvent_t fork, built, stated, state_done, out_done;
+  hipEvent_t fork, built, state_done, out_done;
+  hipEvent_t stated[kMapSlots], output[kMapSlots];  // per map slot: its state pass, its output done
   bool ready;
 };
 Side g_side[kMaxDevices];
@@ -180,14 +197,63 @@ hipError_t side_init(Side& sd) {
   hipError_t e;
   if ((e = hipStreamCreateWithFlags(&sd.state_st, hipStreamNonBlocking)) != hipSuccess) return e;
   if ((e = hipStreamCreateWithFlags(&sd.out_st, hipStreamNonBlocking)) != hipSuccess) return e;
-  for (hipEvent_t* ev : {&sd.fork, &sd.built, &sd.stated, &sd.state_done, &sd.out_done})
+  for (hipEvent_t* ev : {&sd.fork, &sd.built, &sd.state_done, &sd.out_done, &sd.stated[0], &sd.stated[1],
+                         &sd.stated[2], &sd.output[0], &sd.output[1], &sd.output[2]})
     if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) return e;
   sd.ready = true;
+  register_teardown();
   return hipSuccess;
 }
 
+// Frames per segment of the overlapped schedule (GDN_SEGMENT_FRAMES
+// overrides the default; read once).
+int64_t segment_frames() {
+  static const int64_t f = [] {
+    const char* e = std::getenv("GDN_SEGMENT_FRAMES");
+    const long v = e ? std::strtol(e, nullptr, 10) : 0;
+    return v >= 1 && v <= (1L << 24) ? (int64_t)v : int64_t{kSegmentFrames};
+  }();
+  return f;
+}
+
+// Segments of the MFMA path: ceil(T / F) of (nearly) equal length, at most
+// `cap` frames each; the maps of segment i live in slot i % slots of each
+// of the three map buffers.
+struct Segments {
+  int64_t n, cap, slots;
+};
+Segments segments_of(int64_t T) {
+  const int64_t F = segment_frames();
+  const int64_t n = (T + F - 1) / F;
+  return {n, (T + n - 1) / n, n < kMapSlots ? n : kMapSlots};
+}
+size_t slot_bytes(const Dims& d, const Segments& g) { return round256((size_t)(d.heads * g.cap) * kMapFrameBytes); }
+
+void teardown() {
+  {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    for (Side& sd : g_side) {
+      if (!sd.ready) continue;
+      for (hipEvent_t ev : {sd.fork, sd.built, sd.state_done, sd.out_done, sd.stated[0], sd.stated[1],
+                            sd.stated[2], sd.output[0], sd.output[1], sd.output[2]})
+        (void)hipEventDestroy(ev);
+      (void)hipStreamDestroy(sd.state_st);
+      (void)hipStreamDestroy(sd.out_st);
+      sd.ready = false;
+    }
+  }
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  for (auto& pool : g_timing_pool) {
+    for (hipEvent_t ev : pool) (void)hipEventDestroy(ev);
+    pool.clear();
+  }
+}
+
 // Per-device facts the fused path needs, queried once: the launch size of
-// the fused kernel (0 when the device cannot run it cooperatively).
+// the fused kernel (0 when the device cannot host it: no cooperative
+// launch, too few compute units, or workgroups not dealt evenly over eight
+// XCDs with ids 0-7, which the one-time probe in gdn::fused_topology_ok
+// checks).
 struct DevInfo {
   int fused_grid[2];  // [out_bf16]
   bool ready;
@@ -206,22 +272,51 @@ hipError_t dev_info(DevInfo** out) {
     int cus = 0, coop = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev)) != hipSuccess) return e;
-    for (int b = 0; b < 2; ++b) di.fused_grid[b] = coop ? gdn::fused_grid(b != 0, cus) : 0;
+    for (int b = 0; b < 2; ++b) {
+      int grid = coop ? gdn::fused_grid(b != 0, cus) : 0;
+      bool even = false;
+      if (grid > 0 && (e = gdn::fused_topology_ok(grid, &even)) != hipSuccess) return e;
+      di.fused_grid[b] = even ? grid : 0;
+    }
     di.ready = true;
   }
   *out = &di;
   return hipSuccess;
 }
 
-// Frames per segment of the overlapped schedule (GDN_SEGMENT_FRAMES
-// overrides the default; read once).
-int64_t segment_frames() {
-  static const int64_t f = [] {
-    const char* e = std::getenv("GDN_SEGMENT_FRAMES");
-    const long v = e ? std::strtol(e, nullptr, 10) : 0;
-    return v >= 1 && v <= (1L << 24) ? (int64_t)v : int64_t{kSegmentFrames};
-  }();
-  return f;
+// The fused kernel's launch size for a call on the current device, 0 when
+// the call does not take it.  *queried is false when the device could not
+// be queried (no device): callers then assume a device that hosts it.
+int fused_launch(int in_dtype, const Dims& d, bool out_bf16, bool* queried) {
+  *queried = true;
+  if (!fused_path(in_dtype, d)) return 0;
+  DevInfo* di = nullptr;
+  if (dev_info(&di) != hipSuccess) {
+    (void)hipGetLastError();
+    *queried = false;
+    return 0;
+  }
+  return di->fused_grid[out_bf16 ? 1 : 0];
+}
+
+// Workspace bytes of each path (D x D maps of the frames the path holds at
+// once); SIZE_MAX when the path cannot take the shape.
+size_t path_workspace(const Dims& d, int in_dtype, int path) {
+  if (d.in_elems == 0) return 0;
+  switch (path) {
+    case GDN_PATH_FUSED:
+      return fast_path(in_dtype, d.D) && d.T > kFusedMinT ? (size_t)gdn::fused_workspace_bytes(d.heads)
+                                                          : SIZE_MAX;
+    case GDN_PATH_MFMA: {
+      if (!fast_path(in_dtype, d.D)) return SIZE_MAX;
+      const Segments g = segments_of(d.T);
+      return (size_t)(3 * g.slots) * slot_bytes(d, g);
+    }
+    case GDN_PATH_PLAIN:
+      return 3 * round256(d.map_elems * sizeof(float));
+    default:
+      return SIZE_MAX;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -236,42 +331,48 @@ hipError_t timed(Recorder* rec, hipStream_t st, int kind, F&& launch) {
   return rec ? rec->end(st, kind) : hipSuccess;
 }
 
-// The MFMA path: build, state pass and output over ceil(T / F) segments of
-// (nearly) equal length.  Segment i's state pass needs its own build and segment
-// i-1's state pass; its output needs its own state pass.  Builds run on the
-// caller's stream, state passes and outputs on the two side streams, so
-// build(i+1), state(i) and output(i-1) overlap: the state pass is a chain of
-// short latency-bound steps on a few CUs, while build and output stream
-// from HBM on the rest.  With one segment everything runs on the caller's
-// stream.
+// The MFMA path: build, state pass and output over the segments.  Segment
+// i's state pass needs its own build and segment i-1's state pass; its
+// output needs its own state pass.  Builds run on the caller's stream,
+// state passes and outputs on the two side streams, so build(i+1),
+// state(i) and output(i-1) overlap: the state pass is a chain of short
+// latency-bound steps on a few CUs, while build and output stream from HBM
+// on the rest.  The maps of segment i use slot i % 3 of each map buffer, so
+// build(i) also waits for state(i-3) (the last reader of its G, U slot) and
+// state(i) for output(i-3) (the last reader of its M slot); the workspace
+// then holds three segments instead of the whole sequence.  With one
+// segment everything runs on the caller's stream.
 hipError_t run_mfma(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     const float* gamma, const float* beta, const float* state_in, float ks, void* out,
-                    bool out_bf16, float* state_out, void* G, float* U, void* M_all, hipStream_t s,
-                    Recorder* rec) {
-  const int64_t F = segment_frames();
-  const int64_t nseg = (d.T + F - 1) / F;
+                    bool out_bf16, float* state_out, char* ws, hipStream_t s, Recorder* rec) {
+  const Segments g = segments_of(d.T);
+  const size_t sb = slot_bytes(d, g);
   const int S = (int)d.S;
-  auto build = [&](hipStream_t st, int64_t t0, int64_t t1) {
+  // map buffers of segment i: G, U and M slots, each `sb` bytes
+  auto G = [&](int64_t i) { return ws + (size_t)(i % g.slots) * sb; };
+  auto U = [&](int64_t i) { return reinterpret_cast<float*>(ws + (size_t)(g.slots + i % g.slots) * sb); };
+  auto M = [&](int64_t i) { return ws + (size_t)(2 * g.slots + i % g.slots) * sb; };
+  auto build = [&](hipStream_t st, int64_t i, int64_t t0, int64_t t1) {
     return timed(rec, st, 0, [&] {
-      return gdn::launch_build_bf16_d128(k, v, G, true, U, d.heads, d.T, t0, t1, S, ks, st);
+      return gdn::launch_build_bf16_d128(k, v, G(i), true, U(i), d.heads, d.T, t0, t1, S, ks, {g.cap, t0}, st);
     });
   };
-  auto state = [&](hipStream_t st, int64_t t0, int64_t t1) {
+  auto state = [&](hipStream_t st, int64_t i, int64_t t0, int64_t t1) {
     return timed(rec, st, 1, [&] {
-      return gdn::launch_state_d128(G, true, U, gamma, beta, t0 ? state_out : state_in, M_all, false, state_out,
-                                    d.heads, d.T, t0, t1, st);
+      return gdn::launch_state_d128(G(i), true, U(i), gamma, beta, t0 ? state_out : state_in, M(i), false,
+                                    state_out, d.heads, d.T, t0, t1, {g.cap, t0}, st);
     });
   };
-  auto output = [&](hipStream_t st, int64_t t0, int64_t t1) {
+  auto output = [&](hipStream_t st, int64_t i, int64_t t0, int64_t t1) {
     return timed(rec, st, 2, [&] {
-      return gdn::launch_output_bf16_d128(q, M_all, true, out, out_bf16, d.heads, d.T, t0, t1, S, st);
+      return gdn::launch_output_bf16_d128(q, M(i), true, out, out_bf16, d.heads, d.T, t0, t1, S, {g.cap, t0}, st);
     });
   };
   hipError_t e;
-  if (nseg == 1) {
-    if ((e = build(s, 0, d.T)) != hipSuccess) return e;
-    if ((e = state(s, 0, d.T)) != hipSuccess) return e;
-    return output(s, 0, d.T);
+  if (g.n == 1) {
+    if ((e = build(s, 0, 0, d.T)) != hipSuccess) return e;
+    if ((e = state(s, 0, 0, d.T)) != hipSuccess) return e;
+    return output(s, 0, 0, d.T);
   }
   int dev = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
@@ -283,16 +384,22 @@ hipError_t run_mfma(const Dims& d, const uint16_t* q, const uint16_t* k, const u
   if ((e = hipEventRecord(sd.fork, s)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(sd.state_st, sd.fork, 0)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(sd.out_st, sd.fork, 0)) != hipSuccess) return e;
+  // Each wait is enqueued after the record it refers to and before that
+  // event is recorded again (three segments later), so the events are reused.
   hipError_t err = hipSuccess;
-  for (int64_t i = 0; i < nseg && err == hipSuccess; ++i) {
-    const int64_t t0 = i * d.T / nseg, t1 = (i + 1) * d.T / nseg;  // balanced, at most F frames
-    if ((err = build(s, t0, t1)) != hipSuccess) break;
+  for (int64_t i = 0; i < g.n && err == hipSuccess; ++i) {
+    const int64_t t0 = i * d.T / g.n, t1 = (i + 1) * d.T / g.n;  // balanced, at most g.cap frames
+    const int slot = (int)(i % kMapSlots);
+    if (i >= kMapSlots && (err = hipStreamWaitEvent(s, sd.stated[slot], 0)) != hipSuccess) break;
+    if ((err = build(s, i, t0, t1)) != hipSuccess) break;
     if ((err = hipEventRecord(sd.built, s)) != hipSuccess) break;
     if ((err = hipStreamWaitEvent(sd.state_st, sd.built, 0)) != hipSuccess) break;
-    if ((err = state(sd.state_st, t0, t1)) != hipSuccess) break;
-    if ((err = hipEventRecord(sd.stated, sd.state_st)) != hipSuccess) break;
-    if ((err = hipStreamWaitEvent(sd.out_st, sd.stated, 0)) != hipSuccess) break;
-    err = output(sd.out_st, t0, t1);
+    if (i >= kMapSlots && (err = hipStreamWaitEvent(sd.state_st, sd.output[slot], 0)) != hipSuccess) break;
+    if ((err = state(sd.state_st, i, t0, t1)) != hipSuccess) break;
+    if ((err = hipEventRecord(sd.stated[slot], sd.state_st)) != hipSuccess) break;
+    if ((err = hipStreamWaitEvent(sd.out_st, sd.stated[slot], 0)) != hipSuccess) break;
+    if ((err = output(sd.out_st, i, t0, t1)) != hipSuccess) break;
+    err = hipEventRecord(sd.output[slot], sd.out_st);
   }
   // join, also after a failed launch, so the caller's stream stays ordered
   // after whatever was enqueued
@@ -339,15 +446,15 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
   const int64_t H = d.heads, T = d.T;
   auto seg = [&](int64_t i) { return std::make_pair(i * T / nseg, (i + 1) * T / nseg); };
   auto build_kv = [&](hipStream_t st, int64_t t0, int64_t t1) {
-    return gdn::launch_build_bf16_d128(a.k, a.v, b.G, true, b.U, H, T, t0, t1, S, a.ks, st);
+    return gdn::launch_build_bf16_d128(a.k, a.v, b.G, true, b.U, H, T, t0, t1, S, a.ks, {T, 0}, st);
   };
   // P_t = dO_t^T Q_t: the build's second map with (K, V) = (Q, dO); its first (Q^T Q) is not stored
   auto build_p = [&](hipStream_t st, int64_t t0, int64_t t1) {
-    return gdn::launch_build_bf16_d128(a.q, a.d_out, nullptr, false, b.P, H, T, t0, t1, S, 1.f, st);
+    return gdn::launch_build_bf16_d128(a.q, a.d_out, nullptr, false, b.P, H, T, t0, t1, S, 1.f, {T, 0}, st);
   };
   auto state_fwd = [&](hipStream_t st, int64_t t0, int64_t t1) {
     return gdn::launch_state_d128(b.G, true, b.U, a.gamma, a.beta, t0 ? b.fstate : a.state_in, b.M_all, true,
-                                  b.fstate, H, T, t0, t1, st);
+                                  b.fstate, H, T, t0, t1, {T, 0}, st);
   };
   auto dq = [&](hipStream_t st, int64_t t0, int64_t t1) {
     return gdn::launch_output_bwd_d128(a.d_out, b.M_all, a.dq, true, H, T, t0, t1, S, st);  // dq = dO M
@@ -390,7 +497,7 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
     if ((err = build_kv(s, t0, t1)) != hipSuccess) break;
     if ((err = hand_off(s, sd.built, sd.state_st)) != hipSuccess) break;
     if ((err = state_fwd(sd.state_st, t0, t1)) != hipSuccess) break;
-    if ((err = hand_off(sd.state_st, sd.stated, sd.out_st)) != hipSuccess) break;
+    if ((err = hand_off(sd.state_st, sd.stated[0], sd.out_st)) != hipSuccess) break;
     err = dq(sd.out_st, t0, t1);
   }
   for (int64_t i = nseg - 1; i >= 0 && err == hipSuccess; --i) {
@@ -398,7 +505,7 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
     if ((err = build_p(s, t0, t1)) != hipSuccess) break;
     if ((err = hand_off(s, sd.built, sd.state_st)) != hipSuccess) break;
     if ((err = state_bwd(sd.state_st, t0, t1)) != hipSuccess) break;
-    if ((err = hand_off(sd.state_st, sd.stated, sd.out_st)) != hipSuccess) break;
+    if ((err = hand_off(sd.state_st, sd.stated[0], sd.out_st)) != hipSuccess) break;
     err = grads(sd.out_st, t0, t1);
   }
   // join, also after a failed launch, so the caller's stream stays ordered
@@ -422,15 +529,31 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
   const bool has_in = d.in_elems > 0, has_fr = d.frames > 0, has_st = d.heads > 0;
   if ((has_in && (!q || !k || !v || !out)) || (has_fr && (!gamma || !beta)) || (has_st && !state_out))
     return GDN_E_NULLPTR;
-  const size_t need = gdn_workspace_bytes(shape, in_dtype);
-  if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0))
-    return GDN_E_WORKSPACE;
   const size_t inb = d.in_elems * dsize(in_dtype), outb = d.in_elems * dsize(out_dtype);
   const size_t stb = d.state_elems * 4, gb = (size_t)d.frames * 4;
-  const Range outs[] = {{out, outb}, {state_out, stb}, {workspace, need}};
   const Range ins[] = {{q, inb}, {k, inb}, {v, inb}, {gamma, gb}, {beta, gb},
                        {state_in, state_in ? stb : 0}};
-  if (!aliasing_ok(outs, 3, ins, 6, state_out, state_in)) return GDN_E_ALIAS;
+  // The workspace a path needs, checked on the host before anything is
+  // enqueued: null, too small, misaligned or overlapping another buffer.
+  auto workspace_ok = [&](size_t need, int* status) {
+    if (need > 0 && (!workspace || workspace_bytes < need || (uintptr_t)workspace % 256 != 0)) {
+      *status = GDN_E_WORKSPACE;
+      return false;
+    }
+    const Range outs[] = {{out, outb}, {state_out, stb}, {workspace, need}};
+    if (!aliasing_ok(outs, 3, ins, 6, state_out, state_in)) {
+      *status = GDN_E_ALIAS;
+      return false;
+    }
+    return true;
+  };
+  const bool ob = out_dtype == GDN_BF16;
+  const int planned = !has_in ? GDN_PATH_PLAIN
+                      : fused_path(in_dtype, d) ? GDN_PATH_FUSED
+                      : fast_path(in_dtype, d.D) ? GDN_PATH_MFMA
+                                                 : GDN_PATH_PLAIN;
+  // the planned path's workspace first, with no device query
+  if (!workspace_ok(has_in ? path_workspace(d, in_dtype, planned) : 0, &st)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!has_in) {
     // no heads: nothing to do; no frames: state_out = state_in; frames
@@ -442,44 +565,42 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
       return gdn::launch_decay(gamma, state_in, state_out, d.heads, d.T, (int)d.D, s);
     }));
   }
-
-  // Workspace: G_t, U_t, M_t of every frame (packed forms on the MFMA path).
-  const size_t slot = round256(d.map_elems * sizeof(float));
   char* ws = static_cast<char*>(workspace);
-  void* G = ws;
-  float* U = reinterpret_cast<float*>(ws + slot);
-  void* M_all = ws + 2 * slot;
-  const bool ob = out_dtype == GDN_BF16;
-  if (fused_path(in_dtype, d)) {
-    DevInfo* di = nullptr;
-    if (dev_info(&di) != hipSuccess) return GDN_E_HIP;
-    const int grid = di->fused_grid[ob ? 1 : 0];
-    if (grid > 0 && (size_t)gdn::fused_workspace_bytes(d.heads) <= workspace_bytes)
+  if (planned == GDN_PATH_FUSED) {
+    bool queried = true;
+    const int grid = fused_launch(in_dtype, d, ob, &queried);
+    if (!queried) return GDN_E_HIP;
+    if (grid > 0)
       return hip_status(timed(rec, s, 1, [&] {
         return gdn::launch_fused(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                  static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out,
                                  workspace, d.heads, d.T, (int)d.S, ks, spin_limit().load(), grid, s);
       }));
-    // this device cannot host the fused kernel: the three-kernel schedule
+    // this device cannot host the fused kernel: the three-kernel schedule,
+    // whose workspace is larger
+    if (!workspace_ok(path_workspace(d, in_dtype, GDN_PATH_MFMA), &st)) return st;
   }
   if (fast_path(in_dtype, d.D))
     return hip_status(run_mfma(d, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                static_cast<const uint16_t*>(v), gamma, beta, state_in, ks, out, ob, state_out,
-                               G, U, M_all, s, rec));
+                               ws, s, rec));
+  // plain path: G_t, U_t, M_t of every frame in float32
+  const size_t slot = round256(d.map_elems * sizeof(float));
+  float* G = reinterpret_cast<float*>(ws);
+  float* U = reinterpret_cast<float*>(ws + slot);
+  float* M_all = reinterpret_cast<float*>(ws + 2 * slot);
   hipError_t e;
   if ((e = timed(rec, s, 0, [&] {
-         return gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, static_cast<float*>(G), U, d.frames,
-                                          (int)d.S, (int)d.D, ks, s);
+         return gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, G, U, d.frames, (int)d.S, (int)d.D, ks, s);
        })) != hipSuccess)
     return GDN_E_HIP;
   if ((e = timed(rec, s, 1, [&] {
-         return gdn::launch_state_generic(static_cast<float*>(G), U, gamma, beta, state_in,
-                                          static_cast<float*>(M_all), state_out, d.heads, d.T, (int)d.D, s);
+         return gdn::launch_state_generic(G, U, gamma, beta, state_in, M_all, state_out, d.heads, d.T, (int)d.D, s);
        })) != hipSuccess)
     return GDN_E_HIP;
   if ((e = timed(rec, s, 2, [&] {
-         return gdn::launch_output_generic(q, in_dtype == GDN_BF16, static_cast<float*>(M_all), out, ob,
-                                           d.frames, (int)d.S, (int)d.D, s);
+         return gdn::launch_output_generic(q, in_dtype == GDN_BF16, M_all, out, ob, d.frames, (int)d.S, (int)d.D,
+                                           s);
        })) != hipSuccess)
     return GDN_E_HIP;
   return GDN_OK;
@@ -558,6 +679,7 @@ const char* gdn_status_str(int s) {
     case GDN_E_ALIAS: return "an output overlaps another buffer";
     case GDN_E_HIP: return "HIP runtime or launch error";
     case GDN_E_VALUE: return "an argument value is outside its domain (a non-finite key scale)";
+    case GDN_E_TIMEOUT: return "an internal wait of the fused kernel ran out; frames not produced are NaN";
     default: return "unknown status";
   }
 }
@@ -572,14 +694,40 @@ int gdn_path(const gdn_shape* shape, int in_dtype) {
   Dims d;
   if (!valid_dtype(in_dtype) || check_shape(shape, true, &d, true) != GDN_OK) return -1;
   if (d.in_elems == 0) return GDN_PATH_PLAIN;
-  if (fused_path(in_dtype, d)) return GDN_PATH_FUSED;
+  if (fused_path(in_dtype, d)) {
+    bool queried = true;
+    // float32 and bf16 outputs have the same launch size
+    if (fused_launch(in_dtype, d, false, &queried) > 0 || !queried) return GDN_PATH_FUSED;
+  }
   return fast_path(in_dtype, d.D) ? GDN_PATH_MFMA : GDN_PATH_PLAIN;
+}
+
+size_t gdn_path_workspace_bytes(const gdn_shape* shape, int in_dtype, int path) {
+  Dims d;
+  if (!valid_dtype(in_dtype) || check_shape(shape, true, &d, true) != GDN_OK) return SIZE_MAX;
+  return path_workspace(d, in_dtype, path);
 }
 
 size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype) {
   Dims d;
   if (!valid_dtype(in_dtype) || check_shape(shape, true, &d, true) != GDN_OK || d.in_elems == 0) return 0;
-  return 3 * round256(d.map_elems * sizeof(float));
+  if (fused_path(in_dtype, d)) {
+    bool queried = true;
+    const int grid = fused_launch(in_dtype, d, false, &queried);
+    // no device to ask: what the three-kernel schedule needs, the larger
+    return path_workspace(d, in_dtype, grid > 0 ? GDN_PATH_FUSED : GDN_PATH_MFMA);
+  }
+  return path_workspace(d, in_dtype, fast_path(in_dtype, d.D) ? GDN_PATH_MFMA : GDN_PATH_PLAIN);
+}
+
+int gdn_fused_status(const void* workspace, void* stream) {
+  if (!workspace) return GDN_E_NULLPTR;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, gdn::fused_error_word(workspace), sizeof word, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return GDN_E_HIP;
+  return word == 0 ? GDN_OK : GDN_E_TIMEOUT;
 }
 
 int gdn_build_maps(const gdn_shape* shape, int in_dtype, const void* k, const void* v, float* G,
@@ -597,7 +745,7 @@ int gdn_build_maps(const gdn_shape* shape, int in_dtype, const void* k, const vo
   if (fast_path(in_dtype, d.D))
     return hip_status(gdn::launch_build_bf16_d128(static_cast<const uint16_t*>(k),
                                                   static_cast<const uint16_t*>(v), G, false, U,
-                                                  d.heads, d.T, 0, d.T, (int)d.S, 1.f, s));
+                                                  d.heads, d.T, 0, d.T, (int)d.S, 1.f, {d.T, 0}, s));
   return hip_status(gdn::launch_build_generic(k, v, in_dtype == GDN_BF16, G, U, d.frames, (int)d.S,
                                               (int)d.D, 1.f, s));
 }
@@ -616,7 +764,7 @@ int gdn_state_pass(const gdn_shape* shape, const float* G, const float* U, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.D == 128)
     return hip_status(gdn::launch_state_d128(G, false, U, gamma, beta, state_in, M_all, true, state_out,
-                                             d.heads, d.T, 0, d.T, s));
+                                             d.heads, d.T, 0, d.T, {d.T, 0}, s));
   return hip_status(gdn::launch_state_generic(G, U, gamma, beta, state_in, M_all, state_out,
                                               d.heads, d.T, (int)d.D, s));
 }
@@ -636,7 +784,7 @@ int gdn_output(const gdn_shape* shape, int in_dtype, int out_dtype, const void* 
   const bool ob = out_dtype == GDN_BF16;
   if (fast_path(in_dtype, d.D))
     return hip_status(gdn::launch_output_bf16_d128(static_cast<const uint16_t*>(q), M_all, false, out,
-                                                   ob, d.heads, d.T, 0, d.T, (int)d.S, s));
+                                                   ob, d.heads, d.T, 0, d.T, (int)d.S, {d.T, 0}, s));
   return hip_status(gdn::launch_output_generic(q, in_dtype == GDN_BF16, M_all, out, ob, d.frames,
                                                (int)d.S, (int)d.D, s));
 }

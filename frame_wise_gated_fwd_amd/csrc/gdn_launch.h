@@ -14,6 +14,14 @@ namespace gdn {
 // waves read them), which is what gdn_frame_fwd uses.  Every per-frame array
 // is laid out [head][T]; each launcher covers frames [t0, t1) of every head.
 //
+// Where a launch's per-frame maps live: frame t of head h is map slot
+// h * T + (t - t0) of the map buffers (T: frames per head in the buffers).
+// The whole-sequence layout is {T, 0}; the segmented schedule keeps one
+// segment per buffer, {frames per segment, first frame of the segment}.
+struct MapLayout {
+  int64_t T, t0;
+};
+
 // Launches of at most this many frames (heads x frames in the range) take the
 // small-launch variants: a build that splits each frame's output rows over
 // four workgroups and an output that splits each frame's tokens over several
@@ -25,7 +33,7 @@ constexpr int64_t kFewFrames = 128;
 // where G may be null.
 hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
                                   float* U, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, float ks,
-                                  hipStream_t st);
+                                  MapLayout ml, hipStream_t st);
 // State pass over frames [t0, t1) for `heads` heads, starting from state_in
 // (M_{t0-1}; null = zero) and leaving M_{t1-1} in state_out (which may equal
 // state_in).  G and U are both packed or both float32; M_out (may be null)
@@ -33,11 +41,11 @@ hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G,
 hipError_t launch_state_d128(const void* G, bool packed, const float* U, const float* gamma,
                              const float* beta, const float* state_in, void* M_out, bool m_f32,
                              float* state_out, int64_t heads, int64_t T, int64_t t0, int64_t t1,
-                             hipStream_t st);
+                             MapLayout ml, hipStream_t st);
 // O_t = Q_t M_t^T for frames [t0, t1); out_bf16 selects the output dtype.
 hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool packed_m, void* out,
                                    bool out_bf16, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
-                                   hipStream_t st);
+                                   MapLayout ml, hipStream_t st);
 
 // Token parts per frame for a launch of `frames` frames (1 unless the launch
 // is small); the parts only split the tokens, not any reduction.
@@ -52,6 +60,12 @@ int token_split(int64_t frames, int S);
 // before an internal wait gives up (0: the default, a few seconds).
 int64_t fused_workspace_bytes(int64_t heads);
 int fused_grid(bool out_bf16, int num_cus);
+// One-time check that a launch of `grid` workgroups is dealt evenly over
+// eight XCDs with XCC_IDs 0-7 (a probe kernel on the null stream; waits).
+hipError_t fused_topology_ok(int grid, bool* ok);
+// Device address of the error word of the last fused launch that used this
+// workspace (0: every wait completed).
+const void* fused_error_word(const void* workspace);
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                         const float* beta, const float* state_in, void* out, bool out_bf16,
                         float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks,

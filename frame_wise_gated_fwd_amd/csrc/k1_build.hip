@@ -25,12 +25,14 @@ namespace {
 template <bool kPacked>
 __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, void* __restrict__ Gout,
-    float* __restrict__ Uout, int S, int64_t T, int t0, int nt, float ks) {
+    float* __restrict__ Uout, int S, int64_t T, int t0, int nt, float ks, int64_t mT, int64_t mt0) {
   constexpr int D = 128;
   __shared__ u32x4 lds[build_lds_bytes<kPacked>() / 16];
-  // workgroup i: frame t0 + i % nt of head i / nt (frames are [head][T])
-  const int64_t f = (int64_t)(blockIdx.x / nt) * T + t0 + blockIdx.x % nt;
-  const int64_t in_off = f * (int64_t)S * D, mat_off = f * (int64_t)D * D;
+  // workgroup i: frame t0 + i % nt of head i / nt (frames are [head][T];
+  // its maps go to slot head * mT + t - mt0)
+  const int64_t head = blockIdx.x / nt, t = t0 + blockIdx.x % nt;
+  const int64_t f = head * T + t, mf = head * mT + t - mt0;
+  const int64_t in_off = f * (int64_t)S * D, mat_off = mf * (int64_t)D * D;
   build_frame<kPacked>(K + in_off, V + in_off, S, lds, Gout ? static_cast<char*>(Gout) + mat_off * 4 : nullptr,
                        Uout + mat_off, ks);
 }
@@ -46,15 +48,16 @@ constexpr int kSplitDepth = 4;  // token iterations in flight per wave
 
 __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128_split(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, char* __restrict__ Gout,
-    float* __restrict__ Uout, int S, int64_t T, int t0, int nt, int frames, float ks) {
+    float* __restrict__ Uout, int S, int64_t T, int t0, int nt, int frames, float ks, int64_t mT, int64_t mt0) {
   constexpr int D = 128;
   __shared__ u32x4 frag[4][8][kWave];
   // workgroup b = 32 (i / 8) + 8 q + i % 8 holds part q of frame i
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
   const int q = slot & (kParts - 1), i = (slot / kParts) * 8 + xcd;
   if (i >= frames) return;
-  const int64_t f = (int64_t)(i / nt) * T + t0 + i % nt;
-  const int64_t in_off = f * (int64_t)S * D, mat_off = f * (int64_t)D * D * 4;
+  const int64_t head = i / nt, t = t0 + i % nt;
+  const int64_t f = head * T + t, mf = head * mT + t - mt0;
+  const int64_t in_off = f * (int64_t)S * D, mat_off = mf * (int64_t)D * D * 4;
   build_frame_part<kSplitDepth>(K + in_off, V + in_off, S, frag, Gout + mat_off,
                                 reinterpret_cast<char*>(Uout) + mat_off, ks, q);
 }
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128_split(
 
 hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G, bool packed_out,
                                   float* U, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S, float ks,
-                                  hipStream_t st) {
+                                  MapLayout ml, hipStream_t st) {
   const int nt = (int)(t1 - t0);
   const dim3 grid((unsigned)(heads * nt));
   if (packed_out && !G) return hipErrorInvalidValue;  // the packed form always writes G
@@ -71,11 +74,13 @@ hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G,
     const int frames = (int)(heads * nt);
     const dim3 split((unsigned)((frames + 7) / 8 * 8 * kParts));
     hipLaunchKernelGGL(k1_build_bf16_d128_split, split, dim3(256), 0, st, k, v, static_cast<char*>(G), U, S, T,
-                       (int)t0, nt, frames, ks);
+                       (int)t0, nt, frames, ks, ml.T, ml.t0);
   } else if (packed_out)
-    hipLaunchKernelGGL(k1_build_bf16_d128<true>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks);
+    hipLaunchKernelGGL(k1_build_bf16_d128<true>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks, ml.T,
+                       ml.t0);
   else
-    hipLaunchKernelGGL(k1_build_bf16_d128<false>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks);
+    hipLaunchKernelGGL(k1_build_bf16_d128<false>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks, ml.T,
+                       ml.t0);
   return hipGetLastError();
 }
 

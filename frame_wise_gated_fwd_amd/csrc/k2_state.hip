@@ -52,7 +52,7 @@ template <int kRows, bool kPacked, int kDepth, bool kMf32>
 __global__ __launch_bounds__(256, 1) void k2_state_d128(
     const void* __restrict__ Gin, const float* __restrict__ U, const float* __restrict__ gamma,
     const float* __restrict__ beta, const float* state_in, void* __restrict__ Mout,
-    float* state_out, int heads, int T, int tb, int te) {
+    float* state_out, int heads, int T, int tb, int te, int64_t mT, int64_t mt0) {
   constexpr int kRB = kRows / 16;     // 16-row blocks of M per workgroup
   constexpr int kParts = D / kRows;   // workgroups per head
   // [buffer][hi|lo][row][col]
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256, 1) void k2_state_d128(
   auto load_frame = [&](auto jc, int t) {
     constexpr int j = decltype(jc)::value;
     if (t >= te) return;
-    const int64_t fo = ((int64_t)head * T + t) * D * D;
+    const int64_t fo = ((int64_t)head * mT + t - mt0) * D * D;  // map slot of frame t
     if constexpr (kPacked) {
       const char* Gp = static_cast<const char*>(Gin) + fo * 4;
       const char* Up = reinterpret_cast<const char*>(U) + fo * 4;
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void k2_state_d128(
     put_lds(buf ^ 1);
 
     if (Mout) {
-      const int64_t fo = ((int64_t)head * T + t) * D * D;
+      const int64_t fo = ((int64_t)head * mT + t - mt0) * D * D;  // map slot of frame t
       if constexpr (!kMf32) {
         char* Mp = static_cast<char*>(Mout) + fo * 4;
 #pragma unroll
@@ -287,12 +287,12 @@ __global__ __launch_bounds__(256, 1) void k2_state_d128(
 template <int kRows, bool kPacked, int kDepth, bool kMf32>
 hipError_t launch_rows(const void* G, const float* U, const float* gamma, const float* beta,
                        const float* state_in, void* M_out, float* state_out, int64_t heads,
-                       int64_t T, int64_t tb, int64_t te, hipStream_t st) {
+                       int64_t T, int64_t tb, int64_t te, MapLayout ml, hipStream_t st) {
   // Workgroup ids are grouped so that the workgroups of a head share id % 8.
   const int64_t groups = (heads + 7) / 8;
   const unsigned grid = (unsigned)(groups * 8 * (D / kRows));
   hipLaunchKernelGGL((k2_state_d128<kRows, kPacked, kDepth, kMf32>), dim3(grid), dim3(256), 0, st, G, U, gamma,
-                     beta, state_in, M_out, state_out, (int)heads, (int)T, (int)tb, (int)te);
+                     beta, state_in, M_out, state_out, (int)heads, (int)T, (int)tb, (int)te, ml.T, ml.t0);
   return hipGetLastError();
 }
 
@@ -301,12 +301,12 @@ hipError_t launch_rows(const void* G, const float* U, const float* gamma, const 
 hipError_t launch_state_d128(const void* G, bool packed, const float* U, const float* gamma,
                              const float* beta, const float* state_in, void* M_out, bool m_f32,
                              float* state_out, int64_t heads, int64_t T, int64_t tb, int64_t te,
-                             hipStream_t st) {
+                             MapLayout ml, hipStream_t st) {
   if (!packed)
-    return launch_rows<32, false, 2, true>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, st);
+    return launch_rows<32, false, 2, true>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, ml, st);
   if (m_f32)
-    return launch_rows<16, true, 2, true>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, st);
-  return launch_rows<16, true, 2, false>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, st);
+    return launch_rows<16, true, 2, true>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, ml, st);
+  return launch_rows<16, true, 2, false>(G, U, gamma, beta, state_in, M_out, state_out, heads, T, tb, te, ml, st);
 }
 
 }  // namespace gdn

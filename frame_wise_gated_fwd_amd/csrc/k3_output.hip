@@ -21,16 +21,17 @@ namespace {
 template <bool kPackedM, bool kOutBf16, bool kTransM = false>
 __global__ __launch_bounds__(256, 2) void k3_output_bf16_d128(
     const uint16_t* __restrict__ Q, const void* __restrict__ M_all, void* __restrict__ out, int S,
-    int64_t T, int t0, int nt, int nsplit) {
+    int64_t T, int t0, int nt, int nsplit, int64_t mT, int64_t mt0) {
   constexpr int D = 128;
   __shared__ uint16_t Ml[2][D][kOutLdsW];
   // workgroup i: token part i % nsplit of frame t0 + j % nt of head j / nt,
   // j = i / nsplit (frames are [head][T])
   const int j = blockIdx.x / nsplit, part = blockIdx.x % nsplit;
-  const int64_t f = (int64_t)(j / nt) * T + t0 + j % nt;
+  const int64_t head = j / nt, t = t0 + j % nt;
+  const int64_t f = head * T + t, mf = head * mT + t - mt0;  // M_t in slot mf
   const int s0 = (int)((int64_t)part * S / nsplit), s1 = (int)((int64_t)(part + 1) * S / nsplit);
   const int64_t in_off = (f * (int64_t)S + s0) * D;
-  const char* Mt = static_cast<const char*>(M_all) + f * packed::kFrameBytes;
+  const char* Mt = static_cast<const char*>(M_all) + mf * packed::kFrameBytes;
   void* Of = static_cast<char*>(out) + in_off * (kOutBf16 ? 2 : 4);
   output_frame<kPackedM, kOutBf16, 1, kTransM>(Q + in_off, Mt, Of, s1 - s0, Ml, [] {});
 }
@@ -45,17 +46,17 @@ int token_split(int64_t frames, int S) {
 
 template <bool kPackedM>
 hipError_t launch_out(const uint16_t* q, const void* M_all, void* out, bool out_bf16, int64_t heads,
-                      int64_t T, int64_t t0, int64_t t1, int S, hipStream_t st) {
+                      int64_t T, int64_t t0, int64_t t1, int S, MapLayout ml, hipStream_t st) {
   const int nt = (int)(t1 - t0);
   const int64_t frames = heads * nt;
   const int nsplit = token_split(frames, S);
   const dim3 grid((unsigned)(frames * nsplit));
   if (out_bf16)
     hipLaunchKernelGGL((k3_output_bf16_d128<kPackedM, true>), grid, dim3(256), 0, st, q, M_all, out, S, T,
-                       (int)t0, nt, nsplit);
+                       (int)t0, nt, nsplit, ml.T, ml.t0);
   else
     hipLaunchKernelGGL((k3_output_bf16_d128<kPackedM, false>), grid, dim3(256), 0, st, q, M_all, out, S, T,
-                       (int)t0, nt, nsplit);
+                       (int)t0, nt, nsplit, ml.T, ml.t0);
   return hipGetLastError();
 }
 
@@ -66,7 +67,7 @@ hipError_t launch_out_bwd(const uint16_t* q, const float* M_all, float* out, int
   const int64_t frames = heads * nt;
   const int nsplit = token_split(frames, S);
   hipLaunchKernelGGL((k3_output_bf16_d128<false, false, kTransM>), dim3((unsigned)(frames * nsplit)), dim3(256),
-                     0, st, q, M_all, out, S, T, (int)t0, nt, nsplit);
+                     0, st, q, M_all, out, S, T, (int)t0, nt, nsplit, T, int64_t{0});
   return hipGetLastError();
 }
 
@@ -78,9 +79,9 @@ hipError_t launch_output_bwd_d128(const uint16_t* q, const float* M_all, float* 
 
 hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool packed_m, void* out,
                                    bool out_bf16, int64_t heads, int64_t T, int64_t t0, int64_t t1, int S,
-                                   hipStream_t st) {
-  return packed_m ? launch_out<true>(q, M_all, out, out_bf16, heads, T, t0, t1, S, st)
-                 : launch_out<false>(q, M_all, out, out_bf16, heads, T, t0, t1, S, st);
+                                   MapLayout ml, hipStream_t st) {
+  return packed_m ? launch_out<true>(q, M_all, out, out_bf16, heads, T, t0, t1, S, ml, st)
+                 : launch_out<false>(q, M_all, out, out_bf16, heads, T, t0, t1, S, ml, st);
 }
 
 }  // namespace gdn

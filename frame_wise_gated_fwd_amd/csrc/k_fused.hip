@@ -53,6 +53,7 @@
 #include "gdn_launch.h"
 #include "gdn_packed.h"
 
+#include <cstddef>
 #include <type_traits>
 #include <utility>
 
@@ -136,7 +137,7 @@ template <int kSleep, typename Pred>
 __device__ bool spin_until(Ctrl* ctrl, uint32_t limit, Pred pred) {
   for (uint32_t i = 0; i < limit; ++i) {
     if (pred()) return true;
-    if ((i & 63) == 63 && flag_load(&ctrl->error)) return false;
+    if ((i & 63) == 0 && flag_load(&ctrl->error)) return false;
     __builtin_amdgcn_s_sleep(kSleep);
   }
   if ((threadIdx.x & 63) == 0) __hip_atomic_store(&ctrl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -494,6 +495,17 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
 // ---------------------------------------------------------------------------
 // workers
 // ---------------------------------------------------------------------------
+// NaN into rows [0, n) of an output frame (float32 or bf16 elements): what
+// an output item writes when its wait gave up, so that every frame of `out`
+// is either exact or NaN after a failed launch.
+template <bool kOutBf16>
+__device__ void nan_fill(void* of, int n) {
+  constexpr uint32_t w = kOutBf16 ? 0x7fc07fc0u : 0x7fc00000u;
+  constexpr int kRowChunks = D * (kOutBf16 ? 2 : 4) / 16;
+  u32x4* dst = static_cast<u32x4*>(of);
+  for (int c = threadIdx.x; c < n * kRowChunks; c += blockDim.x) dst[c] = (u32x4){w, w, w, w};
+}
+
 template <bool kOutBf16, int kRows>
 __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int xcd, int nh) {
   constexpr int kParts = D / kRows;
@@ -525,7 +537,7 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
         if (tid == 0) bcast[3] = ready;
       }
       __syncthreads();
-      if (!bcast[3]) return;
+      if (!bcast[3]) continue;  // a wait gave up: drain the queue, building nothing
       char* gp = ring + (int64_t)(2 * (it.t % kWG)) * packed::kFrameBytes;
       float* up = reinterpret_cast<float*>(ring + (int64_t)(2 * (it.t % kWG) + 1) * packed::kFrameBytes);
       // two token iterations loaded ahead (one measured no faster); the
@@ -548,13 +560,16 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
         if (tid == 0) bcast[3] = ready;
       }
       __syncthreads();
-      if (!bcast[3]) return;
-      invalidate_l1();
-      const char* mp = ring + (int64_t)(2 * kWG + it.t % kWM) * packed::kFrameBytes;
       const int s0 = it.part < 0 ? 0 : it.part * S / kTailParts;
       const int s1 = it.part < 0 ? S : (it.part + 1) * S / kTailParts;
       const int64_t tok = fr * S + s0;
       void* of = static_cast<char*>(a.out) + tok * D * (kOutBf16 ? 2 : 4);
+      if (!bcast[3]) {  // a wait gave up: this frame's M_t never came
+        nan_fill<kOutBf16>(of, s1 - s0);
+        continue;
+      }
+      invalidate_l1();
+      const char* mp = ring + (int64_t)(2 * kWG + it.t % kWM) * packed::kFrameBytes;
       if (s1 > s0)
         output_frame<true, kOutBf16>(a.q + tok * D, mp, of, s1 - s0, lds.out, [&] {
           if (tid == 0) flag_store(fl + kFlagOutDone + it.t % kWM, (uint32_t)(it.t + 1));
@@ -585,6 +600,12 @@ __global__ __launch_bounds__(256, 2) void k_fused(Args a) {
   } else {
     worker_role<kOutBf16, kRows>(a, lds, bcast, (int)xcd, nh);
   }
+}
+
+// Workgroups per XCC_ID value seen by one launch (the topology probe).
+__device__ uint32_t g_xcc_seen[16];
+__global__ void k_xcc_probe() {
+  if (threadIdx.x == 0) atomicAdd(&g_xcc_seen[xcc_id()], 1u);
 }
 
 __global__ void k_fused_init(uint32_t* words, int n) {
@@ -622,6 +643,30 @@ int fused_grid(bool out_bf16, int num_cus) {
   // every XCD needs its state-pass workgroups and at least as many workers
   const int grid = pc * num_cus;
   return grid / kXcd >= 2 * kMaxHeadsPerXcd * (D / kFusedRows) ? grid : 0;
+}
+
+// The fused kernel hands every head to the XCD whose XCC_ID is h % 8 and
+// counts on each XCD holding an equal share of the launch.  A one-time probe
+// with the fused launch's size checks that the device deals workgroups that
+// way: exactly ids 0-7, grid / 8 workgroups each (e.g. not a partition with
+// fewer XCDs, whose ids would leave heads without workgroups).  Runs on the
+// null stream and waits for it.
+hipError_t fused_topology_ok(int grid, bool* ok) {
+  *ok = false;
+  uint32_t seen[16] = {};
+  hipError_t e;
+  if ((e = hipMemcpyToSymbol(HIP_SYMBOL(g_xcc_seen), seen, sizeof seen)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_xcc_probe, dim3((unsigned)grid), dim3(64), 0, nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = hipMemcpyFromSymbol(seen, HIP_SYMBOL(g_xcc_seen), sizeof seen)) != hipSuccess) return e;
+  bool even = grid % kXcd == 0;
+  for (int i = 0; i < 16; ++i) even = even && seen[i] == (i < kXcd ? (uint32_t)(grid / kXcd) : 0u);
+  *ok = even;
+  return hipSuccess;
+}
+
+const void* fused_error_word(const void* workspace) {
+  return static_cast<const char*>(workspace) + offsetof(Ctrl, error);
 }
 
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,

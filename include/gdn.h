@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
   GDN_OK = 0,
@@ -75,7 +75,9 @@ typedef enum {
   GDN_E_WORKSPACE = 5,      /* workspace NULL or smaller than required        */
   GDN_E_ALIAS = 6,          /* an output overlaps another buffer              */
   GDN_E_HIP = 7,            /* a HIP runtime call or launch failed            */
-  GDN_E_VALUE = 8           /* an argument value is outside its domain        */
+  GDN_E_VALUE = 8,          /* an argument value is outside its domain        */
+  GDN_E_TIMEOUT = 9         /* gdn_fused_status: an internal wait of the fused
+                               kernel ran out (see gdn_set_spin_limit)        */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -109,19 +111,34 @@ int gdn_set_fused(int enabled);
  * which one of its internal waits gives up, for launches made after it
  * returns, process-wide; 0 restores the default (2^22 polls: seconds for a
  * wait of the state pass, about 20 s for one of the other workgroups, which
- * poll less often).  Returns the previous setting.  Every wait is bounded so that a
- * failure ends the kernel instead of hanging it: the first wait that runs
- * out sets an error word, every other wait then gives up at once, and the
- * state pass writes NaN to the rows of state_out it had not finished (out
- * is then unspecified).  A tiny limit makes the waits run out on purpose,
- * with every workgroup still exiting normally.  The next launch starts from
- * a fresh control block.
+ * poll less often).  Returns the previous setting.  Every wait is bounded so
+ * that a failure ends the kernel instead of hanging it: the first wait that
+ * runs out sets an error word in the workspace's control block, every other
+ * wait then gives up at once, the state pass writes NaN to the rows of
+ * state_out it had not finished, and every frame of `out` that was not
+ * produced is written as NaN (each frame is then either exact or NaN).
+ * gdn_fused_status reports the error word.  A tiny limit makes the waits run
+ * out on purpose, with every workgroup still exiting normally.  The next
+ * launch starts from a fresh control block.
  */
 unsigned gdn_set_spin_limit(unsigned polls);
 
 /*
- * Which implementation gdn_frame_fwd uses for this shape and input dtype (a
- * pure function of its arguments):
+ * Outcome of the last fused-path gdn_frame_fwd call (GDN_PATH_FUSED) that
+ * used `workspace`: waits for `stream` (the call's stream), then reads the
+ * error word of the workspace's control block.  GDN_OK: every internal wait
+ * completed and the results are valid; GDN_E_TIMEOUT: a wait ran out (which
+ * cannot happen while every workgroup of the launch is resident), and the
+ * frames of `out` and rows of state_out not produced are NaN.  GDN_E_NULLPTR
+ * for a NULL workspace; GDN_E_HIP if the copy or the wait fails.  Call it
+ * before the workspace is reused; after a call on another path the result
+ * is meaningless.
+ */
+int gdn_fused_status(const void* workspace, void* stream);
+
+/*
+ * Which implementation gdn_frame_fwd uses for this shape and input dtype on
+ * the current device, with the current gdn_set_fused setting:
  *   GDN_PATH_MFMA   bf16, D == 128, T <= 32 (and longer sequences when the
  *                   fused kernel below is unavailable): three bf16-MFMA
  *                   kernels (build, state pass, output) with the per-frame
@@ -144,11 +161,17 @@ unsigned gdn_set_spin_limit(unsigned polls);
  *                   head runs on one XCD and its per-frame G_t, U_t, M_t
  *                   pass between compute units through that XCD's L2 instead
  *                   of HBM.  Every internal wait is bounded: if one runs out
- *                   (it cannot while all workgroups are resident), state_out
- *                   of the affected heads is NaN.  On a device that cannot
- *                   launch it cooperatively at full size, or while the
- *                   fused kernel is disabled (gdn_set_fused), these shapes
- *                   take GDN_PATH_MFMA;
+ *                   (it cannot while all workgroups are resident), the
+ *                   frames and state rows not produced are NaN and
+ *                   gdn_fused_status reports it.  On a device that cannot
+ *                   launch it cooperatively at full size or does not deal
+ *                   workgroups evenly over eight XCDs with ids 0-7 (checked
+ *                   once per device by a probe kernel on the null stream
+ *                   that waits for it, at the first call or query that
+ *                   needs the fact), or while the fused kernel is disabled
+ *                   (gdn_set_fused), these shapes take GDN_PATH_MFMA.  When
+ *                   no device can be queried (no GPU), gdn_path reports the
+ *                   path of a device that hosts the fused kernel;
  *   GDN_PATH_PLAIN  every other supported case: three float32 kernels on
  *                   `stream`; also empty shapes (one small float32 kernel
  *                   or none, see "Empty shapes" above);
@@ -160,12 +183,30 @@ enum { GDN_PATH_PLAIN = 0, GDN_PATH_MFMA = 1, GDN_PATH_FUSED = 2 };
 int gdn_path(const gdn_shape* shape, int in_dtype);
 
 /*
- * Workspace bytes gdn_frame_fwd needs for this shape and input dtype, a pure
- * function of its arguments; 0 when the shape is invalid or empty: G_t, U_t
- * and M_t of every frame, 3 * B*H*T*D*D*4 bytes, each of the three rounded
- * up to 256.
+ * Workspace bytes a gdn_frame_fwd call with this shape and input dtype needs
+ * on the current device: those of gdn_path's path (gdn_path_workspace_bytes),
+ * or, when no device can be queried, of GDN_PATH_MFMA, which is at least as
+ * large as GDN_PATH_FUSED's.  0 when the shape is invalid or empty.
  */
 size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype);
+
+/*
+ * Workspace bytes of one path for this shape and input dtype, a pure
+ * function of its arguments (per frame map, D*D*4 bytes = 64 KiB at D = 128):
+ *   GDN_PATH_FUSED  a control block and per-head flags, then rings of G_t,
+ *                   U_t and M_t slots for at most 16 heads at a time: a few
+ *                   MiB per head whatever T is (71 MiB for 16 heads);
+ *   GDN_PATH_MFMA   the maps of at most three segments at once: with n =
+ *                   ceil(T / 64) segments of at most c = ceil(T / n) frames,
+ *                   3 * min(n, 3) buffers of B*H*c maps, each rounded up to
+ *                   256 bytes (549 MiB for B*H = 16, T = 961);
+ *   GDN_PATH_PLAIN  G_t, U_t and M_t of every frame in float32:
+ *                   3 * B*H*T*D*D*4 bytes, each third rounded up to 256.
+ * 0 for an empty shape; SIZE_MAX for an invalid shape or dtype, an unknown
+ * path, or a path that cannot take the shape (fused: bf16, D == 128 and
+ * T > 32 only; MFMA: bf16 and D == 128 only).
+ */
+size_t gdn_path_workspace_bytes(const gdn_shape* shape, int in_dtype, int path);
 
 /*
  * The whole forward: O and M_T from q, k, v, gamma, beta and M_0.
@@ -174,7 +215,8 @@ size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype);
  *   state_in   M_0 or NULL for zeros.   state_out: M_T (may equal state_in).
  *   workspace  at least gdn_workspace_bytes(shape, in_dtype) bytes of device
  *              memory, 256-byte aligned; its contents on return are
- *              unspecified.
+ *              unspecified.  A call checks it against the need of the path
+ *              it takes: GDN_E_WORKSPACE when NULL, misaligned or smaller.
  */
 int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype,
                   const void* q, const void* k, const void* v,

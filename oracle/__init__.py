@@ -5,6 +5,5 @@ baseline may import this package.  It shares no code with the GPU library.
 """
 from .gdn_ref import (as_f64, frame_maps, transition, gdn_head, gdn_head_residual,
                       build_maps_head, state_pass_head, output_head, compose,
-                      state_pass_chunked, tokenwise_gated_delta, gdn_forward,
-                      gdn_forward_streamed, flops_per_head_frame)
+                      state_pass_chunked, tokenwise_gated_delta, flops_per_head_frame)
 from .gdn_bwd import gdn_head_backward, scalar_loss

@@ -38,7 +38,7 @@ widened exactly, so the oracle sees the same numbers the GPU sees.
 """
 from __future__ import annotations
 
-from typing import Optional, Sequence, Tuple
+from typing import Tuple
 
 import numpy as np
 
@@ -77,21 +77,29 @@ def gdn_head(q, k, v, gamma, beta, state=None, keep_states: bool = False, out_fr
 
     q, k, v: [T, S, D]; gamma, beta: [T]; state: [D, D] or None (zeros).
     Returns (O [T, S, D], M_T [D, D]) and, with keep_states, also the stacked
-    states M_1..M_T [T, D, D].  With out_frames (a list of frame indices) only
-    those frames' outputs are formed and O is [len(out_frames), S, D]."""
+    states M_1..M_T [T, D, D].  With out_frames (a sequence of frame indices,
+    in any order, repeats allowed) row i of O is the output of frame
+    out_frames[i], and O is [len(out_frames), S, D]; an index outside
+    0 .. T-1 raises ValueError."""
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     gamma, beta = as_f64(gamma), as_f64(beta)
     T, S, D = q.shape
     M = np.zeros((D, D)) if state is None else as_f64(state).copy()
-    wanted = list(range(T)) if out_frames is None else list(out_frames)
-    slot = {t: i for i, t in enumerate(wanted)}
+    wanted = list(range(T)) if out_frames is None else [int(t) for t in out_frames]
+    if any(t < 0 or t >= T for t in wanted):
+        raise ValueError(f"out_frames must lie in 0 .. {T - 1}")
+    rows = {}  # frame -> every position of O that wants it
+    for i, t in enumerate(wanted):
+        rows.setdefault(t, []).append(i)
     O = np.empty((len(wanted), S, D))
     states = np.empty((T, D, D)) if keep_states else None
     for t in range(T):
         G, U = frame_maps(k[t], v[t])
         M = M @ transition(G, gamma[t], beta[t]) + beta[t] * U
-        if t in slot:
-            O[slot[t]] = q[t] @ M.T
+        if t in rows:
+            O_t = q[t] @ M.T
+            for i in rows[t]:
+                O[i] = O_t
         if keep_states:
             states[t] = M
     if keep_states:
@@ -210,40 +218,6 @@ def tokenwise_gated_delta(q, k, v, alpha, beta, state=None):
         St = St @ (alpha[n] * (np.eye(D) - beta[n] * kk)) + beta[n] * np.outer(v[n], k[n])
         o[n] = St @ q[n]
     return o, St
-
-
-# ----------------------------------------------------------------------------
-# whole tensors
-# ----------------------------------------------------------------------------
-def gdn_forward(q, k, v, gamma, beta, state=None):
-    """All heads: q, k, v [B, H, T, S, D]; gamma, beta [B, H, T];
-    state [B, H, D, D] or None.  Returns O [B, H, T, S, D], M_T [B, H, D, D]."""
-    q = np.asarray(q)
-    B, H, T, S, D = q.shape
-    O = np.empty((B, H, T, S, D))
-    MT = np.empty((B, H, D, D))
-    for b in range(B):
-        for h in range(H):
-            st = None if state is None else state[b, h]
-            O[b, h], MT[b, h] = gdn_head(q[b, h], k[b, h], v[b, h], gamma[b, h], beta[b, h], st)
-    return O, MT
-
-
-def gdn_forward_streamed(q, k, v, gamma, beta, state, chunks: Sequence[int]):
-    """Same as gdn_forward, as successive calls over frame ranges carrying the
-    state (the chunk-causal rollout of the zhichai.net page, Stage 4)."""
-    q = np.asarray(q)
-    B, H, T, S, D = q.shape
-    assert sum(chunks) == T
-    O = np.empty((B, H, T, S, D))
-    st = state
-    t0 = 0
-    for c in chunks:
-        sl = slice(t0, t0 + c)
-        O[:, :, sl], st = gdn_forward(q[:, :, sl], k[:, :, sl], v[:, :, sl],
-                                      gamma[:, :, sl], beta[:, :, sl], st)
-        t0 += c
-    return O, st
 
 
 # ----------------------------------------------------------------------------

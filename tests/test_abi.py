@@ -11,7 +11,7 @@ from frame_wise_gated_fwd_amd._lib import SIGNATURES, Shape
 
 HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "gdn.h")
 
-OK, NULLPTR, SHAPE, DTYPE, UNSUP_D, WORKSPACE, ALIAS, HIP, VALUE = range(9)
+OK, NULLPTR, SHAPE, DTYPE, UNSUP_D, WORKSPACE, ALIAS, HIP, VALUE, TIMEOUT = range(10)
 F32, BF16 = 0, 1
 
 
@@ -29,12 +29,12 @@ def test_library_exports_every_declared_symbol():
     L = F.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.gdn_abi_version() == 2
+    assert L.gdn_abi_version() == 3
 
 
 def test_status_strings():
     L = F.lib()
-    for s in range(9):
+    for s in range(10):
         assert L.gdn_status_str(s) != b"unknown status"
     assert L.gdn_status_str(99) == b"unknown status"
 
@@ -76,17 +76,66 @@ def test_fused_switch_selects_path():
         L.gdn_set_fused(prev)
 
 
+def _mfma_bytes(B, H, T, D=128):
+    """The three-kernel schedule: three map buffers per segment slot, at
+    most three segments of at most ceil(T / n) frames held at once."""
+    n = -(-T // 64)
+    cap = -(-T // n)
+    slot = (B * H * cap * D * D * 4 + 255) // 256 * 256
+    return 3 * min(n, 3) * slot
+
+
+SIZE_MAX = ctypes.c_size_t(-1).value
+FUSED, MFMA, PLAIN = 2, 1, 0
+
+
 def test_workspace_bytes():
+    """With no device to ask, gdn_workspace_bytes gives the three-kernel
+    schedule's size (an upper bound for the fused path's)."""
     L = F.lib()
-    for s in (_shape(4, 16, 961, 880, 128), _shape(1, 16, 961, 880, 128)):
-        per = s.B * s.H * s.T * 128 * 128 * 4
-        assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == 3 * ((per + 255) // 256 * 256)
+    for s in (_shape(4, 16, 961, 880, 128), _shape(1, 16, 961, 880, 128), _shape(1, 3, 33, 40, 128)):
+        assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == _mfma_bytes(s.B, s.H, s.T)
+        assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) >= \
+            L.gdn_path_workspace_bytes(ctypes.byref(s), BF16, FUSED)
+    # the 60 s workload: 16 segments of at most 61 frames, three held at once
+    assert L.gdn_workspace_bytes(ctypes.byref(_shape(1, 16, 961, 880, 128)), BF16) == 9 * 16 * 61 * 65536
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(T=0)), BF16) == 0
     assert L.gdn_workspace_bytes(ctypes.byref(_shape(D=100)), BF16) == 0
     assert L.gdn_workspace_bytes(ctypes.byref(_shape()), 7) == 0
     s = _shape(1, 3, 5, 7, 48)
     assert L.gdn_workspace_bytes(ctypes.byref(s), F32) == 3 * ((15 * 48 * 48 * 4 + 255) // 256 * 256)
     assert L.gdn_workspace_bytes(None, BF16) == 0
+
+
+def test_path_workspace_bytes():
+    L = F.lib()
+    pw = lambda s, path, dt=BF16: L.gdn_path_workspace_bytes(ctypes.byref(s), dt, path)
+    # fused: rings for at most 16 heads at a time, independent of T and S
+    f16 = pw(_shape(1, 16, 961, 880, 128), FUSED)
+    assert 16 * 3 * 65536 <= f16 <= 80 << 20
+    assert pw(_shape(4, 16, 961, 880, 128), FUSED) == f16
+    assert pw(_shape(1, 16, 4000, 40, 128), FUSED) == f16
+    f1, f2 = pw(_shape(1, 1, 961, 880, 128), FUSED), pw(_shape(1, 2, 961, 880, 128), FUSED)
+    assert f16 - f1 == 15 * (f2 - f1)  # per-head rings
+    # the three-kernel schedule: at most three segments of maps
+    for B, H, T in ((1, 16, 961), (4, 16, 961), (1, 2, 64), (1, 2, 65), (1, 2, 200), (3, 5, 1)):
+        assert pw(_shape(B, H, T, 880, 128), MFMA) == _mfma_bytes(B, H, T)
+    # the plain path: every frame's maps
+    s = _shape(1, 3, 5, 7, 48)
+    assert pw(s, PLAIN, F32) == 3 * ((15 * 48 * 48 * 4 + 255) // 256 * 256)
+    # paths that cannot take the shape, and bad arguments
+    assert pw(_shape(1, 16, 32, 880, 128), FUSED) == SIZE_MAX    # too short for the fused kernel
+    assert pw(_shape(1, 16, 961, 880, 64), FUSED) == SIZE_MAX    # D != 128
+    assert pw(_shape(1, 16, 961, 880, 128), FUSED, F32) == SIZE_MAX
+    assert pw(_shape(1, 16, 961, 880, 128), MFMA, F32) == SIZE_MAX
+    assert pw(_shape(1, 16, 961, 880, 128), 7) == SIZE_MAX
+    assert pw(_shape(D=100), PLAIN) == SIZE_MAX
+    assert L.gdn_path_workspace_bytes(None, BF16, FUSED) == SIZE_MAX
+    assert pw(_shape(T=0), FUSED) == 0 and pw(_shape(S=0), MFMA) == 0
+
+
+def test_fused_status_rejects_null_workspace():
+    assert F.lib().gdn_fused_status(None, None) == NULLPTR
 
 
 # Fake, never-dereferenced device addresses, far apart.

@@ -126,7 +126,7 @@ def test_output_stage(T, S, D, dt, odt):
 # ---------------------------------------------------------------------------
 # the whole forward on the seeded workloads
 # ---------------------------------------------------------------------------
-def _forward_parity(w: Workload, frames=None, heads=None, chunks=None):
+def _forward_parity(w: Workload, frames=None, heads=None, chunks=None, workspace=None):
     """Run the GPU forward on w (optionally streamed in `chunks`), compare O at
     `frames` (all when None) for `heads` (all when None) and the final state."""
     log(f"workload {w.name}: B={w.B} H={w.H} T={w.T} S={w.S} D={w.D} {w.in_dtype}"
@@ -147,18 +147,26 @@ def _forward_parity(w: Workload, frames=None, heads=None, chunks=None):
             t0 += c
         st = state
     else:
-        out, st = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+        out, st = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"], workspace=workspace)
     torch.cuda.synchronize()
     log("  GPU forward done")
     hs = heads or [(b, h) for b in range(w.B) for h in range(w.H)]
     ro, rs = RelL2(), RelL2()
+    worst_frame = worst_state = 0.0  # the largest relL2 of any one frame of any head, of any head's state
     for b, h, O, M in oracle_heads(w, hs, frames):
-        og = out[b, h] if frames is None else out[b, h, list(frames)]
-        ro.add(_to_np(og), O)
-        rs.add(_to_np(st[b, h]), M)
-    log(f"  relL2 O={ro.value:.3e} state={rs.value:.3e} (tol {w.tol:g}); max|dO|={ro.max_abs:.3e}")
+        og = _to_np(out[b, h] if frames is None else out[b, h, list(frames)])
+        ro.add(og, O)
+        sg = _to_np(st[b, h])
+        rs.add(sg, M)
+        for i in range(len(O)):
+            worst_frame = max(worst_frame, rel_l2(og[i], O[i]))
+        worst_state = max(worst_state, rel_l2(sg, M))
+    log(f"  relL2 O={ro.value:.3e} state={rs.value:.3e} (tol {w.tol:g}); max|dO|={ro.max_abs:.3e}; "
+        f"worst frame {worst_frame:.3e}, worst head state {worst_state:.3e}")
     assert np.isfinite(ro.value) and np.isfinite(rs.value)
     assert ro.value <= w.tol and rs.value <= w.tol
+    # every frame and every head's state on its own, not only the whole tensor
+    assert worst_frame <= w.tol and worst_state <= w.tol
     return out, st, x
 
 
@@ -171,7 +179,20 @@ def test_forward_clip5s_bf16():
 
 
 def test_forward_seq60s_full_size():
-    _forward_parity(SEQ_60S, frames=sample_frames(SEQ_60S.T, seed=3))
+    """The 60 s workload on the fused path with exactly the workspace the
+    library asks for (its rings, not the whole sequence's maps)."""
+    import ctypes
+    from frame_wise_gated_fwd_amd._lib import Shape, GDN_BF16, GDN_PATH_FUSED
+    w = SEQ_60S
+    shp = Shape(w.B, w.H, w.T, w.S, w.D)
+    L = F.lib()
+    assert L.gdn_path(ctypes.byref(shp), GDN_BF16) == GDN_PATH_FUSED
+    need = L.gdn_workspace_bytes(ctypes.byref(shp), GDN_BF16)
+    assert need == L.gdn_path_workspace_bytes(ctypes.byref(shp), GDN_BF16, GDN_PATH_FUSED)
+    assert need <= 80 << 20
+    log(f"  workspace {need / 2**20:.1f} MiB")
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    _forward_parity(w, frames=sample_frames(w.T, seed=3), workspace=ws)
 
 
 def test_forward_stream60s_matches_single_call():
@@ -184,10 +205,13 @@ def test_forward_stream60s_matches_single_call():
     assert torch.equal(st_s, st1)
 
 
-def test_forward_stress_b4_sampled():
+def test_forward_stress_b4_all_heads():
+    """All 64 heads' final states, and each head's output at 15 sampled
+    frames.  A launch covers the 16 heads of one batch element, head h on
+    XCD h % 8 in head slot h // 8, so every XCD and both slots are checked
+    in each of the four launches."""
     w = STRESS_B4
-    heads = [(0, 0), (1, 5), (2, 10), (3, 15), (3, 0), (0, 15)]
-    _forward_parity(w, frames=sample_frames(w.T, seed=5), heads=heads)
+    _forward_parity(w, frames=sample_frames(w.T, seed=5))
 
 
 # ---------------------------------------------------------------------------
@@ -202,13 +226,23 @@ def three_kernel_path():
 
 
 def test_segmented_forward_equals_stage_chain_bitwise(three_kernel_path):
-    """T = 140 runs as 3 overlapped segments on three streams; the stage entry
-    points run each kernel once over all frames on one stream, exchanging
-    float32 row-major maps.  Both feed the MFMAs the same bf16 hi/lo operands,
-    so the results agree bit for bit."""
-    w = CLIP_5S.with_(T=140, H=3, S=200, name="clip_t140_s200", state_std=0.02)
+    """T = 330 runs as 6 overlapped segments on three streams, their maps in
+    three workspace slots that each serve two segments (exactly the
+    workspace the library asks for); the stage entry points run each kernel
+    once over all frames on one stream, exchanging float32 row-major maps.
+    Both feed the MFMAs the same bf16 hi/lo operands, so the results agree
+    bit for bit."""
+    import ctypes
+    from frame_wise_gated_fwd_amd._lib import Shape, GDN_BF16, GDN_PATH_MFMA
+    w = CLIP_5S.with_(T=330, H=3, S=200, name="clip_t330_s200", state_std=0.02)
+    shp = Shape(w.B, w.H, w.T, w.S, w.D)
+    L = F.lib()
+    assert L.gdn_path(ctypes.byref(shp), GDN_BF16) == GDN_PATH_MFMA
+    need = L.gdn_workspace_bytes(ctypes.byref(shp), GDN_BF16)
+    assert need == 9 * 3 * 55 * 65536  # 6 segments of 55 frames, three held at once
     x = device_inputs(w, DEV)
-    out, st = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out, st = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"], workspace=ws)
     G, U = F.build_maps(x["k"], x["v"])
     M_all, st2 = F.state_pass(G, U, x["gamma"], x["beta"], x["state"])
     out2 = F.output(x["q"], M_all)
@@ -488,33 +522,44 @@ def test_empty_shapes(B, H, T, S, D, dt):
 
 def test_fused_kernel_wait_failure_ends_without_hang():
     """With a one-poll wait limit the fused kernel's waits run out on
-    purpose: the kernel still ends, every row of state_out is either NaN
-    (its state-pass workgroup gave up) or exact, and the next call, with the
-    default limit, starts from a fresh control block and is exact again."""
+    purpose: the kernel still ends, every row of state_out and every frame
+    of out is either exact or NaN (and some are NaN), gdn_fused_status
+    reports the timeout, and the next call, with the default limit, starts
+    from a fresh control block, is exact again and reports success."""
     import ctypes
     from frame_wise_gated_fwd_amd._lib import Shape
     w = Workload(name="fused_fail", B=1, H=16, T=100, S=64, D=128, in_dtype="bf16", seed=61,
                  gamma_range=(0.95, 1.0), beta_kind="sigmoid_normal", state_std=0.02)
     L = F.lib()
-    assert L.gdn_path(ctypes.byref(Shape(w.B, w.H, w.T, w.S, w.D)), 1) == 2
+    shp = Shape(w.B, w.H, w.T, w.S, w.D)
+    assert L.gdn_path(ctypes.byref(shp), 1) == 2
     x = device_inputs(w, DEV)
     args = (x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
-    ref_out, ref_st = F.frame_fwd(*args)
-    torch.cuda.synchronize()
+    ws = torch.empty(L.gdn_workspace_bytes(ctypes.byref(shp), 1), dtype=torch.uint8, device=DEV)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ws_ptr = ctypes.c_void_p(ws.data_ptr())
+    ref_out, ref_st = F.frame_fwd(*args, workspace=ws)
+    assert L.gdn_fused_status(ws_ptr, stream) == 0
     log("  one-poll waits")
     prev = L.gdn_set_spin_limit(1)
     try:
-        _, st = F.frame_fwd(*args)
-        torch.cuda.synchronize()
+        out, st = F.frame_fwd(*args, workspace=ws)
+        status = L.gdn_fused_status(ws_ptr, stream)
     finally:
         L.gdn_set_spin_limit(prev)
+    assert status == 9, status  # GDN_E_TIMEOUT
     nan_rows = torch.isnan(st).all(dim=-1)
     exact_rows = (st == ref_st).all(dim=-1)
-    log(f"  rows given up: {int(nan_rows.sum())} of {nan_rows.numel()}")
+    nan_frames = torch.isnan(out).flatten(3).all(dim=-1)
+    exact_frames = (out == ref_out).flatten(3).all(dim=-1)
+    log(f"  rows given up: {int(nan_rows.sum())} of {nan_rows.numel()}; "
+        f"frames given up: {int(nan_frames.sum())} of {nan_frames.numel()}")
     assert bool((nan_rows | exact_rows).all())
     assert bool(nan_rows.any())
-    out2, st2 = F.frame_fwd(*args)
-    torch.cuda.synchronize()
+    assert bool((nan_frames | exact_frames).all())
+    assert bool(nan_frames.any())
+    out2, st2 = F.frame_fwd(*args, workspace=ws)
+    assert L.gdn_fused_status(ws_ptr, stream) == 0
     assert torch.equal(out2, ref_out) and torch.equal(st2, ref_st)
 
 
