@@ -18,7 +18,7 @@ GDN_PATH_PLAIN, GDN_PATH_MFMA, GDN_PATH_FUSED = 0, 1, 2
 
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_E_NULLPTR", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE",
                 4: "GDN_E_UNSUPPORTED_D", 5: "GDN_E_WORKSPACE", 6: "GDN_E_ALIAS", 7: "GDN_E_HIP",
-                8: "GDN_E_VALUE", 9: "GDN_E_TIMEOUT"}
+                8: "GDN_E_VALUE", 9: "GDN_E_TIMEOUT", 10: "GDN_E_TOO_LARGE"}
 
 # Every symbol include/gdn.h declares, with (restype, argtypes).
 _vp, _cvp = ctypes.c_void_p, ctypes.c_void_p
@@ -43,6 +43,7 @@ SIGNATURES = {
     "gdn_fused_status": (_i, [_cvp, _vp]),
     "gdn_set_spin_limit": (ctypes.c_uint, [ctypes.c_uint]),
     "gdn_frame_fwd": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp]),
+    "gdn_frame_fwd_noalloc": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp]),
     "gdn_frame_fwd_ks": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _f, _vp, _vp, _vp, _sz, _vp]),
     "gdn_frame_fwd_timed": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp,
                                  ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),

@@ -661,6 +661,17 @@ int frame_bwd_impl(const gdn_shape* shape, int in_dtype, const void* q, const vo
 
 }  // namespace
 
+namespace gdn {
+// gdn_frame_fwd on a workspace the caller provides by other means (the
+// no-allocation entry point's scratch array).
+int frame_fwd_in(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k, const void* v,
+                 const float* gamma, const float* beta, const float* state_in, void* out, float* state_out,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, gamma, beta, state_in, 1.f, out, state_out, workspace,
+                        workspace_bytes, stream, nullptr);
+}
+}  // namespace gdn
+
 // ---------------------------------------------------------------------------
 // entry points
 // ---------------------------------------------------------------------------
@@ -680,6 +691,8 @@ const char* gdn_status_str(int s) {
     case GDN_E_HIP: return "HIP runtime or launch error";
     case GDN_E_VALUE: return "an argument value is outside its domain (a non-finite key scale)";
     case GDN_E_TIMEOUT: return "an internal wait of the fused kernel ran out; frames not produced are NaN";
+    case GDN_E_TOO_LARGE:
+      return "the call needs more scratch memory than gdn_frame_fwd_noalloc holds (GDN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

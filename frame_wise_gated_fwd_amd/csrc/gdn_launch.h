@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn.h"
+
 namespace gdn {
 
 // ---- MFMA path: bf16 inputs, D == 128 --------------------------------------
@@ -92,5 +94,11 @@ hipError_t launch_decay(const float* gamma, const float* state_in, float* state_
 // and d_state_in (may equal d_state_out; either state may be null = zero).
 hipError_t launch_decay_bwd(const float* gamma, const float* state_in, const float* d_state_out, float* dgamma,
                             float* dbeta, float* d_state_in, int64_t heads, int64_t T, int D, hipStream_t st);
+
+// ---- gdn_api.cpp ------------------------------------------------------------
+// gdn_frame_fwd's whole call on a caller-provided workspace (see gdn.h).
+int frame_fwd_in(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
+                 const void* v, const float* gamma, const float* beta, const float* state_in, void* out,
+                 float* state_out, void* workspace, size_t workspace_bytes, void* stream);
 
 }  // namespace gdn

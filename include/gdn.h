@@ -76,8 +76,10 @@ typedef enum {
   GDN_E_ALIAS = 6,          /* an output overlaps another buffer              */
   GDN_E_HIP = 7,            /* a HIP runtime call or launch failed            */
   GDN_E_VALUE = 8,          /* an argument value is outside its domain        */
-  GDN_E_TIMEOUT = 9         /* gdn_fused_status: an internal wait of the fused
+  GDN_E_TIMEOUT = 9,        /* gdn_fused_status: an internal wait of the fused
                                kernel ran out (see gdn_set_spin_limit)        */
+  GDN_E_TOO_LARGE = 10      /* gdn_frame_fwd_noalloc: the call needs more
+                               scratch than GDN_NOALLOC_SCRATCH_BYTES         */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -223,6 +225,30 @@ int gdn_frame_fwd(const gdn_shape* shape, int in_dtype, int out_dtype,
                   const float* gamma, const float* beta,
                   const float* state_in, void* out, float* state_out,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_frame_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: its kernels use a scratch array of
+ * GDN_NOALLOC_SCRATCH_BYTES compiled into the library, one copy per GPU,
+ * resident from the first call on that GPU until the process ends.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the caller still provides every input and output.  Shapes whose
+ * workspace (gdn_workspace_bytes) exceeds the array return GDN_E_TOO_LARGE
+ * before anything is enqueued: this covers every shape on the fused path
+ * (bf16, D == 128, T > 32, any B*H) and three-kernel calls of up to about
+ * 500 head-frames (16 heads x 32 frames).  Every call on a GPU shares that
+ * GPU's array and leaves its contents behind: calls that overlap on one GPU
+ * (concurrent streams, threads or processes sharing the library instance)
+ * race and give wrong results; serialise them.  The state the kernels need
+ * zeroed is cleared by a kernel at the start of each call.  Everything else
+ * as gdn_frame_fwd (no key scale; same results bit for bit).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (96u << 20)
+int gdn_frame_fwd_noalloc(const gdn_shape* shape, int in_dtype, int out_dtype,
+                          const void* q, const void* k, const void* v,
+                          const float* gamma, const float* beta,
+                          const float* state_in, void* out, float* state_out, void* stream);
 
 /*
  * gdn_frame_fwd with the key scaling fused into the build: the keys K_t are

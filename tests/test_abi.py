@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = F.lib()
-    for s in range(10):
+    for s in range(11):
         assert L.gdn_status_str(s) != b"unknown status"
     assert L.gdn_status_str(99) == b"unknown status"
 
@@ -132,6 +132,23 @@ def test_path_workspace_bytes():
     assert pw(_shape(D=100), PLAIN) == SIZE_MAX
     assert L.gdn_path_workspace_bytes(None, BF16, FUSED) == SIZE_MAX
     assert pw(_shape(T=0), FUSED) == 0 and pw(_shape(S=0), MFMA) == 0
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch_on_the_host():
+    """Three-kernel calls too large for the built-in scratch are refused
+    before any device is touched; invalid arguments are reported as by
+    gdn_frame_fwd."""
+    L = F.lib()
+
+    def na(shape, **kw):
+        a = dict(q=P[0], k=P[1], v=P[2], gamma=P[3], beta=P[4], state_in=None, out=P[5], state_out=P[6])
+        a.update(kw)
+        return L.gdn_frame_fwd_noalloc(ctypes.byref(shape) if shape else None, BF16, F32, a["q"], a["k"], a["v"],
+                                       a["gamma"], a["beta"], a["state_in"], a["out"], a["state_out"], None)
+    assert na(_shape(4, 16, 32, 16, 128)) == 10   # 3 x 2048 maps of 64 KiB: GDN_E_TOO_LARGE
+    assert na(None) == NULLPTR
+    assert na(_shape(D=100)) == UNSUP_D
+    assert na(_shape(B=0), q=None, k=None, v=None, gamma=None, beta=None, out=None, state_out=None) == OK
 
 
 def test_fused_status_rejects_null_workspace():
