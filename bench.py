@@ -6,7 +6,10 @@ A step is one gdn_frame_fwd call over the whole 60 s, 720p workload
 float32 state and output) with every input already resident in HBM.
 value = frame-steps/s = B*T / seconds per step.  One JSON line is printed;
 besides the forward it carries the backward pass (gdn_frame_bwd) on the same
-workload, the same frames as streamed calls, and single-frame latency.
+workload, the same frames as streamed calls, single-frame latency, the gated
+call (gates from activations), the 5 s clip and B = 4 stress workloads with
+sampled parity, the softmax attention block with sinks and a local window,
+and the host it ran on.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --copy-calibration     # plain copy of a known size, for counters
@@ -344,6 +347,201 @@ def copy_calibration(gib=1.0, reps=5):
                       "GBps_read_plus_write": 2 * n * 4 / ms / 1e6}), flush=True)
 
 
+def host_info():
+    """CPU model and ROCm / HIP versions of the machine the line was measured on."""
+    import torch
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                rocm = f.read().strip()
+                break
+        except OSError:
+            continue
+    return {"cpu_model": cpu, "host_cores": len(os.sched_getaffinity(0)), "rocm": rocm,
+            "hip_runtime": getattr(torch.version, "hip", None), "torch": torch.__version__,
+            "gpu": torch.cuda.get_device_name(0)}
+
+
+def _oracle_config_head(args):
+    """Oracle output at the sampled frames and final state of one head of a
+    workload, beside the GPU's (relative L2 per frame and for the state)."""
+    w, b, h, frames, o_gpu, m_gpu = args
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from synth import head_inputs
+    with threadpool_limits(1):
+        d = head_inputs(w, b, h)
+        O, M = oracle.gdn_head(d["q"], d["k"], d["v"], d["gamma"], d["beta"], d["state"], out_frames=frames)
+    per_frame = [float(np.linalg.norm(o_gpu[i] - O[i]) / np.linalg.norm(O[i])) for i in range(len(frames))]
+    return max(per_frame), float(np.linalg.norm(m_gpu - M) / np.linalg.norm(M))
+
+
+def config_leg(w, L, dev, stream, steps, heads, frames, workers):
+    """One more workload through gdn_frame_fwd: ms per call, frame-steps/s,
+    HBM fraction on its algorithmic bytes, and the worst per-frame and
+    per-head-state relative L2 against the oracle on sampled heads."""
+    import torch
+    from concurrent.futures import ProcessPoolExecutor
+    from frame_wise_gated_fwd_amd._lib import Shape, check, GDN_BF16, GDN_F32
+    B, H, T, S, D = w.B, w.H, w.T, w.S, w.D
+    t0 = time.perf_counter()
+    x = device_inputs(w, dev)
+    log(f"  {w.name}: inputs on device in {time.perf_counter() - t0:.1f} s")
+    shp = Shape(B, H, T, S, D)
+    out = torch.empty((B, H, T, S, D), dtype=torch.float32, device=dev)
+    st_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    wsb = L.gdn_workspace_bytes(ctypes.byref(shp), GDN_BF16)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    def call():
+        check(L.gdn_frame_fwd(ctypes.byref(shp), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]), P(x["v"]), P(x["gamma"]),
+                              P(x["beta"]), P(x["state"]), P(out), P(st_out), P(ws), wsb, stream), "gdn_frame_fwd")
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = per_head_frame_bytes(S, D)["step"] * B * H * T
+    res = {"workload": w.name, "B": B, "H": H, "T": T, "S": S, "D": D, "ms": round(ms, 4), "steps": steps,
+           "frame_steps_per_s": round(B * T / (ms * 1e-3), 1), "algorithmic_bytes": alg,
+           "GBps": round(alg / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "path": {1: "three kernels", 2: "fused"}.get(L.gdn_path(ctypes.byref(shp), GDN_BF16), "plain")}
+    idx = np.asarray(frames)
+    jobs = [(w, b, h, list(frames), out[b, h, idx].cpu().numpy().astype(np.float64),
+             st_out[b, h].cpu().numpy().astype(np.float64)) for b, h in heads]
+    with ProcessPoolExecutor(max_workers=min(workers, len(jobs))) as ex:
+        par = list(ex.map(_oracle_config_head, jobs))
+    res["parity"] = {"heads": len(heads), "frames": len(frames), "max_frame_out_relL2": round(max(p[0] for p in par), 9),
+                     "max_head_state_relL2": round(max(p[1] for p in par), 9), "tolerance": w.tol}
+    del x, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def _oracle_attn_head(args):
+    w, b, h, frames, o_gpu, l_gpu = args
+    from threadpoolctl import threadpool_limits
+    from oracle.attn_ref import Layout, attn_head
+    from synth import attn_head_inputs
+    with threadpool_limits(1):
+        d = attn_head_inputs(w, b, h)
+        O, lse = attn_head(d["q"], d["k"], d["v"], Layout(w.sink, w.first_chunk, w.chunk, w.window),
+                           out_frames=frames)
+    return (max(float(np.linalg.norm(o_gpu[i] - O[i]) / np.linalg.norm(O[i])) for i in range(len(frames))),
+            max(float(np.linalg.norm(l_gpu[i] - lse[i]) / np.linalg.norm(lse[i])) for i in range(len(frames))))
+
+
+def attention_leg(L, dev, stream, steps, workers):
+    """The softmax attention block with sinks and a local window on the 60 s
+    token layout (gdn_attn_fwd): ms, TFLOP/s against the bf16 MFMA peak (the
+    dense count; the weights' hi/lo split executes 1.5x the MFMA work), and
+    the oracle on 4 sampled frames of every head."""
+    import torch
+    from concurrent.futures import ProcessPoolExecutor
+    from frame_wise_gated_fwd_amd._lib import Shape, AttnLayout, check, GDN_BF16
+    from synth import ATTN_60S as w, attn_head_inputs
+    from oracle.attn_ref import Layout, attn_flops
+    B, H, T, S, D = w.B, w.H, w.T, w.S, w.D
+    x = {key: torch.empty((B, H, T, S, D), dtype=torch.bfloat16, device=dev) for key in "qkv"}
+    for b in range(B):
+        for h in range(H):
+            d = attn_head_inputs(w, b, h)
+            for key in "qkv":
+                x[key][b, h].copy_(torch.from_numpy(d[key].view(np.int16)).view(torch.bfloat16))
+    out = torch.empty((B, H, T, S, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, T, S), dtype=torch.float32, device=dev)
+    shp, lay = Shape(B, H, T, S, D), AttnLayout(w.sink, w.first_chunk, w.chunk, w.window)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def call():
+        check(L.gdn_attn_fwd(ctypes.byref(shp), GDN_BF16, ctypes.byref(lay), P(x["q"]), P(x["k"]), P(x["v"]), P(out),
+                             P(lse), stream), "gdn_attn_fwd")
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = attn_flops(T, S, D, Layout(w.sink, w.first_chunk, w.chunk, w.window)) * B * H
+    frames = [0, 5, 480, 960]
+    jobs = [(w, b, h, frames, out[b, h, frames].cpu().numpy().astype(np.float64),
+             lse[b, h, frames].cpu().numpy().astype(np.float64)) for b in range(B) for h in range(H)]
+    with ProcessPoolExecutor(max_workers=min(workers, len(jobs))) as ex:
+        par = list(ex.map(_oracle_attn_head, jobs))
+    tf = fl / (ms * 1e-3) / 1e12
+    res = {"workload": w.name, "layout": {"sink": w.sink, "first_chunk": w.first_chunk, "chunk": w.chunk,
+                                          "window": w.window},
+           "ms": round(ms, 3), "steps": steps, "dense_TFLOP": round(fl / 1e12, 3), "TFLOPs": round(tf, 1),
+           "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "executed_mfma_frac": round(1.5 * tf / BF16_PEAK_TFLOPS, 4),
+           "parity": {"heads": len(jobs), "frames": len(frames),
+                      "max_frame_out_relL2": round(max(p[0] for p in par), 9),
+                      "max_frame_lse_relL2": round(max(p[1] for p in par), 9), "tolerance": w.tol}}
+    del x, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def gated_leg(x, L, w, dev, stream, steps):
+    """gdn_frame_fwd_gated on the 60 s tensors: the gates from per-token
+    pre-activations (seeded, N(-2, 1) and N(0, 2) in float32) and the key
+    scale applied in the build, timed like the headline call (the keys are
+    already scaled, so only the time is used)."""
+    import torch
+    from frame_wise_gated_fwd_amd._lib import Shape, check, GDN_BF16, GDN_F32
+    B, H, T, S, D = w.B, w.H, w.T, w.S, w.D
+    gen = torch.Generator(device=dev).manual_seed(77)
+    ga = torch.randn((B, H, T, S), generator=gen, device=dev) - 2.0
+    gb = torch.randn((B, H, T, S), generator=gen, device=dev) * 2.0
+    A_log = torch.zeros(H, device=dev)
+    bias = torch.zeros(H, device=dev)
+    out = torch.empty((B, H, T, S, D), dtype=torch.float32, device=dev)
+    st = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    gam, bet = torch.empty((B, H, T), device=dev), torch.empty((B, H, T), device=dev)
+    shp = Shape(B, H, T, S, D)
+    wsb = L.gdn_workspace_bytes(ctypes.byref(shp), GDN_BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    ks = 1.0 / math.sqrt(D * S)
+
+    def call():
+        check(L.gdn_frame_fwd_gated(ctypes.byref(shp), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]), P(x["v"]), P(ga),
+                                    P(gb), P(A_log), P(bias), P(x["state"]), ks, P(out), P(st), P(gam), P(bet),
+                                    P(ws), wsb, stream), "gdn_frame_fwd_gated")
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = per_head_frame_bytes(S, D)["step"] * B * H * T + 2 * B * H * T * S * 4
+    del ga, gb, out, ws
+    return {"ms": round(ms, 4), "frame_steps_per_s": round(B * T / (ms * 1e-3), 1), "algorithmic_bytes": alg,
+            "GBps": round(alg / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,6 +556,9 @@ def main():
                     help="skip the streamed-calls and single-frame latency measurements")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--backward-steps", type=int, default=5)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 5 s clip and B = 4 stress workloads")
+    ap.add_argument("--no-attention", action="store_true", help="skip the softmax attention block")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -510,6 +711,33 @@ def main():
         key_scale_call = {"ms": round(ks_ms, 4), "frame_steps_per_s": round(B * T / (ks_ms * 1e-3), 1)}
         log(f"key-scale call: {key_scale_call}")
 
+    gated = None
+    if not args.no_extras:
+        log("gated call (gates from activations, key scale in the build)")
+        gated = gated_leg(x, L, w, dev, stream, args.steps)
+        log(f"gated: {gated}")
+
+    configs = None
+    attention = None
+    workers = min(default_workers(), 16)
+    if not args.no_configs:
+        from synth import CLIP_5S, STRESS_B4
+        configs = []
+        log("5 s clip workload")
+        configs.append(config_leg(CLIP_5S, L, dev, stream, max(args.steps, 20),
+                                  [(0, h) for h in range(CLIP_5S.H)], [0, 1, 40, 79, 80], workers))
+        log(f"  {configs[-1]}")
+        log("B = 4 stress workload")
+        # 16 heads: head h of batch element h % 4, so every XCD and both head
+        # slots of each launch are among them; 8 frames each
+        configs.append(config_leg(STRESS_B4, L, dev, stream, max(3, args.steps // 4),
+                                  [(h % 4, h) for h in range(16)], [0, 1, 240, 480, 720, 958, 959, 960], workers))
+        log(f"  {configs[-1]}")
+    if not args.no_attention:
+        log("softmax attention block (sinks + local window)")
+        attention = attention_leg(L, dev, stream, 3, workers)
+        log(f"  {attention}")
+
     cpu = None
     if not args.no_cpu_baseline:
         workers = min(default_workers(), B * H)
@@ -556,6 +784,10 @@ def main():
         "key_scale_call": key_scale_call,
         "streamed_calls": streamed,
         "t1_call": t1,
+        "gated_call": gated,
+        "other_configs": configs,
+        "attention": attention,
+        "host": host_info(),
     }
     print(json.dumps(res), flush=True)
 

@@ -1,4 +1,5 @@
-"""ctypes loader for libgdn.so (the C ABI declared in include/gdn.h).
+"""ctypes loader for libgdn.so (the C ABI declared in include/gdn.h and
+include/gdn_attn.h).
 
 The library is built in-tree by frame_wise_gated_fwd_amd.build.  Loading
 fails loudly when it is missing: there is no fallback implementation.
@@ -32,6 +33,12 @@ class Shape(ctypes.Structure):
 
 _PS = ctypes.POINTER(Shape)
 
+
+class AttnLayout(ctypes.Structure):
+    """gdn_attn_layout (include/gdn_attn.h)."""
+    _fields_ = [("sink", ctypes.c_int64), ("first_chunk", ctypes.c_int64), ("chunk", ctypes.c_int64),
+                ("window", ctypes.c_int64)]
+
 SIGNATURES = {
     "gdn_abi_version": (_i, []),
     "gdn_status_str": (ctypes.c_char_p, [_i]),
@@ -44,6 +51,8 @@ SIGNATURES = {
     "gdn_set_spin_limit": (ctypes.c_uint, [ctypes.c_uint]),
     "gdn_frame_fwd": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp]),
     "gdn_frame_fwd_noalloc": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp]),
+    "gdn_frame_fwd_gated": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _f, _vp, _vp, _vp,
+                                 _vp, _vp, _sz, _vp]),
     "gdn_frame_fwd_ks": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _f, _vp, _vp, _vp, _sz, _vp]),
     "gdn_frame_fwd_timed": (_i, [_PS, _i, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp, _sz, _vp,
                                  ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]),
@@ -52,6 +61,7 @@ SIGNATURES = {
                            _vp, _vp, _sz, _vp]),
     "gdn_frame_bwd_ks": (_i, [_PS, _i, _cvp, _cvp, _cvp, _cvp, _cvp, _cvp, _f, _cvp, _cvp, _vp, _vp, _vp, _vp,
                               _vp, _vp, _vp, _sz, _vp]),
+    "gdn_attn_fwd": (_i, [_PS, _i, ctypes.POINTER(AttnLayout), _cvp, _cvp, _cvp, _vp, _vp, _vp]),
     "gdn_build_maps": (_i, [_PS, _i, _cvp, _cvp, _vp, _vp, _vp]),
     "gdn_state_pass": (_i, [_PS, _cvp, _cvp, _cvp, _cvp, _cvp, _vp, _vp, _vp]),
     "gdn_output": (_i, [_PS, _i, _i, _cvp, _cvp, _vp, _vp]),

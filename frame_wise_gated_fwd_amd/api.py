@@ -112,6 +112,44 @@ def frame_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Te
     return out, state_out
 
 
+def frame_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate_a: torch.Tensor, gate_b: torch.Tensor,
+                    A_log: torch.Tensor, dt_bias: torch.Tensor, state: Optional[torch.Tensor] = None,
+                    key_scale: float = 1.0, out_dtype: torch.dtype = torch.float32, *,
+                    workspace: Optional[torch.Tensor] = None):
+    """Frame-wise GDN forward with its gates computed from activations
+    (gdn_frame_fwd_gated): gamma_t = exp(-exp(A_log[h]) * softplus(mean_s
+    gate_a + dt_bias[h])), beta_t = sigmoid(mean_s gate_b), keys multiplied
+    by key_scale.  gate_a, gate_b: [B, H, T, S] f32; A_log, dt_bias: [H] f32.
+    Returns (out, state_out, gamma [B, H, T], beta [B, H, T])."""
+    shp = shape_of(q)
+    B, H, T, S, D = q.shape
+    dev = q.device
+    _need(q, "q", (B, H, T, S, D), None, dev)
+    _need(k, "k", (B, H, T, S, D), q.dtype, dev)
+    _need(v, "v", (B, H, T, S, D), q.dtype, dev)
+    _need(gate_a, "gate_a", (B, H, T, S), torch.float32, dev)
+    _need(gate_b, "gate_b", (B, H, T, S), torch.float32, dev)
+    _need(A_log, "A_log", (H,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H,), torch.float32, dev)
+    if state is not None:
+        _need(state, "state", (B, H, D, D), torch.float32, dev)
+    out = torch.empty((B, H, T, S, D), dtype=out_dtype, device=dev)
+    state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    gamma = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    beta = torch.empty_like(gamma)
+    L = lib()
+    in_code = _dtype_code(q.dtype)
+    wsb = int(L.gdn_workspace_bytes(ctypes.byref(shp), in_code))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = L.gdn_frame_fwd_gated(ctypes.byref(shp), in_code, _dtype_code(out_dtype), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(gate_a), _ptr(gate_b), _ptr(A_log), _ptr(dt_bias), _ptr(state),
+                               float(key_scale), _ptr(out), _ptr(state_out), _ptr(gamma), _ptr(beta),
+                               _ptr(workspace), workspace.numel(), _stream(dev))
+    check(st, "gdn_frame_fwd_gated")
+    return out, state_out, gamma, beta
+
+
 def frame_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor,
               d_out: torch.Tensor, state: Optional[torch.Tensor] = None,
               d_state_out: Optional[torch.Tensor] = None, *,
@@ -200,3 +238,32 @@ def output(q: torch.Tensor, M_all: torch.Tensor, out_dtype: torch.dtype = torch.
                           _ptr(M_all), _ptr(out), _stream(dev))
     check(st, "gdn_output")
     return out
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sink: int, first_chunk: int, chunk: int,
+             window: int, *, out: Optional[torch.Tensor] = None,
+             lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """Softmax attention with attention sinks and a local temporal window
+    (gdn_attn_fwd, include/gdn_attn.h).
+
+    q, k, v: [B, H, T, S, 128] bf16.  A query of generation chunk c (chunk 0:
+    the first `first_chunk` frames, then `chunk` frames each) sees the tokens
+    of chunks c - window + 1 .. c and of the first `sink` frames up to chunk c.
+    Returns (out [B, H, T, S, 128] f32, lse [B, H, T, S] f32 or None)."""
+    shp = shape_of(q)
+    B, H, T, S, D = q.shape
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, (B, H, T, S, D), torch.bfloat16, dev)
+    if out is None:
+        out = torch.empty((B, H, T, S, D), dtype=torch.float32, device=dev)
+    _need(out, "out", (B, H, T, S, D), torch.float32, dev)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, T, S), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (B, H, T, S), torch.float32, dev)
+    lay = _lib.AttnLayout(int(sink), int(first_chunk), int(chunk), int(window))
+    st = lib().gdn_attn_fwd(ctypes.byref(shp), GDN_BF16, ctypes.byref(lay), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                            _ptr(lse), _stream(dev))
+    check(st, "gdn_attn_fwd")
+    return out, lse

@@ -6,6 +6,7 @@
 // the side streams of the segmented schedule, fused-kernel launch sizes);
 // the two schedules of the MFMA path; the extern "C" entry points.
 #include "gdn.h"
+#include "gdn_attn.h"
 
 #include <hip/hip_runtime.h>
 
@@ -516,10 +517,18 @@ hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStre
   return err == hipSuccess ? reduce() : err;
 }
 
+// Gates computed from activations (gdn_frame_fwd_gated): per-token
+// pre-activations a, b [B, H, T, S], per-head A_log, dt_bias [H]; the gates
+// are written to gamma, beta [B, H, T].
+struct GateIn {
+  const float *a, *b, *A_log, *dt_bias;
+  float *gamma, *beta;
+};
+
 int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
                    const void* v, const float* gamma, const float* beta, const float* state_in, float ks,
                    void* out, float* state_out, void* workspace, size_t workspace_bytes,
-                   void* stream, Recorder* rec) {
+                   void* stream, Recorder* rec, const GateIn* gate = nullptr) {
   Dims d;
   int st = check_shape(shape, true, &d, true);
   if (st != GDN_OK) return st;
@@ -527,12 +536,24 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GDN_E_DTYPE;
   // a pointer may be null exactly when its tensor has no elements
   const bool has_in = d.in_elems > 0, has_fr = d.frames > 0, has_st = d.heads > 0;
+  if (gate) {
+    // a frame's gates average its tokens: frames need tokens
+    if (has_fr && d.S == 0) return GDN_E_SHAPE;
+    if (has_fr && (!gate->a || !gate->b || !gate->A_log || !gate->dt_bias || !gate->gamma || !gate->beta))
+      return GDN_E_NULLPTR;
+    gamma = gate->gamma;
+    beta = gate->beta;
+  }
   if ((has_in && (!q || !k || !v || !out)) || (has_fr && (!gamma || !beta)) || (has_st && !state_out))
     return GDN_E_NULLPTR;
   const size_t inb = d.in_elems * dsize(in_dtype), outb = d.in_elems * dsize(out_dtype);
   const size_t stb = d.state_elems * 4, gb = (size_t)d.frames * 4;
-  const Range ins[] = {{q, inb}, {k, inb}, {v, inb}, {gamma, gb}, {beta, gb},
-                       {state_in, state_in ? stb : 0}};
+  const size_t gab = (size_t)d.frames * (size_t)d.S * 4, parb = (size_t)d.H * 4;
+  // inputs (gamma, beta only when given) and, with gates, their inputs
+  const Range ins[] = {{q, inb}, {k, inb}, {v, inb}, {gate ? nullptr : gamma, gb}, {gate ? nullptr : beta, gb},
+                       {state_in, state_in ? stb : 0}, {gate ? gate->a : nullptr, gab},
+                       {gate ? gate->b : nullptr, gab}, {gate ? gate->A_log : nullptr, parb},
+                       {gate ? gate->dt_bias : nullptr, parb}};
   // The workspace a path needs, checked on the host before anything is
   // enqueued: null, too small, misaligned or overlapping another buffer.
   auto workspace_ok = [&](size_t need, int* status) {
@@ -540,8 +561,9 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
       *status = GDN_E_WORKSPACE;
       return false;
     }
-    const Range outs[] = {{out, outb}, {state_out, stb}, {workspace, need}};
-    if (!aliasing_ok(outs, 3, ins, 6, state_out, state_in)) {
+    const Range outs[] = {{out, outb}, {state_out, stb}, {workspace, need}, {gate ? gamma : nullptr, gb},
+                          {gate ? beta : nullptr, gb}};
+    if (!aliasing_ok(outs, 5, ins, 10, state_out, state_in)) {
       *status = GDN_E_ALIAS;
       return false;
     }
@@ -557,7 +579,8 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!has_in) {
     // no heads: nothing to do; no frames: state_out = state_in; frames
-    // without tokens: G_t = U_t = 0, each step only decays the state
+    // without tokens: G_t = U_t = 0, each step only decays the state (not
+    // with computed gates, refused above)
     if (!has_st) return GDN_OK;
     if (!has_fr)
       return hip_status(timed(rec, s, 1, [&] { return gdn::launch_state_fill(state_in, state_out, d.state_elems, s); }));
@@ -570,16 +593,25 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
     bool queried = true;
     const int grid = fused_launch(in_dtype, d, ob, &queried);
     if (!queried) return GDN_E_HIP;
-    if (grid > 0)
+    if (grid > 0) {
+      const gdn::FusedGates fg{gate ? gate->a : nullptr, gate ? gate->b : nullptr, gate ? gate->A_log : nullptr,
+                               gate ? gate->dt_bias : nullptr, (int)d.H};
       return hip_status(timed(rec, s, 1, [&] {
         return gdn::launch_fused(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                  static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out,
-                                 workspace, d.heads, d.T, (int)d.S, ks, spin_limit().load(), grid, s);
+                                 workspace, d.heads, d.T, (int)d.S, ks, spin_limit().load(), grid, s, &fg);
       }));
+    }
     // this device cannot host the fused kernel: the three-kernel schedule,
     // whose workspace is larger
     if (!workspace_ok(path_workspace(d, in_dtype, GDN_PATH_MFMA), &st)) return st;
   }
+  // separate kernels: the gates first, into gamma, beta
+  if (gate && timed(rec, s, 0, [&] {
+        return gdn::launch_frame_gates(gate->a, gate->b, gate->A_log, gate->dt_bias, gate->gamma, gate->beta,
+                                       d.frames, (int)d.H, (int)d.T, (int)d.S, s);
+      }) != hipSuccess)
+    return GDN_E_HIP;
   if (fast_path(in_dtype, d.D))
     return hip_status(run_mfma(d, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                static_cast<const uint16_t*>(v), gamma, beta, state_in, ks, out, ob, state_out,
@@ -733,6 +765,33 @@ size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype) {
   return path_workspace(d, in_dtype, fast_path(in_dtype, d.D) ? GDN_PATH_MFMA : GDN_PATH_PLAIN);
 }
 
+int gdn_attn_fwd(const gdn_shape* shape, int in_dtype, const gdn_attn_layout* layout, const void* q, const void* k,
+                 const void* v, float* out, float* lse, void* stream) {
+  if (!shape || !layout) return GDN_E_NULLPTR;
+  const int64_t B = shape->B, H = shape->H, T = shape->T, S = shape->S, D = shape->D;
+  if (B < 0 || H < 0 || T < 0 || S < 0) return GDN_E_SHAPE;
+  if (!valid_dtype(in_dtype)) return GDN_E_DTYPE;
+  if (D != 128) return GDN_E_UNSUPPORTED_D;
+  if (in_dtype != GDN_BF16) return GDN_E_DTYPE;
+  const gdn_attn_layout& L = *layout;
+  if (L.sink < 0 || L.first_chunk < 1 || L.chunk < 1 || L.window < 1) return GDN_E_VALUE;
+  int64_t heads, tokens, elems;
+  if (!mul_ok(B, H, &heads) || !mul_ok(T, S, &tokens) || tokens >= (int64_t{1} << 30)) return GDN_E_SHAPE;
+  if (!mul_ok(heads, tokens, &elems) || elems > (int64_t{1} << 40)) return GDN_E_SHAPE;
+  if (elems == 0) return GDN_OK;
+  if (!q || !k || !v || !out) return GDN_E_NULLPTR;
+  const size_t inb = (size_t)elems * D * 2, outb = (size_t)elems * D * 4, lseb = (size_t)elems * 4;
+  const Range outs[] = {{out, outb}, {lse, lse ? lseb : 0}};
+  const Range ins[] = {{q, inb}, {k, inb}, {v, inb}};
+  if (!aliasing_ok(outs, 2, ins, 3)) return GDN_E_ALIAS;
+  // layout fields beyond T frames change nothing; clamp them into int range
+  auto clampT = [&](int64_t x) { return (int)(x < T + 1 ? x : T + 1); };
+  return hip_status(gdn::launch_attn_d128(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                          static_cast<const uint16_t*>(v), out, lse, heads, (int)T, (int)S,
+                                          clampT(L.sink), clampT(L.first_chunk), clampT(L.chunk), clampT(L.window),
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int gdn_fused_status(const void* workspace, void* stream) {
   if (!workspace) return GDN_E_NULLPTR;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -815,6 +874,15 @@ int gdn_frame_fwd_ks(const gdn_shape* shape, int in_dtype, int out_dtype, const 
                      void* out, float* state_out, void* workspace, size_t workspace_bytes, void* stream) {
   return frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, gamma, beta, state_in, key_scale, out, state_out,
                         workspace, workspace_bytes, stream, nullptr);
+}
+
+int gdn_frame_fwd_gated(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q, const void* k,
+                        const void* v, const float* gate_a, const float* gate_b, const float* A_log,
+                        const float* dt_bias, const float* state_in, float key_scale, void* out, float* state_out,
+                        float* gamma, float* beta, void* workspace, size_t workspace_bytes, void* stream) {
+  const GateIn g{gate_a, gate_b, A_log, dt_bias, gamma, beta};
+  return frame_fwd_impl(shape, in_dtype, out_dtype, q, k, v, nullptr, nullptr, state_in, key_scale, out, state_out,
+                        workspace, workspace_bytes, stream, nullptr, &g);
 }
 
 int gdn_frame_fwd_timed(const gdn_shape* shape, int in_dtype, int out_dtype, const void* q,

@@ -53,6 +53,18 @@ hipError_t launch_output_bf16_d128(const uint16_t* q, const void* M_all, bool pa
 // is small); the parts only split the tokens, not any reduction.
 int token_split(int64_t frames, int S);
 
+// ---- gates from activations (k_gate.hip, frame_gate.h) --------------------
+// gamma, beta [frames] of every frame of [B, H, T] from the per-token gate
+// pre-activations a, b [frames, S] and the per-head A_log, dt_bias [H].
+hipError_t launch_frame_gates(const float* a, const float* b, const float* A_log, const float* dt_bias, float* gamma,
+                              float* beta, int64_t frames, int H, int T, int S, hipStream_t st);
+// What the fused kernel needs to compute the gates inside its build items
+// (null `a`: the gates are given as gamma, beta inputs).
+struct FusedGates {
+  const float *a, *b, *A_log, *dt_bias;
+  int H;  // heads per batch element: head i of the call uses parameter i % H
+};
+
 // ---- fused MFMA path: the three stages in one persistent kernel -------------
 // bf16, D == 128.  Heads go in groups of at most 16, one cooperative launch
 // (plus a tiny flag reset) per group.  fused_grid returns the launch size
@@ -68,10 +80,13 @@ hipError_t fused_topology_ok(int grid, bool* ok);
 // Device address of the error word of the last fused launch that used this
 // workspace (0: every wait completed).
 const void* fused_error_word(const void* workspace);
+// With gates.a set, the build items compute gamma_t, beta_t from the
+// activations and write them to gamma, beta (outputs), which the state pass
+// then reads frame by frame; otherwise gamma, beta are inputs.
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                         const float* beta, const float* state_in, void* out, bool out_bf16,
                         float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks,
-                        uint32_t spin_limit, int grid, hipStream_t st);
+                        uint32_t spin_limit, int grid, hipStream_t st, const FusedGates* gates = nullptr);
 
 // ---- plain float32 path: any supported D, f32 or bf16 inputs ---------------
 hipError_t launch_build_generic(const void* k, const void* v, bool in_bf16, float* G, float* U,
@@ -94,6 +109,12 @@ hipError_t launch_decay(const float* gamma, const float* state_in, float* state_
 // and d_state_in (may equal d_state_out; either state may be null = zero).
 hipError_t launch_decay_bwd(const float* gamma, const float* state_in, const float* d_state_out, float* dgamma,
                             float* dbeta, float* d_state_in, int64_t heads, int64_t T, int D, hipStream_t st);
+
+// ---- softmax attention with sinks and a local window (k_attn.hip) ---------
+// bf16, D == 128; heads * (T * S) tokens; out float32, lse float32 or null.
+hipError_t launch_attn_d128(const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out, float* lse,
+                            int64_t heads, int T, int S, int sink, int first_chunk, int chunk, int window,
+                            hipStream_t st);
 
 // ---- gdn_api.cpp ------------------------------------------------------------
 // gdn_frame_fwd's whole call on a caller-provided workspace (see gdn.h).

@@ -48,6 +48,7 @@
 // other wait then gives up, the state pass writes NaN to state_out, and the
 // kernel ends.
 #include "frame_build.h"
+#include "frame_gate.h"
 #include "frame_output.h"
 #include "gdn_common.h"
 #include "gdn_launch.h"
@@ -162,6 +163,12 @@ struct Args {
   int heads, T, S;
   float ks;             // key scale: the build items write ks^2 G_t and ks U_t
   uint32_t spin_limit;  // polls before a wait gives up
+  // gates from activations (the kGated kernels): per-token pre-activations
+  // ga, gb [heads, T, S], per-head A_log, dt_bias (head i of the launch uses
+  // entry (h0 + i) % H); the build items write gamma_t, beta_t to gout, bout
+  const float *ga, *gb, *A_log, *dt_bias;
+  float *gout, *bout;
+  int H, h0;
 };
 
 __host__ __device__ constexpr int64_t ring_head_bytes(int wg, int wm) {
@@ -238,7 +245,7 @@ union __attribute__((aligned(16))) Lds {
 // ahead.  Two barriers per step: after G_t is in LDS, and for the LDS
 // hand-off of M between the waves.  A wave whose wait fails sets `abort` in
 // LDS; after the barrier every wave sees it and all leave together.
-template <int kRows>
+template <int kRows, bool kGated>
 __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int head, int part) {
   constexpr int kParts = D / kRows;
   constexpr int kRB = kRows / 16;
@@ -296,18 +303,23 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
   // barrier, set to 1 by any wave whose wait fails, and read by every wave
   // only after the next barrier, so all waves leave the loop together.
 
-  // gamma/beta: 64-frame windows per lane, read with readlane (scalar loads
-  // would share the LDS wait counter)
-  const float* gh = a.gamma + (int64_t)head * T;
-  const float* bh = a.beta + (int64_t)head * T;
+  // gamma/beta given: 64-frame windows per lane, read with readlane (scalar
+  // loads would share the LDS wait counter).  Gates computed by the build
+  // items (kGated): read with the frame's G_t and U_t, once its flag is set,
+  // as device-scope loads (never through the scalar cache, which the flag
+  // protocol does not invalidate).
+  const float* gh = (kGated ? a.gout : a.gamma) + (int64_t)head * T;
+  const float* bh = (kGated ? a.bout : a.beta) + (int64_t)head * T;
   auto win_load = [&](int t0, float& gv, float& bv) {
     const int tt = t0 + l;
     gv = tt < T ? gh[tt] : 0.f;
     bv = tt < T ? bh[tt] : 0.f;
   };
-  float gwin, bwin, gnxt, bnxt;
-  win_load(0, gwin, bwin);
-  win_load(64, gnxt, bnxt);
+  float gwin = 0.f, bwin = 0.f, gnxt = 0.f, bnxt = 0.f;  // kGated: gate of the frame loaded ahead, in gnxt, bnxt
+  if constexpr (!kGated) {
+    win_load(0, gwin, bwin);
+    win_load(64, gnxt, bnxt);
+  }
 
   // one-frame register ring: 9 of the 2304 16-byte chunks of G_t's upper
   // triangle (the builders write only those halves of the packed units) and
@@ -331,6 +343,10 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
   f32x4 ru[2][kRB];
   auto load_frame = [&](int t) {
     if (t >= T) return;
+    if constexpr (kGated) {
+      gnxt = __uint_as_float(flag_load(reinterpret_cast<const uint32_t*>(gh + t)));
+      bnxt = __uint_as_float(flag_load(reinterpret_cast<const uint32_t*>(bh + t)));
+    }
     const char* Gp = gp_slot(t);
     const char* Up = up_slot(t);
 #pragma unroll
@@ -360,13 +376,19 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
     // gamma_t and beta_t now, with nothing in flight: a readlane after the
     // flag loads below would wait for those loads too (the compiler cannot
     // count the loads in flight there, so it waits for all of them)
-    const int tw = t & 63;
-    const float gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwin), tw));
-    const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwin), tw));
-    if (tw == 63) {
-      gwin = gnxt;
-      bwin = bnxt;
-      win_load(t + 65, gnxt, bnxt);
+    float gm, bt;
+    if constexpr (kGated) {
+      gm = gnxt;  // frame t's gates, loaded with its G_t (load_frame(t + 1) below reloads them)
+      bt = bnxt;
+    } else {
+      const int tw = t & 63;
+      gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwin), tw));
+      bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwin), tw));
+      if (tw == 63) {
+        gwin = gnxt;
+        bwin = bnxt;
+        win_load(t + 65, gnxt, bnxt);
+      }
     }
     bool good = true;
     if (l == 0) {
@@ -506,8 +528,8 @@ __device__ void nan_fill(void* of, int n) {
   for (int c = threadIdx.x; c < n * kRowChunks; c += blockDim.x) dst[c] = (u32x4){w, w, w, w};
 }
 
-template <bool kOutBf16, int kRows>
-__device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int xcd, int nh) {
+template <bool kOutBf16, int kRows, bool kGated>
+__device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, float* red, int xcd, int nh) {
   constexpr int kParts = D / kRows;
   const int T = a.T, S = a.S;
   constexpr int kWG = kRing.wg, kWM = kRing.wm;
@@ -538,6 +560,16 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
       }
       __syncthreads();
       if (!bcast[3]) continue;  // a wait gave up: drain the queue, building nothing
+      if constexpr (kGated) {
+        // the frame's gates, published with its maps (the stores complete
+        // before the flag below is set)
+        const int hp = (a.h0 + head) % a.H;
+        const Gates gt = frame_gates(a.ga + fr * S, a.gb + fr * S, S, a.A_log[hp], a.dt_bias[hp], red);
+        if (tid == 0) {
+          a.gout[fr] = gt.gamma;
+          a.bout[fr] = gt.beta;
+        }
+      }
       char* gp = ring + (int64_t)(2 * (it.t % kWG)) * packed::kFrameBytes;
       float* up = reinterpret_cast<float*>(ring + (int64_t)(2 * (it.t % kWG) + 1) * packed::kFrameBytes);
       // two token iterations loaded ahead (one measured no faster); the
@@ -578,11 +610,12 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int
   }
 }
 
-template <bool kOutBf16, int kRows>
+template <bool kOutBf16, int kRows, bool kGated>
 __global__ __launch_bounds__(256, 2) void k_fused(Args a) {
   constexpr int kParts = D / kRows;
   __shared__ Lds<kRows> lds;
   __shared__ uint32_t bcast[4];
+  __shared__ float red[kGated ? 8 : 1];  // the gate reduction of a build item
   const uint32_t xcd = xcc_id();
   if (xcd >= (uint32_t)kXcd) return;  // not an MI355X XCD id: take no part
   const int nh = (int)xcd < a.heads ? (a.heads - (int)xcd + kXcd - 1) / kXcd : 0;
@@ -596,9 +629,9 @@ __global__ __launch_bounds__(256, 2) void k_fused(Args a) {
   if (nh == 0) return;
   if (ticket < nh * kParts) {
     __builtin_amdgcn_s_setprio(3);
-    state_role<kRows>(a, lds, bcast, (ticket / kParts) * kXcd + (int)xcd, ticket % kParts);
+    state_role<kRows, kGated>(a, lds, bcast, (ticket / kParts) * kXcd + (int)xcd, ticket % kParts);
   } else {
-    worker_role<kOutBf16, kRows>(a, lds, bcast, (int)xcd, nh);
+    worker_role<kOutBf16, kRows, kGated>(a, lds, bcast, red, (int)xcd, nh);
   }
 }
 
@@ -618,9 +651,9 @@ __global__ void k_fused_init(uint32_t* words, int n) {
 // workload).
 constexpr int kFusedRows = 16;
 
-template <bool kOutBf16>
+template <bool kOutBf16, bool kGated = false>
 const void* fused_kernel() {
-  return reinterpret_cast<const void*>(&k_fused<kOutBf16, kFusedRows>);
+  return reinterpret_cast<const void*>(&k_fused<kOutBf16, kFusedRows, kGated>);
 }
 
 
@@ -633,13 +666,13 @@ int64_t fused_workspace_bytes(int64_t heads) {
 }
 
 int fused_grid(bool out_bf16, int num_cus) {
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<false>(), 256, 0) != hipSuccess)
-    return 0;
-  int per_cu16 = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu16, fused_kernel<true>(), 256, 0) != hipSuccess)
-    return 0;
-  const int pc = out_bf16 ? per_cu16 : per_cu;
+  // the launch size of both variants (gates given or computed) of this output dtype
+  int pc = 0, pg = 0;
+  const void* k0 = out_bf16 ? fused_kernel<true>() : fused_kernel<false>();
+  const void* k1 = out_bf16 ? fused_kernel<true, true>() : fused_kernel<false, true>();
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, k0, 256, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pg, k1, 256, 0) != hipSuccess) return 0;
+  pc = pg < pc ? pg : pc;
   // every XCD needs its state-pass workgroups and at least as many workers
   const int grid = pc * num_cus;
   return grid / kXcd >= 2 * kMaxHeadsPerXcd * (D / kFusedRows) ? grid : 0;
@@ -672,7 +705,7 @@ const void* fused_error_word(const void* workspace) {
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                         const float* beta, const float* state_in, void* out, bool out_bf16,
                         float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks,
-                        uint32_t spin_limit, int grid, hipStream_t st) {
+                        uint32_t spin_limit, int grid, hipStream_t st, const FusedGates* gates) {
   char* ws = static_cast<char*>(workspace);
   const int64_t group = kXcd * kMaxHeadsPerXcd;
   const int64_t ctrl_bytes = (int64_t)sizeof(Ctrl) + group * kFlagWords * 4;
@@ -697,13 +730,23 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     a.S = S;
     a.ks = ks;
     a.spin_limit = spin_limit ? spin_limit : kSpinLimit;
+    const bool gated = gates && gates->a;
+    a.ga = gated ? gates->a + h0 * T * S : nullptr;
+    a.gb = gated ? gates->b + h0 * T * S : nullptr;
+    a.A_log = gated ? gates->A_log : nullptr;
+    a.dt_bias = gated ? gates->dt_bias : nullptr;
+    a.gout = gated ? const_cast<float*>(gamma) + h0 * T : nullptr;
+    a.bout = gated ? const_cast<float*>(beta) + h0 * T : nullptr;
+    a.H = gated ? gates->H : 1;
+    a.h0 = (int)h0;
     hipLaunchKernelGGL(k_fused_init, dim3((nwords + 255) / 256), dim3(256), 0, st,
                        reinterpret_cast<uint32_t*>(ws), nwords);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     void* params[] = {&a};
-    e = hipLaunchCooperativeKernel(out_bf16 ? fused_kernel<true>() : fused_kernel<false>(), dim3((unsigned)grid),
-                                   dim3(256), params, 0, st);
+    const void* kern = gated ? (out_bf16 ? fused_kernel<true, true>() : fused_kernel<false, true>())
+                             : (out_bf16 ? fused_kernel<true>() : fused_kernel<false>());
+    e = hipLaunchCooperativeKernel(kern, dim3((unsigned)grid), dim3(256), params, 0, st);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for a later, unrelated check
       return e;

@@ -267,6 +267,40 @@ int gdn_frame_fwd_ks(const gdn_shape* shape, int in_dtype, int out_dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn_frame_fwd with the gates computed from activations and the key scale
+ * applied inside the build: the gate prologue fused into the scan (the pages
+ * fuse "the GDN scan and gate operations" into custom kernels: "SANA-WM:
+ * NVIDIA puts a one-minute world model on a single GPU", zhichai.net,
+ * training pipeline).  The pages call gamma a learned decay scalar and beta
+ * the delta-rule strength (section 1) but do not give their
+ * parameterisation; the one taken here, per frame t of head h:
+ *     gamma_t = exp(-exp(A_log[h]) * softplus(mean_s gate_a[t, s] + dt_bias[h]))
+ *     beta_t  = sigmoid(mean_s gate_b[t, s])
+ * with gate_a, gate_b the per-token pre-activations of the layer's gate
+ * projections (one scalar per token and head) averaged over the frame's S
+ * tokens, because one recurrent step consumes a whole latent frame.  Then the
+ * recurrence of gdn_frame_fwd runs on key_scale * K with these gates.
+ *   gate_a, gate_b  [B, H, T, S] float32 (device)
+ *   A_log, dt_bias  [H] float32 (device): head h of every batch element
+ *   gamma, beta     [B, H, T] float32 (device) outputs: the gates used
+ *   key_scale       finite (else GDN_E_VALUE); 1 for keys already scaled
+ * Everything else, the workspace included, as gdn_frame_fwd.  S must be at
+ * least 1 when there are frames (a frame's gates average its tokens; else
+ * GDN_E_SHAPE).  The fused path computes the gates inside its build items
+ * and the state pass reads them frame by frame; the other paths run one
+ * small kernel for the gates first.  Both give the same float32 gates
+ * (the token sums are reduced in one fixed order), so results do not depend
+ * on the path beyond what gdn_frame_fwd's do.
+ */
+int gdn_frame_fwd_gated(const gdn_shape* shape, int in_dtype, int out_dtype,
+                        const void* q, const void* k, const void* v,
+                        const float* gate_a, const float* gate_b,
+                        const float* A_log, const float* dt_bias,
+                        const float* state_in, float key_scale, void* out, float* state_out,
+                        float* gamma, float* beta,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gdn_frame_fwd, plus per-kernel durations: a pair of HIP events is recorded
  * around every kernel launch of the call, on the stream that launch uses;
  * the call waits for `stream` (which the call joins back to) and writes,

@@ -83,6 +83,42 @@ STRESS_B4 = Workload(
 
 WORKLOADS = {w.name: w for w in (TINY_F32, CLIP_5S, SEQ_60S, STREAM_60S, STRESS_B4)}
 
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    """A softmax attention block with attention sinks and a local temporal
+    window over the same token layout as the GDN block ([B, H, T, S, D]).
+    The pages name sinks and windows for the chunk-causal variant but give
+    no sizes; sink, first_chunk, chunk and window are this workload's
+    choice (frames of sink, frames of chunk 0, frames per later chunk,
+    chunks per window)."""
+    name: str
+    B: int
+    H: int
+    T: int
+    S: int
+    D: int
+    seed: int
+    sink: int
+    first_chunk: int
+    chunk: int
+    window: int
+    tol: float = 2e-3
+
+    def with_(self, **kw) -> "AttnWorkload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return AttnWorkload(**d)
+
+
+# The 60 s sequence's token layout: the clip's first latent frame alone as
+# chunk 0 and as the attention sink, then chunks of 4 latent frames (a
+# quarter second at 16 latent frames per second), each query seeing its own
+# chunk and the one before it: at most 1 + 8 frames = 7,920 keys.
+ATTN_60S = AttnWorkload(name="attn60s_sink1_chunk4_win2_bf16", B=1, H=16, T=961, S=880, D=128, seed=7,
+                        sink=1, first_chunk=1, chunk=4, window=2)
+ATTN_WORKLOADS = {ATTN_60S.name: ATTN_60S}
+
 # The workload the throughput figure is quoted on (one GPU's share of the
 # 60 s, 720p sequence).
 BENCH_WORKLOAD = SEQ_60S

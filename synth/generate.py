@@ -30,7 +30,7 @@ from typing import Dict, Iterable, List, Optional, Tuple
 
 import numpy as np
 
-from .configs import Workload
+from .configs import AttnWorkload, Workload
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -87,6 +87,19 @@ def head_inputs(w: Workload, b: int, h: int) -> Dict[str, np.ndarray]:
     elif w.in_dtype != "f32":
         raise ValueError(f"unknown in_dtype {w.in_dtype!r}")
     return {"q": q, "k": k, "v": v, "gamma": gamma, "beta": beta, "state": state}
+
+
+def attn_head_inputs(w: AttnWorkload, b: int, h: int) -> Dict[str, np.ndarray]:
+    """q, k, v of one head of an attention workload: [T, S, D] standard
+    normals (float32, drawn q then k then v from SeedSequence([seed, b, h]))
+    rounded to bfloat16 bits."""
+    T, S, D = w.T, w.S, w.D
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([w.seed, b, h])))
+    n = T * S * D
+    out = {}
+    for key in ("q", "k", "v"):
+        out[key] = f32_to_bf16_bits(rng.standard_normal(n, dtype=np.float32).reshape(T, S, D))
+    return out
 
 
 def _head_job(args):

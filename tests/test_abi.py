@@ -9,14 +9,15 @@ import pytest
 import frame_wise_gated_fwd_amd as F
 from frame_wise_gated_fwd_amd._lib import SIGNATURES, Shape
 
-HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "gdn.h")
+INCLUDE = os.path.join(os.path.dirname(__file__), "..", "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 OK, NULLPTR, SHAPE, DTYPE, UNSUP_D, WORKSPACE, ALIAS, HIP, VALUE, TIMEOUT = range(10)
 F32, BF16 = 0, 1
 
 
 def declared_functions():
-    txt = open(HEADER).read()
+    txt = "".join(open(h).read() for h in HEADERS)
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", txt)))
 
@@ -313,3 +314,48 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_attention_argument_errors_on_the_host():
+    """gdn_attn_fwd rejects bad arguments before launching anything."""
+    from frame_wise_gated_fwd_amd._lib import AttnLayout
+    L = F.lib()
+
+    def att(shape=None, dt=BF16, lay=(1, 1, 4, 2), q=P[0], k=P[1], v=P[2], out=P[3], lse=P[4]):
+        s = shape if shape is not None else _shape(1, 2, 9, 40, 128)
+        lo = AttnLayout(*lay) if lay is not None else None
+        return L.gdn_attn_fwd(ctypes.byref(s), dt, ctypes.byref(lo) if lo is not None else None, q, k, v, out, lse,
+                              None)
+    assert L.gdn_attn_fwd(None, BF16, None, P[0], P[1], P[2], P[3], None, None) == NULLPTR
+    assert att(lay=None) == NULLPTR
+    for bad in ({"q": None}, {"k": None}, {"v": None}, {"out": None}):
+        assert att(**bad) == NULLPTR, bad
+    assert att(dt=F32) == DTYPE
+    assert att(dt=7) == DTYPE
+    assert att(shape=_shape(1, 2, 9, 40, 64)) == UNSUP_D
+    assert att(shape=_shape(1, -2, 9, 40, 128)) == SHAPE
+    assert att(shape=_shape(1, 1, 1 << 16, 1 << 14, 128)) == SHAPE   # 2^30 tokens per head
+    for lay in ((-1, 1, 4, 2), (1, 0, 4, 2), (1, 1, 0, 2), (1, 1, 4, 0)):
+        assert att(lay=lay) == VALUE, lay
+    assert att(out=P[0]) == ALIAS                 # out over q
+    assert att(lse=P[3] + 64) == ALIAS            # lse inside out
+    assert att(shape=_shape(0, 2, 9, 40, 128), q=None, k=None, v=None, out=None, lse=None) == OK
+
+
+def test_gated_argument_errors_on_the_host():
+    L = F.lib()
+    s = _shape()
+    wsb = L.gdn_workspace_bytes(ctypes.byref(s), BF16)
+
+    def gated(shape=s, ga=P[7] + (1 << 33), gb=P[7] + (2 << 33), A=P[8], bias=P[8] + 4096, gam=P[9], bet=P[10],
+              ks=1.0, ws=P[11], wsb_=wsb):
+        return L.gdn_frame_fwd_gated(ctypes.byref(shape), BF16, F32, P[0], P[1], P[2], ga, gb, A, bias, None, ks,
+                                     P[5], P[6], gam, bet, ws, wsb_, None)
+    for bad in ({"ga": None}, {"gb": None}, {"A": None}, {"bias": None}, {"gam": None}, {"bet": None}):
+        assert gated(**bad) == NULLPTR, bad
+    assert gated(ks=float("nan")) == VALUE
+    assert gated(shape=_shape(S=0), ws=None, wsb_=0) == SHAPE      # a frame's gates average its tokens
+    assert gated(gam=P[5]) == ALIAS                               # gamma written over out
+    assert gated(gam=P[9], bet=P[9] + 8) == ALIAS                 # gamma and beta overlap
+    assert gated(ga=P[5]) == ALIAS                                # out written over a gate input
+    assert gated(shape=_shape(B=0), ws=None, wsb_=0) == OK
