@@ -11,8 +11,8 @@
 // step consumes a whole frame).
 //
 // The token sums are reduced in a fixed order (per thread, then a butterfly
-// inside each wave, then the four waves in order), so every caller of
-// frame_gates gets the same float32 values for the same frame.
+// inside each wave, then the four waves in order), so the gates of a frame
+// are the same float32 values whatever launch computes them.
 #pragma once
 
 #include "gdn_common.h"
@@ -23,8 +23,26 @@ struct Gates {
   float gamma, beta;
 };
 
+// Sum over the 64 lanes of a wave by an xor butterfly: every lane ends with
+// the same bits (each step adds the same two values in either order).
+__device__ __forceinline__ float wave_sum_butterfly(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// The gates from the frame's token sums ta, tb (over its S tokens).
+__device__ __forceinline__ Gates gates_from_sums(float ta, float tb, int S, float A_log, float dt_bias) {
+  const float x = ta / (float)S + dt_bias;
+  const float sp = x > 20.f ? x : log1pf(expf(x));  // softplus; above 20 it equals x in float32
+  return {expf(-expf(A_log) * sp), 1.f / (1.f + expf(-(tb / (float)S)))};
+}
+
 // All 256 threads of the workgroup call it with the same arguments; `red`
 // is 8 floats of LDS.  S >= 1.  Returns the frame's gates in every thread.
+// Order of the token sums: thread i adds tokens i, i + 256, i + 512, ... in
+// that order, starting from 0; then the butterfly in each wave; then the
+// four waves' sums as ((w0 + w1) + w2) + w3.
 __device__ inline Gates frame_gates(const float* __restrict__ a, const float* __restrict__ b, int S, float A_log,
                                     float dt_bias, float* red) {
   float sa = 0.f, sb = 0.f;
@@ -32,11 +50,8 @@ __device__ inline Gates frame_gates(const float* __restrict__ a, const float* __
     sa += a[s];
     sb += b[s];
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    sa += __shfl_xor(sa, off);
-    sb += __shfl_xor(sb, off);
-  }
+  sa = wave_sum_butterfly(sa);
+  sb = wave_sum_butterfly(sb);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     red[w] = sa;
@@ -46,9 +61,7 @@ __device__ inline Gates frame_gates(const float* __restrict__ a, const float* __
   const float ta = ((red[0] + red[1]) + red[2]) + red[3];
   const float tb = ((red[4] + red[5]) + red[6]) + red[7];
   __syncthreads();  // `red` may be written again after this
-  const float x = ta / (float)S + dt_bias;
-  const float sp = x > 20.f ? x : log1pf(expf(x));  // softplus; above 20 it equals x in float32
-  return {expf(-expf(A_log) * sp), 1.f / (1.f + expf(-(tb / (float)S)))};
+  return gates_from_sums(ta, tb, S, A_log, dt_bias);
 }
 
 }  // namespace gdn

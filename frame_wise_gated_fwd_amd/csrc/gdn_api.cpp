@@ -594,12 +594,18 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
     const int grid = fused_launch(in_dtype, d, ob, &queried);
     if (!queried) return GDN_E_HIP;
     if (grid > 0) {
-      const gdn::FusedGates fg{gate ? gate->a : nullptr, gate ? gate->b : nullptr, gate ? gate->A_log : nullptr,
-                               gate ? gate->dt_bias : nullptr, (int)d.H};
+      // the gates first, into gamma, beta, which the fused kernel then reads
+      // as inputs (one pass over the activations, which the state pass has
+      // no slack to take on, nor the build items, the kernel's throughput)
+      if (gate && timed(rec, s, 0, [&] {
+            return gdn::launch_frame_gates(gate->a, gate->b, gate->A_log, gate->dt_bias, gate->gamma, gate->beta,
+                                           d.frames, (int)d.H, (int)d.T, (int)d.S, s);
+          }) != hipSuccess)
+        return GDN_E_HIP;
       return hip_status(timed(rec, s, 1, [&] {
         return gdn::launch_fused(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                  static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out,
-                                 workspace, d.heads, d.T, (int)d.S, ks, spin_limit().load(), grid, s, &fg);
+                                 workspace, d.heads, d.T, (int)d.S, ks, spin_limit().load(), grid, s);
       }));
     }
     // this device cannot host the fused kernel: the three-kernel schedule,

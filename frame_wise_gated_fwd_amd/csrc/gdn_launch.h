@@ -58,12 +58,6 @@ int token_split(int64_t frames, int S);
 // pre-activations a, b [frames, S] and the per-head A_log, dt_bias [H].
 hipError_t launch_frame_gates(const float* a, const float* b, const float* A_log, const float* dt_bias, float* gamma,
                               float* beta, int64_t frames, int H, int T, int S, hipStream_t st);
-// What the fused kernel needs to compute the gates inside its build items
-// (null `a`: the gates are given as gamma, beta inputs).
-struct FusedGates {
-  const float *a, *b, *A_log, *dt_bias;
-  int H;  // heads per batch element: head i of the call uses parameter i % H
-};
 
 // ---- fused MFMA path: the three stages in one persistent kernel -------------
 // bf16, D == 128.  Heads go in groups of at most 16, one cooperative launch
@@ -80,13 +74,10 @@ hipError_t fused_topology_ok(int grid, bool* ok);
 // Device address of the error word of the last fused launch that used this
 // workspace (0: every wait completed).
 const void* fused_error_word(const void* workspace);
-// With gates.a set, the build items compute gamma_t, beta_t from the
-// activations and write them to gamma, beta (outputs), which the state pass
-// then reads frame by frame; otherwise gamma, beta are inputs.
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                         const float* beta, const float* state_in, void* out, bool out_bf16,
                         float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks,
-                        uint32_t spin_limit, int grid, hipStream_t st, const FusedGates* gates = nullptr);
+                        uint32_t spin_limit, int grid, hipStream_t st);
 
 // ---- plain float32 path: any supported D, f32 or bf16 inputs ---------------
 hipError_t launch_build_generic(const void* k, const void* v, bool in_bf16, float* G, float* U,

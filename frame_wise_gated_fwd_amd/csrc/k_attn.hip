@@ -65,14 +65,24 @@ __device__ __forceinline__ void chunk_frames(const AttnArgs& a, int c, int& f0, 
   }
 }
 
-__device__ __forceinline__ float wave_max4(float x) {  // over lanes n, n+16, n+32, n+48
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+// Reductions over the four lanes of a query (n, n + 16, n + 32, n + 48)
+// with gfx950's row swaps, in registers: v_permlane16_swap exchanges the odd
+// 16-lane rows of one operand with the even rows of the other, so with both
+// operands x each lane ends with the pair (x of its even row, x of its odd
+// row); v_permlane32_swap does the same for the two halves.  Combining the
+// two results gives every lane of a pair the same value.
+__device__ __forceinline__ float pair16(float x, bool mx) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return mx ? fmaxf(a, b) : a + b;
 }
-__device__ __forceinline__ float wave_sum4(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+__device__ __forceinline__ float pair32(float x, bool mx) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return mx ? fmaxf(a, b) : a + b;
 }
+__device__ __forceinline__ float wave_max4(float x) { return pair32(pair16(x, true), true); }
+__device__ __forceinline__ float wave_sum4(float x) { return pair32(pair16(x, false), false); }
 
 __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile][kLdsW];

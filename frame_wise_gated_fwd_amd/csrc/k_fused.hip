@@ -48,7 +48,6 @@
 // other wait then gives up, the state pass writes NaN to state_out, and the
 // kernel ends.
 #include "frame_build.h"
-#include "frame_gate.h"
 #include "frame_output.h"
 #include "gdn_common.h"
 #include "gdn_launch.h"
@@ -163,12 +162,6 @@ struct Args {
   int heads, T, S;
   float ks;             // key scale: the build items write ks^2 G_t and ks U_t
   uint32_t spin_limit;  // polls before a wait gives up
-  // gates from activations (the kGated kernels): per-token pre-activations
-  // ga, gb [heads, T, S], per-head A_log, dt_bias (head i of the launch uses
-  // entry (h0 + i) % H); the build items write gamma_t, beta_t to gout, bout
-  const float *ga, *gb, *A_log, *dt_bias;
-  float *gout, *bout;
-  int H, h0;
 };
 
 __host__ __device__ constexpr int64_t ring_head_bytes(int wg, int wm) {
@@ -245,7 +238,7 @@ union __attribute__((aligned(16))) Lds {
 // ahead.  Two barriers per step: after G_t is in LDS, and for the LDS
 // hand-off of M between the waves.  A wave whose wait fails sets `abort` in
 // LDS; after the barrier every wave sees it and all leave together.
-template <int kRows, bool kGated>
+template <int kRows>
 __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int head, int part) {
   constexpr int kParts = D / kRows;
   constexpr int kRB = kRows / 16;
@@ -303,23 +296,18 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
   // barrier, set to 1 by any wave whose wait fails, and read by every wave
   // only after the next barrier, so all waves leave the loop together.
 
-  // gamma/beta given: 64-frame windows per lane, read with readlane (scalar
-  // loads would share the LDS wait counter).  Gates computed by the build
-  // items (kGated): read with the frame's G_t and U_t, once its flag is set,
-  // as device-scope loads (never through the scalar cache, which the flag
-  // protocol does not invalidate).
-  const float* gh = (kGated ? a.gout : a.gamma) + (int64_t)head * T;
-  const float* bh = (kGated ? a.bout : a.beta) + (int64_t)head * T;
+  // gamma/beta: 64-frame windows per lane, read with readlane (scalar loads
+  // would share the LDS wait counter)
+  const float* gh = a.gamma + (int64_t)head * T;
+  const float* bh = a.beta + (int64_t)head * T;
   auto win_load = [&](int t0, float& gv, float& bv) {
     const int tt = t0 + l;
     gv = tt < T ? gh[tt] : 0.f;
     bv = tt < T ? bh[tt] : 0.f;
   };
-  float gwin = 0.f, bwin = 0.f, gnxt = 0.f, bnxt = 0.f;  // kGated: gate of the frame loaded ahead, in gnxt, bnxt
-  if constexpr (!kGated) {
-    win_load(0, gwin, bwin);
-    win_load(64, gnxt, bnxt);
-  }
+  float gwin, bwin, gnxt, bnxt;
+  win_load(0, gwin, bwin);
+  win_load(64, gnxt, bnxt);
 
   // one-frame register ring: 9 of the 2304 16-byte chunks of G_t's upper
   // triangle (the builders write only those halves of the packed units) and
@@ -343,10 +331,6 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
   f32x4 ru[2][kRB];
   auto load_frame = [&](int t) {
     if (t >= T) return;
-    if constexpr (kGated) {
-      gnxt = __uint_as_float(flag_load(reinterpret_cast<const uint32_t*>(gh + t)));
-      bnxt = __uint_as_float(flag_load(reinterpret_cast<const uint32_t*>(bh + t)));
-    }
     const char* Gp = gp_slot(t);
     const char* Up = up_slot(t);
 #pragma unroll
@@ -376,19 +360,13 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
     // gamma_t and beta_t now, with nothing in flight: a readlane after the
     // flag loads below would wait for those loads too (the compiler cannot
     // count the loads in flight there, so it waits for all of them)
-    float gm, bt;
-    if constexpr (kGated) {
-      gm = gnxt;  // frame t's gates, loaded with its G_t (load_frame(t + 1) below reloads them)
-      bt = bnxt;
-    } else {
-      const int tw = t & 63;
-      gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwin), tw));
-      bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwin), tw));
-      if (tw == 63) {
-        gwin = gnxt;
-        bwin = bnxt;
-        win_load(t + 65, gnxt, bnxt);
-      }
+    const int tw = t & 63;
+    const float gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gwin), tw));
+    const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bwin), tw));
+    if (tw == 63) {
+      gwin = gnxt;
+      bwin = bnxt;
+      win_load(t + 65, gnxt, bnxt);
     }
     bool good = true;
     if (l == 0) {
@@ -519,17 +497,18 @@ __device__ void state_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int 
 // ---------------------------------------------------------------------------
 // NaN into rows [0, n) of an output frame (float32 or bf16 elements): what
 // an output item writes when its wait gave up, so that every frame of `out`
-// is either exact or NaN after a failed launch.
+// is either exact or NaN after a failed launch.  Kept out of line: inlined,
+// its registers made the worker loop spill (and the kernel 4 % slower).
 template <bool kOutBf16>
-__device__ void nan_fill(void* of, int n) {
+__device__ __attribute__((noinline)) void nan_fill(void* of, int n) {
   constexpr uint32_t w = kOutBf16 ? 0x7fc07fc0u : 0x7fc00000u;
   constexpr int kRowChunks = D * (kOutBf16 ? 2 : 4) / 16;
   u32x4* dst = static_cast<u32x4*>(of);
   for (int c = threadIdx.x; c < n * kRowChunks; c += blockDim.x) dst[c] = (u32x4){w, w, w, w};
 }
 
-template <bool kOutBf16, int kRows, bool kGated>
-__device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, float* red, int xcd, int nh) {
+template <bool kOutBf16, int kRows>
+__device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, int xcd, int nh) {
   constexpr int kParts = D / kRows;
   const int T = a.T, S = a.S;
   constexpr int kWG = kRing.wg, kWM = kRing.wm;
@@ -560,16 +539,6 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, flo
       }
       __syncthreads();
       if (!bcast[3]) continue;  // a wait gave up: drain the queue, building nothing
-      if constexpr (kGated) {
-        // the frame's gates, published with its maps (the stores complete
-        // before the flag below is set)
-        const int hp = (a.h0 + head) % a.H;
-        const Gates gt = frame_gates(a.ga + fr * S, a.gb + fr * S, S, a.A_log[hp], a.dt_bias[hp], red);
-        if (tid == 0) {
-          a.gout[fr] = gt.gamma;
-          a.bout[fr] = gt.beta;
-        }
-      }
       char* gp = ring + (int64_t)(2 * (it.t % kWG)) * packed::kFrameBytes;
       float* up = reinterpret_cast<float*>(ring + (int64_t)(2 * (it.t % kWG) + 1) * packed::kFrameBytes);
       // two token iterations loaded ahead (one measured no faster); the
@@ -594,14 +563,14 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, flo
       __syncthreads();
       const int s0 = it.part < 0 ? 0 : it.part * S / kTailParts;
       const int s1 = it.part < 0 ? S : (it.part + 1) * S / kTailParts;
-      const int64_t tok = fr * S + s0;
-      void* of = static_cast<char*>(a.out) + tok * D * (kOutBf16 ? 2 : 4);
       if (!bcast[3]) {  // a wait gave up: this frame's M_t never came
-        nan_fill<kOutBf16>(of, s1 - s0);
+        nan_fill<kOutBf16>(static_cast<char*>(a.out) + (fr * S + s0) * D * (kOutBf16 ? 2 : 4), s1 - s0);
         continue;
       }
       invalidate_l1();
       const char* mp = ring + (int64_t)(2 * kWG + it.t % kWM) * packed::kFrameBytes;
+      const int64_t tok = fr * S + s0;
+      void* of = static_cast<char*>(a.out) + tok * D * (kOutBf16 ? 2 : 4);
       if (s1 > s0)
         output_frame<true, kOutBf16>(a.q + tok * D, mp, of, s1 - s0, lds.out, [&] {
           if (tid == 0) flag_store(fl + kFlagOutDone + it.t % kWM, (uint32_t)(it.t + 1));
@@ -610,12 +579,11 @@ __device__ void worker_role(const Args& a, Lds<kRows>& lds, uint32_t* bcast, flo
   }
 }
 
-template <bool kOutBf16, int kRows, bool kGated>
+template <bool kOutBf16, int kRows>
 __global__ __launch_bounds__(256, 2) void k_fused(Args a) {
   constexpr int kParts = D / kRows;
   __shared__ Lds<kRows> lds;
   __shared__ uint32_t bcast[4];
-  __shared__ float red[kGated ? 8 : 1];  // the gate reduction of a build item
   const uint32_t xcd = xcc_id();
   if (xcd >= (uint32_t)kXcd) return;  // not an MI355X XCD id: take no part
   const int nh = (int)xcd < a.heads ? (a.heads - (int)xcd + kXcd - 1) / kXcd : 0;
@@ -629,9 +597,9 @@ __global__ __launch_bounds__(256, 2) void k_fused(Args a) {
   if (nh == 0) return;
   if (ticket < nh * kParts) {
     __builtin_amdgcn_s_setprio(3);
-    state_role<kRows, kGated>(a, lds, bcast, (ticket / kParts) * kXcd + (int)xcd, ticket % kParts);
+    state_role<kRows>(a, lds, bcast, (ticket / kParts) * kXcd + (int)xcd, ticket % kParts);
   } else {
-    worker_role<kOutBf16, kRows, kGated>(a, lds, bcast, red, (int)xcd, nh);
+    worker_role<kOutBf16, kRows>(a, lds, bcast, (int)xcd, nh);
   }
 }
 
@@ -651,9 +619,9 @@ __global__ void k_fused_init(uint32_t* words, int n) {
 // workload).
 constexpr int kFusedRows = 16;
 
-template <bool kOutBf16, bool kGated = false>
+template <bool kOutBf16>
 const void* fused_kernel() {
-  return reinterpret_cast<const void*>(&k_fused<kOutBf16, kFusedRows, kGated>);
+  return reinterpret_cast<const void*>(&k_fused<kOutBf16, kFusedRows>);
 }
 
 
@@ -666,13 +634,10 @@ int64_t fused_workspace_bytes(int64_t heads) {
 }
 
 int fused_grid(bool out_bf16, int num_cus) {
-  // the launch size of both variants (gates given or computed) of this output dtype
-  int pc = 0, pg = 0;
-  const void* k0 = out_bf16 ? fused_kernel<true>() : fused_kernel<false>();
-  const void* k1 = out_bf16 ? fused_kernel<true, true>() : fused_kernel<false, true>();
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, k0, 256, 0) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pg, k1, 256, 0) != hipSuccess) return 0;
-  pc = pg < pc ? pg : pc;
+  int pc = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, out_bf16 ? fused_kernel<true>() : fused_kernel<false>(), 256,
+                                                   0) != hipSuccess)
+    return 0;
   // every XCD needs its state-pass workgroups and at least as many workers
   const int grid = pc * num_cus;
   return grid / kXcd >= 2 * kMaxHeadsPerXcd * (D / kFusedRows) ? grid : 0;
@@ -705,7 +670,7 @@ const void* fused_error_word(const void* workspace) {
 hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                         const float* beta, const float* state_in, void* out, bool out_bf16,
                         float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks,
-                        uint32_t spin_limit, int grid, hipStream_t st, const FusedGates* gates) {
+                        uint32_t spin_limit, int grid, hipStream_t st) {
   char* ws = static_cast<char*>(workspace);
   const int64_t group = kXcd * kMaxHeadsPerXcd;
   const int64_t ctrl_bytes = (int64_t)sizeof(Ctrl) + group * kFlagWords * 4;
@@ -730,23 +695,13 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     a.S = S;
     a.ks = ks;
     a.spin_limit = spin_limit ? spin_limit : kSpinLimit;
-    const bool gated = gates && gates->a;
-    a.ga = gated ? gates->a + h0 * T * S : nullptr;
-    a.gb = gated ? gates->b + h0 * T * S : nullptr;
-    a.A_log = gated ? gates->A_log : nullptr;
-    a.dt_bias = gated ? gates->dt_bias : nullptr;
-    a.gout = gated ? const_cast<float*>(gamma) + h0 * T : nullptr;
-    a.bout = gated ? const_cast<float*>(beta) + h0 * T : nullptr;
-    a.H = gated ? gates->H : 1;
-    a.h0 = (int)h0;
     hipLaunchKernelGGL(k_fused_init, dim3((nwords + 255) / 256), dim3(256), 0, st,
                        reinterpret_cast<uint32_t*>(ws), nwords);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     void* params[] = {&a};
-    const void* kern = gated ? (out_bf16 ? fused_kernel<true, true>() : fused_kernel<false, true>())
-                             : (out_bf16 ? fused_kernel<true>() : fused_kernel<false>());
-    e = hipLaunchCooperativeKernel(kern, dim3((unsigned)grid), dim3(256), params, 0, st);
+    e = hipLaunchCooperativeKernel(out_bf16 ? fused_kernel<true>() : fused_kernel<false>(), dim3((unsigned)grid),
+                                   dim3(256), params, 0, st);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for a later, unrelated check
       return e;

@@ -1,6 +1,8 @@
 // The gates of every frame from activations (frame_gate.h), one workgroup
-// per frame, for the paths that run the frame-wise GDN as separate kernels;
-// the fused kernel computes the same values inside its build items.
+// per frame, before the frame-wise GDN on every path.  (Computed inside the
+// fused kernel instead, by its build items or by its state pass, the same
+// call measured 8 % and 27 % slower: the build items set the kernel's
+// throughput and the state pass its chain; this pass costs about 1 %.)
 #include "frame_gate.h"
 #include "gdn_launch.h"
 

@@ -286,11 +286,10 @@ int gdn_frame_fwd_ks(const gdn_shape* shape, int in_dtype, int out_dtype,
  *   key_scale       finite (else GDN_E_VALUE); 1 for keys already scaled
  * Everything else, the workspace included, as gdn_frame_fwd.  S must be at
  * least 1 when there are frames (a frame's gates average its tokens; else
- * GDN_E_SHAPE).  The fused path computes the gates inside its build items
- * and the state pass reads them frame by frame; the other paths run one
- * small kernel for the gates first.  Both give the same float32 gates
- * (the token sums are reduced in one fixed order), so results do not depend
- * on the path beyond what gdn_frame_fwd's do.
+ * GDN_E_SHAPE).  One small kernel computes the gates (one pass over the
+ * pre-activations, token sums in one fixed order), then the call proceeds as
+ * gdn_frame_fwd_ks on its path with them; results do not depend on the path
+ * beyond what gdn_frame_fwd's do.
  */
 int gdn_frame_fwd_gated(const gdn_shape* shape, int in_dtype, int out_dtype,
                         const void* q, const void* k, const void* v,
