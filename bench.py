@@ -353,10 +353,14 @@ def host_info():
     cpu = None
     try:
         with open("/proc/cpuinfo") as f:
+            fields = {}
             for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    fields.setdefault(k.strip(), v.strip())
+        cpu = fields.get("model name")
+        if fields.get("cpu family") and fields.get("model"):
+            cpu = f"{cpu} (family {fields['cpu family']}, model {fields['model']})"
     except OSError:
         pass
     rocm = None
@@ -369,7 +373,9 @@ def host_info():
             continue
     return {"cpu_model": cpu, "host_cores": len(os.sched_getaffinity(0)), "rocm": rocm,
             "hip_runtime": getattr(torch.version, "hip", None), "torch": torch.__version__,
-            "gpu": torch.cuda.get_device_name(0)}
+            "gpu": torch.cuda.get_device_name(0) or None,
+            "gpu_arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+            "compute_units": torch.cuda.get_device_properties(0).multi_processor_count}
 
 
 def _oracle_config_head(args):

@@ -205,6 +205,33 @@ def test_forward_stream60s_matches_single_call():
     assert torch.equal(st_s, st1)
 
 
+def test_checkpoint_resume_is_bitwise(tmp_path):
+    """A chunk-causal rollout stopped after 70 of 161 frames: state_out goes
+    to disk (a float32 .npy file), every device buffer is dropped, the state
+    is loaded back into a fresh tensor and the rollout continues; out and the
+    final state equal one uninterrupted call bit for bit (the state is the
+    whole memory of the recurrence and crosses the file exactly)."""
+    import os
+    w = CLIP_5S.with_(T=161, H=16, S=200, name="clip_t161_resume", state_std=0.02)
+    x = device_inputs(w, DEV)
+    out1, st1 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    cut = 70
+    a = {k_: x[k_][:, :, :cut].contiguous() for k_ in ("q", "k", "v", "gamma", "beta")}
+    o_a, st_a = F.frame_fwd(a["q"], a["k"], a["v"], a["gamma"], a["beta"], x["state"])
+    torch.cuda.synchronize()
+    path = os.path.join(tmp_path, "state.npy")
+    np.save(path, st_a.cpu().numpy())
+    o_a = o_a.cpu()
+    del a, st_a
+    torch.cuda.empty_cache()
+    state = torch.from_numpy(np.load(path)).to(DEV)
+    b = {k_: x[k_][:, :, cut:].contiguous() for k_ in ("q", "k", "v", "gamma", "beta")}
+    o_b, st_b = F.frame_fwd(b["q"], b["k"], b["v"], b["gamma"], b["beta"], state)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o_a, o_b.cpu()], dim=2), out1.cpu())
+    assert torch.equal(st_b, st1)
+
+
 def test_forward_stress_b4_all_heads():
     """All 64 heads' final states, and each head's output at 15 sampled
     frames.  A launch covers the 16 heads of one batch element, head h on
