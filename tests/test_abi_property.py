@@ -24,8 +24,8 @@ def _mul(a, b):
 
 def model(shape, in_dt, out_dt, ks, ptrs, ws, wsb):
     """(status, launches) per the contract: the checks in the order the
-    header states them (shape, key scale, dtypes, pointers, workspace,
-    aliasing)."""
+    header states them (shape, key scale, dtypes, pointers, workspace of the
+    planned path, aliasing)."""
     if shape is None:
         return NULLPTR, False
     B, H, T, S, D = shape
@@ -54,7 +54,7 @@ def model(shape, in_dt, out_dt, ks, ptrs, ws, wsb):
     q, k, v, gamma, beta, state_in, out, state_out = ptrs
     if (need_in and None in (q, k, v, out)) or (need_fr and None in (gamma, beta)) or (need_st and state_out is None):
         return NULLPTR, False
-    need = 0 if in_elems == 0 else 3 * ((map_elems * 4 + 255) // 256 * 256)
+    need = 0 if in_elems == 0 else _planned_need(shape, in_dt, frames, map_elems)
     if need > 0 and (ws is None or wsb < need or ws % 256):
         return WORKSPACE, False
     isz, osz = (2 if in_dt == 1 else 4), (2 if out_dt == 1 else 4)
@@ -73,6 +73,21 @@ def model(shape, in_dt, out_dt, ks, ptrs, ws, wsb):
             if overlap(o, o2):
                 return ALIAS, False
     return OK, need_st
+
+
+def _planned_need(shape, in_dt, frames, map_elems):
+    """Workspace of the path the call plans before asking the device: the
+    fused kernel's (bf16, D = 128, T > 32, as gdn_path_workspace_bytes
+    reports it), the three-kernel schedule's three segments of maps (bf16,
+    D = 128), else every frame's maps."""
+    B, H, T, S, D = shape
+    if in_dt == 1 and D == 128 and T > 32:
+        return F.lib().gdn_path_workspace_bytes(ctypes.byref(Shape(*shape)), in_dt, 2)
+    if in_dt == 1 and D == 128:
+        n = -(-T // 64)
+        cap = -(-T // n)
+        return 3 * min(n, 3) * ((B * H * cap * D * D * 4 + 255) // 256 * 256)
+    return 3 * ((map_elems * 4 + 255) // 256 * 256)
 
 
 sizes = st.one_of(st.integers(0, 3), st.sampled_from([-1, 5, 64, 65, 880, 1 << 20, 1 << 40]))
