@@ -36,7 +36,6 @@ namespace {
 constexpr int D = 128;
 constexpr int kQTile = 128;        // queries per workgroup, 32 per wave
 constexpr int kKTile = 64;         // keys per step
-constexpr int kLdsW = D + 16;      // padded LDS row (bf16): 288 bytes
 constexpr int kXcd = 8;
 
 struct AttnArgs {
@@ -84,9 +83,19 @@ __device__ __forceinline__ float pair32(float x, bool mx) {
 __device__ __forceinline__ float wave_max4(float x) { return pair32(pair16(x, true), true); }
 __device__ __forceinline__ float wave_sum4(float x) { return pair32(pair16(x, false), false); }
 
+// Key and value tiles in LDS: 64 rows of 256 bytes, unpadded; the 16-byte
+// slot c of row r holds the row's chunk c ^ (r % 16).  Written by direct
+// global-to-LDS loads (lane l of a load instruction fills bytes 16 l .. of
+// its 1 KiB run), read as MFMA operands with no bank conflicts among the 16
+// rows a read touches.
+constexpr int kRowBytes = D * 2;
+constexpr int kTileBytes = kKTile * kRowBytes;  // 16 KiB
+
 __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKTile][kLdsW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kKTile][kLdsW];
+  // [2] K tiles and [2] V tiles
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * kTileBytes];
+  unsigned char* Kbuf = lds;
+  unsigned char* Vbuf = lds + 2 * kTileBytes;
 
   // XCD-aware order: the workgroups of one XCD (id % 8) take a contiguous
   // run of (head, chunk, tile) items, so consecutive chunks of a head, which
@@ -145,28 +154,35 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
                               : (u32x4){0u, 0u, 0u, 0u};
   }
 
-  // staging: chunk i of a tile is row (tid + 256 i) / 16, 16-byte column (tid + 256 i) % 16
-  u32x4 kst[4], vst[4];
-  auto load_tile = [&](int s) {
+  // Direct loads of step s's K or V tile into `dst`: instruction i of wave w
+  // fills LDS chunks 256 i + 64 w + lane, i.e. row 16 i + 4 w + lane / 16,
+  // slot lane % 16, which receives the row's chunk slot ^ (row % 16).  Rows
+  // past the range's end read its last key (finite values; their scores are
+  // masked, so they add nothing).
+  auto load_tile = [&](const uint16_t* src, unsigned char* dst, int s) {
     int base, end;
     step_base(s, base, end);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 256 * i, row = ch >> 4, col = ch & 15;
-      const int key = base + row;
-      const bool ok = key < end;
-      kst[i] = ok ? ld_nt(reinterpret_cast<const u32x4*>(a.k + (hbase + key) * D) + col) : (u32x4){0u, 0u, 0u, 0u};
-      vst[i] = ok ? ld_nt(reinterpret_cast<const u32x4*>(a.v + (hbase + key) * D) + col) : (u32x4){0u, 0u, 0u, 0u};
+      const int row = 16 * i + 4 * w + (l >> 4), slot = l & 15;
+      const int key = min(base + row, end - 1);
+      const uint16_t* gp = src + (hbase + key) * D + 8 * (slot ^ (row & 15));
+      __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)(dst + (256 * i + 64 * w) * 16),
+                                       16, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 256 * i, row = ch >> 4, col = ch & 15;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row][8 * col]) = kst[i];
-      *reinterpret_cast<u32x4*>(&Vs[buf][row][8 * col]) = vst[i];
-    }
-  };
+
+  // LDS read addresses.  K operand of key block kk, dim block kb: row 16 kk + n,
+  // chunk 4 kb + g, in slot (4 kb + g) ^ n = (4 kb) ^ (g ^ n): the kb part
+  // flips bits 6-7 of the byte address, the kk part adds whole rows.
+  const int kaddr = n * kRowBytes + (((g ^ n) & 15) << 4);
+  // V^T operand of d block db: the addressing lane 4 e1 + jj (e1 = n / 4,
+  // jj = n % 4) names key 4g + e1 (+16 for the second read, +32 ks for the
+  // key step) and columns 16 db + 4 jj .. +3, which are bytes 8 (jj % 2) ..
+  // of chunk 2 db + jj / 2 in slot (2 db) ^ (jj / 2 ^ row % 16): the db part
+  // flips bits 5-7, the key offsets add whole rows.
+  const int vrow = 4 * g + (n >> 2);
+  const int vaddr = vrow * kRowBytes + (((((n >> 1) & 1) ^ vrow) & 15) << 4) + (n & 1) * 8;
 
   f32x4 acc[8][2];  // O^T: d block db, query block qb; lane (n, g): dims 16db + 4g + i of query n
 #pragma unroll
@@ -176,17 +192,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
   float m[2] = {-__builtin_inff(), -__builtin_inff()};  // running max (log2 domain) of query n, per qb
   float lsum[2] = {0.f, 0.f};                             // this lane's part of the row sum
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) load_tile(s + 1);  // in flight during this step
-    int base, end;
-    step_base(s, base, end);
-
-    // S^T = K Q^T for 64 keys x 32 queries
-    f32x4 sc[4][2];
+  // S^T = K Q^T for 64 keys x 32 queries from a K tile in LDS
+  auto qk = [&](const unsigned char* Kt, f32x4 (&sc)[4][2]) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -195,44 +202,95 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(&Ks[buf][16 * kk + n][32 * kb + 8 * g]);
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(Kt + (kaddr ^ (kb << 6)) + kk * 16 * kRowBytes);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) sc[kk][qb] = mfma16x16x32(ka, qop[qb][kb], sc[kk][qb]);
       }
+  };
 
-    // online softmax; lane (n, g) holds keys base + 16 kk + 4g + i of query n
-    float p[4][2][4];
+  // Pipeline: step s's scores are computed in step s - 1, so that their
+  // softmax (vector ALU) overlaps the next tile's Q K^T (matrix cores).
+  // Buffers: K tiles of steps s + 1 (read) and s + 2 (loading), V tiles of
+  // steps s (read) and s + 1 (loading); every overwrite waits for the
+  // barrier that ended the last reads of that buffer.
+  load_tile(a.k, Kbuf, 0);
+  if (nsteps > 1) load_tile(a.k, Kbuf + kTileBytes, 1);
+  load_tile(a.v, Vbuf, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+  __syncthreads();
+  f32x4 sc[4][2];
+  qk(Kbuf, sc);
+  __syncthreads();  // every wave's reads of K buffer 0 are done before step 0 refills it
+
+  for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
+    if (s + 2 < nsteps) load_tile(a.k, Kbuf + cur * kTileBytes, s + 2);
+    if (s + 1 < nsteps) load_tile(a.v, Vbuf + (cur ^ 1) * kTileBytes, s + 1);
+    int base, end;
+    step_base(s, base, end);
+
+    // Online softmax of step s into weights p = 2^(x c - m), c = log2(e) /
+    // sqrt(D); lane (n, g) holds keys base + 16 kk + 4g + i of query n.  Row
+    // maxima are taken in the log2 domain (c is positive, so scaling the raw
+    // maximum gives the maximum of the scaled scores).  The slots past the
+    // range's end hold copies of its last key, so they leave the maximum as
+    // it is; their weights are zeroed below.  The running maximum m is
+    // raised only when a row's new maximum exceeds it by more than 8 (then
+    // for every row of the wave, each to its exact maximum): the weights stay
+    // below 2^8, and O and the row sums need no rescale in the other steps.
+    // The result is the same softmax.
+    float mx[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mx = -__builtin_inff();
+      float v = sc[0][qb][0];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool valid = base + 16 * kk + 4 * g + i < end;
-          const float x = valid ? sc[kk][qb][i] * a.scale_log2 : -__builtin_inff();
-          p[kk][qb][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = wave_max4(mx);
-      const float mn = fmaxf(m[qb], mx);  // finite: every step has a visible key
-      const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
-      m[qb] = mn;
+        for (int i = 0; i < 4; ++i) v = fmaxf(v, sc[kk][qb][i]);
+      mx[qb] = wave_max4(v) * a.scale_log2;
+    }
+    if (__builtin_amdgcn_ballot_w64(mx[0] > m[0] + 8.f || mx[1] > m[1] + 8.f)) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float mn = fmaxf(m[qb], mx[qb]);
+        const float alpha = __builtin_amdgcn_exp2f(m[qb] - mn);
+        m[qb] = mn;
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[db][qb] *= alpha;
+      }
+    }
+    float p[4][2][4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[kk][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk][qb][i], a.scale_log2, -m[qb]));
+    if (end - base < kKTile) {
+      const int lim = end - base - 4 * g;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) p[kk][qb][i] = 16 * kk + i < lim ? p[kk][qb][i] : 0.f;
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       float sum = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(p[kk][qb][i] - mn);
-          p[kk][qb][i] = e;
-          sum += e;
-        }
-      lsum[qb] = lsum[qb] * alpha + sum;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) acc[db][qb] *= alpha;
+        for (int i = 0; i < 4; ++i) sum += p[kk][qb][i];
+      lsum[qb] += sum;
     }
 
+    // the next step's scores, on the matrix cores while the above runs
+    if (s + 1 < nsteps) qk(Kbuf + (cur ^ 1) * kTileBytes, sc);
+
     // O^T += V^T P^T over two 32-key steps, P as bf16 hi + lo
+    const unsigned char* Vt = Vbuf + cur * kTileBytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 phi[2], plo[2];
@@ -252,11 +310,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
       }
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        // lane (i, g) of the A operand: V[key(g, e)][16 db + i]; the addressing lane
-        // 4e' + jj names key 32 ks + 4g + e' (+16 for the second read), columns 16 db + 4 jj
-        const int e1 = n >> 2, jj = n & 3;
-        const u32x2 v0 = lds_read_tr16(&Vs[buf][32 * ks + 4 * g + e1][16 * db + 4 * jj]);
-        const u32x2 v1 = lds_read_tr16(&Vs[buf][32 * ks + 16 + 4 * g + e1][16 * db + 4 * jj]);
+        // lane (i, g) of the A operand: V[key(g, e)][16 db + i]
+        const unsigned char* vp = Vt + (vaddr ^ (db << 5)) + 32 * ks * kRowBytes;
+        const u32x2 v0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vp));
+        const u32x2 v1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vp + 16 * kRowBytes));
         const u32x4 vt = {v0.x, v0.y, v1.x, v1.y};
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -266,9 +323,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
       }
     }
 
-    // buffer buf ^ 1 was last read in step s - 1, before the barrier that ended it
-    if (s + 1 < nsteps) store_tile(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads for the next steps have landed
+    __syncthreads();               // and everyone's; the buffers read in this step are free
   }
 
   // normalise and store: lane (n, g) writes dims 16 db + 4g .. +3 of query 16 qb + n
