@@ -84,12 +84,35 @@ __device__ __forceinline__ float wave_max4(float x) { return pair32(pair16(x, tr
 __device__ __forceinline__ float wave_sum4(float x) { return pair32(pair16(x, false), false); }
 
 // Key and value tiles in LDS: 64 rows of 256 bytes, unpadded; the 16-byte
-// slot c of row r holds the row's chunk c ^ (r % 16).  Written by direct
+// slot c of row r holds the row's chunk c ^ rsw(r % 16), where rsw rotates
+// the four row bits (rsw(r) = 2 (r % 8) + r / 8).  Written by direct
 // global-to-LDS loads (lane l of a load instruction fills bytes 16 l .. of
-// its 1 KiB run), read as MFMA operands with no bank conflicts among the 16
-// rows a read touches.
+// its 1 KiB run).  The LDS serves 256 bytes a clock from 64 four-byte banks:
+// a 16-byte read of one chunk by 16 consecutive rows, and an 8-byte
+// transposed read of 32 bytes from each of 8 consecutive rows, both touch
+// every bank once, because rsw is one-to-one on the 16 row classes and
+// rsw(r) / 2 is one-to-one on each run of 8.
 constexpr int kRowBytes = D * 2;
 constexpr int kTileBytes = kKTile * kRowBytes;  // 16 KiB
+
+// A key row of zeros: the V rows past the end of a key range are loaded from it.
+__device__ __attribute__((aligned(256))) uint32_t g_zero_row[kRowBytes / 4];
+
+__device__ __forceinline__ int rsw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+// (a, b) as packed bf16 hi = bf16(x) and lo = bf16(x - hi); x - hi is exact
+// in float32 and comes from one dot2 each: hi . (-1, 0) + a, hi . (0, -1) + b.
+// The masks (-1, 0) and (0, -1) are passed in registers: as an operand
+// constant the compiler encodes 0x0000bf80 as the inline constant -1.0, which
+// this instruction reads as the float32 pattern 0xbf800000, i.e. (0, -1).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 split2_dot(float a, float b, uint32_t m_lo, uint32_t m_hi) {
+  const uint32_t hi = cvt2bf(a, b);
+  const bf16x2_t h = __builtin_bit_cast(bf16x2_t, hi);
+  const float la = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2_t, m_lo), a, false);
+  const float lb = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2_t, m_hi), b, false);
+  return (u32x2){hi, cvt2bf(la, lb)};
+}
 
 __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
   // [2] K tiles and [2] V tiles
@@ -139,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
   };
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;  // w: wave-uniform
   const int n = l & 15, g = l >> 4;
 
   // Q of this wave as B operands: lane (n, g) holds query 16 qb + n, dims 32 kb + 8g .. +7
@@ -156,33 +179,52 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
 
   // Direct loads of step s's K or V tile into `dst`: instruction i of wave w
   // fills LDS chunks 256 i + 64 w + lane, i.e. row 16 i + 4 w + lane / 16,
-  // slot lane % 16, which receives the row's chunk slot ^ (row % 16).  Rows
-  // past the range's end read its last key (finite values; their scores are
-  // masked, so they add nothing).
-  auto load_tile = [&](const uint16_t* src, unsigned char* dst, int s) {
+  // slot lane % 16, which receives the row's chunk slot ^ rsw(row % 16).  The
+  // lane's byte offset within a 16-row block is the same for every i, so a
+  // full tile needs one address per instruction, uniform over the wave.  In
+  // a range's last, partial tile the K rows past its end read the range's
+  // last key (so the scores there repeat one of the range) and the V rows
+  // past its end read a row of zeros (so those slots add nothing to O).
+  const int lrow = 4 * w + (l >> 4);
+  const unsigned loff = lrow * kRowBytes + (((l & 15) ^ rsw(lrow)) << 4);
+  auto load_tile = [&](const uint16_t* src, unsigned char* dst, int s, bool is_v) {
     int base, end;
     step_base(s, base, end);
+    const unsigned char* tile = reinterpret_cast<const unsigned char*>(src + (hbase + base) * D);
+    if (end - base >= kKTile) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * i + 4 * w + (l >> 4), slot = l & 15;
-      const int key = min(base + row, end - 1);
-      const uint16_t* gp = src + (hbase + key) * D + 8 * (slot ^ (row & 15));
-      __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)(dst + (256 * i + 64 * w) * 16),
-                                       16, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(tile + i * 16 * kRowBytes + loff,
+                                         (__attribute__((address_space(3))) void*)(dst + (256 * i + 64 * w) * 16), 16, 0, 0);
+    } else {
+      const int nvalid = end - base;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * i + lrow;
+        const unsigned char* gp = row < nvalid ? tile + row * kRowBytes
+                                  : is_v     ? reinterpret_cast<const unsigned char*>(g_zero_row)
+                                             : tile + (nvalid - 1) * kRowBytes;
+        __builtin_amdgcn_global_load_lds(gp + (loff & (kRowBytes - 1)),
+                                         (__attribute__((address_space(3))) void*)(dst + (256 * i + 64 * w) * 16), 16, 0, 0);
+      }
     }
   };
 
   // LDS read addresses.  K operand of key block kk, dim block kb: row 16 kk + n,
-  // chunk 4 kb + g, in slot (4 kb + g) ^ n = (4 kb) ^ (g ^ n): the kb part
+  // chunk 4 kb + g, in slot (4 kb + g) ^ rsw(n) = (4 kb) ^ (g ^ rsw(n)): the kb part
   // flips bits 6-7 of the byte address, the kk part adds whole rows.
-  const int kaddr = n * kRowBytes + (((g ^ n) & 15) << 4);
+  const int kaddr = n * kRowBytes + ((g ^ rsw(n)) << 4);
   // V^T operand of d block db: the addressing lane 4 e1 + jj (e1 = n / 4,
   // jj = n % 4) names key 4g + e1 (+16 for the second read, +32 ks for the
   // key step) and columns 16 db + 4 jj .. +3, which are bytes 8 (jj % 2) ..
-  // of chunk 2 db + jj / 2 in slot (2 db) ^ (jj / 2 ^ row % 16): the db part
+  // of chunk 2 db + jj / 2 in slot (2 db) ^ (jj / 2 ^ rsw(row % 16)): the db part
   // flips bits 5-7, the key offsets add whole rows.
   const int vrow = 4 * g + (n >> 2);
-  const int vaddr = vrow * kRowBytes + (((((n >> 1) & 1) ^ vrow) & 15) << 4) + (n & 1) * 8;
+  const int vaddr = vrow * kRowBytes + ((((n >> 1) & 1) ^ rsw(vrow)) << 4) + (n & 1) * 8;
+
+  // (-1, 0) and (0, -1) as packed bf16, opaque to constant folding
+  uint32_t m_lo = 0x0000bf80u, m_hi = 0xbf800000u;
+  asm volatile("" : "+s"(m_lo), "+s"(m_hi));
 
   f32x4 acc[8][2];  // O^T: d block db, query block qb; lane (n, g): dims 16db + 4g + i of query n
 #pragma unroll
@@ -208,47 +250,52 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
       }
   };
 
-  // Pipeline: step s's scores are computed in step s - 1, so that their
-  // softmax (vector ALU) overlaps the next tile's Q K^T (matrix cores).
-  // Buffers: K tiles of steps s + 1 (read) and s + 2 (loading), V tiles of
-  // steps s (read) and s + 1 (loading); every overwrite waits for the
-  // barrier that ended the last reads of that buffer.
-  load_tile(a.k, Kbuf, 0);
-  if (nsteps > 1) load_tile(a.k, Kbuf + kTileBytes, 1);
-  load_tile(a.v, Vbuf, 0);
+  // Row maxima of a step's scores in the log2 domain: c = log2(e) / sqrt(D)
+  // is positive, so scaling the raw maximum gives the maximum of the scaled
+  // scores.  The slots past a range's end repeat one of its scores and leave
+  // the maximum as it is.
+  auto rowmax = [&](const f32x4(&x)[4][2], float(&mx)[2]) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float v = x[0][qb][0];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaxf(v, x[kk][qb][i]);
+      mx[qb] = wave_max4(v) * a.scale_log2;
+    }
+  };
+
+  // Pipeline: step s's scores and their row maxima are computed in step
+  // s - 1, so that the softmax (vector ALU) overlaps the next tile's Q K^T
+  // and this tile's P V (matrix cores).  Buffers: K tiles of steps s + 1
+  // (read) and s + 2 (loading), V tiles of steps s (read) and s + 1
+  // (loading); every overwrite waits for the barrier that ended the last
+  // reads of that buffer.
+  load_tile(a.k, Kbuf, 0, false);
+  if (nsteps > 1) load_tile(a.k, Kbuf + kTileBytes, 1, false);
+  load_tile(a.v, Vbuf, 0, true);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
   __syncthreads();
   f32x4 sc[4][2];
+  float mx[2];
   qk(Kbuf, sc);
+  rowmax(sc, mx);
   __syncthreads();  // every wave's reads of K buffer 0 are done before step 0 refills it
 
   for (int s = 0; s < nsteps; ++s) {
     const int cur = s & 1;
-    if (s + 2 < nsteps) load_tile(a.k, Kbuf + cur * kTileBytes, s + 2);
-    if (s + 1 < nsteps) load_tile(a.v, Vbuf + (cur ^ 1) * kTileBytes, s + 1);
+    if (s + 2 < nsteps) load_tile(a.k, Kbuf + cur * kTileBytes, s + 2, false);
+    if (s + 1 < nsteps) load_tile(a.v, Vbuf + (cur ^ 1) * kTileBytes, s + 1, true);
     int base, end;
     step_base(s, base, end);
 
-    // Online softmax of step s into weights p = 2^(x c - m), c = log2(e) /
-    // sqrt(D); lane (n, g) holds keys base + 16 kk + 4g + i of query n.  Row
-    // maxima are taken in the log2 domain (c is positive, so scaling the raw
-    // maximum gives the maximum of the scaled scores).  The slots past the
-    // range's end hold copies of its last key, so they leave the maximum as
-    // it is; their weights are zeroed below.  The running maximum m is
+    // Online softmax of step s into weights p = 2^(x c - m); lane (n, g)
+    // holds keys base + 16 kk + 4g + i of query n.  The running maximum m is
     // raised only when a row's new maximum exceeds it by more than 8 (then
     // for every row of the wave, each to its exact maximum): the weights stay
     // below 2^8, and O and the row sums need no rescale in the other steps.
     // The result is the same softmax.
-    float mx[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float v = sc[0][qb][0];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v = fmaxf(v, sc[kk][qb][i]);
-      mx[qb] = wave_max4(v) * a.scale_log2;
-    }
     if (__builtin_amdgcn_ballot_w64(mx[0] > m[0] + 8.f || mx[1] > m[1] + 8.f)) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -267,15 +314,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[kk][qb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kk][qb][i], a.scale_log2, -m[qb]));
-    if (end - base < kKTile) {
-      const int lim = end - base - 4 * g;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) p[kk][qb][i] = 16 * kk + i < lim ? p[kk][qb][i] : 0.f;
-    }
+    // slot (3, 3): past the end whenever any slot of this lane is
+    const float pdup[2] = {p[3][0][3], p[3][1][3]};
+    // the next step's scores, on the matrix cores while the exponentials run
+    // (in the last step from a stale buffer, and never used)
+    qk(Kbuf + (cur ^ 1) * kTileBytes, sc);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float sum = 0.f;
@@ -285,9 +328,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
         for (int i = 0; i < 4; ++i) sum += p[kk][qb][i];
       lsum[qb] += sum;
     }
-
-    // the next step's scores, on the matrix cores while the above runs
-    if (s + 1 < nsteps) qk(Kbuf + (cur ^ 1) * kTileBytes, sc);
 
     // O^T += V^T P^T over two 32-key steps, P as bf16 hi + lo
     const unsigned char* Vt = Vbuf + cur * kTileBytes;
@@ -301,7 +341,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
         for (int e2 = 0; e2 < 4; ++e2) {
           // slot pair (2 e2, 2 e2 + 1): e < 4 from key block 2 ks, else 2 ks + 1
           const int kk = 2 * ks + (e2 >> 1), i0 = 2 * (e2 & 1);
-          const u32x2 sp = split2(p[kk][qb][i0], p[kk][qb][i0 + 1]);
+          const u32x2 sp = split2_dot(p[kk][qb][i0], p[kk][qb][i0 + 1], m_lo, m_hi);
           h[e2] = sp.x;
           lo[e2] = sp.y;
         }
@@ -323,6 +363,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_d128(AttnArgs a) {
       }
     }
 
+    rowmax(sc, mx);  // of the next step's scores
+    // The slots past the range's end carry one weight each, that of the
+    // range's last key (the same score); their V rows are zero, so only the
+    // row sums counted them.
+    if (end - base < kKTile) {
+      int past = 0;  // this lane's slots past the end: keys 16 kk + 4g + i >= end - base
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) past += 4 - min(max(end - base - 16 * kk - 4 * g, 0), 4);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) lsum[qb] -= (float)past * pdup[qb];
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads for the next steps have landed
     __syncthreads();               // and everyone's; the buffers read in this step are free
   }
