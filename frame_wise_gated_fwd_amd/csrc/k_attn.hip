@@ -15,8 +15,8 @@
 //
 // One workgroup per 128 queries of one chunk (all of them see the same keys,
 // so no per-element mask is needed except past the end of a key range).
-// Key tiles of 64 tokens are staged through LDS (double-buffered, loaded a
-// tile ahead through registers).  Each wave owns 32 queries and computes
+// Key and value tiles of 64 tokens go to LDS by direct global-to-LDS loads,
+// a step ahead (two buffers each).  Each wave owns 32 queries and computes
 //   S^T = K Q^T   (A = K rows from LDS, B = Q held in registers),
 // so that every lane holds scores of one query, n = lane % 16 of its
 // 16-query block, for keys 4g .. 4g+3 (g = lane / 16) of each 16-key block.
@@ -26,7 +26,9 @@
 // from gfx950's transposed LDS read.  The online softmax's row maximum is
 // combined over the four lanes of a query; row sums stay per lane until the
 // end.  P enters the MFMA as a bf16 hi/lo pair (two passes), which keeps the
-// weights to about 2^-17 relative, so O has float32 accuracy.
+// weights to about 2^-17 relative, so O has float32 accuracy.  A step's
+// scores come from the step before, so that its exponentials run beside the
+// next tile's Q K^T and its own P V on the matrix cores.
 #include "gdn_common.h"
 #include "gdn_launch.h"
 
@@ -87,11 +89,11 @@ __device__ __forceinline__ float wave_sum4(float x) { return pair32(pair16(x, fa
 // slot c of row r holds the row's chunk c ^ rsw(r % 16), where rsw rotates
 // the four row bits (rsw(r) = 2 (r % 8) + r / 8).  Written by direct
 // global-to-LDS loads (lane l of a load instruction fills bytes 16 l .. of
-// its 1 KiB run).  The LDS serves 256 bytes a clock from 64 four-byte banks:
-// a 16-byte read of one chunk by 16 consecutive rows, and an 8-byte
+// its 1 KiB run).  The swizzle spreads reads over 64 four-byte banks: a
+// 16-byte read of one chunk by 16 consecutive rows, and an 8-byte
 // transposed read of 32 bytes from each of 8 consecutive rows, both touch
-// every bank once, because rsw is one-to-one on the 16 row classes and
-// rsw(r) / 2 is one-to-one on each run of 8.
+// every bank once (rsw is one-to-one on the 16 row classes, rsw(r) / 2 on
+// each run of 8).
 constexpr int kRowBytes = D * 2;
 constexpr int kTileBytes = kKTile * kRowBytes;  // 16 KiB
 
