@@ -86,21 +86,24 @@ __device__ __forceinline__ float wave_max4(float x) { return pair32(pair16(x, tr
 __device__ __forceinline__ float wave_sum4(float x) { return pair32(pair16(x, false), false); }
 
 // Key and value tiles in LDS: 64 rows of 256 bytes, unpadded; the 16-byte
-// slot c of row r holds the row's chunk c ^ rsw(r % 16), where rsw rotates
-// the four row bits (rsw(r) = 2 (r % 8) + r / 8).  Written by direct
-// global-to-LDS loads (lane l of a load instruction fills bytes 16 l .. of
-// its 1 KiB run).  The swizzle spreads reads over 64 four-byte banks: a
-// 16-byte read of one chunk by 16 consecutive rows, and an 8-byte
-// transposed read of 32 bytes from each of 8 consecutive rows, both touch
-// every bank once (rsw is one-to-one on the 16 row classes, rsw(r) / 2 on
-// each run of 8).
+// slot c of row r holds the row's chunk c ^ rsw(r % 16), with the bits of
+// rsw(r) = (r2, r0, r1, r2 ^ r3) for the bits r0 .. r3 of r.  Written by
+// direct global-to-LDS loads (lane l of a load instruction fills bytes
+// 16 l .. of its 1 KiB run).  The LDS serves 128 bytes a clock from 32
+// four-byte banks: a 16-byte read in 8-lane groups (here 8 rows, one chunk
+// each), an 8-byte read in 16-lane groups (here 4 rows, 32 bytes each).  The
+// first needs rsw % 8 one-to-one on each run of 8 rows, the second
+// rsw / 2 % 4 one-to-one on each aligned run of 4; rsw gives both, and also
+// stays conflict-free for 64 banks and twice the group sizes (rsw one-to-one
+// on all 16 rows, rsw / 2 on each run of 8).  The bank-conflict counter
+// reads zero.
 constexpr int kRowBytes = D * 2;
 constexpr int kTileBytes = kKTile * kRowBytes;  // 16 KiB
 
 // A key row of zeros: the V rows past the end of a key range are loaded from it.
 __device__ __attribute__((aligned(256))) uint32_t g_zero_row[kRowBytes / 4];
 
-__device__ __forceinline__ int rsw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int rsw(int r) { return ((r >> 2) & 1) | ((r & 3) << 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 3); }
 
 // (a, b) as packed bf16 hi = bf16(x) and lo = bf16(x - hi); x - hi is exact
 // in float32 and comes from one dot2 each: hi . (-1, 0) + a, hi . (0, -1) + b.
