@@ -251,10 +251,9 @@ void teardown() {
 }
 
 // Per-device facts the fused path needs, queried once: the launch size of
-// the fused kernel (0 when the device cannot host it: no cooperative
-// launch, too few compute units, or workgroups not dealt evenly over eight
-// XCDs with ids 0-7, which the one-time probe in gdn::fused_topology_ok
-// checks).
+// the fused kernel (0 when the device cannot host it: too few compute
+// units, or workgroups not dealt evenly over eight XCDs with ids 0-7, which
+// the one-time probe in gdn::fused_topology_ok checks).
 struct DevInfo {
   int fused_grid[2];  // [out_bf16]
   bool ready;
@@ -270,11 +269,10 @@ hipError_t dev_info(DevInfo** out) {
   std::lock_guard<std::mutex> lock(g_dev_mu);
   DevInfo& di = g_dev[dev];
   if (!di.ready) {
-    int cus = 0, coop = 0;
+    int cus = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev)) != hipSuccess) return e;
     for (int b = 0; b < 2; ++b) {
-      int grid = coop ? gdn::fused_grid(b != 0, cus) : 0;
+      int grid = gdn::fused_grid(b != 0, cus);
       bool even = false;
       if (grid > 0 && (e = gdn::fused_topology_ok(grid, &even)) != hipSuccess) return e;
       di.fused_grid[b] = even ? grid : 0;

@@ -60,8 +60,8 @@ hipError_t launch_frame_gates(const float* a, const float* b, const float* A_log
                               float* beta, int64_t frames, int H, int T, int S, hipStream_t st);
 
 // ---- fused MFMA path: the three stages in one persistent kernel -------------
-// bf16, D == 128.  Heads go in groups of at most 16, one cooperative launch
-// (plus a tiny flag reset) per group.  fused_grid returns the launch size
+// bf16, D == 128.  Heads go in groups of at most 16, one launch (plus a
+// tiny flag reset) per group.  fused_grid returns the launch size
 // (workgroups resident at once on num_cus CUs) or 0 when the device cannot
 // host the kernel's roles.  The workspace holds a control block, per-head
 // flags and per-head rings (fused_workspace_bytes).  spin_limit: polls

@@ -1,5 +1,5 @@
 // The whole frame-wise GDN forward (bf16 inputs, head dim 128) as one
-// persistent, cooperatively launched kernel that overlaps the three stages:
+// persistent kernel that overlaps the three stages:
 //   build   G_t = K_t^T K_t, U_t = V_t^T K_t      (parallel over frames)
 //   state   M_t = M_{t-1} gamma_t (I - beta_t G_t) + beta_t U_t   (sequential)
 //   output  O_t = Q_t M_t^T                        (parallel over frames)
@@ -20,9 +20,22 @@
 // kRows rows of M; rows of M evolve independently), the rest become
 // workers that pull build and output items from the XCD's queue.  Two
 // workgroups fit on a CU (every role stays within 256 registers per lane
-// and 80 KB of LDS), and the launch is cooperative, so every workgroup is
-// resident at once; state-pass waves raise their issue priority so that a
-// worker sharing their CU does not stretch the sequential chain.
+// and 80 KB of LDS) and the launch fills the device; state-pass waves raise
+// their issue priority so that a worker sharing their CU does not stretch
+// the sequential chain.
+//
+// Progress without a co-residency guarantee.  The launch is an ordinary one
+// (a cooperative launch costs about 20 us more per call and guarantees
+// nothing the design needs).  Roles follow the order in which workgroups
+// start on an XCD, not their ids: the first nh * kParts to take a ticket
+// run the state pass, so a worker runs only once every state-pass
+// workgroup of its XCD is running.  State-pass workgroups wait only for
+// items, and every item waits only for earlier items or for state-pass
+// progress that needs only earlier items (see the ring notes below), so any
+// running worker can finish the lowest unfinished item.  The state pass
+// holds at most 16 of an XCD's 64 workgroup slots, so as long as other work
+// on the device drains, workers start.  Should none start within the bounded
+// waits, the call ends with the error word set (see below), never hangs.
 //
 // Hand-off between CUs of one XCD.  The L2 is shared by the XCD's CUs and
 // the vector L1 is write-through, so a producer makes data visible by
@@ -700,8 +713,8 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     void* params[] = {&a};
-    e = hipLaunchCooperativeKernel(out_bf16 ? fused_kernel<true>() : fused_kernel<false>(), dim3((unsigned)grid),
-                                   dim3(256), params, 0, st);
+    e = hipLaunchKernel(out_bf16 ? fused_kernel<true>() : fused_kernel<false>(), dim3((unsigned)grid), dim3(256),
+                        params, 0, st);
     if (e != hipSuccess) {
       (void)hipGetLastError();  // do not leave the error for a later, unrelated check
       return e;

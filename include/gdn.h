@@ -158,15 +158,17 @@ int gdn_fused_status(const void* workspace, void* stream);
  *                   replaces the 64.  Otherwise all three run on `stream`;
  *   GDN_PATH_FUSED  bf16, D == 128, T > 32: build, state pass and output in
  *                   one persistent kernel per group of at most 16 heads,
- *                   launched cooperatively on `stream` (every workgroup
- *                   resident at once) after a tiny flag-reset kernel.  Each
- *                   head runs on one XCD and its per-frame G_t, U_t, M_t
- *                   pass between compute units through that XCD's L2 instead
- *                   of HBM.  Every internal wait is bounded: if one runs out
- *                   (it cannot while all workgroups are resident), the
- *                   frames and state rows not produced are NaN and
- *                   gdn_fused_status reports it.  On a device that cannot
- *                   launch it cooperatively at full size or does not deal
+ *                   launched on `stream` at the size that fills the device
+ *                   after a tiny flag-reset kernel.  Each head runs on one
+ *                   XCD and its per-frame G_t, U_t, M_t pass between compute
+ *                   units through that XCD's L2 instead of HBM.  Roles go
+ *                   by the order in which workgroups start, so the kernel
+ *                   makes progress with any number of them resident.  Every
+ *                   internal wait is bounded: if one runs out (only when
+ *                   other work holds the device's compute units for longer
+ *                   than the limit), the frames and state rows not produced
+ *                   are NaN and gdn_fused_status reports it.  On a device
+ *                   that cannot host its roles at full size or does not deal
  *                   workgroups evenly over eight XCDs with ids 0-7 (checked
  *                   once per device by a probe kernel on the null stream
  *                   that waits for it, at the first call or query that

@@ -279,7 +279,7 @@ def test_segmented_forward_equals_stage_chain_bitwise(three_kernel_path):
 
 
 def test_fused_kernel_equals_three_kernel_path_bitwise():
-    """The fused kernel (one cooperative launch, rings on chip) and the
+    """The fused kernel (one launch, rings on chip) and the
     three-kernel schedule run the same per-element arithmetic: identical
     results on the 5 s workload (16 heads, 81 frames) and on 20 heads (two
     head groups, the second partial) with a bf16 output."""
