@@ -590,6 +590,51 @@ def test_fused_kernel_wait_failure_ends_without_hang():
     assert torch.equal(out2, ref_out) and torch.equal(st2, ref_st)
 
 
+def test_fused_kernel_completes_beside_other_work():
+    """The fused kernel is launched the ordinary way, with no guarantee that
+    all its workgroups are resident at once: roles go by start order, so it
+    must make progress while another stream holds compute units and its
+    workgroups start piecemeal.  Large copies run on a side stream while
+    fused calls are launched on the main one; every call must equal the call
+    made alone, bit for bit, and report success."""
+    import ctypes
+    from frame_wise_gated_fwd_amd._lib import Shape
+    w = CLIP_5S.with_(T=100, S=300, name="clip_t100_s300_busy", state_std=0.02)
+    L = F.lib()
+    shp = Shape(w.B, w.H, w.T, w.S, w.D)
+    assert L.gdn_path(ctypes.byref(shp), 1) == 2
+    x = device_inputs(w, DEV)
+    args = (x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    ws = torch.empty(L.gdn_workspace_bytes(ctypes.byref(shp), 1), dtype=torch.uint8, device=DEV)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ws_ptr = ctypes.c_void_p(ws.data_ptr())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    ref_out, ref_st = F.frame_fwd(*args, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    alone = e0.elapsed_time(e1)
+    src = torch.empty(1 << 29, dtype=torch.float32, device=DEV).fill_(1.0)  # 2 GiB
+    dst = torch.empty_like(src)
+    side = torch.cuda.Stream()
+    for rnd in range(3):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                dst.copy_(src)
+        e0.record()
+        out, st = F.frame_fwd(*args, workspace=ws)
+        e1.record()
+        status = L.gdn_fused_status(ws_ptr, stream)
+        torch.cuda.synchronize()
+        # a longer call than alone means the copies held compute units meanwhile
+        log(f"  round {rnd}: status {status}, {e0.elapsed_time(e1):.3f} ms beside the copies, {alone:.3f} ms alone")
+        assert status == 0
+        assert torch.equal(out, ref_out) and torch.equal(st, ref_st)
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def test_fused_kernel_long_sequence():
     """4,000 frames, four times the 60 s workload's chain: the fused kernel's
     rings wrap 125 times and the state carries through 4,000 dependent steps;
