@@ -736,22 +736,22 @@ def main():
         gated = gated_leg(x, L, w, dev, stream, args.steps)
         log(f"gated: {gated}")
 
-    configs = None
+    config_runs = None
     attention = None
     workers = min(default_workers(), 16)
     if not args.no_configs:
         from synth import CLIP_5S, STRESS_B4
-        configs = []
+        config_runs = []
         log("5 s clip workload")
-        configs.append(config_leg(CLIP_5S, L, dev, stream, max(args.steps, 20),
+        config_runs.append(config_leg(CLIP_5S, L, dev, stream, max(args.steps, 20),
                                   [(0, h) for h in range(CLIP_5S.H)], [0, 1, 40, 79, 80], workers))
-        log(f"  {configs[-1]}")
+        log(f"  {config_runs[-1]}")
         log("B = 4 stress workload")
         # 16 heads: head h of batch element h % 4, so every XCD and both head
         # slots of each launch are among them; 8 frames each
-        configs.append(config_leg(STRESS_B4, L, dev, stream, max(3, args.steps // 4),
+        config_runs.append(config_leg(STRESS_B4, L, dev, stream, max(3, args.steps // 4),
                                   [(h % 4, h) for h in range(16)], [0, 1, 240, 480, 720, 958, 959, 960], workers))
-        log(f"  {configs[-1]}")
+        log(f"  {config_runs[-1]}")
     if not args.no_attention:
         log("softmax attention block (sinks + local window)")
         attention = attention_leg(L, dev, stream, 3, workers)
@@ -804,7 +804,7 @@ def main():
         "streamed_calls": streamed,
         "t1_call": t1,
         "gated_call": gated,
-        "other_configs": configs,
+        "other_configs": config_runs,
         "attention": attention,
         "host": host_info(),
     }
