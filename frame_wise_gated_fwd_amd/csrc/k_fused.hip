@@ -89,16 +89,18 @@ constexpr uint32_t kSpinLimit = 1u << 22;  // default polls before a wait gives 
 // steps (a build takes ~40 us, a step ~4 us); every wait then depends only
 // on earlier items as long as lag > kPrefetch + 1 and lag <= wg + wm (see
 // the ring notes above).  Measured on the 60 s workload (same box, same
-// inputs): with the wave-wide polls above, 4-8 M slots are 1-2 % faster
-// than 12-28 (which are within 1 % of each other) on two boxes, 3 are 3 %
-// slower; 24, 20 or 16 G/U slots starve the state pass (+30-40 %), and
-// queue lags of 20-28 are within 1 %.  (Before those polls, with one lane
+// inputs): with the wave-wide polls above and a cooperative launch, 4-8 M
+// slots were 1-2 % faster than 12-28 (which are within 1 % of each other)
+// on two boxes, 3 were 3 % slower; 24, 20 or 16 G/U slots starve the state
+// pass (+30-40 %), and queue lags of 20-28 are within 1 %.  With the
+// ordinary launch, 12 M slots against 6: the 961-frame call the same, an
+// 81-frame call 1.5 % and 40-frame calls 1 % faster (20 slots: between).  (Before those polls, with one lane
 // loading each flag, 20 M slots were 2-3.5 % faster than 12, 36-40 G/U
 // slots lost 2-5 %, and 96 overflowed the memory-side cache, +20 %.)
 struct RingShape {
   int wg, wm, lag;
 };
-constexpr RingShape kRing{32, 6, 24};
+constexpr RingShape kRing{32, 12, 24};
 static_assert(kRing.wg >= kPrefetch + 2 && kRing.wm >= 2 &&
                   kRing.lag > kPrefetch + 1 && kRing.lag <= kRing.wg + kRing.wm,
               "ring shape could stall the queue");

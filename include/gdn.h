@@ -199,7 +199,7 @@ size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype);
  * function of its arguments (per frame map, D*D*4 bytes = 64 KiB at D = 128):
  *   GDN_PATH_FUSED  a control block and per-head flags, then rings of G_t,
  *                   U_t and M_t slots for at most 16 heads at a time: a few
- *                   MiB per head whatever T is (71 MiB for 16 heads);
+ *                   MiB per head whatever T is (76 MiB for 16 heads);
  *   GDN_PATH_MFMA   the maps of at most three segments at once: with n =
  *                   ceil(T / 64) segments of at most c = ceil(T / n) frames,
  *                   3 * min(n, 3) buffers of B*H*c maps, each rounded up to
