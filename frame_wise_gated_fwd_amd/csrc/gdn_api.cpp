@@ -206,6 +206,24 @@ hipError_t side_init(Side& sd) {
   return hipSuccess;
 }
 
+// Fused launches on one device run one after another.  The fused kernel
+// needs no co-residency guarantee, but each launch holds up to 16
+// state-pass workgroups of every XCD while they wait for workers, so enough
+// of them at once on several streams could fill an XCD's 64 slots with
+// state-pass workgroups and leave none for workers (their bounded waits
+// would then end them with an error).  Per device: the event recorded after
+// the last fused launch and its stream; a launch on another stream waits
+// for it on the GPU.  Not under stream capture, whose graph must not depend
+// on work outside it.  A stream handle reused after its stream was
+// destroyed counts as the same stream.
+struct FusedOrder {
+  hipEvent_t done;
+  hipStream_t last;
+  bool have, ready;
+};
+FusedOrder g_fused_order[kMaxDevices];
+std::mutex g_fused_mu;
+
 // Frames per segment of the overlapped schedule (GDN_SEGMENT_FRAMES
 // overrides the default; read once).
 int64_t segment_frames() {
@@ -241,6 +259,14 @@ void teardown() {
       (void)hipStreamDestroy(sd.state_st);
       (void)hipStreamDestroy(sd.out_st);
       sd.ready = false;
+    }
+  }
+  {
+    std::lock_guard<std::mutex> lock(g_fused_mu);
+    for (FusedOrder& fo : g_fused_order) {
+      if (!fo.ready) continue;
+      (void)hipEventDestroy(fo.done);
+      fo.ready = fo.have = false;
     }
   }
   std::lock_guard<std::mutex> lock(g_timing_mu);
@@ -592,6 +618,19 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
     const int grid = fused_launch(in_dtype, d, ob, &queried);
     if (!queried) return GDN_E_HIP;
     if (grid > 0) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_E_HIP;
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(s, &cap) != hipSuccess) return GDN_E_HIP;
+      const bool ordered = cap == hipStreamCaptureStatusNone;
+      std::lock_guard<std::mutex> lock(g_fused_mu);
+      FusedOrder& fo = g_fused_order[dev];
+      if (ordered && !fo.ready) {
+        if (hipEventCreateWithFlags(&fo.done, hipEventDisableTiming) != hipSuccess) return GDN_E_HIP;
+        fo.ready = true;
+        register_teardown();
+      }
+      if (ordered && fo.have && fo.last != s && hipStreamWaitEvent(s, fo.done, 0) != hipSuccess) return GDN_E_HIP;
       // the gates first, into gamma, beta, which the fused kernel then reads
       // as inputs (one pass over the activations, which the state pass has
       // no slack to take on, nor the build items, the kernel's throughput)
@@ -600,11 +639,18 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
                                            d.frames, (int)d.H, (int)d.T, (int)d.S, s);
           }) != hipSuccess)
         return GDN_E_HIP;
-      return hip_status(timed(rec, s, 1, [&] {
+      const hipError_t e = timed(rec, s, 1, [&] {
         return gdn::launch_fused(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                  static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out,
                                  workspace, d.heads, d.T, (int)d.S, ks, spin_limit().load(), grid, s);
-      }));
+      });
+      if (e != hipSuccess) return GDN_E_HIP;
+      if (ordered) {
+        if (hipEventRecord(fo.done, s) != hipSuccess) return GDN_E_HIP;
+        fo.last = s;
+        fo.have = true;
+      }
+      return GDN_OK;
     }
     // this device cannot host the fused kernel: the three-kernel schedule,
     // whose workspace is larger

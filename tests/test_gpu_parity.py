@@ -635,6 +635,43 @@ def test_fused_kernel_completes_beside_other_work():
     torch.cuda.empty_cache()
 
 
+def test_fused_calls_on_many_streams():
+    """Fused calls issued on six streams at once, each with its own
+    workspace and output: the library runs fused launches of one device one
+    after another (each holds up to 16 state-pass workgroups per XCD while it
+    waits for workers), so all of them finish, equal the call made alone bit
+    for bit, and report success."""
+    import ctypes
+    from frame_wise_gated_fwd_amd._lib import Shape
+    w = CLIP_5S.with_(T=40, S=200, name="clip_t40_s200_streams", state_std=0.02)
+    L = F.lib()
+    shp = Shape(w.B, w.H, w.T, w.S, w.D)
+    assert L.gdn_path(ctypes.byref(shp), 1) == 2
+    x = device_inputs(w, DEV)
+    args = (x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    ref_out, ref_st = F.frame_fwd(*args)
+    torch.cuda.synchronize()
+    n = 6
+    streams = [torch.cuda.Stream() for _ in range(n)]
+    wsb = L.gdn_workspace_bytes(ctypes.byref(shp), 1)
+    wss = [torch.empty(wsb, dtype=torch.uint8, device=DEV) for _ in range(n)]
+    outs = [torch.empty_like(ref_out) for _ in range(n)]
+    sts = [torch.empty_like(ref_st) for _ in range(n)]
+    for rnd in range(2):
+        for i in range(n):
+            outs[i].fill_(float("nan"))
+        torch.cuda.synchronize()
+        for i in range(n):
+            with torch.cuda.stream(streams[i]):
+                F.frame_fwd(*args, out=outs[i], state_out=sts[i], workspace=wss[i])
+        torch.cuda.synchronize()
+        for i in range(n):
+            status = L.gdn_fused_status(ctypes.c_void_p(wss[i].data_ptr()), ctypes.c_void_p(streams[i].cuda_stream))
+            assert status == 0, (rnd, i, status)
+            assert torch.equal(outs[i], ref_out) and torch.equal(sts[i], ref_st), (rnd, i)
+        log(f"  round {rnd}: {n} streams exact")
+
+
 def test_fused_kernel_long_sequence():
     """4,000 frames, four times the 60 s workload's chain: the fused kernel's
     rings wrap 125 times and the state carries through 4,000 dependent steps;
