@@ -163,7 +163,10 @@ int gdn_fused_status(const void* workspace, void* stream);
  *                   XCD and its per-frame G_t, U_t, M_t pass between compute
  *                   units through that XCD's L2 instead of HBM.  Roles go
  *                   by the order in which workgroups start, so the kernel
- *                   makes progress with any number of them resident.  Every
+ *                   makes progress with any number of them resident; fused
+ *                   calls issued on different streams of one device run one
+ *                   after another (ordered on the GPU by an event, except
+ *                   while the stream is being captured).  Every
  *                   internal wait is bounded: if one runs out (only when
  *                   other work holds the device's compute units for longer
  *                   than the limit), the frames and state rows not produced
