@@ -34,8 +34,10 @@
 // progress that needs only earlier items (see the ring notes below), so any
 // running worker can finish the lowest unfinished item.  The state pass
 // holds at most 16 of an XCD's 64 workgroup slots, so as long as other work
-// on the device drains, workers start.  Should none start within the bounded
-// waits, the call ends with the error word set (see below), never hangs.
+// on the device drains, workers start (the library runs its fused launches
+// of one device one at a time, so they never hold those slots together).
+// Should none start within the bounded waits, the call ends with the error
+// word set (see below), never hangs.
 //
 // Hand-off between CUs of one XCD.  The L2 is shared by the XCD's CUs and
 // the vector L1 is write-through, so a producer makes data visible by
@@ -94,9 +96,10 @@ constexpr uint32_t kSpinLimit = 1u << 22;  // default polls before a wait gives 
 // on two boxes, 3 were 3 % slower; 24, 20 or 16 G/U slots starve the state
 // pass (+30-40 %), and queue lags of 20-28 are within 1 %.  With the
 // ordinary launch, 12 M slots against 6: the 961-frame call the same, an
-// 81-frame call 1.5 % and 40-frame calls 1 % faster (20 slots: between).  (Before those polls, with one lane
-// loading each flag, 20 M slots were 2-3.5 % faster than 12, 36-40 G/U
-// slots lost 2-5 %, and 96 overflowed the memory-side cache, +20 %.)
+// 81-frame call 1.5 % and 40-frame calls 1 % faster (20 slots: between).
+// (Before those polls, with one lane loading each flag, 20 M slots were
+// 2-3.5 % faster than 12, 36-40 G/U slots lost 2-5 %, and 96 overflowed the
+// memory-side cache, +20 %.)
 struct RingShape {
   int wg, wm, lag;
 };
