@@ -15,7 +15,7 @@ LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
 GDN_OK = 0
 GDN_F32 = 0
 GDN_BF16 = 1
-GDN_PATH_PLAIN, GDN_PATH_MFMA, GDN_PATH_FUSED = 0, 1, 2
+GDN_PATH_PLAIN, GDN_PATH_MFMA, GDN_PATH_FUSED, GDN_PATH_FRAME = 0, 1, 2, 3
 
 STATUS_NAMES = {0: "GDN_OK", 1: "GDN_E_NULLPTR", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE",
                 4: "GDN_E_UNSUPPORTED_D", 5: "GDN_E_WORKSPACE", 6: "GDN_E_ALIAS", 7: "GDN_E_HIP",
@@ -45,6 +45,7 @@ SIGNATURES = {
     "gdn_supports_d": (_i, [ctypes.c_int64]),
     "gdn_path": (_i, [_PS, _i]),
     "gdn_set_fused": (_i, [_i]),
+    "gdn_set_single_frame": (_i, [_i]),
     "gdn_workspace_bytes": (_sz, [_PS, _i]),
     "gdn_path_workspace_bytes": (_sz, [_PS, _i, _i]),
     "gdn_fused_status": (_i, [_cvp, _vp]),

@@ -59,6 +59,12 @@ def set_fused(enabled: bool) -> bool:
     return bool(lib().gdn_set_fused(1 if enabled else 0))
 
 
+def set_single_frame(enabled: bool) -> bool:
+    """gdn_set_single_frame: enable or disable the single-frame kernels for
+    later calls (process-wide); returns the previous setting."""
+    return bool(lib().gdn_set_single_frame(1 if enabled else 0))
+
+
 def workspace_bytes(B: int, H: int, T: int, S: int, D: int, in_dtype: torch.dtype) -> int:
     shp = Shape(B, H, T, S, D)
     return int(lib().gdn_workspace_bytes(ctypes.byref(shp), _dtype_code(in_dtype)))

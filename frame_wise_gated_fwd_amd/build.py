@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libgdn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["gdn_api.cpp", "k1_build.hip", "k2_state.hip", "k3_output.hip", "k_fused.hip", "k_backward.hip", "k_generic.hip", "k_empty.hip",
-           "gdn_noalloc.hip", "k_attn.hip", "k_gate.hip"]
+           "gdn_noalloc.hip", "k_attn.hip", "k_gate.hip", "k_frame1.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -131,6 +131,21 @@ bool fused_path(int in_dtype, const Dims& d) {
   return fused_enabled().load() && fast_path(in_dtype, d.D) && d.T > kFusedMinT;
 }
 
+// The single-frame kernels take bf16, D == 128 calls of one frame while
+// they are enabled: gdn_set_single_frame switches them; GDN_SINGLE_FRAME=0
+// in the environment makes the default "disabled".
+std::atomic<int>& single_frame_enabled() {
+  static std::atomic<int> on{[] {
+    const char* e = std::getenv("GDN_SINGLE_FRAME");
+    return e && std::atoi(e) == 0 ? 0 : 1;
+  }()};
+  return on;
+}
+
+bool frame1_path(int in_dtype, const Dims& d) {
+  return single_frame_enabled().load() && fast_path(in_dtype, d.D) && d.T == 1;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t{255}; }
@@ -332,6 +347,8 @@ size_t path_workspace(const Dims& d, int in_dtype, int path) {
     case GDN_PATH_FUSED:
       return fast_path(in_dtype, d.D) && d.T > kFusedMinT ? (size_t)gdn::fused_workspace_bytes(d.heads)
                                                           : SIZE_MAX;
+    case GDN_PATH_FRAME:
+      return fast_path(in_dtype, d.D) && d.T == 1 ? 0 : SIZE_MAX;
     case GDN_PATH_MFMA: {
       if (!fast_path(in_dtype, d.D)) return SIZE_MAX;
       const Segments g = segments_of(d.T);
@@ -596,6 +613,7 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
   const bool ob = out_dtype == GDN_BF16;
   const int planned = !has_in ? GDN_PATH_PLAIN
                       : fused_path(in_dtype, d) ? GDN_PATH_FUSED
+                      : frame1_path(in_dtype, d) ? GDN_PATH_FRAME
                       : fast_path(in_dtype, d.D) ? GDN_PATH_MFMA
                                                  : GDN_PATH_PLAIN;
   // the planned path's workspace first, with no device query
@@ -655,6 +673,18 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
     // this device cannot host the fused kernel: the three-kernel schedule,
     // whose workspace is larger
     if (!workspace_ok(path_workspace(d, in_dtype, GDN_PATH_MFMA), &st)) return st;
+  }
+  if (planned == GDN_PATH_FRAME) {
+    if (gate && timed(rec, s, 0, [&] {
+          return gdn::launch_frame_gates(gate->a, gate->b, gate->A_log, gate->dt_bias, gate->gamma, gate->beta,
+                                         d.frames, (int)d.H, (int)d.T, (int)d.S, s);
+        }) != hipSuccess)
+      return GDN_E_HIP;
+    return hip_status(timed(rec, s, 1, [&] {
+      return gdn::launch_frame1(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out,
+                                d.heads, (int)d.S, ks, s);
+    }));
   }
   // separate kernels: the gates first, into gamma, beta
   if (gate && timed(rec, s, 0, [&] {
@@ -781,6 +811,8 @@ const char* gdn_status_str(int s) {
 
 int gdn_set_fused(int enabled) { return fused_enabled().exchange(enabled ? 1 : 0); }
 
+int gdn_set_single_frame(int enabled) { return single_frame_enabled().exchange(enabled ? 1 : 0); }
+
 unsigned gdn_set_spin_limit(unsigned polls) { return spin_limit().exchange(polls); }
 
 int gdn_supports_d(int64_t D) { return D >= 16 && D <= 128 && D % 16 == 0; }
@@ -794,6 +826,7 @@ int gdn_path(const gdn_shape* shape, int in_dtype) {
     // float32 and bf16 outputs have the same launch size
     if (fused_launch(in_dtype, d, false, &queried) > 0 || !queried) return GDN_PATH_FUSED;
   }
+  if (frame1_path(in_dtype, d)) return GDN_PATH_FRAME;
   return fast_path(in_dtype, d.D) ? GDN_PATH_MFMA : GDN_PATH_PLAIN;
 }
 
@@ -812,6 +845,7 @@ size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype) {
     // no device to ask: what the three-kernel schedule needs, the larger
     return path_workspace(d, in_dtype, grid > 0 ? GDN_PATH_FUSED : GDN_PATH_MFMA);
   }
+  if (frame1_path(in_dtype, d)) return 0;
   return path_workspace(d, in_dtype, fast_path(in_dtype, d.D) ? GDN_PATH_MFMA : GDN_PATH_PLAIN);
 }
 

@@ -79,6 +79,13 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         float* state_out, void* workspace, int64_t heads, int64_t T, int S, float ks,
                         uint32_t spin_limit, int grid, hipStream_t st);
 
+// ---- single frame (k_frame1.hip): T == 1, bf16, D == 128 -----------------
+// Two launches on `st`, no workspace: row workgroups write M' (state_out),
+// then output workgroups O = Q M'^T.
+hipError_t launch_frame1(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
+                         const float* beta, const float* state_in, void* out, bool out_bf16, float* state_out,
+                         int64_t heads, int S, float ks, hipStream_t st);
+
 // ---- plain float32 path: any supported D, f32 or bf16 inputs ---------------
 hipError_t launch_build_generic(const void* k, const void* v, bool in_bf16, float* G, float* U,
                                 int64_t frames, int S, int D, float ks, hipStream_t st);

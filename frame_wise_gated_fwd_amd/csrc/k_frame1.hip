@@ -1,0 +1,410 @@
+// The forward of a single frame (T = 1; bf16 inputs, head dim 128), for
+// frame-by-frame (chunk-causal) generation, where every call carries one
+// latent frame (bilibili cv49203711, second key point; the zhichai.net
+// page's Stage 4 rollout at constant memory).
+//
+// One step of the recurrence (zhichai.net, section 1: decay gate gamma,
+// delta-rule correction beta),
+//   M' = gamma (M - beta M G) + beta U,   G = K^T K,  U = V^T K,
+// equals, with G and U written out as sums over the frame's tokens,
+//   M' = gamma M + beta sum_s (v_s - gamma M k_s) k_s^T:
+// every token adds the residual of its value against the decayed state's
+// prediction (the delta rule) times its key.  Rows of M' then depend only on
+// the same rows of M: row block r of M' needs M's rows in r, the values'
+// columns in r and all keys.  So one frame spreads over 8 workgroups per
+// head (16 rows each) with no reduction between workgroups, where the
+// frame-parallel kernels give a frame to one workgroup (or four).
+//
+// Two launches, with no waits between workgroups and no workspace:
+//  * rows (k_frame1_rows): 8 workgroups of 8 waves per head, workgroup r
+//    owning rows [16r, 16r + 16) of M'.  Each reads all of the frame's keys,
+//    its 16 columns of the values and its 16 rows of M, and writes its rows
+//    of M' to state_out.  Head h's workgroups have ids that the dispatcher
+//    deals to one XCD (ids h % 8 + 8 j), so one fetch of the keys from HBM
+//    serves all 8 through that XCD's L2; each workgroup starts on another
+//    tile, so the first fetches cover the frame.  A workgroup takes a whole
+//    CU (160 KB of LDS), so two never share one;
+//  * outputs (k_frame1_out): O = Q M'^T for 64-token tiles, after the rows
+//    (stream order).
+//
+#include "gdn_common.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int D = 128;
+constexpr int kXcd = 8;
+constexpr int kTile = 64;        // tokens per MFMA tile
+constexpr int kRowWgs = 8;       // row workgroups per head, 16 rows of M' each
+constexpr int kRowWaves = 8;     // waves per row workgroup
+constexpr int kMaxOutParts = 16; // output workgroups per head
+
+struct Args {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* gamma;
+  const float* beta;
+  const float* state_in;  // null: zero state
+  void* out;
+  float* state_out;
+  int64_t heads;
+  int S;
+  int oparts, otiles;     // output workgroups per head, 64-token tiles each
+  float ks;
+};
+
+// This wave's LDS writes are done before its later LDS reads (the tiles a
+// wave writes are read only by its own lanes).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// A key tile in LDS: 64 token rows x 256 bytes.  Row s keeps its sixteen
+// 16-byte chunks in the order c ^ swz(s): for 8 consecutive rows swz is a
+// permutation of 0..7 (16-byte writes of one chunk from 8 rows hit 8
+// distinct 4-bank groups), and for rows 4a .. 4a+3 it is 0, 2, 4, 6 or
+// 1, 3, 5, 7, so the transposed 8-byte reads of a chunk pair from 4 rows
+// cover all 32 banks once.
+__device__ __forceinline__ int swz(int s) { return ((s & 3) << 1) | ((s >> 2) & 1); }
+__device__ __forceinline__ int tile_off(int s, int c) { return s * 256 + ((c ^ swz(s)) << 4); }
+
+// Global loads are contiguous (a wave's 16-byte loads cover whole rows),
+// and the MFMA operands are read from LDS: loading a 16-row operand layout
+// straight from memory (each load instruction 16 rows x 64 bytes) moves a
+// workgroup's 128 KB at about a third of the rate of contiguous loads.
+//
+// Rows of float32 M (row length 512 bytes) into LDS as bf16 hi and lo
+// planes in the tile layout above (row stride 256 bytes per plane): float4
+// q of row r (q = 0..31) goes to the 8-byte half q % 2 of chunk q / 2.
+__device__ __forceinline__ void stage_m4(char* planes, int plane_bytes, int r, int q, f32x4 x) {
+  const u32x2 p0 = split2(x[0], x[1]), p1 = split2(x[2], x[3]);
+  const int off = tile_off(r, q >> 1) + 8 * (q & 1);
+  *reinterpret_cast<u32x2*>(planes + off) = (u32x2){p0.x, p1.x};
+  *reinterpret_cast<u32x2*>(planes + plane_bytes + off) = (u32x2){p0.y, p1.y};
+}
+
+// LDS of a row workgroup: per wave a key tile (16 KB) and its residuals as
+// [token][16 rows] bf16, hi and lo planes (4 KB); after the token loop the
+// same bytes hold the waves' sums for the reduction (8 KB per wave).
+constexpr int kWaveLds = kTile * 256 + 2 * kTile * 32;
+constexpr int kRowLds = kRowWaves * kWaveLds;
+static_assert(kRowLds <= 160 * 1024, "a row workgroup's LDS fits a CU");
+static_assert(kRowLds >= kRowWaves * 8 * 64 * 16, "the reduction reuses the tiles' LDS");
+
+// ---------------------------------------------------------------------------
+// launch 1: rows [16rb, 16rb + 16) of head h's M', one workgroup each
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1_rows(Args a) {
+  __shared__ __attribute__((aligned(16))) char lds[kRowLds];
+  // ids h % 8 + 8 j: head h's workgroups on one XCD when the dispatcher
+  // deals ids to the 8 XCDs in turn (only the L2 sharing depends on it)
+  const int xs = blockIdx.x % kXcd, local = blockIdx.x / kXcd;
+  const int64_t hl = xs + (int64_t)kXcd * (local / kRowWgs);
+  const int rb = local % kRowWgs;
+  if (hl >= a.heads) return;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
+  const int S = a.S, r0 = 16 * rb;
+  const int ntiles = (S + kTile - 1) / kTile;
+  const uint16_t* Kh = a.k + hl * S * D;
+  const uint16_t* Vh = a.v + hl * S * D;
+  const float* Mi = a.state_in ? a.state_in + hl * D * D : nullptr;
+  float* Mo = a.state_out + hl * D * D;
+  char* Kt = lds + w * kWaveLds;
+  char* Rt = Kt + kTile * 256;
+  const float gks = a.gamma[hl] * a.ks;
+
+  // this wave's tiles: t = (w + rb) % 8 + 8 j, so that the head's 8
+  // workgroups start on different tiles
+  const int first = (w + rb) % kRowWaves;
+
+  // a tile's keys, loaded row by row (load i of lane l: token 4i + l / 16,
+  // 16-byte chunk l % 16), and this lane's values (token 16tb + n, dims
+  // r0 + 4g .. +3).  Tokens past the frame load its last token and are
+  // zeroed, so that all loads are issued at once.
+  u32x4 kx[16];
+  u32x2 vv[4];
+  auto load_tile = [&](int tile) {
+    const int s0 = tile * kTile, last = S - 1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      kx[i] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)min(s0 + 4 * i + (l >> 4), last) * D + 8 * (l & 15));
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+      vv[tb] = *reinterpret_cast<const u32x2*>(Vh + (int64_t)min(s0 + 16 * tb + n, last) * D + r0 + 4 * g);
+  };
+  if (first < ntiles) load_tile(first);
+
+  // M's rows r0 .. r0 + 15 as MFMA A operands (lane (m, g): row r0 + m,
+  // columns 32kb + 8g .. +7, bf16 hi/lo), staged once through LDS: one
+  // 16-byte load per thread
+  u32x4 mh[4], ml[4];
+  if (Mi) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(Mi + (r0 + (tid >> 5)) * D + 4 * (tid & 31));
+    stage_m4(lds, 16 * 256, tid >> 5, tid & 31, x);
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      mh[kb] = *reinterpret_cast<const u32x4*>(lds + tile_off(n, 4 * kb + g));
+      ml[kb] = *reinterpret_cast<const u32x4*>(lds + 16 * 256 + tile_off(n, 4 * kb + g));
+    }
+    __syncthreads();  // wave 0's tile overwrites the staging area
+  }
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int jb = 0; jb < 8; ++jb) acc[jb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // the transposed reads: lane L = 4e + q of a 16-lane group names row
+  // base + e, 4 columns from 4q
+  const int tre = (l & 15) >> 2, trq = l & 3;
+
+  for (int tile = first; tile < ntiles; tile += kRowWaves) {
+    const int cnt = min(kTile, S - tile * kTile);
+    // the keys into LDS (rows past the frame as zeros)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 4 * i + (l >> 4);
+      *reinterpret_cast<u32x4*>(Kt + tile_off(row, l & 15)) = row < cnt ? kx[i] : (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+      if (16 * tb + n >= cnt) vv[tb] = (u32x2){0u, 0u};
+    wave_lds_sync();
+    // the keys as MFMA B operands: lane (n, g) token 16tb + n, dims 32kb + 8g .. +7
+    u32x4 kf[4][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) kf[tb][kb] = *reinterpret_cast<const u32x4*>(Kt + tile_off(16 * tb + n, 4 * kb + g));
+    // C^T = M_r K^T: lane (n, g) ends with (M k_s)[r0 + 4g + i], s = 16tb + n
+    f32x4 c[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) c[tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (Mi) {
+      // the four accumulators in turn, so that no MFMA waits for the one
+      // just before it
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) c[tb] = mfma16x16x32(mh[kb], kf[tb][kb], c[tb]);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) c[tb] = mfma16x16x32(ml[kb], kf[tb][kb], c[tb]);
+      }
+    }
+    // residuals, one rounding each, into LDS as [token][row] hi/lo
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const float r0v = __builtin_fmaf(-gks, c[tb][0], bf2f(vv[tb].x & 0xffffu));
+      const float r1v = __builtin_fmaf(-gks, c[tb][1], bf2f(vv[tb].x >> 16));
+      const float r2v = __builtin_fmaf(-gks, c[tb][2], bf2f(vv[tb].y & 0xffffu));
+      const float r3v = __builtin_fmaf(-gks, c[tb][3], bf2f(vv[tb].y >> 16));
+      const u32x2 p0 = split2(r0v, r1v), p1 = split2(r2v, r3v);
+      const int off = (16 * tb + n) * 32 + 8 * g;
+      *reinterpret_cast<u32x2*>(Rt + off) = (u32x2){p0.x, p1.x};
+      *reinterpret_cast<u32x2*>(Rt + kTile * 32 + off) = (u32x2){p0.y, p1.y};
+    }
+    // the next tile's loads are in flight during this tile's products
+    if (tile + kRowWaves < ntiles) load_tile(tile + kRowWaves);
+    wave_lds_sync();
+    // P_w += R^T K over the tile's tokens
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int row0 = 32 * kb + 8 * g + tre;
+      u32x4 ra[2];
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl) {
+        const u32x2 x0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(Rt + pl * kTile * 32 + row0 * 32 + 8 * trq));
+        const u32x2 x1 =
+            lds_read_tr16(reinterpret_cast<const uint16_t*>(Rt + pl * kTile * 32 + (row0 + 4) * 32 + 8 * trq));
+        ra[pl] = (u32x4){x0.x, x0.y, x1.x, x1.y};
+      }
+      u32x4 kt[8];
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) {
+        const int ch = 2 * jb + (trq >> 1), hf = 8 * (trq & 1);
+        const u32x2 x0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(Kt + tile_off(row0, ch) + hf));
+        const u32x2 x1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(Kt + tile_off(row0 + 4, ch) + hf));
+        kt[jb] = (u32x4){x0.x, x0.y, x1.x, x1.y};
+      }
+      // all hi products, then all lo products: consecutive MFMAs update
+      // different accumulators
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) acc[jb] = mfma16x16x32(ra[0], kt[jb], acc[jb]);
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) acc[jb] = mfma16x16x32(ra[1], kt[jb], acc[jb]);
+    }
+    wave_lds_sync();  // this tile's LDS reads are done before the next tile's writes
+  }
+
+  // M's elements this lane updates: rows r0 + 4g + i, column 16 w + n
+  // (wave w finishes column block w)
+  float m_old[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m_old[i] = Mi ? Mi[(r0 + 4 * g + i) * D + 16 * w + n] : 0.f;
+  // the waves' sums, added in the order w = 0..7: lane (n, g) holds
+  // P[r0 + 4g + i][16jb + n] in acc[jb]
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
+#pragma unroll
+  for (int jb = 0; jb < 8; ++jb) red[(w * 8 + jb) * 64 + l] = acc[jb];
+  __syncthreads();
+  const float gam = a.gamma[hl], bks = a.beta[hl] * a.ks;
+  f32x4 sum = red[w * 64 + l];
+#pragma unroll
+  for (int v = 1; v < kRowWaves; ++v) sum += red[(v * 8 + w) * 64 + l];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Mo[(r0 + 4 * g + i) * D + 16 * w + n] = __builtin_fmaf(bks, sum[i], gam * m_old[i]);
+}
+
+// ---------------------------------------------------------------------------
+// launch 2: O = Q M'^T, workgroup (head, part) for the part's 64-token tiles
+// ---------------------------------------------------------------------------
+// LDS of an output workgroup: the Q tile (16 KB) and each wave's 32 rows of
+// M' as bf16 hi/lo (16 KB per wave).
+constexpr int kOutLds = kTile * 256 + 4 * 2 * 32 * 256;
+
+template <bool kOutBf16>
+__global__ __launch_bounds__(256, 2) void k_frame1_out(Args a) {
+  __shared__ __attribute__((aligned(16))) char lds[kOutLds];
+  const int64_t hl = blockIdx.x / a.oparts;
+  const int op = blockIdx.x % a.oparts;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
+  const int S = a.S;
+  const int t0 = op * a.otiles * kTile;
+  const int t1 = min(S, t0 + a.otiles * kTile);
+  const uint16_t* Qh = a.q + hl * S * D;
+  constexpr int kOutB = kOutBf16 ? 2 : 4;
+  char* Oh = static_cast<char*>(a.out) + hl * S * D * kOutB;
+
+  char* Qt = lds;
+  char* Mw = lds + kTile * 256 + w * (2 * 32 * 256);  // this wave's M' rows, hi then lo plane
+
+  // a Q tile, row by row: load i of thread t is token (t + 256 i) / 16,
+  // chunk (t + 256 i) % 16; tokens past the range load its last token (their
+  // outputs are not stored)
+  u32x4 qx[4];
+  auto load_q = [&](int s0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int x = tid + 256 * i;
+      qx[i] = *reinterpret_cast<const u32x4*>(Qh + (int64_t)min(s0 + (x >> 4), t1 - 1) * D + 8 * (x & 15));
+    }
+  };
+  load_q(t0);
+  // this wave's rows 32w .. 32w + 31 of M', row by row (load i of lane l:
+  // row 32w + 2i + l / 32, float4 l % 32), into LDS as bf16 hi/lo
+  {
+    const float* Mo = a.state_out + hl * D * D;
+    f32x4 x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = *reinterpret_cast<const f32x4*>(Mo + (32 * w + 2 * i + (l >> 5)) * D + 4 * (l & 31));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) stage_m4(Mw, 32 * 256, 2 * i + (l >> 5), l & 31, x[i]);
+  }
+  wave_lds_sync();
+  u32x4 mh[2][4], ml[2][4];
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      mh[ib][kb] = *reinterpret_cast<const u32x4*>(Mw + tile_off(16 * ib + n, 4 * kb + g));
+      ml[ib][kb] = *reinterpret_cast<const u32x4*>(Mw + 32 * 256 + tile_off(16 * ib + n, 4 * kb + g));
+    }
+
+  for (int s0 = t0; s0 < t1; s0 += kTile) {
+    if (s0 > t0) {
+      __syncthreads();  // every wave is done with the previous tile
+      load_q(s0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int x = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(Qt + tile_off(x >> 4, x & 15)) = qx[i];
+    }
+    __syncthreads();
+    // B operands: lane (n, g) token 16tb + n, dims 32kb + 8g .. +7
+    u32x4 qf[4][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) qf[tb][kb] = *reinterpret_cast<const u32x4*>(Qt + tile_off(16 * tb + n, 4 * kb + g));
+    f32x4 o[2][4];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) o[ib][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) o[ib][tb] = mfma16x16x32(mh[ib][kb], qf[tb][kb], o[ib][tb]);
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) o[ib][tb] = mfma16x16x32(ml[ib][kb], qf[tb][kb], o[ib][tb]);
+    }
+    // lane (n, g): O[s0 + 16tb + n][32w + 16ib + 4g .. +3]
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int s = s0 + 16 * tb + n;
+      if (s >= t1) continue;
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        const int64_t e = (int64_t)s * D + 32 * w + 16 * ib + 4 * g;
+        if constexpr (kOutBf16)
+          st_nt(reinterpret_cast<u32x2*>(Oh + e * 2),
+                (u32x2){cvt2bf(o[ib][tb][0], o[ib][tb][1]), cvt2bf(o[ib][tb][2], o[ib][tb][3])});
+        else
+          st_nt(reinterpret_cast<f32x4*>(Oh + e * 4), o[ib][tb]);
+      }
+    }
+  }
+}
+
+// Output workgroups of a frame of S tokens: at most kMaxOutParts, each a
+// whole number of 64-token tiles.
+void split_tiles(int S, int* parts, int* tiles_each) {
+  const int tiles = (S + kTile - 1) / kTile;
+  const int want = tiles < kMaxOutParts ? tiles : kMaxOutParts;
+  *tiles_each = (tiles + want - 1) / want;
+  *parts = (tiles + *tiles_each - 1) / *tiles_each;
+}
+
+}  // namespace
+
+hipError_t launch_frame1(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
+                         const float* beta, const float* state_in, void* out, bool out_bf16, float* state_out,
+                         int64_t heads, int S, float ks, hipStream_t st) {
+  Args a;
+  split_tiles(S, &a.oparts, &a.otiles);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.state_in = state_in;
+  a.out = out;
+  a.state_out = state_out;
+  a.heads = heads;
+  a.S = S;
+  a.ks = ks;
+  const int64_t rows_grid = (heads + kXcd - 1) / kXcd * kXcd * kRowWgs;
+  const int64_t out_grid = heads * a.oparts;
+  if (rows_grid > 0x7fffffff || out_grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_frame1_rows, dim3((unsigned)rows_grid), dim3(64 * kRowWaves), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (out_bf16)
+    hipLaunchKernelGGL(k_frame1_out<true>, dim3((unsigned)out_grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_frame1_out<false>, dim3((unsigned)out_grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -713,8 +713,11 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     a.S = S;
     a.ks = ks;
     a.spin_limit = spin_limit ? spin_limit : kSpinLimit;
+    // the error word (word 0) is cleared for the first group only, so that
+    // a wait that ran out in any group of the call stays reported
+    const int skip = h0 == 0 ? 0 : 1;
     hipLaunchKernelGGL(k_fused_init, dim3((nwords + 255) / 256), dim3(256), 0, st,
-                       reinterpret_cast<uint32_t*>(ws), nwords);
+                       reinterpret_cast<uint32_t*>(ws) + skip, nwords - skip);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     void* params[] = {&a};

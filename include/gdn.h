@@ -109,6 +109,18 @@ int gdn_supports_d(int64_t D);
 int gdn_set_fused(int enabled);
 
 /*
+ * Enables (nonzero) or disables (0) the single-frame kernels
+ * (GDN_PATH_FRAME below) for calls made after it returns, process-wide;
+ * returns the previous setting.  The default is enabled unless the
+ * environment variable GDN_SINGLE_FRAME is 0 when the library first needs
+ * the setting.  They sum a frame's tokens in another order than the other
+ * paths, so a single-frame call agrees with the first frame of a longer call
+ * to float32 rounding; disabled, single-frame calls take GDN_PATH_MFMA and
+ * reproduce a longer call over the same frames bit for bit.
+ */
+int gdn_set_single_frame(int enabled);
+
+/*
  * Testing aid for the fused kernel's failure path: the number of polls after
  * which one of its internal waits gives up, for launches made after it
  * returns, process-wide; 0 restores the default (2^22 polls: seconds for a
@@ -179,6 +191,16 @@ int gdn_fused_status(const void* workspace, void* stream);
  *                   (gdn_set_fused), these shapes take GDN_PATH_MFMA.  When
  *                   no device can be queried (no GPU), gdn_path reports the
  *                   path of a device that hosts the fused kernel;
+ *   GDN_PATH_FRAME  bf16, D == 128, T == 1 (one frame per call, as in
+ *                   frame-by-frame generation): two launches on `stream`,
+ *                   no workspace.  The step written per token, M' = gamma M
+ *                   + beta sum_s (v_s - gamma M k_s) k_s^T, gives each block
+ *                   of 16 rows of M' to one workgroup (8 per head, with no
+ *                   reduction or waits between workgroups); the second
+ *                   launch computes O = Q M'^T.  Deterministic; equal to
+ *                   GDN_PATH_MFMA's result to float32 rounding, not bit for
+ *                   bit (gdn_set_single_frame).  While disabled,
+ *                   GDN_PATH_MFMA;
  *   GDN_PATH_PLAIN  every other supported case: three float32 kernels on
  *                   `stream`; also empty shapes (one small float32 kernel
  *                   or none, see "Empty shapes" above);
@@ -186,7 +208,7 @@ int gdn_fused_status(const void* workspace, void* stream);
  * Results do not depend on the segmentation: the state pass carries the
  * float32 state exactly from one segment to the next.
  */
-enum { GDN_PATH_PLAIN = 0, GDN_PATH_MFMA = 1, GDN_PATH_FUSED = 2 };
+enum { GDN_PATH_PLAIN = 0, GDN_PATH_MFMA = 1, GDN_PATH_FUSED = 2, GDN_PATH_FRAME = 3 };
 int gdn_path(const gdn_shape* shape, int in_dtype);
 
 /*
@@ -203,6 +225,7 @@ size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype);
  *   GDN_PATH_FUSED  a control block and per-head flags, then rings of G_t,
  *                   U_t and M_t slots for at most 16 heads at a time: a few
  *                   MiB per head whatever T is (76 MiB for 16 heads);
+ *   GDN_PATH_FRAME  none (0); T == 1 only;
  *   GDN_PATH_MFMA   the maps of at most three segments at once: with n =
  *                   ceil(T / 64) segments of at most c = ceil(T / n) frames,
  *                   3 * min(n, 3) buffers of B*H*c maps, each rounded up to
@@ -211,7 +234,8 @@ size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype);
  *                   3 * B*H*T*D*D*4 bytes, each third rounded up to 256.
  * 0 for an empty shape; SIZE_MAX for an invalid shape or dtype, an unknown
  * path, or a path that cannot take the shape (fused: bf16, D == 128 and
- * T > 32 only; MFMA: bf16 and D == 128 only).
+ * T > 32 only; single frame: bf16, D == 128 and T == 1 only; MFMA: bf16 and
+ * D == 128 only).
  */
 size_t gdn_path_workspace_bytes(const gdn_shape* shape, int in_dtype, int path);
 

@@ -55,6 +55,11 @@ def test_path_selection():
     assert L.gdn_path(ctypes.byref(_shape(1, 16, 961, 880, 128)), BF16) == 2
     assert L.gdn_path(ctypes.byref(_shape(4, 16, 961, 880, 128)), BF16) == 2
     assert L.gdn_path(ctypes.byref(_shape(1, 16, 32, 880, 128)), BF16) == 1
+    assert L.gdn_path(ctypes.byref(_shape(1, 16, 1, 880, 128)), BF16) == 3
+    assert L.gdn_path(ctypes.byref(_shape(5, 16, 1, 1, 128)), BF16) == 3
+    assert L.gdn_path(ctypes.byref(_shape(1, 16, 2, 880, 128)), BF16) == 1
+    assert L.gdn_path(ctypes.byref(_shape(1, 16, 1, 880, 64)), BF16) == 0
+    assert L.gdn_path(ctypes.byref(_shape(1, 16, 1, 880, 128)), F32) == 0
     assert L.gdn_path(ctypes.byref(_shape(1, 16, 33, 880, 128)), BF16) == 2
     assert L.gdn_path(ctypes.byref(_shape(1, 16, 64, 880, 128)), BF16) == 2
     assert L.gdn_path(ctypes.byref(_shape(1, 16, 961, 880, 128)), F32) == 0
@@ -77,6 +82,30 @@ def test_fused_switch_selects_path():
         L.gdn_set_fused(prev)
 
 
+def test_single_frame_switch_selects_path():
+    L = F.lib()
+    s = _shape(1, 16, 1, 880, 128)
+    prev = L.gdn_set_single_frame(0)
+    try:
+        assert L.gdn_path(ctypes.byref(s), BF16) == 1
+        assert L.gdn_set_single_frame(1) == 0
+        assert L.gdn_path(ctypes.byref(s), BF16) == 3
+        assert F.set_single_frame(False) is True
+        assert L.gdn_path(ctypes.byref(s), BF16) == 1
+        # the fused switch leaves single frames alone
+        assert F.set_fused(False) is True
+        assert F.set_single_frame(True) is False
+        assert L.gdn_path(ctypes.byref(s), BF16) == 3
+    finally:
+        L.gdn_set_single_frame(prev)
+        F.set_fused(True)
+
+
+def _frame_bytes(H, S, B=1):
+    """The single-frame kernels need no workspace."""
+    return 0
+
+
 def _mfma_bytes(B, H, T, D=128):
     """The three-kernel schedule: three map buffers per segment slot, at
     most three segments of at most ceil(T / n) frames held at once."""
@@ -87,7 +116,7 @@ def _mfma_bytes(B, H, T, D=128):
 
 
 SIZE_MAX = ctypes.c_size_t(-1).value
-FUSED, MFMA, PLAIN = 2, 1, 0
+FRAME, FUSED, MFMA, PLAIN = 3, 2, 1, 0
 
 
 def test_workspace_bytes():
@@ -106,6 +135,16 @@ def test_workspace_bytes():
     s = _shape(1, 3, 5, 7, 48)
     assert L.gdn_workspace_bytes(ctypes.byref(s), F32) == 3 * ((15 * 48 * 48 * 4 + 255) // 256 * 256)
     assert L.gdn_workspace_bytes(None, BF16) == 0
+    # a single frame: none
+    for B, H, S in ((1, 16, 880), (1, 1, 1), (4, 16, 5000), (1, 40, 64)):
+        s = _shape(B, H, 1, S, 128)
+        assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == 0
+    prev = L.gdn_set_single_frame(0)
+    try:
+        s = _shape(1, 16, 1, 880, 128)
+        assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == _mfma_bytes(1, 16, 1)
+    finally:
+        L.gdn_set_single_frame(prev)
 
 
 def test_path_workspace_bytes():
@@ -121,6 +160,13 @@ def test_path_workspace_bytes():
     # the three-kernel schedule: at most three segments of maps
     for B, H, T in ((1, 16, 961), (4, 16, 961), (1, 2, 64), (1, 2, 65), (1, 2, 200), (3, 5, 1)):
         assert pw(_shape(B, H, T, 880, 128), MFMA) == _mfma_bytes(B, H, T)
+    # single frame: a control block only
+    assert pw(_shape(1, 16, 1, 880, 128), FRAME) == 0
+    for B, H, S in ((1, 1, 1), (1, 3, 64), (1, 3, 65), (2, 16, 1024), (1, 16, 1025), (1, 5, 5000)):
+        assert pw(_shape(B, H, 1, S, 128), FRAME) == _frame_bytes(H, S, B)
+    assert pw(_shape(1, 16, 2, 880, 128), FRAME) == SIZE_MAX
+    assert pw(_shape(1, 16, 1, 880, 64), FRAME) == SIZE_MAX
+    assert pw(_shape(1, 16, 1, 880, 128), FRAME, F32) == SIZE_MAX
     # the plain path: every frame's maps
     s = _shape(1, 3, 5, 7, 48)
     assert pw(s, PLAIN, F32) == 3 * ((15 * 48 * 48 * 4 + 255) // 256 * 256)

@@ -79,14 +79,15 @@ def _planned_need(shape, in_dt, frames, map_elems):
     """Workspace of the path the call plans before asking the device: the
     fused kernel's (bf16, D = 128, T > 32, as gdn_path_workspace_bytes
     reports it), the three-kernel schedule's three segments of maps (bf16,
-    D = 128), else every frame's maps."""
+    D = 128; none for a single frame), else every frame's maps."""
     B, H, T, S, D = shape
     if in_dt == 1 and D == 128 and T > 32:
         return F.lib().gdn_path_workspace_bytes(ctypes.byref(Shape(*shape)), in_dt, 2)
     if in_dt == 1 and D == 128:
         n = -(-T // 64)
         cap = -(-T // n)
-        return 3 * min(n, 3) * ((B * H * cap * D * D * 4 + 255) // 256 * 256)
+        mfma = 3 * min(n, 3) * ((B * H * cap * D * D * 4 + 255) // 256 * 256)
+        return 0 if T == 1 else mfma  # a single frame needs no workspace
     return 3 * ((map_elems * 4 + 255) // 256 * 256)
 
 

@@ -195,7 +195,20 @@ def test_forward_seq60s_full_size():
     _forward_parity(w, frames=sample_frames(w.T, seed=3), workspace=ws)
 
 
-def test_forward_stream60s_matches_single_call():
+@pytest.fixture
+def mfma_single_frames():
+    """Single-frame calls through the three-kernel path, which sums a frame's
+    tokens in the same order as a longer call."""
+    prev = F.set_single_frame(False)
+    yield
+    F.set_single_frame(prev)
+
+
+def test_forward_stream60s_matches_single_call(mfma_single_frames):
+    """24 calls of 40 frames and one of a single frame, the state carried in
+    place, against one call: same kernels and arithmetic, bit for bit (the
+    single frame through the three-kernel path; the single-frame kernels are
+    checked against the oracle below)."""
     w = STREAM_60S
     out_s, st_s, x = _forward_parity(w, frames=sample_frames(w.T, seed=4), chunks=w.stream_chunks)
     out1, st1 = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
@@ -299,7 +312,7 @@ def test_fused_kernel_equals_three_kernel_path_bitwise():
         assert torch.equal(s1, s2) and torch.equal(o1, o2), w.name
 
 
-def test_single_frame_calls_equal_one_call_bitwise():
+def test_single_frame_calls_equal_one_call_bitwise(mfma_single_frames):
     """Launches of a few frames take the small-launch kernels (a build with
     more loads in flight, an output split over token parts); 12 successive
     T=1 calls must reproduce one T=12 call (16 x 12 frames, full-size
@@ -335,7 +348,7 @@ def test_small_launch_threshold_is_bitwise():
 
 
 @pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
-def test_single_frame_launch_is_bitwise(odt):
+def test_single_frame_launch_is_bitwise(odt, mfma_single_frames):
     """A single-frame call's output equals the first frame of a two-frame
     call, for either output type, and its state equals the stage entry
     points' (float32 maps, 32-row state pass)."""

@@ -1,7 +1,8 @@
 """gdn_frame_fwd_noalloc (the entry point for callers that cannot allocate)
 against gdn_frame_fwd through the C ABI: two calls in a row on one GPU, the
 second with a smaller input (so it runs on what the first left in the shared
-scratch array), and a third on the three-kernel path.  Both entry points run
+scratch array), a third on the three-kernel path and a fourth on the
+single-frame kernels (two head groups).  Both entry points run
 the same kernels, so the results must agree bit for bit."""
 import ctypes
 
@@ -40,7 +41,9 @@ def _noalloc(x, w, out_dtype=torch.float32):
 def test_noalloc_matches_frame_fwd_on_successive_calls(w):
     smaller = w.with_(name="noalloc_small", H=5, T=40, S=64, seed=72)
     short = w.with_(name="noalloc_three_kernel", H=3, T=8, S=50, seed=73, state_std=None)
-    for wk, odt in ((w, torch.float32), (smaller, torch.bfloat16), (short, torch.float32)):
+    single = w.with_(name="noalloc_single_frame", H=20, T=1, S=880, seed=75)
+    for wk, odt in ((w, torch.float32), (smaller, torch.bfloat16), (short, torch.float32),
+                    (single, torch.float32)):
         log(f"noalloc {wk.name}: B={wk.B} H={wk.H} T={wk.T} S={wk.S} out {odt}")
         x = device_inputs(wk, DEV)
         ref_out, ref_st = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"], out_dtype=odt)
