@@ -15,17 +15,33 @@
 // head (16 rows each) with no reduction between workgroups, where the
 // frame-parallel kernels give a frame to one workgroup (or four).
 //
-// Two launches, with no waits between workgroups and no workspace:
-//  * rows (k_frame1_rows): 8 workgroups of 8 waves per head, workgroup r
-//    owning rows [16r, 16r + 16) of M'.  Each reads all of the frame's keys,
-//    its 16 columns of the values and its 16 rows of M, and writes its rows
-//    of M' to state_out.  Head h's workgroups have ids that the dispatcher
-//    deals to one XCD (ids h % 8 + 8 j), so one fetch of the keys from HBM
-//    serves all 8 through that XCD's L2; each workgroup starts on another
-//    tile, so the first fetches cover the frame.  A workgroup takes a whole
-//    CU (160 KB of LDS), so two never share one;
-//  * outputs (k_frame1_out): O = Q M'^T for 64-token tiles, after the rows
-//    (stream order).
+// Output columns in row block r need only the same rows of M':
+// O[:, r] = Q M'_r^T.  So a workgroup that owns rows r of M' also finishes
+// columns r of O, and the whole step is one launch with no waits between
+// workgroups and no workspace: 8 workgroups of 8 waves per head, workgroup
+// r owning rows and output columns [16r, 16r + 16).  Each reads all of the
+// frame's keys and queries, its 16 columns of the values and its 16 rows of
+// M.  Head h's workgroups have ids that the dispatcher deals to one XCD
+// (ids h % 8 + 8 j), so one fetch of the keys and queries from HBM serves
+// all 8 through that XCD's L2; each workgroup starts on another tile, so the
+// first fetches cover the frame.  A workgroup takes a whole CU (160 KB of
+// LDS), so two never share one.
+//
+// Arithmetic, per workgroup: each wave takes every eighth 64-token tile.
+// For a tile, C = M_r K^T (M's 16 rows as a bf16 hi/lo pair, about 2^-17
+// relative; the keys exact in bf16), the residuals R = V_r - (gamma ks) C in
+// float32 (one rounding), then P_w += R^T K with R as a bf16 hi/lo pair, on
+// 16x16x32 bf16 MFMA with float32 sums.  The eight waves' P_w are added in
+// the order w = 0..7 and M'_r = gamma M_r + (beta ks) P; then, over the
+// tiles again, O[:, r] = Q M'_r^T with M'_r as a bf16 hi/lo pair.  The
+// tokens are summed in another order than by the frame-parallel kernels, so
+// results agree with theirs to rounding, not bit for bit; they are
+// deterministic.
+//
+// Global loads are contiguous (a wave's 16-byte loads cover whole rows) and
+// the MFMA operands are read from LDS: loading a 16-row operand layout
+// straight from memory (each load instruction 16 rows x 64 bytes) moves a
+// workgroup's 128 KB at about a third of the rate of contiguous loads.
 //
 #include "gdn_common.h"
 #include "gdn_launch.h"
@@ -38,7 +54,6 @@ constexpr int kXcd = 8;
 constexpr int kTile = 64;        // tokens per MFMA tile
 constexpr int kRowWgs = 8;       // row workgroups per head, 16 rows of M' each
 constexpr int kRowWaves = 8;     // waves per row workgroup
-constexpr int kMaxOutParts = 16; // output workgroups per head
 
 struct Args {
   const uint16_t* q;
@@ -51,7 +66,6 @@ struct Args {
   float* state_out;
   int64_t heads;
   int S;
-  int oparts, otiles;     // output workgroups per head, 64-token tiles each
   float ks;
 };
 
@@ -71,11 +85,6 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ int swz(int s) { return ((s & 3) << 1) | ((s >> 2) & 1); }
 __device__ __forceinline__ int tile_off(int s, int c) { return s * 256 + ((c ^ swz(s)) << 4); }
 
-// Global loads are contiguous (a wave's 16-byte loads cover whole rows),
-// and the MFMA operands are read from LDS: loading a 16-row operand layout
-// straight from memory (each load instruction 16 rows x 64 bytes) moves a
-// workgroup's 128 KB at about a third of the rate of contiguous loads.
-//
 // Rows of float32 M (row length 512 bytes) into LDS as bf16 hi and lo
 // planes in the tile layout above (row stride 256 bytes per plane): float4
 // q of row r (q = 0..31) goes to the 8-byte half q % 2 of chunk q / 2.
@@ -95,9 +104,10 @@ static_assert(kRowLds <= 160 * 1024, "a row workgroup's LDS fits a CU");
 static_assert(kRowLds >= kRowWaves * 8 * 64 * 16, "the reduction reuses the tiles' LDS");
 
 // ---------------------------------------------------------------------------
-// launch 1: rows [16rb, 16rb + 16) of head h's M', one workgroup each
+// rows and output columns [16rb, 16rb + 16) of head h, one workgroup each
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1_rows(Args a) {
+template <bool kOutBf16>
+__global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
   __shared__ __attribute__((aligned(16))) char lds[kRowLds];
   // ids h % 8 + 8 j: head h's workgroups on one XCD when the dispatcher
   // deals ids to the 8 XCDs in turn (only the L2 sharing depends on it)
@@ -128,11 +138,15 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1_rows(Args a) {
   // zeroed, so that all loads are issued at once.
   u32x4 kx[16];
   u32x2 vv[4];
-  auto load_tile = [&](int tile) {
+  auto load_rows = [&](const uint16_t* X, int tile) {
     const int s0 = tile * kTile, last = S - 1;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      kx[i] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)min(s0 + 4 * i + (l >> 4), last) * D + 8 * (l & 15));
+      kx[i] = *reinterpret_cast<const u32x4*>(X + (int64_t)min(s0 + 4 * i + (l >> 4), last) * D + 8 * (l & 15));
+  };
+  auto load_tile = [&](int tile) {
+    load_rows(Kh, tile);
+    const int s0 = tile * kTile, last = S - 1;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
       vv[tb] = *reinterpret_cast<const u32x2*>(Vh + (int64_t)min(s0 + 16 * tb + n, last) * D + r0 + 4 * g);
@@ -174,25 +188,23 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1_rows(Args a) {
     for (int tb = 0; tb < 4; ++tb)
       if (16 * tb + n >= cnt) vv[tb] = (u32x2){0u, 0u};
     wave_lds_sync();
-    // the keys as MFMA B operands: lane (n, g) token 16tb + n, dims 32kb + 8g .. +7
-    u32x4 kf[4][4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) kf[tb][kb] = *reinterpret_cast<const u32x4*>(Kt + tile_off(16 * tb + n, 4 * kb + g));
     // C^T = M_r K^T: lane (n, g) ends with (M k_s)[r0 + 4g + i], s = 16tb + n
     f32x4 c[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) c[tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
     if (Mi) {
-      // the four accumulators in turn, so that no MFMA waits for the one
-      // just before it
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
+        // the keys as MFMA B operands: lane (n, g) token 16tb + n, dims 32kb + 8g .. +7
+        u32x4 kf[4];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) c[tb] = mfma16x16x32(mh[kb], kf[tb][kb], c[tb]);
+        for (int tb = 0; tb < 4; ++tb) kf[tb] = *reinterpret_cast<const u32x4*>(Kt + tile_off(16 * tb + n, 4 * kb + g));
+        // the four accumulators in turn, so that no MFMA waits for the one
+        // just before it
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) c[tb] = mfma16x16x32(ml[kb], kf[tb][kb], c[tb]);
+        for (int tb = 0; tb < 4; ++tb) c[tb] = mfma16x16x32(mh[kb], kf[tb], c[tb]);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) c[tb] = mfma16x16x32(ml[kb], kf[tb], c[tb]);
       }
     }
     // residuals, one rounding each, into LDS as [token][row] hi/lo
@@ -240,15 +252,20 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1_rows(Args a) {
     wave_lds_sync();  // this tile's LDS reads are done before the next tile's writes
   }
 
+  // the queries of this wave's first tile: in flight during the reduction
+  const uint16_t* Qh = a.q + hl * S * D;
+  if (first < ntiles) load_rows(Qh, first);
+
   // M's elements this lane updates: rows r0 + 4g + i, column 16 w + n
-  // (wave w finishes column block w)
+  // (wave w finishes column block w).  Only this workgroup reads or writes
+  // M's rows r0 .. r0 + 15, so state_out may be state_in.
   float m_old[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) m_old[i] = Mi ? Mi[(r0 + 4 * g + i) * D + 16 * w + n] : 0.f;
   // the waves' sums, added in the order w = 0..7: lane (n, g) holds
   // P[r0 + 4g + i][16jb + n] in acc[jb]
   __syncthreads();
-  f32x4* red = reinterpret_cast<f32x4*>(lds);
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // 64 KB
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) red[(w * 8 + jb) * 64 + l] = acc[jb];
   __syncthreads();
@@ -256,124 +273,63 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1_rows(Args a) {
   f32x4 sum = red[w * 64 + l];
 #pragma unroll
   for (int v = 1; v < kRowWaves; ++v) sum += red[(v * 8 + w) * 64 + l];
+  // M'_r to state_out, and into LDS as bf16 hi/lo (after the reduction
+  // buffer) for the output's A operands
+  char* Ms = lds + 64 * 1024;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) Mo[(r0 + 4 * g + i) * D + 16 * w + n] = __builtin_fmaf(bks, sum[i], gam * m_old[i]);
-}
+  for (int i = 0; i < 4; ++i) {
+    const float mn = __builtin_fmaf(bks, sum[i], gam * m_old[i]);
+    Mo[(r0 + 4 * g + i) * D + 16 * w + n] = mn;
+    const uint32_t hi = f2bf(mn), lo = f2bf(mn - bf2f(hi));
+    const int off = tile_off(4 * g + i, 2 * w + (n >> 3)) + 2 * (n & 7);
+    *reinterpret_cast<uint16_t*>(Ms + off) = (uint16_t)hi;
+    *reinterpret_cast<uint16_t*>(Ms + 16 * 256 + off) = (uint16_t)lo;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    mh[kb] = *reinterpret_cast<const u32x4*>(Ms + tile_off(n, 4 * kb + g));
+    ml[kb] = *reinterpret_cast<const u32x4*>(Ms + 16 * 256 + tile_off(n, 4 * kb + g));
+  }
+  __syncthreads();  // the tiles below reuse the reduction buffer and the staging
 
-// ---------------------------------------------------------------------------
-// launch 2: O = Q M'^T, workgroup (head, part) for the part's 64-token tiles
-// ---------------------------------------------------------------------------
-// LDS of an output workgroup: the Q tile (16 KB) and each wave's 32 rows of
-// M' as bf16 hi/lo (16 KB per wave).
-constexpr int kOutLds = kTile * 256 + 4 * 2 * 32 * 256;
-
-template <bool kOutBf16>
-__global__ __launch_bounds__(256, 2) void k_frame1_out(Args a) {
-  __shared__ __attribute__((aligned(16))) char lds[kOutLds];
-  const int64_t hl = blockIdx.x / a.oparts;
-  const int op = blockIdx.x % a.oparts;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
-  const int S = a.S;
-  const int t0 = op * a.otiles * kTile;
-  const int t1 = min(S, t0 + a.otiles * kTile);
-  const uint16_t* Qh = a.q + hl * S * D;
+  // O[:, r0 .. r0 + 15] = Q M'_r^T over this wave's tiles: lane (n, g) ends
+  // with O[s][r0 + 4g + i], s = 16tb + n
   constexpr int kOutB = kOutBf16 ? 2 : 4;
   char* Oh = static_cast<char*>(a.out) + hl * S * D * kOutB;
-
-  char* Qt = lds;
-  char* Mw = lds + kTile * 256 + w * (2 * 32 * 256);  // this wave's M' rows, hi then lo plane
-
-  // a Q tile, row by row: load i of thread t is token (t + 256 i) / 16,
-  // chunk (t + 256 i) % 16; tokens past the range load its last token (their
-  // outputs are not stored)
-  u32x4 qx[4];
-  auto load_q = [&](int s0) {
+  for (int tile = first; tile < ntiles; tile += kRowWaves) {
+    const int s0 = tile * kTile;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int x = tid + 256 * i;
-      qx[i] = *reinterpret_cast<const u32x4*>(Qh + (int64_t)min(s0 + (x >> 4), t1 - 1) * D + 8 * (x & 15));
-    }
-  };
-  load_q(t0);
-  // this wave's rows 32w .. 32w + 31 of M', row by row (load i of lane l:
-  // row 32w + 2i + l / 32, float4 l % 32), into LDS as bf16 hi/lo
-  {
-    const float* Mo = a.state_out + hl * D * D;
-    f32x4 x[16];
+    for (int i = 0; i < 16; ++i) *reinterpret_cast<u32x4*>(Kt + tile_off(4 * i + (l >> 4), l & 15)) = kx[i];
+    wave_lds_sync();
+    // the next tile's queries are in flight during this tile's products
+    if (tile + kRowWaves < ntiles) load_rows(Qh, tile + kRowWaves);
+    f32x4 o[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = *reinterpret_cast<const f32x4*>(Mo + (32 * w + 2 * i + (l >> 5)) * D + 4 * (l & 31));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) stage_m4(Mw, 32 * 256, 2 * i + (l >> 5), l & 31, x[i]);
-  }
-  wave_lds_sync();
-  u32x4 mh[2][4], ml[2][4];
-#pragma unroll
-  for (int ib = 0; ib < 2; ++ib)
+    for (int tb = 0; tb < 4; ++tb) o[tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      mh[ib][kb] = *reinterpret_cast<const u32x4*>(Mw + tile_off(16 * ib + n, 4 * kb + g));
-      ml[ib][kb] = *reinterpret_cast<const u32x4*>(Mw + 32 * 256 + tile_off(16 * ib + n, 4 * kb + g));
+      // B operands: lane (n, g) token 16tb + n, dims 32kb + 8g .. +7
+      u32x4 qf[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) qf[tb] = *reinterpret_cast<const u32x4*>(Kt + tile_off(16 * tb + n, 4 * kb + g));
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) o[tb] = mfma16x16x32(mh[kb], qf[tb], o[tb]);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) o[tb] = mfma16x16x32(ml[kb], qf[tb], o[tb]);
     }
-
-  for (int s0 = t0; s0 < t1; s0 += kTile) {
-    if (s0 > t0) {
-      __syncthreads();  // every wave is done with the previous tile
-      load_q(s0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int x = tid + 256 * i;
-      *reinterpret_cast<u32x4*>(Qt + tile_off(x >> 4, x & 15)) = qx[i];
-    }
-    __syncthreads();
-    // B operands: lane (n, g) token 16tb + n, dims 32kb + 8g .. +7
-    u32x4 qf[4][4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) qf[tb][kb] = *reinterpret_cast<const u32x4*>(Qt + tile_off(16 * tb + n, 4 * kb + g));
-    f32x4 o[2][4];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) o[ib][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) o[ib][tb] = mfma16x16x32(mh[ib][kb], qf[tb][kb], o[ib][tb]);
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) o[ib][tb] = mfma16x16x32(ml[ib][kb], qf[tb][kb], o[ib][tb]);
-    }
-    // lane (n, g): O[s0 + 16tb + n][32w + 16ib + 4g .. +3]
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int s = s0 + 16 * tb + n;
-      if (s >= t1) continue;
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-        const int64_t e = (int64_t)s * D + 32 * w + 16 * ib + 4 * g;
-        if constexpr (kOutBf16)
-          st_nt(reinterpret_cast<u32x2*>(Oh + e * 2),
-                (u32x2){cvt2bf(o[ib][tb][0], o[ib][tb][1]), cvt2bf(o[ib][tb][2], o[ib][tb][3])});
-        else
-          st_nt(reinterpret_cast<f32x4*>(Oh + e * 4), o[ib][tb]);
-      }
+      if (s >= S) continue;
+      const int64_t e = (int64_t)s * D + r0 + 4 * g;
+      if constexpr (kOutBf16)
+        st_nt(reinterpret_cast<u32x2*>(Oh + e * 2), (u32x2){cvt2bf(o[tb][0], o[tb][1]), cvt2bf(o[tb][2], o[tb][3])});
+      else
+        st_nt(reinterpret_cast<f32x4*>(Oh + e * 4), o[tb]);
     }
+    wave_lds_sync();  // this tile's LDS reads are done before the next tile's writes
   }
-}
-
-// Output workgroups of a frame of S tokens: at most kMaxOutParts, each a
-// whole number of 64-token tiles.
-void split_tiles(int S, int* parts, int* tiles_each) {
-  const int tiles = (S + kTile - 1) / kTile;
-  const int want = tiles < kMaxOutParts ? tiles : kMaxOutParts;
-  *tiles_each = (tiles + want - 1) / want;
-  *parts = (tiles + *tiles_each - 1) / *tiles_each;
 }
 
 }  // namespace
@@ -382,7 +338,6 @@ hipError_t launch_frame1(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          const float* beta, const float* state_in, void* out, bool out_bf16, float* state_out,
                          int64_t heads, int S, float ks, hipStream_t st) {
   Args a;
-  split_tiles(S, &a.oparts, &a.otiles);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -394,16 +349,12 @@ hipError_t launch_frame1(const uint16_t* q, const uint16_t* k, const uint16_t* v
   a.heads = heads;
   a.S = S;
   a.ks = ks;
-  const int64_t rows_grid = (heads + kXcd - 1) / kXcd * kXcd * kRowWgs;
-  const int64_t out_grid = heads * a.oparts;
-  if (rows_grid > 0x7fffffff || out_grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_frame1_rows, dim3((unsigned)rows_grid), dim3(64 * kRowWaves), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const int64_t grid = (heads + kXcd - 1) / kXcd * kXcd * kRowWgs;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (out_bf16)
-    hipLaunchKernelGGL(k_frame1_out<true>, dim3((unsigned)out_grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_frame1<true>, dim3((unsigned)grid), dim3(64 * kRowWaves), 0, st, a);
   else
-    hipLaunchKernelGGL(k_frame1_out<false>, dim3((unsigned)out_grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_frame1<false>, dim3((unsigned)grid), dim3(64 * kRowWaves), 0, st, a);
   return hipGetLastError();
 }
 
