@@ -276,10 +276,27 @@ def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
         e1.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e3)
     del flush
+    # the same call through the three-kernel path, for comparison
+    path = {0: "plain", 1: "three_kernel", 2: "fused", 3: "single_frame"}.get(
+        L.gdn_path(ctypes.byref(Shape(B, H, 1, S, D)), GDN_BF16), "unknown")
+    prev = L.gdn_set_single_frame(0)
+    try:
+        for _ in range(10):
+            call(one, state)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(t1_reps):
+            call(one, state)
+        e1.record()
+        torch.cuda.synchronize()
+        three = e0.elapsed_time(e1) / t1_reps * 1e3
+    finally:
+        L.gdn_set_single_frame(prev)
     return {"calls": len(chunks), "ms": round(stream_ms, 4),
             "frame_steps_per_s": round(B * T / (stream_ms * 1e-3), 1)}, \
-           {"isolated_us_median": round(float(np.median(iso)), 2), "back_to_back_us": round(back_to_back, 2),
-            "cold_us_median": round(float(np.median(cold)), 2)}
+           {"path": path, "isolated_us_median": round(float(np.median(iso)), 2),
+            "back_to_back_us": round(back_to_back, 2), "cold_us_median": round(float(np.median(cold)), 2),
+            "three_kernel_back_to_back_us": round(three, 2)}
 
 
 def backward_leg(x, L, w, stream, steps=5, warmup=1):

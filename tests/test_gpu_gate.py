@@ -48,9 +48,10 @@ def _run(w, path_fused, frames=None, key_scale=None, odt=torch.float32):
     ks = 1.0 if key_scale is None else key_scale
     prev = F.set_fused(path_fused)
     try:
+        mfma = w.in_dtype == "bf16" and w.D == 128
+        want = 2 if path_fused else 3 if mfma and w.T == 1 else 1 if mfma else 0  # 3: the single-frame kernel
         assert F.lib().gdn_path(ctypes.byref(Shape(w.B, w.H, w.T, w.S, w.D)),
-                                GDN_BF16 if w.in_dtype == "bf16" else GDN_F32) == (2 if path_fused else
-                                                                                   (1 if w.in_dtype == "bf16" and w.D == 128 else 0))
+                                GDN_BF16 if w.in_dtype == "bf16" else GDN_F32) == want
         out, st, gam, bet = F.frame_fwd_gated(q, k, v, torch.from_numpy(ga).to(DEV), torch.from_numpy(gb).to(DEV),
                                               torch.from_numpy(A_log).to(DEV), torch.from_numpy(dt_bias).to(DEV),
                                               state, key_scale=ks, out_dtype=odt)
