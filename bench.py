@@ -292,10 +292,15 @@ def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
         three = e0.elapsed_time(e1) / t1_reps * 1e3
     finally:
         L.gdn_set_single_frame(prev)
+    # algorithmic bytes of one frame: q, k, v in (bf16), O out (f32), the
+    # state in and out (f32)
+    t1_bytes = B * H * (3 * S * D * 2 + S * D * 4 + 2 * D * D * 4)
     return {"calls": len(chunks), "ms": round(stream_ms, 4),
             "frame_steps_per_s": round(B * T / (stream_ms * 1e-3), 1)}, \
            {"path": path, "isolated_us_median": round(float(np.median(iso)), 2),
             "back_to_back_us": round(back_to_back, 2), "cold_us_median": round(float(np.median(cold)), 2),
+            "algorithmic_bytes": t1_bytes, "GBps": round(t1_bytes / (back_to_back * 1e-6) / 1e9, 1),
+            "hbm_frac": round(t1_bytes / (back_to_back * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "three_kernel_back_to_back_us": round(three, 2)}
 
 
