@@ -332,9 +332,10 @@ int gdn_frame_fwd_gated(const gdn_shape* shape, int in_dtype, int out_dtype,
  * gdn_frame_fwd, plus per-kernel durations: a pair of HIP events is recorded
  * around every kernel launch of the call, on the stream that launch uses;
  * the call waits for `stream` (which the call joins back to) and writes,
- * for kernel kinds 0 = build, 1 = state pass (the whole fused kernel on the
- * fused path, flag reset included), 2 = output, the summed elapsed
- * milliseconds to kernel_ms[kind] and the number of launches to
+ * for kernel kinds 0 = build, 1 = state pass (the whole fused kernel on
+ * the fused path, flag reset included; the single-frame kernel on
+ * GDN_PATH_FRAME), 2 = output, the summed elapsed milliseconds to
+ * kernel_ms[kind] and the number of launches to
  * launches[kind] (both host arrays of 3).  Launches of different kinds may overlap in time, so the
  * three sums can add up to more than the call.  Results are identical to
  * gdn_frame_fwd.  The events are created as needed and kept for the life of
