@@ -80,8 +80,8 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint32_t spin_limit, int grid, hipStream_t st);
 
 // ---- single frame (k_frame1.hip): T == 1, bf16, D == 128 -----------------
-// Two launches on `st`, no workspace: row workgroups write M' (state_out),
-// then output workgroups O = Q M'^T.
+// One launch on `st`, no workspace: each workgroup owns 16 rows of one
+// head's M' (written to state_out) and the same 16 columns of O = Q M'^T.
 hipError_t launch_frame1(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                          const float* beta, const float* state_in, void* out, bool out_bf16, float* state_out,
                          int64_t heads, int S, float ks, hipStream_t st);

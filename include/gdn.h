@@ -192,15 +192,15 @@ int gdn_fused_status(const void* workspace, void* stream);
  *                   no device can be queried (no GPU), gdn_path reports the
  *                   path of a device that hosts the fused kernel;
  *   GDN_PATH_FRAME  bf16, D == 128, T == 1 (one frame per call, as in
- *                   frame-by-frame generation): two launches on `stream`,
- *                   no workspace.  The step written per token, M' = gamma M
- *                   + beta sum_s (v_s - gamma M k_s) k_s^T, gives each block
+ *                   frame-by-frame generation): one launch on `stream`, no
+ *                   workspace.  The step written per token, M' = gamma M +
+ *                   beta sum_s (v_s - gamma M k_s) k_s^T, gives each block
  *                   of 16 rows of M' to one workgroup (8 per head, with no
- *                   reduction or waits between workgroups); the second
- *                   launch computes O = Q M'^T.  Deterministic; equal to
- *                   GDN_PATH_MFMA's result to float32 rounding, not bit for
- *                   bit (gdn_set_single_frame).  While disabled,
- *                   GDN_PATH_MFMA;
+ *                   reduction or waits between workgroups), which then
+ *                   computes the same 16 columns of O = Q M'^T.
+ *                   Deterministic; equal to GDN_PATH_MFMA's result to
+ *                   float32 rounding, not bit for bit
+ *                   (gdn_set_single_frame).  While disabled, GDN_PATH_MFMA;
  *   GDN_PATH_PLAIN  every other supported case: three float32 kernels on
  *                   `stream`; also empty shapes (one small float32 kernel
  *                   or none, see "Empty shapes" above);
