@@ -86,6 +86,7 @@ def test_single_frame_switch_selects_path():
     L = F.lib()
     s = _shape(1, 16, 1, 880, 128)
     prev = L.gdn_set_single_frame(0)
+    prev_fused = L.gdn_set_fused(1)
     try:
         assert L.gdn_path(ctypes.byref(s), BF16) == 1
         assert L.gdn_set_single_frame(1) == 0
@@ -98,7 +99,7 @@ def test_single_frame_switch_selects_path():
         assert L.gdn_path(ctypes.byref(s), BF16) == 3
     finally:
         L.gdn_set_single_frame(prev)
-        F.set_fused(True)
+        L.gdn_set_fused(prev_fused)
 
 
 def _frame_bytes(H, S, B=1):
