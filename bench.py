@@ -451,15 +451,20 @@ def config_leg(w, L, dev, stream, steps, heads, frames, workers):
         check(L.gdn_frame_fwd(ctypes.byref(shp), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]), P(x["v"]), P(x["gamma"]),
                               P(x["beta"]), P(x["state"]), P(out), P(st_out), P(ws), wsb, stream), "gdn_frame_fwd")
     warm_up(call)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    # one event between consecutive calls: the per-call times sum to the
+    # timed region
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
         call()
-    e1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = evs[0].elapsed_time(evs[-1]) / steps
+    per_call = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     alg = per_head_frame_bytes(S, D)["step"] * B * H * T
-    res = {"workload": w.name, "B": B, "H": H, "T": T, "S": S, "D": D, "ms": round(ms, 4), "steps": steps,
+    res = {"workload": w.name, "B": B, "H": H, "T": T, "S": S, "D": D, "ms": round(ms, 4),
+           "median_ms": round(float(np.median(per_call)), 4), "min_ms": round(float(np.min(per_call)), 4),
+           "steps": steps,
            "frame_steps_per_s": round(B * T / (ms * 1e-3), 1), "algorithmic_bytes": alg,
            "GBps": round(alg / (ms * 1e-3) / 1e9, 1), "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "path": {1: "three kernels", 2: "fused"}.get(L.gdn_path(ctypes.byref(shp), GDN_BF16), "plain")}
@@ -660,6 +665,7 @@ def main():
     kinds = PATH_KERNELS[path]
     tot = {kinds[i][0]: 0.0 for i in kinds}
     nl = {kinds[i][0]: 0 for i in kinds}
+    per_call = {kinds[i][0]: [] for i in kinds}          # ms per launch, call by call
     kbuf, lbuf = (ctypes.c_float * 3)(), (ctypes.c_int * 3)()
     for _ in range(args.steps):
         check(L.gdn_frame_fwd_timed(ctypes.byref(shp), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]),
@@ -668,6 +674,8 @@ def main():
         for i, (name, _, _) in kinds.items():
             tot[name] += kbuf[i]
             nl[name] += lbuf[i]
+            if lbuf[i] > 0:
+                per_call[name].append(kbuf[i] / lbuf[i])
     kms = {k: tot[k] / args.steps for k in tot}          # per call, summed over its launches
     launches = {k: nl[k] // args.steps for k in nl}      # launches per call
     log("kernels (ms per call, launches): " + ", ".join(f"{k} {kms[k]:.3f} x{launches[k]}" for k in kms))
@@ -686,6 +694,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": ksym, "launches_per_step": launches[dom], "avg_launch_ms": round(avg_ms, 5),
+                "median_launch_ms": round(float(np.median(per_call[dom])), 5),
+                "min_launch_ms": round(float(np.min(per_call[dom])), 5),
                 "bytes_per_launch": round(per_launch)}
     step_bytes = bytes_hf["step"] * hf + (2 if x["state"] is not None else 1) * B * H * D * D * 4
     step_gbs = step_bytes / (ms * 1e-3) / 1e9
