@@ -5,8 +5,10 @@ frame on its own), against the three-kernel path (the same step with the
 frame's tokens summed in another order), over many calls in a row, and on
 their edge cases: head counts that are not a multiple of 8, one
 token, more token tiles than waves, a zero state, the state updated in
-place, bf16 output, the key scale and gates from activations."""
+place, bf16 output, the key scale and gates from activations, and sizes
+whose byte offsets pass 2^31 (many heads; one very long frame)."""
 import ctypes
+import math
 
 import pytest
 import torch
@@ -163,3 +165,75 @@ def test_single_frame_switch_off_takes_three_kernel_path():
     finally:
         F.set_single_frame(prev)
     assert _path(w) == GDN_PATH_FRAME
+
+
+# ---------------------------------------------------------------------------
+# maximum sizes: byte offsets past 2^31
+# ---------------------------------------------------------------------------
+def _device_frame(B, H, S, seed):
+    """One frame per head, seeded on the device (these sizes are beyond the
+    host generators' reach): q, v ~ N(0, 1) and keys N(0, 1) / sqrt(D S),
+    all rounded to bf16; gamma ~ U(0.9, 1); beta = sigmoid(N(0, 1)); a
+    N(0, 0.05^2) float32 state."""
+    D = 128
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    x = {"q": torch.randn((B, H, 1, S, D), generator=g, device=DEV).to(torch.bfloat16)}
+    x["k"] = (torch.randn((B, H, 1, S, D), generator=g, device=DEV) / (D * S) ** 0.5).to(torch.bfloat16)
+    x["v"] = torch.randn((B, H, 1, S, D), generator=g, device=DEV).to(torch.bfloat16)
+    x["gamma"] = torch.rand((B, H, 1), generator=g, device=DEV) * 0.1 + 0.9
+    x["beta"] = torch.sigmoid(torch.randn((B, H, 1), generator=g, device=DEV))
+    x["state"] = torch.randn((B, H, D, D), generator=g, device=DEV) * 0.05
+    torch.cuda.synchronize()
+    return x
+
+
+def _oracle_head(x, out, st, b, h):
+    """The oracle on head (b, h) of the device inputs (bf16 as its bit
+    patterns, which the oracle widens exactly); relL2 of the output and the
+    state."""
+    import oracle
+    bits = lambda t: t[b, h].contiguous().view(torch.int16).cpu().numpy().view("uint16")
+    f64 = lambda t: t[b, h].double().cpu().numpy()
+    O, M = oracle.gdn_head(bits(x["q"]), bits(x["k"]), bits(x["v"]), f64(x["gamma"]), f64(x["beta"]),
+                           f64(x["state"]))
+    return _rel(out[b, h], torch.from_numpy(O)), _rel(st[b, h], torch.from_numpy(M))
+
+
+def test_single_frame_many_heads_past_2gib():
+    """12288 heads (B = 96, H = 128) of 880 tokens in one call: 2.8 GB per
+    input and 5.5 GB of output, so the inputs of heads from 9533 on and the
+    output of heads from 4767 on lie beyond 2^31 bytes.  Sampled heads on
+    both sides of those lines, and the last, against the oracle."""
+    B, H, S = 96, 128, 880
+    log(f"single frame, {B * H} heads x {S} tokens")
+    assert F.lib().gdn_path(ctypes.byref(Shape(B, H, 1, S, 128)), GDN_BF16) == GDN_PATH_FRAME
+    x = _device_frame(B, H, S, seed=11)
+    out, st = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    torch.cuda.synchronize()
+    for hd in (0, 4766, 4767, 9532, 9533, 12001, B * H - 1):
+        b, h = divmod(hd, H)
+        ro, rs = _oracle_head(x, out, st, b, h)
+        log(f"  head {hd}: relL2 O={ro:.3e} state={rs:.3e}")
+        assert ro <= TOL and rs <= TOL
+
+
+def test_single_frame_long_frame_past_2gib():
+    """One head with 4,194,513 tokens (2^22 + 209): 1.07 GB per input, and
+    the float32 output of the tokens after the 2^22nd lies beyond 2^31
+    bytes; a ragged last tile.  The whole output and the state against the
+    oracle.
+
+    Tolerance: each float32 accumulator of the state's sum adds about
+    S / 256 products of 32 tokens in sequence (S / 8 tokens per wave, 32
+    per MFMA), whose rounding grows like u sqrt(S / 256) (u = 2^-24; 7.6e-6
+    here), so the bound is the 880-token one plus four times that.  A wrong
+    address past 2^31 bytes would be an O(1) error."""
+    S = (1 << 22) + 209
+    tol = TOL + 4 * 2.0 ** -24 * math.sqrt(S / 256)
+    log(f"single frame, one head x {S} tokens (tol {tol:.2e})")
+    x = _device_frame(1, 1, S, seed=12)
+    out, st = F.frame_fwd(x["q"], x["k"], x["v"], x["gamma"], x["beta"], x["state"])
+    torch.cuda.synchronize()
+    ro, rs = _oracle_head(x, out, st, 0, 0)
+    log(f"  relL2 O={ro:.3e} state={rs:.3e}")
+    assert ro <= tol and rs <= tol
