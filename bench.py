@@ -224,11 +224,12 @@ def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
     wsb = max(L.gdn_workspace_bytes(ctypes.byref(Shape(B, H, c["q"].shape[2], S, D)), GDN_BF16) for c in chunks)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
 
-    def call(c, st_in):
+    def call(c, st_in, use_ws=True):
         n = c["q"].shape[2]
         shp = Shape(B, H, n, S, D)
         check(L.gdn_frame_fwd(ctypes.byref(shp), GDN_BF16, GDN_F32, P(c["q"]), P(c["k"]), P(c["v"]),
-                              P(c["gamma"]), P(c["beta"]), P(st_in), P(out), P(state), P(ws), wsb, stream),
+                              P(c["gamma"]), P(c["beta"]), P(st_in), P(out), P(state),
+                              P(ws) if use_ws else None, wsb if use_ws else 0, stream),
               "gdn_frame_fwd")
 
     def pass_():
@@ -257,6 +258,17 @@ def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
     e1.record()
     torch.cuda.synchronize()
     back_to_back = e0.elapsed_time(e1) / t1_reps * 1e3
+    # without a workspace the single-frame kernel runs one workgroup per
+    # 16-row block instead of splitting its token tiles over two
+    for _ in range(10):
+        call(one, state, use_ws=False)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(t1_reps):
+        call(one, state, use_ws=False)
+    e1.record()
+    torch.cuda.synchronize()
+    one_wg = e0.elapsed_time(e1) / t1_reps * 1e3
     iso = []
     for _ in range(50):
         e0.record()
@@ -301,6 +313,7 @@ def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
             "back_to_back_us": round(back_to_back, 2), "cold_us_median": round(float(np.median(cold)), 2),
             "algorithmic_bytes": t1_bytes, "GBps": round(t1_bytes / (back_to_back * 1e-6) / 1e9, 1),
             "hbm_frac": round(t1_bytes / (back_to_back * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "one_workgroup_per_row_block_back_to_back_us": round(one_wg, 2),
             "three_kernel_back_to_back_us": round(three, 2)}
 
 

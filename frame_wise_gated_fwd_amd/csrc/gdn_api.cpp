@@ -120,7 +120,8 @@ std::atomic<int>& fused_enabled() {
   return on;
 }
 
-// Polls before a wait of the fused kernel gives up (0: the kernel's default);
+// Polls before a bounded wait of the fused kernel or of the split single-frame
+// kernel gives up (0: each kernel's default);
 // gdn_set_spin_limit sets it.
 std::atomic<uint32_t>& spin_limit() {
   static std::atomic<uint32_t> polls{0};
@@ -144,6 +145,15 @@ std::atomic<int>& single_frame_enabled() {
 
 bool frame1_path(int in_dtype, const Dims& d) {
   return single_frame_enabled().load() && fast_path(in_dtype, d.D) && d.T == 1;
+}
+
+// A new nonzero value for every split single-frame call: the kernel's pair
+// words carry it, so a word left by an earlier call never matches.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> epoch{0};
+  uint32_t e = epoch.fetch_add(1) + 1;
+  while (e == 0) e = epoch.fetch_add(1) + 1;
+  return e;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
@@ -297,6 +307,7 @@ void teardown() {
 // the one-time probe in gdn::fused_topology_ok checks).
 struct DevInfo {
   int fused_grid[2];  // [out_bf16]
+  bool frame_pairs;   // the split single-frame form can run (gdn::frame1_pairs_share_xcd)
   bool ready;
 };
 DevInfo g_dev[kMaxDevices];
@@ -318,6 +329,7 @@ hipError_t dev_info(DevInfo** out) {
       if (grid > 0 && (e = gdn::fused_topology_ok(grid, &even)) != hipSuccess) return e;
       di.fused_grid[b] = even ? grid : 0;
     }
+    if ((e = gdn::frame1_pairs_share_xcd(&di.frame_pairs)) != hipSuccess) return e;
     di.ready = true;
   }
   *out = &di;
@@ -348,7 +360,7 @@ size_t path_workspace(const Dims& d, int in_dtype, int path) {
       return fast_path(in_dtype, d.D) && d.T > kFusedMinT ? (size_t)gdn::fused_workspace_bytes(d.heads)
                                                           : SIZE_MAX;
     case GDN_PATH_FRAME:
-      return fast_path(in_dtype, d.D) && d.T == 1 ? 0 : SIZE_MAX;
+      return fast_path(in_dtype, d.D) && d.T == 1 ? (size_t)gdn::frame1_workspace_bytes(d.heads) : SIZE_MAX;
     case GDN_PATH_MFMA: {
       if (!fast_path(in_dtype, d.D)) return SIZE_MAX;
       const Segments g = segments_of(d.T);
@@ -616,8 +628,9 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
                       : frame1_path(in_dtype, d) ? GDN_PATH_FRAME
                       : fast_path(in_dtype, d.D) ? GDN_PATH_MFMA
                                                  : GDN_PATH_PLAIN;
-  // the planned path's workspace first, with no device query
-  if (!workspace_ok(has_in ? path_workspace(d, in_dtype, planned) : 0, &st)) return st;
+  // the planned path's workspace first, with no device query (the
+  // single-frame kernel runs without one, and uses one that is big enough)
+  if (!workspace_ok(has_in && planned != GDN_PATH_FRAME ? path_workspace(d, in_dtype, planned) : 0, &st)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!has_in) {
     // no heads: nothing to do; no frames: state_out = state_in; frames
@@ -675,6 +688,24 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
     if (!workspace_ok(path_workspace(d, in_dtype, GDN_PATH_MFMA), &st)) return st;
   }
   if (planned == GDN_PATH_FRAME) {
+    // the token halves of a row block on two workgroups when the workspace
+    // holds their hand-off (checked for overlap like any workspace) and the
+    // stream is not being captured (a graph would replay the call's epoch)
+    void* pair_ws = nullptr;
+    const size_t pneed = path_workspace(d, in_dtype, GDN_PATH_FRAME);
+    if (pneed > 0 && workspace && workspace_bytes >= pneed && (uintptr_t)workspace % 256 == 0) {
+      if (!workspace_ok(pneed, &st)) return st;
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(s, &cap) != hipSuccess) return GDN_E_HIP;
+      DevInfo* di = nullptr;
+      if (cap == hipStreamCaptureStatusNone) {
+        if (dev_info(&di) != hipSuccess) {
+          (void)hipGetLastError();
+          return GDN_E_HIP;
+        }
+        if (di->frame_pairs) pair_ws = workspace;
+      }
+    }
     if (gate && timed(rec, s, 0, [&] {
           return gdn::launch_frame_gates(gate->a, gate->b, gate->A_log, gate->dt_bias, gate->gamma, gate->beta,
                                          d.frames, (int)d.H, (int)d.T, (int)d.S, s);
@@ -683,7 +714,8 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
     return hip_status(timed(rec, s, 1, [&] {
       return gdn::launch_frame1(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                 static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out,
-                                d.heads, (int)d.S, ks, s);
+                                d.heads, (int)d.S, ks, pair_ws, pair_ws ? next_epoch() : 0,
+                                spin_limit().load(), s);
     }));
   }
   // separate kernels: the gates first, into gamma, beta
@@ -845,7 +877,7 @@ size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype) {
     // no device to ask: what the three-kernel schedule needs, the larger
     return path_workspace(d, in_dtype, grid > 0 ? GDN_PATH_FUSED : GDN_PATH_MFMA);
   }
-  if (frame1_path(in_dtype, d)) return 0;
+  if (frame1_path(in_dtype, d)) return path_workspace(d, in_dtype, GDN_PATH_FRAME);
   return path_workspace(d, in_dtype, fast_path(in_dtype, d.D) ? GDN_PATH_MFMA : GDN_PATH_PLAIN);
 }
 

@@ -80,11 +80,24 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint32_t spin_limit, int grid, hipStream_t st);
 
 // ---- single frame (k_frame1.hip): T == 1, bf16, D == 128 -----------------
-// One launch on `st`, no workspace: each workgroup owns 16 rows of one
-// head's M' (written to state_out) and the same 16 columns of O = Q M'^T.
+// One launch on `st`: every 16-row block of a head's M' (written to
+// state_out) and the same 16 columns of O = Q M'^T.  With pair_ws (at least
+// frame1_workspace_bytes(heads) bytes, 256-byte aligned; nonzero only for
+// at most 16 heads), on a device where frame1_pairs_share_xcd holds, and a
+// nonzero epoch that no earlier call on pair_ws used, each row block's
+// tokens split over two workgroups that swap partial sums through pair_ws;
+// otherwise one workgroup per row block.  The two forms agree to float32
+// rounding.  spin_limit: polls of the swap's bounded wait (0: the default,
+// about a second); a workgroup whose wait runs out writes NaN to its output
+// columns.
+int64_t frame1_workspace_bytes(int64_t heads);
+// Whether this device deals workgroups b and b + 8 to one XCD, which the
+// split form needs (a one-time probe; null stream, synchronous).
+hipError_t frame1_pairs_share_xcd(bool* ok);
 hipError_t launch_frame1(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                          const float* beta, const float* state_in, void* out, bool out_bf16, float* state_out,
-                         int64_t heads, int S, float ks, hipStream_t st);
+                         int64_t heads, int S, float ks, void* pair_ws, uint32_t epoch, uint32_t spin_limit,
+                         hipStream_t st);
 
 // ---- plain float32 path: any supported D, f32 or bf16 inputs ---------------
 hipError_t launch_build_generic(const void* k, const void* v, bool in_bf16, float* G, float* U,

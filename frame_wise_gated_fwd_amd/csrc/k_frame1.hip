@@ -11,36 +11,58 @@
 // every token adds the residual of its value against the decayed state's
 // prediction (the delta rule) times its key.  Rows of M' then depend only on
 // the same rows of M: row block r of M' needs M's rows in r, the values'
-// columns in r and all keys.  So one frame spreads over 8 workgroups per
-// head (16 rows each) with no reduction between workgroups, where the
-// frame-parallel kernels give a frame to one workgroup (or four).
+// columns in r and all keys.  Output columns in row block r need only the
+// same rows of M': O[:, r] = Q M'_r^T.  So the step spreads over row blocks
+// of 16 rows, 8 per head, with no reduction between row blocks.
 //
-// Output columns in row block r need only the same rows of M':
-// O[:, r] = Q M'_r^T.  So a workgroup that owns rows r of M' also finishes
-// columns r of O, and the whole step is one launch with no waits between
-// workgroups and no workspace: 8 workgroups of 8 waves per head, workgroup
-// r owning rows and output columns [16r, 16r + 16).  Each reads all of the
-// frame's keys and queries, its 16 columns of the values and its 16 rows of
-// M.  Head h's workgroups have ids that the dispatcher deals to one XCD
-// (ids h % 8 + 8 j), so one fetch of the keys and queries from HBM serves
-// all 8 through that XCD's L2; each workgroup starts on another tile, so the
-// first fetches cover the frame.  A workgroup takes a whole CU (160 KB of
-// LDS), so two never share one.
+// Token halves.  With at most 16 heads (8 x 16 row blocks: half the CUs) a
+// row block is split over a pair of workgroups: half p takes the 64-token
+// tiles t with t % 2 == p, sums its part P_p of P, and the two swap their
+// parts, so that each has P = P_0 + P_1 and writes the output columns of
+// its own tiles.  With more heads, with no room for the swap in the
+// workspace, or under stream capture, one workgroup sums all the tiles and
+// writes all of its columns.  The two forms add the tokens' products in
+// different orders, so they agree to float32 rounding, not bit for bit;
+// each is deterministic.
 //
-// Arithmetic, per workgroup: each wave takes every eighth 64-token tile.
-// For a tile, C = M_r K^T (M's 16 rows as a bf16 hi/lo pair, about 2^-17
-// relative; the keys exact in bf16), the residuals R = V_r - (gamma ks) C in
-// float32 (one rounding), then P_w += R^T K with R as a bf16 hi/lo pair, on
-// 16x16x32 bf16 MFMA with float32 sums.  The eight waves' P_w are added in
-// the order w = 0..7 and M'_r = gamma M_r + (beta ks) P; then, over the
-// tiles again, O[:, r] = Q M'_r^T with M'_r as a bf16 hi/lo pair.  The
-// tokens are summed in another order than by the frame-parallel kernels, so
-// results agree with theirs to rounding, not bit for bit; they are
-// deterministic.
+// The swap.  Head h's workgroups have ids h % 8 + 8 j, which the
+// dispatcher deals to XCD h % 8 (the library uses this form only on a
+// device where a probe has seen that dealing), so the two halves of a pair,
+// 8 ids apart, share that XCD's L2, the point where its CUs' stores meet.
+// Per pair there is one 64-bit word (the call's epoch, the half and the XCD
+// id) and each half's partial sums.  A half stores its sums, waits for all
+// of its memory operations (its reads of state_in included), then
+// atomically exchanges the word with its own value.  If the old value
+// carries this call's epoch, the other half and this XCD, the partner is
+// already done and this workgroup is the second: it invalidates its L1,
+// reads the partner's sums and alone writes the pair's rows of state_out
+// (both halves have read state_in by then, so state_out may equal
+// state_in).  Otherwise it is the first: it polls the word, a bounded
+// number of times, until the partner's value appears, then reads the
+// partner's sums.  The halves wait only for each other and an XCD starts
+// its workgroups in id order, so at most the last few pairs started on an
+// XCD can be waiting on a partner while the others finish and make room.
+// A first half that still gives up (about a second by default) writes NaN
+// to its output columns; the second, when it comes, writes the correct
+// state.  Epochs are new for every call, so a word left by an earlier call
+// never passes for this call's partner; a captured graph would replay its
+// epoch, so captured calls take the one-workgroup form.
 //
-// Global loads are contiguous (a wave's 16-byte loads cover whole rows) and
-// the MFMA operands are read from LDS: loading a 16-row operand layout
-// straight from memory (each load instruction 16 rows x 64 bytes) moves a
+// Arithmetic, per workgroup: for a tile, C = M_r K^T (M's 16 rows as a bf16
+// hi/lo pair, about 2^-17 relative; the keys exact in bf16), the residuals
+// R = V_r - (gamma ks) C in float32 (one rounding), then P_w += R^T K with R
+// as a bf16 hi/lo pair, on 16x16x32 bf16 MFMA with float32 sums;
+// M'_r = gamma M_r + (beta ks) P; then, over the tiles again,
+// O[:, r] = Q M'_r^T with M'_r as a bf16 hi/lo pair.  The tokens are summed
+// in another order than by the frame-parallel kernels, so results agree
+// with theirs to rounding, not bit for bit; they are deterministic.
+//
+// Placement.  Head h's workgroups have ids h % 8 + 8 j, which the dispatcher
+// deals to one XCD, so one fetch of the keys and queries from HBM serves all
+// of them through that XCD's L2.  A workgroup takes a whole CU (160 KB of LDS).  Global
+// loads are contiguous (a wave's 16-byte loads cover whole rows) and the
+// MFMA operands are read from LDS: loading a 16-row operand layout straight
+// from memory (each load instruction 16 rows x 64 bytes) moves a
 // workgroup's 128 KB at about a third of the rate of contiguous loads.
 //
 #include "gdn_common.h"
@@ -52,8 +74,16 @@ namespace {
 constexpr int D = 128;
 constexpr int kXcd = 8;
 constexpr int kTile = 64;        // tokens per MFMA tile
-constexpr int kRowWgs = 8;       // row workgroups per head, 16 rows of M' each
+constexpr int kRowWgs = 8;       // row blocks per head, 16 rows of M' each
 constexpr int kRowWaves = 8;     // waves per row workgroup
+
+// Row blocks are split over two workgroups for at most this many heads
+// (16 heads: 256 workgroups, one per CU).
+constexpr int64_t kSplitMaxHeads = 16;
+constexpr int64_t kPairWordBytes = 128;                 // one pair word per 128-byte line
+constexpr int64_t kHalfSumBytes = kRowWaves * 64 * 16;  // a half's partial sums: 8 KB
+constexpr int kPairSleep = 2;                            // s_sleep between polls (~128 clocks)
+constexpr uint32_t kPairSpinLimit = 1u << 20;            // default polls (about a second)
 
 struct Args {
   const uint16_t* q;
@@ -67,6 +97,10 @@ struct Args {
   int64_t heads;
   int S;
   float ks;
+  uint64_t* words;  // pair words, kPairWordBytes apart; null: one workgroup per row block
+  f32x4* sums;      // [pair][half][wave][lane] partial sums
+  uint32_t epoch;   // nonzero, new for every call
+  uint32_t spin_limit;
 };
 
 // This wave's LDS writes are done before its later LDS reads (the tiles a
@@ -74,6 +108,11 @@ struct Args {
 __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  // HW_REG_XCC_ID, bits [3:0]
+  return __builtin_amdgcn_s_getreg((15 << 11) | (0 << 6) | 20) & 0xfu;
 }
 
 // A key tile in LDS: 64 token rows x 256 bytes.  Row s keeps its sixteen
@@ -96,24 +135,32 @@ __device__ __forceinline__ void stage_m4(char* planes, int plane_bytes, int r, i
 }
 
 // LDS of a row workgroup: per wave a key tile (16 KB) and its residuals as
-// [token][16 rows] bf16, hi and lo planes (4 KB); after the token loop the
-// same bytes hold the waves' sums for the reduction (8 KB per wave).
+// [token][16 rows] bf16, hi and lo planes (4 KB); after a token loop the
+// same bytes hold the waves' sums for the reduction (8 KB per wave), the
+// pair's hand-off words (past the reduction) and M' for the output.
 constexpr int kWaveLds = kTile * 256 + 2 * kTile * 32;
 constexpr int kRowLds = kRowWaves * kWaveLds;
+constexpr int kRedBytes = kRowWaves * 8 * 64 * 16;
+constexpr int kBcastOff = kRedBytes + 32 * 1024;  // clear of the reduction and of M' (at kRedBytes)
 static_assert(kRowLds <= 160 * 1024, "a row workgroup's LDS fits a CU");
-static_assert(kRowLds >= kRowWaves * 8 * 64 * 16, "the reduction reuses the tiles' LDS");
+static_assert(kRowLds >= kRedBytes + 32 * 1024 + 16, "the reduction, M' and the hand-off reuse the tiles' LDS");
 
 // ---------------------------------------------------------------------------
-// rows and output columns [16rb, 16rb + 16) of head h, one workgroup each
+// rows [16rb, 16rb + 16) of head h and the output columns of the same index,
+// over one or both token halves
 // ---------------------------------------------------------------------------
 template <bool kOutBf16>
 __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
   __shared__ __attribute__((aligned(16))) char lds[kRowLds];
   // ids h % 8 + 8 j: head h's workgroups on one XCD when the dispatcher
-  // deals ids to the 8 XCDs in turn (only the L2 sharing depends on it)
+  // deals ids to the 8 XCDs in turn; the two halves of a pair 8 ids apart
+  const bool split = a.words != nullptr;
+  const int per_head = split ? 2 * kRowWgs : kRowWgs;
   const int xs = blockIdx.x % kXcd, local = blockIdx.x / kXcd;
-  const int64_t hl = xs + (int64_t)kXcd * (local / kRowWgs);
-  const int rb = local % kRowWgs;
+  const int64_t hl = xs + (int64_t)kXcd * (local / per_head);
+  const int within = local % per_head;
+  const int rb = split ? within >> 1 : within;
+  const int half = split ? within & 1 : 0;
   if (hl >= a.heads) return;
 
   const int tid = threadIdx.x;
@@ -122,14 +169,15 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
   const int ntiles = (S + kTile - 1) / kTile;
   const uint16_t* Kh = a.k + hl * S * D;
   const uint16_t* Vh = a.v + hl * S * D;
+  const uint16_t* Qh = a.q + hl * S * D;
   const float* Mi = a.state_in ? a.state_in + hl * D * D : nullptr;
   float* Mo = a.state_out + hl * D * D;
   char* Kt = lds + w * kWaveLds;
   char* Rt = Kt + kTile * 256;
   const float gks = a.gamma[hl] * a.ks;
 
-  // this wave's tiles: t = (w + rb) % 8 + 8 j, so that the head's 8
-  // workgroups start on different tiles
+  // this wave's tiles: i = (w + rb) % 8 + 8 j (tile tstep i + toff below), so
+  // that the head's row blocks start on different tiles
   const int first = (w + rb) % kRowWaves;
 
   // a tile's keys, loaded row by row (load i of lane l: token 4i + l / 16,
@@ -151,7 +199,10 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
     for (int tb = 0; tb < 4; ++tb)
       vv[tb] = *reinterpret_cast<const u32x2*>(Vh + (int64_t)min(s0 + 16 * tb + n, last) * D + r0 + 4 * g);
   };
-  if (first < ntiles) load_tile(first);
+  // the tiles of this workgroup: all of them, or every second from `half`
+  const int tstep = split ? 2 : 1, toff = split ? half : 0;
+  const int nt = split ? (ntiles + 1 - half) >> 1 : ntiles;  // tiles tstep i + toff, i < nt
+  if (first < nt) load_tile(tstep * first + toff);
 
   // M's rows r0 .. r0 + 15 as MFMA A operands (lane (m, g): row r0 + m,
   // columns 32kb + 8g .. +7, bf16 hi/lo), staged once through LDS: one
@@ -176,13 +227,14 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
   // base + e, 4 columns from 4q
   const int tre = (l & 15) >> 2, trq = l & 3;
 
-  for (int tile = first; tile < ntiles; tile += kRowWaves) {
+  for (int i = first; i < nt; i += kRowWaves) {
+    const int tile = tstep * i + toff;
     const int cnt = min(kTile, S - tile * kTile);
     // the keys into LDS (rows past the frame as zeros)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 4 * i + (l >> 4);
-      *reinterpret_cast<u32x4*>(Kt + tile_off(row, l & 15)) = row < cnt ? kx[i] : (u32x4){0u, 0u, 0u, 0u};
+    for (int r = 0; r < 16; ++r) {
+      const int row = 4 * r + (l >> 4);
+      *reinterpret_cast<u32x4*>(Kt + tile_off(row, l & 15)) = row < cnt ? kx[r] : (u32x4){0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb)
@@ -220,7 +272,7 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
       *reinterpret_cast<u32x2*>(Rt + kTile * 32 + off) = (u32x2){p0.y, p1.y};
     }
     // the next tile's loads are in flight during this tile's products
-    if (tile + kRowWaves < ntiles) load_tile(tile + kRowWaves);
+    if (i + kRowWaves < nt) load_tile(tstep * (i + kRowWaves) + toff);
     wave_lds_sync();
     // P_w += R^T K over the tile's tokens
 #pragma unroll
@@ -252,13 +304,13 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
     wave_lds_sync();  // this tile's LDS reads are done before the next tile's writes
   }
 
-  // the queries of this wave's first tile: in flight during the reduction
-  const uint16_t* Qh = a.q + hl * S * D;
-  if (first < ntiles) load_rows(Qh, first);
+  // the queries of this wave's first output tile: in flight during the
+  // reduction (when split, during the swap below)
+  if (!split && first < nt) load_rows(Qh, tstep * first + toff);
 
   // M's elements this lane updates: rows r0 + 4g + i, column 16 w + n
-  // (wave w finishes column block w).  Only this workgroup reads or writes
-  // M's rows r0 .. r0 + 15, so state_out may be state_in.
+  // (wave w finishes column block w).  Only the workgroups of this row
+  // block read or write M's rows r0 .. r0 + 15.
   float m_old[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) m_old[i] = Mi ? Mi[(r0 + 4 * g + i) * D + 16 * w + n] : 0.f;
@@ -269,17 +321,65 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) red[(w * 8 + jb) * 64 + l] = acc[jb];
   __syncthreads();
-  const float gam = a.gamma[hl], bks = a.beta[hl] * a.ks;
   f32x4 sum = red[w * 64 + l];
 #pragma unroll
   for (int v = 1; v < kRowWaves; ++v) sum += red[(v * 8 + w) * 64 + l];
-  // M'_r to state_out, and into LDS as bf16 hi/lo (after the reduction
+
+  bool writer = true;
+  if (split) {
+    // the swap: this half's sums out, the word exchanged, the partner's in
+    const int64_t pair = hl * kRowWgs + rb;
+    a.sums[(pair * 2 + half) * (kRowWaves * 64) + w * 64 + l] = sum;
+    // every earlier memory operation of this workgroup is done (its sums
+    // are in the L2, its reads of state_in are over) before the exchange;
+    // the queries of its first output tile, issued after them, stay in
+    // flight (vector memory operations retire in issue order, and a query
+    // tile is 16 loads)
+    asm volatile("" ::: "memory");
+    if (first < nt) {
+      load_rows(Qh, tstep * first + toff);
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    uint32_t* bc = reinterpret_cast<uint32_t*>(lds + kBcastOff);
+    if (tid == 0) {
+      uint64_t* word = a.words + pair * (kPairWordBytes / 8);
+      const uint64_t xcc = xcc_id();
+      const uint64_t val = (uint64_t)a.epoch | ((uint64_t)half << 32) | (xcc << 40);
+      const uint64_t want = (uint64_t)a.epoch | ((uint64_t)(1 - half) << 32) | (xcc << 40);
+      const bool second = __hip_atomic_exchange(word, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
+      bool ok = second;
+      for (uint32_t i = 0; !ok && i < a.spin_limit; ++i) {
+        __builtin_amdgcn_s_sleep(kPairSleep);
+        ok = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
+      }
+      bc[0] = second;
+      bc[1] = ok;
+    }
+    __syncthreads();
+    writer = bc[0] != 0;
+    if (bc[1] != 0) {
+      asm volatile("buffer_inv sc0" ::: "memory");  // no stale line of the partner's sums in L1
+      // P = P_0 + P_1: float addition is commutative, so both halves get
+      // the same bits
+      sum += a.sums[(pair * 2 + (1 - half)) * (kRowWaves * 64) + w * 64 + l];
+    } else {
+      // no partner on this XCD in time: this workgroup's output columns are NaN
+      sum = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+  }
+
+  // M'_r to state_out (by one workgroup of the row block, after every read
+  // of state_in in it), and into LDS as bf16 hi/lo (after the reduction
   // buffer) for the output's A operands
-  char* Ms = lds + 64 * 1024;
+  const float gam = a.gamma[hl], bks = a.beta[hl] * a.ks;
+  char* Ms = lds + kRedBytes;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float mn = __builtin_fmaf(bks, sum[i], gam * m_old[i]);
-    Mo[(r0 + 4 * g + i) * D + 16 * w + n] = mn;
+    if (writer) Mo[(r0 + 4 * g + i) * D + 16 * w + n] = mn;
     const uint32_t hi = f2bf(mn), lo = f2bf(mn - bf2f(hi));
     const int off = tile_off(4 * g + i, 2 * w + (n >> 3)) + 2 * (n & 7);
     *reinterpret_cast<uint16_t*>(Ms + off) = (uint16_t)hi;
@@ -293,17 +393,17 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
   }
   __syncthreads();  // the tiles below reuse the reduction buffer and the staging
 
-  // O[:, r0 .. r0 + 15] = Q M'_r^T over this wave's tiles: lane (n, g) ends
-  // with O[s][r0 + 4g + i], s = 16tb + n
+  // O[:, r0 .. r0 + 15] = Q M'_r^T over this wave's output tiles: lane
+  // (n, g) ends with O[s][r0 + 4g + i], s = 16tb + n
   constexpr int kOutB = kOutBf16 ? 2 : 4;
   char* Oh = static_cast<char*>(a.out) + hl * S * D * kOutB;
-  for (int tile = first; tile < ntiles; tile += kRowWaves) {
-    const int s0 = tile * kTile;
+  for (int i = first; i < nt; i += kRowWaves) {
+    const int s0 = (tstep * i + toff) * kTile;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) *reinterpret_cast<u32x4*>(Kt + tile_off(4 * i + (l >> 4), l & 15)) = kx[i];
+    for (int r = 0; r < 16; ++r) *reinterpret_cast<u32x4*>(Kt + tile_off(4 * r + (l >> 4), l & 15)) = kx[r];
     wave_lds_sync();
     // the next tile's queries are in flight during this tile's products
-    if (tile + kRowWaves < ntiles) load_rows(Qh, tile + kRowWaves);
+    if (i + kRowWaves < nt) load_rows(Qh, tstep * (i + kRowWaves) + toff);
     f32x4 o[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) o[tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -332,11 +432,43 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
   }
 }
 
+int64_t pair_words_bytes(int64_t heads) { return (heads * kRowWgs * kPairWordBytes + 255) & ~int64_t{255}; }
+
+// XCC_ID seen by each workgroup of the largest split launch (the probe).
+constexpr int kProbeWgs = 2 * kSplitMaxHeads * kRowWgs;
+__device__ uint32_t g_pair_xcc[kProbeWgs];
+__global__ void k_pair_probe() {
+  if (threadIdx.x == 0) g_pair_xcc[blockIdx.x] = xcc_id();
+}
+
 }  // namespace
+
+// Whether workgroups b and b + 8 of a launch run on one XCD (ids dealt to
+// the 8 XCDs in turn), as the split form's swap needs: a probe launch of the
+// split form's largest size records each workgroup's XCC_ID.  Runs on the
+// null stream and waits for it.
+hipError_t frame1_pairs_share_xcd(bool* ok) {
+  *ok = false;
+  hipLaunchKernelGGL(k_pair_probe, dim3(kProbeWgs), dim3(64 * kRowWaves), 0, nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  uint32_t seen[kProbeWgs];
+  if ((e = hipMemcpyFromSymbol(seen, HIP_SYMBOL(g_pair_xcc), sizeof seen)) != hipSuccess) return e;
+  bool same = true;
+  for (int b = 0; b < kProbeWgs; ++b) same = same && seen[b] < (uint32_t)kXcd && seen[b] == seen[b % kXcd];
+  *ok = same;
+  return hipSuccess;
+}
+
+int64_t frame1_workspace_bytes(int64_t heads) {
+  if (heads <= 0 || heads > kSplitMaxHeads) return 0;
+  return pair_words_bytes(heads) + heads * kRowWgs * 2 * kHalfSumBytes;
+}
 
 hipError_t launch_frame1(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* gamma,
                          const float* beta, const float* state_in, void* out, bool out_bf16, float* state_out,
-                         int64_t heads, int S, float ks, hipStream_t st) {
+                         int64_t heads, int S, float ks, void* pair_ws, uint32_t epoch, uint32_t spin_limit,
+                         hipStream_t st) {
   Args a;
   a.q = q;
   a.k = k;
@@ -349,7 +481,12 @@ hipError_t launch_frame1(const uint16_t* q, const uint16_t* k, const uint16_t* v
   a.heads = heads;
   a.S = S;
   a.ks = ks;
-  const int64_t grid = (heads + kXcd - 1) / kXcd * kXcd * kRowWgs;
+  const bool split = pair_ws && frame1_workspace_bytes(heads) > 0 && epoch != 0;
+  a.words = split ? static_cast<uint64_t*>(pair_ws) : nullptr;
+  a.sums = split ? reinterpret_cast<f32x4*>(static_cast<char*>(pair_ws) + pair_words_bytes(heads)) : nullptr;
+  a.epoch = epoch;
+  a.spin_limit = spin_limit ? spin_limit : kPairSpinLimit;
+  const int64_t grid = (heads + kXcd - 1) / kXcd * kXcd * kRowWgs * (split ? 2 : 1);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (out_bf16)
     hipLaunchKernelGGL(k_frame1<true>, dim3((unsigned)grid), dim3(64 * kRowWaves), 0, st, a);

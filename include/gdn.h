@@ -121,11 +121,20 @@ int gdn_set_fused(int enabled);
 int gdn_set_single_frame(int enabled);
 
 /*
- * Testing aid for the fused kernel's failure path: the number of polls after
- * which one of its internal waits gives up, for launches made after it
- * returns, process-wide; 0 restores the default (2^22 polls: seconds for a
- * wait of the state pass, about 20 s for one of the other workgroups, which
- * poll less often).  Returns the previous setting.  Every wait is bounded so
+ * Testing aid for the failure paths of the kernels that wait on other
+ * workgroups: the number of polls after which one of their waits gives up,
+ * for launches made after it returns, process-wide; 0 restores each
+ * kernel's default.  Returns the previous setting.
+ *
+ * Single frame, two-workgroup form (GDN_PATH_FRAME): the first of a pair to
+ * finish its partial sums waits for the other's (default 2^20 polls, about
+ * a second).  If the wait runs out, that workgroup writes NaN to its output
+ * columns; the other, the second of the pair, still writes the pair's rows
+ * of state_out correctly, and values that are not NaN are exact.
+ *
+ * Fused kernel (default 2^22 polls: seconds for a wait of the state pass,
+ * about 20 s for one of the other workgroups, which poll less often).
+ * Every wait is bounded so
  * that a failure ends the kernel instead of hanging it: the first wait that
  * runs out sets an error word in the workspace's control block, every other
  * wait then gives up at once, the state pass writes NaN to the rows of
@@ -192,15 +201,24 @@ int gdn_fused_status(const void* workspace, void* stream);
  *                   no device can be queried (no GPU), gdn_path reports the
  *                   path of a device that hosts the fused kernel;
  *   GDN_PATH_FRAME  bf16, D == 128, T == 1 (one frame per call, as in
- *                   frame-by-frame generation): one launch on `stream`, no
- *                   workspace.  The step written per token, M' = gamma M +
- *                   beta sum_s (v_s - gamma M k_s) k_s^T, gives each block
- *                   of 16 rows of M' to one workgroup (8 per head, with no
- *                   reduction or waits between workgroups), which then
- *                   computes the same 16 columns of O = Q M'^T.
- *                   Deterministic; equal to GDN_PATH_MFMA's result to
- *                   float32 rounding, not bit for bit
- *                   (gdn_set_single_frame).  While disabled, GDN_PATH_MFMA;
+ *                   frame-by-frame generation): one launch on `stream`.
+ *                   The step written per token, M' = gamma M + beta sum_s
+ *                   (v_s - gamma M k_s) k_s^T, splits M' into blocks of 16
+ *                   rows (8 per head) with no reduction between them; a
+ *                   block's workgroup then computes the same 16 columns of
+ *                   O = Q M'^T.  With at most 16 heads, a workspace of
+ *                   gdn_workspace_bytes (the call runs without one), a
+ *                   stream that is not being captured, and a device that
+ *                   deals workgroups b and b + 8 to one XCD (a one-time
+ *                   probe on the null stream), each block's even and odd
+ *                   64-token tiles go to two workgroups that swap partial
+ *                   sums through the workspace (bounded waits, see
+ *                   gdn_set_spin_limit); otherwise one workgroup takes all
+ *                   of a block's tiles.  The two forms agree to float32
+ *                   rounding; each is deterministic.  Equal to
+ *                   GDN_PATH_MFMA's result to float32 rounding, not bit for
+ *                   bit (gdn_set_single_frame).  While disabled,
+ *                   GDN_PATH_MFMA;
  *   GDN_PATH_PLAIN  every other supported case: three float32 kernels on
  *                   `stream`; also empty shapes (one small float32 kernel
  *                   or none, see "Empty shapes" above);
@@ -225,7 +243,13 @@ size_t gdn_workspace_bytes(const gdn_shape* shape, int in_dtype);
  *   GDN_PATH_FUSED  a control block and per-head flags, then rings of G_t,
  *                   U_t and M_t slots for at most 16 heads at a time: a few
  *                   MiB per head whatever T is (76 MiB for 16 heads);
- *   GDN_PATH_FRAME  none (0); T == 1 only;
+ *   GDN_PATH_FRAME  up to 16 heads (B*H), what the two-workgroup form
+ *                   uses: per 16-row block (8 per head) a 128-byte pair
+ *                   word and two 8 KiB halves of partial sums, the words
+ *                   rounded up to 256 bytes (2.0 MiB for 16 heads); 0 for
+ *                   more heads; T == 1 only.  A single-frame call needs no
+ *                   workspace: with a smaller one (or NULL) it runs one
+ *                   workgroup per block;
  *   GDN_PATH_MFMA   the maps of at most three segments at once: with n =
  *                   ceil(T / 64) segments of at most c = ceil(T / n) frames,
  *                   3 * min(n, 3) buffers of B*H*c maps, each rounded up to

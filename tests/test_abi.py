@@ -103,8 +103,15 @@ def test_single_frame_switch_selects_path():
 
 
 def _frame_bytes(H, S, B=1):
-    """The single-frame kernels need no workspace."""
-    return 0
+    """The single-frame kernel runs without a workspace; up to 16 heads it
+    asks for one that holds, per 16-row block (8 per head), a 128-byte pair
+    word and two halves' partial sums of 8 KiB, so that the block's token
+    halves can go to two workgroups."""
+    heads = B * H
+    if heads == 0 or heads > 16:
+        return 0
+    pairs = 8 * heads
+    return (pairs * 128 + 255) // 256 * 256 + pairs * 2 * 8192
 
 
 def _mfma_bytes(B, H, T, D=128):
@@ -136,10 +143,12 @@ def test_workspace_bytes():
     s = _shape(1, 3, 5, 7, 48)
     assert L.gdn_workspace_bytes(ctypes.byref(s), F32) == 3 * ((15 * 48 * 48 * 4 + 255) // 256 * 256)
     assert L.gdn_workspace_bytes(None, BF16) == 0
-    # a single frame: none
-    for B, H, S in ((1, 16, 880), (1, 1, 1), (4, 16, 5000), (1, 40, 64)):
+    # a single frame: the split form's hand-off up to 16 heads, else none
+    for B, H, S in ((1, 16, 880), (1, 1, 1), (4, 16, 5000), (1, 40, 64), (2, 8, 100), (1, 17, 880)):
         s = _shape(B, H, 1, S, 128)
-        assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == 0
+        assert L.gdn_workspace_bytes(ctypes.byref(s), BF16) == _frame_bytes(H, S, B)
+    assert _frame_bytes(16, 880) == 16 * 8 * (128 + 2 * 8192)
+    assert _frame_bytes(17, 880) == 0 and _frame_bytes(8, 880, B=3) == 0
     prev = L.gdn_set_single_frame(0)
     try:
         s = _shape(1, 16, 1, 880, 128)
@@ -161,8 +170,8 @@ def test_path_workspace_bytes():
     # the three-kernel schedule: at most three segments of maps
     for B, H, T in ((1, 16, 961), (4, 16, 961), (1, 2, 64), (1, 2, 65), (1, 2, 200), (3, 5, 1)):
         assert pw(_shape(B, H, T, 880, 128), MFMA) == _mfma_bytes(B, H, T)
-    # single frame: a control block only
-    assert pw(_shape(1, 16, 1, 880, 128), FRAME) == 0
+    # single frame: the split form's hand-off (none beyond 16 heads)
+    assert pw(_shape(1, 16, 1, 880, 128), FRAME) == _frame_bytes(16, 880)
     for B, H, S in ((1, 1, 1), (1, 3, 64), (1, 3, 65), (2, 16, 1024), (1, 16, 1025), (1, 5, 5000)):
         assert pw(_shape(B, H, 1, S, 128), FRAME) == _frame_bytes(H, S, B)
     assert pw(_shape(1, 16, 2, 880, 128), FRAME) == SIZE_MAX

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import frame_wise_gated_fwd_amd as F
-from frame_wise_gated_fwd_amd._lib import Shape, GDN_BF16, GDN_PATH_FRAME, GDN_PATH_MFMA
+from frame_wise_gated_fwd_amd._lib import Shape, GDN_BF16, GDN_F32, GDN_PATH_FRAME, GDN_PATH_MFMA
 from synth import CLIP_5S, Workload
 
 from gpu_util import device_inputs, rel_l2, log
@@ -117,6 +117,115 @@ def test_single_frame_deterministic_and_in_place():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     assert torch.equal(o1, o3) and torch.equal(s1, st)
+
+
+def _raw_frame_call(x, out, state_out, ws):
+    """gdn_frame_fwd through the C ABI with an explicit workspace (None: no
+    workspace, so the single-frame kernel runs one workgroup per row block)."""
+    B, H, _, S, D = x["q"].shape
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rc = F.lib().gdn_frame_fwd(ctypes.byref(Shape(B, H, 1, S, D)), GDN_BF16, GDN_F32, P(x["q"]), P(x["k"]),
+                               P(x["v"]), P(x["gamma"]), P(x["beta"]), P(x["state"]), P(out), P(state_out),
+                               P(ws), 0 if ws is None else ws.numel(), st)
+    assert rc == 0, f"gdn_frame_fwd returned {rc}"
+
+
+def _split_ws(x):
+    B, H, _, S, D = x["q"].shape
+    n = F.lib().gdn_workspace_bytes(ctypes.byref(Shape(B, H, 1, S, D)), GDN_BF16)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=DEV), n
+
+
+@pytest.mark.parametrize("H,S", [(16, 880), (3, 100), (1, 64), (16, 17)], ids=lambda v: str(v))
+def test_single_frame_split_and_one_workgroup_forms(H, S):
+    """Up to 16 heads, with the workspace the query asks for, a row block's
+    even and odd token tiles go to two workgroups that swap their partial
+    sums; without a workspace one workgroup sums all of them.  Both forms
+    against the oracle at float32-grade tolerance, and against each other
+    (they add the same products in another order).  S = 64 and 17: one tile,
+    so the odd half of every pair has no tokens."""
+    w = CLIP_5S.with_(T=1, H=H, S=S, name=f"frame1_split_{H}_{S}", state_std=0.05, seed=400 + H + S)
+    x = device_inputs(w, DEV)
+    ws, n = _split_ws(x)
+    assert n > 0
+    o_split = torch.empty(x["q"].shape, dtype=torch.float32, device=DEV)
+    s_split = torch.empty(x["state"].shape, dtype=torch.float32, device=DEV)
+    o_one, s_one = torch.empty_like(o_split), torch.empty_like(s_split)
+    _raw_frame_call(x, o_split, s_split, ws)
+    _raw_frame_call(x, o_one, s_one, None)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for h in range(H):
+        for o, st in ((o_split, s_split), (o_one, s_one)):
+            ro, rs = _oracle_head(x, o, st, 0, h)
+            worst = max(worst, ro, rs)
+    ro, rs = _rel(o_split, o_one), _rel(s_split, s_one)
+    log(f"  split vs one workgroup: relL2 O={ro:.3e} state={rs:.3e}; worst against the oracle {worst:.3e}")
+    assert worst <= TOL
+    assert ro <= 1e-6 and rs <= 1e-6
+    assert torch.isfinite(o_split).all() and torch.isfinite(s_split).all()
+
+
+def test_single_frame_split_in_place_over_many_calls():
+    """The split form with state_out == state_in: the workgroup that writes a
+    pair's rows is the second of the pair to finish its sums, after both have
+    read them.  20 calls in a row in place equal 20 calls alternating two
+    state buffers, bit for bit, on fresh inputs each call."""
+    w = CLIP_5S.with_(T=20, H=16, S=880, name="frame1_split_inplace", state_std=0.05, seed=431)
+    x = device_inputs(w, DEV)
+    ws, _ = _split_ws({"q": x["q"][:, :, :1]})
+    st_in = x["state"].clone()
+    bufs = [x["state"].clone(), torch.empty_like(x["state"])]
+    o_a = torch.empty((w.B, w.H, 1, w.S, w.D), dtype=torch.float32, device=DEV)
+    o_b = torch.empty_like(o_a)
+    for t in range(w.T):
+        f = {k: x[k][:, :, t:t + 1].contiguous() for k in ("q", "k", "v", "gamma", "beta")}
+        _raw_frame_call(dict(f, state=st_in), o_a, st_in, ws)
+        _raw_frame_call(dict(f, state=bufs[t % 2]), o_b, bufs[(t + 1) % 2], ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o_a, o_b), f"frame {t}: out"
+        assert torch.equal(st_in, bufs[(t + 1) % 2]), f"frame {t}: state"
+    log(f"  {w.T} in-place split calls equal the two-buffer calls")
+
+
+def test_single_frame_split_wait_that_runs_out():
+    """A tiny spin limit (set from the host) makes the first workgroup of a
+    pair give up on its partner almost at once.  Every output value is then
+    either the normal result, bit for bit, or NaN (the columns of a
+    workgroup that gave up), and the state, which the second of each pair
+    writes, is the normal result in place and out of place."""
+    w = CLIP_5S.with_(T=1, H=16, S=880, name="frame1_split_giveup", state_std=0.05, seed=433)
+    x = device_inputs(w, DEV)
+    ws, _ = _split_ws(x)
+    o_ref = torch.empty(x["q"].shape, dtype=torch.float32, device=DEV)
+    s_ref = torch.empty(x["state"].shape, dtype=torch.float32, device=DEV)
+    _raw_frame_call(x, o_ref, s_ref, ws)
+    L = F.lib()
+    prev = L.gdn_set_spin_limit(1)
+    try:
+        nan_calls = 0
+        for i in range(5):
+            o = torch.empty_like(o_ref)
+            s = torch.empty_like(s_ref)
+            _raw_frame_call(x, o, s, ws)
+            st = x["state"].clone()
+            o2 = torch.empty_like(o_ref)
+            _raw_frame_call(dict(x, state=st), o2, st, ws)
+            torch.cuda.synchronize()
+            for out in (o, o2):
+                nan = torch.isnan(out)
+                assert torch.equal(out[~nan], o_ref[~nan]), f"call {i}: a value that is neither NaN nor the result"
+                nan_calls += int(nan.any())
+            assert torch.equal(s, s_ref) and torch.equal(st, s_ref), f"call {i}: state"
+        log(f"  spin limit 1: {nan_calls} of 10 calls had a workgroup give up")
+    finally:
+        L.gdn_set_spin_limit(prev)
+    o = torch.empty_like(o_ref)
+    s = torch.empty_like(s_ref)
+    _raw_frame_call(x, o, s, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
 
 
 def test_single_frame_bf16_output_is_rounded_f32():
