@@ -147,14 +147,6 @@ bool frame1_path(int in_dtype, const Dims& d) {
   return single_frame_enabled().load() && fast_path(in_dtype, d.D) && d.T == 1;
 }
 
-// A new nonzero value for every split single-frame call: the kernel's pair
-// words carry it, so a word left by an earlier call never matches.
-uint32_t next_epoch() {
-  static std::atomic<uint32_t> epoch{0};
-  uint32_t e = epoch.fetch_add(1) + 1;
-  while (e == 0) e = epoch.fetch_add(1) + 1;
-  return e;
-}
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
@@ -301,10 +293,11 @@ void teardown() {
   }
 }
 
-// Per-device facts the fused path needs, queried once: the launch size of
-// the fused kernel (0 when the device cannot host it: too few compute
-// units, or workgroups not dealt evenly over eight XCDs with ids 0-7, which
-// the one-time probe in gdn::fused_topology_ok checks).
+// Per-device facts queried once: the launch size of the fused kernel (0
+// when the device cannot host it: too few compute units, or workgroups not
+// dealt evenly over eight XCDs with ids 0-7, which the one-time probe in
+// gdn::fused_topology_ok checks), and whether workgroups b and b + 8 share
+// an XCD, as the split single-frame form needs (gdn::frame1_pairs_share_xcd).
 struct DevInfo {
   int fused_grid[2];  // [out_bf16]
   bool frame_pairs;   // the split single-frame form can run (gdn::frame1_pairs_share_xcd)
@@ -334,6 +327,30 @@ hipError_t dev_info(DevInfo** out) {
   }
   *out = &di;
   return hipSuccess;
+}
+
+// Whether the current device's facts are known already (no probe needed):
+// then *pairs says if the split single-frame form can run on it.
+bool known_frame_pairs(bool* pairs) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return false;
+  }
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (!g_dev[dev].ready) return false;
+  *pairs = g_dev[dev].frame_pairs;
+  return true;
+}
+
+// A new nonzero value for every eager split single-frame call: the
+// kernel's pair words carry it, so a word left by an earlier call never
+// matches.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> epoch{0};
+  uint32_t e = epoch.fetch_add(1) + 1;
+  while (e == 0) e = epoch.fetch_add(1) + 1;
+  return e;
 }
 
 // The fused kernel's launch size for a call on the current device, 0 when
@@ -690,20 +707,30 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
   if (planned == GDN_PATH_FRAME) {
     // the token halves of a row block on two workgroups when the workspace
     // holds their hand-off (checked for overlap like any workspace) and the
-    // stream is not being captured (a graph would replay the call's epoch)
+    // device deals each pair of workgroups to one XCD (its one-time probe
+    // runs on the null stream: not while this stream is being captured, so
+    // a capture before any eager call on the device takes one workgroup per
+    // block)
     void* pair_ws = nullptr;
+    uint32_t epoch = 0;  // 0: the captured form of the swap
     const size_t pneed = path_workspace(d, in_dtype, GDN_PATH_FRAME);
     if (pneed > 0 && workspace && workspace_bytes >= pneed && (uintptr_t)workspace % 256 == 0) {
       if (!workspace_ok(pneed, &st)) return st;
       hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
       if (hipStreamIsCapturing(s, &cap) != hipSuccess) return GDN_E_HIP;
-      DevInfo* di = nullptr;
-      if (cap == hipStreamCaptureStatusNone) {
+      const bool eager = cap == hipStreamCaptureStatusNone;
+      bool pairs = false;
+      if (!known_frame_pairs(&pairs) && eager) {
+        DevInfo* di = nullptr;
         if (dev_info(&di) != hipSuccess) {
           (void)hipGetLastError();
           return GDN_E_HIP;
         }
-        if (di->frame_pairs) pair_ws = workspace;
+        pairs = di->frame_pairs;
+      }
+      if (pairs) {
+        pair_ws = workspace;
+        if (eager) epoch = next_epoch();
       }
     }
     if (gate && timed(rec, s, 0, [&] {
@@ -714,8 +741,7 @@ int frame_fwd_impl(const gdn_shape* shape, int in_dtype, int out_dtype, const vo
     return hip_status(timed(rec, s, 1, [&] {
       return gdn::launch_frame1(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                 static_cast<const uint16_t*>(v), gamma, beta, state_in, out, ob, state_out,
-                                d.heads, (int)d.S, ks, pair_ws, pair_ws ? next_epoch() : 0,
-                                spin_limit().load(), s);
+                                d.heads, (int)d.S, ks, pair_ws, epoch, spin_limit().load(), s);
     }));
   }
   // separate kernels: the gates first, into gamma, beta

@@ -83,9 +83,10 @@ hipError_t launch_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 // One launch on `st`: every 16-row block of a head's M' (written to
 // state_out) and the same 16 columns of O = Q M'^T.  With pair_ws (at least
 // frame1_workspace_bytes(heads) bytes, 256-byte aligned; nonzero only for
-// at most 16 heads), on a device where frame1_pairs_share_xcd holds, and a
-// nonzero epoch that no earlier call on pair_ws used, each row block's
-// tokens split over two workgroups that swap partial sums through pair_ws;
+// at most 16 heads) on a device where frame1_pairs_share_xcd holds, each
+// row block's tokens split over two workgroups that swap partial sums
+// through pair_ws (epoch: nonzero and new for every eager call, 0 for a
+// call under stream capture);
 // otherwise one workgroup per row block.  The two forms agree to float32
 // rounding.  spin_limit: polls of the swap's bounded wait (0: the default,
 // about a second); a workgroup whose wait runs out writes NaN to its output

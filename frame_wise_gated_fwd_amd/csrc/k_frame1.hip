@@ -19,9 +19,9 @@
 // row block is split over a pair of workgroups: half p takes the 64-token
 // tiles t with t % 2 == p, sums its part P_p of P, and the two swap their
 // parts, so that each has P = P_0 + P_1 and writes the output columns of
-// its own tiles.  With more heads, with no room for the swap in the
-// workspace, or under stream capture, one workgroup sums all the tiles and
-// writes all of its columns.  The two forms add the tokens' products in
+// its own tiles.  With more heads, or with no room for the swap in the
+// workspace, one workgroup sums all the tiles and writes all of its
+// columns.  The two forms add the tokens' products in
 // different orders, so they agree to float32 rounding, not bit for bit;
 // each is deterministic.
 //
@@ -29,24 +29,27 @@
 // dispatcher deals to XCD h % 8 (the library uses this form only on a
 // device where a probe has seen that dealing), so the two halves of a pair,
 // 8 ids apart, share that XCD's L2, the point where its CUs' stores meet.
-// Per pair there is one 64-bit word (the call's epoch, the half and the XCD
-// id) and each half's partial sums.  A half stores its sums, waits for all
-// of its memory operations (its reads of state_in included), then
-// atomically exchanges the word with its own value.  If the old value
-// carries this call's epoch, the other half and this XCD, the partner is
-// already done and this workgroup is the second: it invalidates its L1,
-// reads the partner's sums and alone writes the pair's rows of state_out
-// (both halves have read state_in by then, so state_out may equal
-// state_in).  Otherwise it is the first: it polls the word, a bounded
-// number of times, until the partner's value appears, then reads the
-// partner's sums.  The halves wait only for each other and an XCD starts
-// its workgroups in id order, so at most the last few pairs started on an
-// XCD can be waiting on a partner while the others finish and make room.
-// A first half that still gives up (about a second by default) writes NaN
-// to its output columns; the second, when it comes, writes the correct
-// state.  Epochs are new for every call, so a word left by an earlier call
-// never passes for this call's partner; a captured graph would replay its
-// epoch, so captured calls take the one-workgroup form.
+// Per pair there is one 64-bit word and each half's partial sums.  A half
+// stores its sums and waits for all of its memory operations (its reads of
+// state_in included) before it touches the word; the workgroup that finds
+// its partner already there is the second: it invalidates its L1, reads the
+// partner's sums and alone writes the pair's rows of state_out (both halves
+// have read state_in by then, so state_out may equal state_in).  The other
+// is the first: it polls the word, a bounded number of times, until the
+// second has been there, then reads the second's sums.  An eager call
+// carries a new epoch from the host: each half exchanges the word for
+// (epoch, half, XCD id) in one atomic operation, and a word of an earlier
+// call never passes for this call's partner.  A captured graph replays its
+// arguments, epoch included, so a captured call flips a tagged toggle with
+// a compare-and-swap instead (idle to waiting, waiting to idle; a load and
+// an atomic operation more on the second's path): each arrival flips it
+// once, every call leaves it idle, and an untagged word (an eager call's,
+// or fresh memory) reads as idle.  The halves wait only for
+// each other and an XCD starts its workgroups in id order, so at most the
+// last few pairs started on an XCD can be waiting on a partner while the
+// others finish and make room.  A first half that still gives up (about a
+// second by default) writes NaN to its output columns; the second, when it
+// comes, writes the correct state.
 //
 // Arithmetic, per workgroup: for a tile, C = M_r K^T (M's 16 rows as a bf16
 // hi/lo pair, about 2^-17 relative; the keys exact in bf16), the residuals
@@ -83,6 +86,7 @@ constexpr int64_t kSplitMaxHeads = 16;
 constexpr int64_t kPairWordBytes = 128;                 // one pair word per 128-byte line
 constexpr int64_t kHalfSumBytes = kRowWaves * 64 * 16;  // a half's partial sums: 8 KB
 constexpr int kPairSleep = 2;                            // s_sleep between polls (~128 clocks)
+constexpr uint64_t kPairMagic = 0x9d3a61;               // tag of a pair word in use
 constexpr uint32_t kPairSpinLimit = 1u << 20;            // default polls (about a second)
 
 struct Args {
@@ -99,7 +103,7 @@ struct Args {
   float ks;
   uint64_t* words;  // pair words, kPairWordBytes apart; null: one workgroup per row block
   f32x4* sums;      // [pair][half][wave][lane] partial sums
-  uint32_t epoch;   // nonzero, new for every call
+  uint32_t epoch;   // eager calls: nonzero, new for every call; 0 under stream capture
   uint32_t spin_limit;
 };
 
@@ -347,16 +351,48 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
     if (tid == 0) {
       uint64_t* word = a.words + pair * (kPairWordBytes / 8);
       const uint64_t xcc = xcc_id();
-      const uint64_t val = (uint64_t)a.epoch | ((uint64_t)half << 32) | (xcc << 40);
-      const uint64_t want = (uint64_t)a.epoch | ((uint64_t)(1 - half) << 32) | (xcc << 40);
-      const bool second = __hip_atomic_exchange(word, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
-      bool ok = second;
-      for (uint32_t i = 0; !ok && i < a.spin_limit; ++i) {
-        __builtin_amdgcn_s_sleep(kPairSleep);
-        ok = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
+      bool second, ok;
+      uint64_t seen, from;  // the partner's value, and its XCD id
+      if (a.epoch != 0) {
+        // eager calls: one exchange.  The word: this call's epoch in bits
+        // 0-31, the half in bit 32, the XCD id in bits 40-47.
+        const uint64_t mine = (uint64_t)a.epoch | ((uint64_t)half << 32);
+        const uint64_t want = (uint64_t)a.epoch | ((uint64_t)(1 - half) << 32);
+        auto partner = [&](uint64_t x) { return (x & 0x1ffffffffull) == want && (x >> 40) < 256; };
+        seen = __hip_atomic_exchange(word, mine | (xcc << 40), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        second = partner(seen);
+        ok = second;
+        for (uint32_t i = 0; !ok && i < a.spin_limit; ++i) {
+          __builtin_amdgcn_s_sleep(kPairSleep);
+          seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = partner(seen);
+        }
+        from = seen >> 40;
+      } else {
+        // captured calls (a graph replays its arguments, so no epoch): a
+        // toggle.  The word: kPairMagic in bits 40-63 (anything else, an
+        // epoch word or fresh memory, reads as idle), the XCD id of the
+        // last workgroup to arrive in bits 32-39, bit 0 set while the first
+        // of the pair waits.  Each arrival flips it once, so every call
+        // leaves it idle.
+        seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (;;) {
+          second = (seen >> 40) == kPairMagic && (seen & 1u);
+          const uint64_t next = (kPairMagic << 40) | (xcc << 32) | (second ? 0u : 1u);
+          if (__hip_atomic_compare_exchange_strong(word, &seen, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT))
+            break;
+        }
+        ok = second;
+        for (uint32_t i = 0; !ok && i < a.spin_limit; ++i) {
+          __builtin_amdgcn_s_sleep(kPairSleep);
+          seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = !(seen & 1u);
+        }
+        from = (seen >> 32) & 0xffu;
       }
       bc[0] = second;
-      bc[1] = ok;
+      bc[1] = ok && from == xcc;  // the partner's sums are in this XCD's L2
     }
     __syncthreads();
     writer = bc[0] != 0;
@@ -366,7 +402,9 @@ __global__ __launch_bounds__(64 * kRowWaves, 1) void k_frame1(Args a) {
       // the same bits
       sum += a.sums[(pair * 2 + (1 - half)) * (kRowWaves * 64) + w * 64 + l];
     } else {
-      // no partner on this XCD in time: this workgroup's output columns are NaN
+      // no partner in time (or, on a device that does not deal pairs to
+      // one XCD, none whose sums this L2 holds): NaN, in this workgroup's
+      // output columns and, when it is the second, in the pair's state rows
       sum = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     }
   }
@@ -481,7 +519,7 @@ hipError_t launch_frame1(const uint16_t* q, const uint16_t* k, const uint16_t* v
   a.heads = heads;
   a.S = S;
   a.ks = ks;
-  const bool split = pair_ws && frame1_workspace_bytes(heads) > 0 && epoch != 0;
+  const bool split = pair_ws && frame1_workspace_bytes(heads) > 0;
   a.words = split ? static_cast<uint64_t*>(pair_ws) : nullptr;
   a.sums = split ? reinterpret_cast<f32x4*>(static_cast<char*>(pair_ws) + pair_words_bytes(heads)) : nullptr;
   a.epoch = epoch;

@@ -207,15 +207,17 @@ int gdn_fused_status(const void* workspace, void* stream);
  *                   rows (8 per head) with no reduction between them; a
  *                   block's workgroup then computes the same 16 columns of
  *                   O = Q M'^T.  With at most 16 heads, a workspace of
- *                   gdn_workspace_bytes (the call runs without one), a
- *                   stream that is not being captured, and a device that
- *                   deals workgroups b and b + 8 to one XCD (a one-time
- *                   probe on the null stream), each block's even and odd
- *                   64-token tiles go to two workgroups that swap partial
- *                   sums through the workspace (bounded waits, see
+ *                   gdn_workspace_bytes (the call runs without one) and a
+ *                   device that deals workgroups b and b + 8 to one XCD
+ *                   (a one-time probe on the null stream at the first
+ *                   call; a capture made before any eager call on the
+ *                   device takes the other form), each block's even and
+ *                   odd 64-token tiles go to two workgroups that swap
+ *                   partial sums through the workspace (bounded waits, see
  *                   gdn_set_spin_limit); otherwise one workgroup takes all
  *                   of a block's tiles.  The two forms agree to float32
- *                   rounding; each is deterministic.  Equal to
+ *                   rounding; each is deterministic, captured or not.
+ *                   Equal to
  *                   GDN_PATH_MFMA's result to float32 rounding, not bit for
  *                   bit (gdn_set_single_frame).  While disabled,
  *                   GDN_PATH_MFMA;

@@ -4,8 +4,8 @@ same buffers bit for bit.
 
 Covered: the fused kernel through gdn_frame_fwd_noalloc (the entry point
 meant for capture) and through gdn_frame_fwd, over more than 16 heads (two
-launches of it, each after its flag-reset kernel), the two launches of the
-single-frame kernels, and the overlapped
+launches of it, each after its flag-reset kernel), the single-frame kernel
+in both of its forms, and the overlapped
 three-kernel schedule, whose builds, state passes and outputs fork onto the
 library's own streams and join back.  Each capture follows an eager call of
 the same shape, since the first call on a device queries it (a probe kernel
@@ -111,9 +111,12 @@ def test_frame_fwd_fused_in_a_graph():
     _replay_and_check(g, static, sets[1:], out, st, torch.float32, "frame_fwd fused graph")
 
 
-def test_single_frame_kernels_in_a_graph():
-    """Both launches of the single-frame kernels for 20 heads (two groups)."""
-    w = BASE.with_(T=1, S=880, seed=97)
+@pytest.mark.parametrize("H", [20, 16])
+def test_single_frame_kernels_in_a_graph(H):
+    """The single-frame kernel: 20 heads take one workgroup per 16-row block;
+    16 heads two, which swap partial sums through per-block words that every
+    call (eager or replayed) leaves ready for the next."""
+    w = BASE.with_(H=H, T=1, S=880, seed=97)
     assert F.lib().gdn_path(ctypes.byref(Shape(w.B, w.H, w.T, w.S, w.D)), GDN_BF16) == 3
     sets = _input_sets(w, REPLAYS + 1)
     static = {key: t.clone() for key, t in sets[0].items()}
