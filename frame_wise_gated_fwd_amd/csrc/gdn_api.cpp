@@ -25,6 +25,15 @@ namespace {
 
 constexpr int64_t kMaxFrames = (int64_t{1} << 24) - 1;  // B*H*T: one workgroup per frame
 constexpr int64_t kSegmentFrames = 64;                   // frames per segment, overlapped schedule
+// The backward cuts a sequence into at most 3 segments of at least
+// kSegmentFrames frames.  Its reverse chain waits on a cross-stream hand-off
+// per segment, and fewer, longer segments pay fewer of them while still
+// overlapping the chains with the streaming kernels.  Measured on the 60 s
+// workload (two boxes, segments of F frames, each box against itself):
+// F = 32, 64, 96, 128, 192: 12.69, 12.55, 12.54, 12.38, 12.21 ms; then
+// F = 192, 256, 321, 481, 961 (3 segments at 321, one at 961): 11.99,
+// 11.91, 11.81, 12.01, 14.13 ms.
+constexpr int64_t kBwdMaxSegments = 3;
 constexpr int64_t kFusedMinT = 32;                       // shorter sequences take the three-kernel path
 constexpr int64_t kMapSlots = 3;                         // segments whose maps the MFMA path holds at once
 constexpr size_t kMapFrameBytes = 128 * 128 * 4;         // one packed G, U or M of one frame (D = 128)
@@ -494,7 +503,7 @@ struct BwdBuffers {
   float *G, *U, *M_all, *P, *LB, *partials, *fstate;
 };
 
-// gdn_frame_bwd over ceil(T / F) segments, on the side streams of the
+// gdn_frame_bwd over min(ceil(T / F), kBwdMaxSegments) segments, on the side streams of the
 // overlapped forward schedule.  First the forward is recomputed (G_t, U_t in
 // the packed forms of the forward, every M_t in float32): (K, V) builds on
 // the caller's stream, the state pass (a chain)
@@ -512,7 +521,7 @@ struct BwdBuffers {
 // on the caller's stream.
 hipError_t run_bwd(const Dims& d, const BwdArgs& a, const BwdBuffers& b, hipStream_t s) {
   const int64_t F = segment_frames();
-  const int64_t nseg = (d.T + F - 1) / F;
+  const int64_t nseg = std::min((d.T + F - 1) / F, kBwdMaxSegments);
   const int S = (int)d.S;
   const int64_t H = d.heads, T = d.T;
   auto seg = [&](int64_t i) { return std::make_pair(i * T / nseg, (i + 1) * T / nseg); };

@@ -418,9 +418,10 @@ int gdn_output(const gdn_shape* shape, int in_dtype, int out_dtype, const void* 
  * last chunk first, each given the next chunk's d_state_in as d_state_out
  * and its own forward state_in, gives the one-call result bit for bit).
  * The forward states are recomputed from q, k, v, gamma, beta and state_in.
- * Asynchronous on `stream`; for T > 64 the work runs in 64-frame segments on
- * the same library-owned side streams as gdn_frame_fwd, forked from and
- * joined back to `stream`, and results do not depend on the segmentation.
+ * Asynchronous on `stream`; for T > 64 the work runs in min(ceil(T / 64), 3)
+ * segments of nearly equal length on the same library-owned side streams
+ * as gdn_frame_fwd, forked from and joined back to `stream`, and results do
+ * not depend on the segmentation.
  * Argument errors return before any launch.  workspace: at least
  * gdn_bwd_workspace_bytes(shape, in_dtype) bytes of device memory
  * (5 * B*H*T*D*D*4 bytes for the per-frame maps, plus 64 bytes per frame of

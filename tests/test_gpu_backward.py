@@ -104,7 +104,7 @@ def test_backward_stress_slice():
 
 def test_backward_seq60s_full_size_sampled_heads():
     """The 60 s workload at full size, in the configuration bench.py times
-    (one call over all 16 heads and 961 frames, 16 segments); two heads are
+    (one call over all 16 heads and 961 frames, 3 segments); two heads are
     checked whole against the oracle.  d_out and d_state_out are drawn on the
     device (seeded) and the checked heads' values copied back for the oracle."""
     from synth import SEQ_60S
