@@ -44,9 +44,11 @@ constexpr int build_lds_bytes() { return kPacked ? 65536 : 32768; }
 // lie on or above the diagonal in 16 x 16 blocks are written (G_t is
 // symmetric bit for bit: both entries of a pair are the same products
 // summed in the same order).
+// kWithG = false (float32 output only, Gout null): G_t is not formed at all,
+// half the MFMAs (the backward's P_t = dO_t^T Q_t needs only the second map).
 // All 256 threads of the workgroup must call it.  On return this thread's
 // stores are issued, not necessarily complete.
-template <bool kPacked, int kDepth = 1, bool kUpperG = false>
+template <bool kPacked, int kDepth = 1, bool kUpperG = false, bool kWithG = true>
 __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, const uint16_t* __restrict__ Vf,
                                             int S, u32x4* __restrict__ lds, void* __restrict__ Gout,
                                             float* __restrict__ Uout, float ks) {
@@ -119,7 +121,7 @@ __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, con
         const u32x4 vr = frag[2 + sl][2 * w + jj][l];
 #pragma unroll
         for (int jp = 0; jp < 8; ++jp) {
-          accG[jj][jp] = mfma16x16x32(kr, kf[jp], accG[jj][jp]);
+          if constexpr (kWithG) accG[jj][jp] = mfma16x16x32(kr, kf[jp], accG[jj][jp]);
           accU[jj][jp] = mfma16x16x32(vr, kf[jp], accU[jj][jp]);
         }
       }
@@ -140,7 +142,7 @@ __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, con
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      accG[a][b] *= ks2;
+      if constexpr (kWithG) accG[a][b] *= ks2;
       accU[a][b] *= ks;
     }
 
@@ -189,7 +191,7 @@ __device__ __forceinline__ void build_frame(const uint16_t* __restrict__ Kf, con
         const int row = 32 * g + 8 * i + j;
         f32x4* gp = reinterpret_cast<f32x4*>(static_cast<float*>(Gout) + row * D + 8 * c);
         f32x4* up = reinterpret_cast<f32x4*>(Uout + row * D + 8 * c);
-        if (Gout) {
+        if (kWithG && Gout) {
           gp[0] = (f32x4){accG[jj][0][i], accG[jj][1][i], accG[jj][2][i], accG[jj][3][i]};
           gp[1] = (f32x4){accG[jj][4][i], accG[jj][5][i], accG[jj][6][i], accG[jj][7][i]};
         }

@@ -22,7 +22,7 @@
 namespace gdn {
 namespace {
 
-template <bool kPacked>
+template <bool kPacked, bool kWithG>
 __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, void* __restrict__ Gout,
     float* __restrict__ Uout, int S, int64_t T, int t0, int nt, float ks, int64_t mT, int64_t mt0) {
@@ -33,8 +33,8 @@ __global__ __launch_bounds__(256, 2) void k1_build_bf16_d128(
   const int64_t head = blockIdx.x / nt, t = t0 + blockIdx.x % nt;
   const int64_t f = head * T + t, mf = head * mT + t - mt0;
   const int64_t in_off = f * (int64_t)S * D, mat_off = mf * (int64_t)D * D;
-  build_frame<kPacked>(K + in_off, V + in_off, S, lds, Gout ? static_cast<char*>(Gout) + mat_off * 4 : nullptr,
-                       Uout + mat_off, ks);
+  build_frame<kPacked, 1, false, kWithG>(K + in_off, V + in_off, S, lds,
+                                         Gout ? static_cast<char*>(Gout) + mat_off * 4 : nullptr, Uout + mat_off, ks);
 }
 
 // The same maps for launches too small to fill the GPU (a few frames): the
@@ -76,11 +76,14 @@ hipError_t launch_build_bf16_d128(const uint16_t* k, const uint16_t* v, void* G,
     hipLaunchKernelGGL(k1_build_bf16_d128_split, split, dim3(256), 0, st, k, v, static_cast<char*>(G), U, S, T,
                        (int)t0, nt, frames, ks, ml.T, ml.t0);
   } else if (packed_out)
-    hipLaunchKernelGGL(k1_build_bf16_d128<true>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks, ml.T,
-                       ml.t0);
-  else
-    hipLaunchKernelGGL(k1_build_bf16_d128<false>, grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks, ml.T,
-                       ml.t0);
+    hipLaunchKernelGGL((k1_build_bf16_d128<true, true>), grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks,
+                       ml.T, ml.t0);
+  else if (G)
+    hipLaunchKernelGGL((k1_build_bf16_d128<false, true>), grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks,
+                       ml.T, ml.t0);
+  else  // U_t only (the backward's P_t): G_t is not formed
+    hipLaunchKernelGGL((k1_build_bf16_d128<false, false>), grid, dim3(256), 0, st, k, v, G, U, S, T, (int)t0, nt, ks,
+                       ml.T, ml.t0);
   return hipGetLastError();
 }
 
