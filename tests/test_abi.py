@@ -415,3 +415,24 @@ def test_gated_argument_errors_on_the_host():
     assert gated(gam=P[9], bet=P[9] + 8) == ALIAS                 # gamma and beta overlap
     assert gated(ga=P[5]) == ALIAS                                # out written over a gate input
     assert gated(shape=_shape(B=0), ws=None, wsb_=0) == OK
+
+
+def test_single_frame_workspace_is_optional_but_checked():
+    """A single-frame call (bf16, D = 128, T = 1) needs no workspace: without
+    one, or with one too small or misaligned for the two-workgroup form, the
+    host checks pass and the call goes on to the device (here, with no GPU,
+    to GDN_E_HIP).  A workspace big enough for that form is checked like any
+    other: overlapping an input or output is GDN_E_ALIAS."""
+    L = F.lib()
+    prev = L.gdn_set_single_frame(1)
+    try:
+        s = _shape(1, 16, 1, 880, 128)
+        need = L.gdn_workspace_bytes(ctypes.byref(s), BF16)
+        assert need == _frame_bytes(16, 880)
+        for ws, wsb in ((None, 0), (P[7], need - 1), (P[7] + 8, need), (P[7], need)):
+            assert fwd(s, ws=ws, wsb=wsb) == HIP, (ws, wsb)
+        assert fwd(s, ws=P[1], wsb=need) == ALIAS        # over k
+        assert fwd(s, ws=P[6] - 256, wsb=need) == ALIAS  # over state_out
+        assert fwd(s, ws=P[1], wsb=need - 1) == HIP      # too small to be used: not checked
+    finally:
+        L.gdn_set_single_frame(prev)
