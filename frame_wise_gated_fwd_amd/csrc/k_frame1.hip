@@ -1,7 +1,7 @@
 // The forward of a single frame (T = 1; bf16 inputs, head dim 128), for
 // frame-by-frame (chunk-causal) generation, where every call carries one
-// latent frame (bilibili cv49203711, second key point; the zhichai.net
-// page's Stage 4 rollout at constant memory).
+// latent frame (bilibili cv49203711, second key point; the zhichai.net page's
+// Stage 4 rollout at constant memory).
 //
 // One step of the recurrence (zhichai.net, section 1: decay gate gamma,
 // delta-rule correction beta),
@@ -18,38 +18,36 @@
 // Token halves.  With at most 16 heads (8 x 16 row blocks: half the CUs) a
 // row block is split over a pair of workgroups: half p takes the 64-token
 // tiles t with t % 2 == p, sums its part P_p of P, and the two swap their
-// parts, so that each has P = P_0 + P_1 and writes the output columns of
-// its own tiles.  With more heads, or with no room for the swap in the
-// workspace, one workgroup sums all the tiles and writes all of its
-// columns.  The two forms add the tokens' products in
-// different orders, so they agree to float32 rounding, not bit for bit;
-// each is deterministic.
+// parts, so that each has P = P_0 + P_1 and writes the output columns of its
+// own tiles.  With more heads, or with no room for the swap in the workspace,
+// one workgroup sums all the tiles and writes all of its columns.  The two
+// forms add the tokens' products in different orders, so they agree to
+// float32 rounding, not bit for bit; each is deterministic.
 //
-// The swap.  Head h's workgroups have ids h % 8 + 8 j, which the
-// dispatcher deals to XCD h % 8 (the library uses this form only on a
-// device where a probe has seen that dealing), so the two halves of a pair,
-// 8 ids apart, share that XCD's L2, the point where its CUs' stores meet.
-// Per pair there is one 64-bit word and each half's partial sums.  A half
-// stores its sums and waits for all of its memory operations (its reads of
-// state_in included) before it touches the word; the workgroup that finds
-// its partner already there is the second: it invalidates its L1, reads the
-// partner's sums and alone writes the pair's rows of state_out (both halves
-// have read state_in by then, so state_out may equal state_in).  The other
-// is the first: it polls the word, a bounded number of times, until the
-// second has been there, then reads the second's sums.  An eager call
-// carries a new epoch from the host: each half exchanges the word for
-// (epoch, half, XCD id) in one atomic operation, and a word of an earlier
-// call never passes for this call's partner.  A captured graph replays its
-// arguments, epoch included, so a captured call flips a tagged toggle with
-// a compare-and-swap instead (idle to waiting, waiting to idle; a load and
-// an atomic operation more on the second's path): each arrival flips it
-// once, every call leaves it idle, and an untagged word (an eager call's,
-// or fresh memory) reads as idle.  The halves wait only for
-// each other and an XCD starts its workgroups in id order, so at most the
-// last few pairs started on an XCD can be waiting on a partner while the
-// others finish and make room.  A first half that still gives up (about a
-// second by default) writes NaN to its output columns; the second, when it
-// comes, writes the correct state.
+// The swap.  Head h's workgroups have ids h % 8 + 8 j, which the dispatcher
+// deals to XCD h % 8 (the library uses this form only on a device where a
+// probe has seen that dealing), so the two halves of a pair, 8 ids apart,
+// share that XCD's L2, the point where its CUs' stores meet.  Per pair there
+// is one 64-bit word and each half's partial sums.  A half stores its sums
+// and waits for all of its memory operations (its reads of state_in included)
+// before it touches the word; the workgroup that finds its partner already
+// there is the second: it invalidates its L1, reads the partner's sums and
+// alone writes the pair's rows of state_out (both halves have read state_in
+// by then, so state_out may equal state_in).  The other is the first: it
+// polls the word, a bounded number of times, until the second has been there,
+// then reads the second's sums.  An eager call carries a new epoch from the
+// host: each half exchanges the word for (epoch, half, XCD id) in one atomic
+// operation, and a word of an earlier call never passes for this call's
+// partner.  A captured graph replays its arguments, epoch included, so a
+// captured call flips a tagged toggle with a compare-and-swap instead (idle
+// to waiting, waiting to idle; a load and an atomic operation more on the
+// second's path): each arrival flips it once, every call leaves it idle, and
+// an untagged word (an eager call's, or fresh memory) reads as idle.  The
+// halves wait only for each other and an XCD starts its workgroups in id
+// order, so at most the last few pairs started on an XCD can be waiting on a
+// partner while the others finish and make room.  A first half that still
+// gives up (about a second by default) writes NaN to its output columns; the
+// second, when it comes, writes the correct state.
 //
 // Arithmetic, per workgroup: for a tile, C = M_r K^T (M's 16 rows as a bf16
 // hi/lo pair, about 2^-17 relative; the keys exact in bf16), the residuals
@@ -57,16 +55,17 @@
 // as a bf16 hi/lo pair, on 16x16x32 bf16 MFMA with float32 sums;
 // M'_r = gamma M_r + (beta ks) P; then, over the tiles again,
 // O[:, r] = Q M'_r^T with M'_r as a bf16 hi/lo pair.  The tokens are summed
-// in another order than by the frame-parallel kernels, so results agree
-// with theirs to rounding, not bit for bit; they are deterministic.
+// in another order than by the frame-parallel kernels, so results agree with
+// theirs to rounding, not bit for bit; they are deterministic.
 //
 // Placement.  Head h's workgroups have ids h % 8 + 8 j, which the dispatcher
 // deals to one XCD, so one fetch of the keys and queries from HBM serves all
-// of them through that XCD's L2.  A workgroup takes a whole CU (160 KB of LDS).  Global
-// loads are contiguous (a wave's 16-byte loads cover whole rows) and the
-// MFMA operands are read from LDS: loading a 16-row operand layout straight
-// from memory (each load instruction 16 rows x 64 bytes) moves a
-// workgroup's 128 KB at about a third of the rate of contiguous loads.
+// of them through that XCD's L2.  A workgroup takes a whole CU (160 KB of
+// LDS).  Global loads are contiguous (a wave's 16-byte loads cover whole
+// rows) and the MFMA operands are read from LDS: loading a 16-row operand
+// layout straight from memory (each load instruction 16 rows x 64 bytes)
+// moves a workgroup's 128 KB at about a third of the rate of contiguous
+// loads.
 //
 #include "gdn_common.h"
 #include "gdn_launch.h"
