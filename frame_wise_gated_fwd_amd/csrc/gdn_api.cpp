@@ -156,7 +156,6 @@ bool frame1_path(int in_dtype, const Dims& d) {
   return single_frame_enabled().load() && fast_path(in_dtype, d.D) && d.T == 1;
 }
 
-
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t{255}; }
