@@ -224,12 +224,12 @@ def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
     wsb = max(L.gdn_workspace_bytes(ctypes.byref(Shape(B, H, c["q"].shape[2], S, D)), GDN_BF16) for c in chunks)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
 
-    def call(c, st_in, use_ws=True):
+    def call(c, st_in, use_ws=True, st=None):
         n = c["q"].shape[2]
         shp = Shape(B, H, n, S, D)
         check(L.gdn_frame_fwd(ctypes.byref(shp), GDN_BF16, GDN_F32, P(c["q"]), P(c["k"]), P(c["v"]),
                               P(c["gamma"]), P(c["beta"]), P(st_in), P(out), P(state),
-                              P(ws) if use_ws else None, wsb if use_ws else 0, stream),
+                              P(ws) if use_ws else None, wsb if use_ws else 0, stream if st is None else st),
               "gdn_frame_fwd")
 
     def pass_():
@@ -269,6 +269,34 @@ def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
     e1.record()
     torch.cuda.synchronize()
     one_wg = e0.elapsed_time(e1) / t1_reps * 1e3
+    # the same call captured into a HIP graph, 20 calls in a row carrying the
+    # state (a serving loop captures many steps at once: replaying a graph
+    # of one kernel costs more than launching the kernel), replayed back to
+    # back; the capture follows eager calls on a side stream, as a capture
+    # must.  Per call.
+    per_graph = 20
+    cur = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(one, state, st=cur())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            call(one, state, st=cur())
+    torch.cuda.synchronize()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(t1_reps // per_graph):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    replay = e0.elapsed_time(e1) / (t1_reps // per_graph * per_graph) * 1e3
+    del graph
     iso = []
     for _ in range(50):
         e0.record()
@@ -314,6 +342,7 @@ def streaming_and_t1(x, L, w, stream, reps=5, t1_reps=200):
             "algorithmic_bytes": t1_bytes, "GBps": round(t1_bytes / (back_to_back * 1e-6) / 1e9, 1),
             "hbm_frac": round(t1_bytes / (back_to_back * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "one_workgroup_per_row_block_back_to_back_us": round(one_wg, 2),
+            "graph_of_20_calls_per_call_us": round(replay, 2),
             "three_kernel_back_to_back_us": round(three, 2)}
 
 
